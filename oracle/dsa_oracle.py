@@ -1,0 +1,270 @@
+"""Plain CPU oracle for DSA decode over a packed paged cache.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. It shares no code
+with the HIP library or its Python binding, and it never imports either.
+
+What it computes follows vLLM "Day-0 support for Kimi K3.1 Pro", section
+"Sparse attention in K3.1 Pro" (an indexer scores every earlier token with 32
+light heads, the 2,048 best are kept, and MLA attention runs exactly over only
+those), together with the fixed definitions the method is graded by:
+
+* indexer score   s_t = sum_h w_h * ReLU(q_h . k_t)        (32 heads x 128 dims)
+* selection       the min(k, n) largest s_t, equal scores -> lower token index,
+                  compared in fp32 (the precision the GPU kernel decides in)
+* attention       softmax_t((q . c_t) / sqrt(576)) weighted sum of c_t[:512],
+                  per latent-query head, plus the natural-log LSE.
+
+Every floating-point step runs in float64 from exactly dequantised values
+(e4m3 / e2m1 codes times their fp32 / E8M0 scales). There is no blocking,
+fusion or reordering beyond a chunked matrix product over tokens.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+H_IDX = 32
+D_IDX = 128
+H_Q = 96
+D_LAT = 576
+D_V = 512
+MX_GROUP = 32
+
+# ---------------------------------------------------------------------------
+# Dequantisation tables, written out from the format definitions.
+# ---------------------------------------------------------------------------
+
+def e4m3fn_value(code: int) -> float:
+    """OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+    S.1111.111 is NaN; exponent 0 encodes subnormals m/8 * 2^-6. Max 448.
+    (The cache's FP8 latent and index keys, page 1, KV-cache section.)"""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e8m0_value(code: int) -> float:
+    """E8M0 shared scale of the MX formats: 2^(code - 127); 0xFF is NaN."""
+    if code == 0xFF:
+        return float("nan")
+    return 2.0 ** (code - 127)
+
+
+def e2m1_value(nibble: int) -> float:
+    """E2M1 (FP4): 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent 0 is
+    subnormal m * 0.5. Magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}."""
+    sign = -1.0 if nibble & 0x8 else 1.0
+    e = (nibble >> 1) & 0x3
+    m = nibble & 0x1
+    if e == 0:
+        return sign * m * 0.5
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+E4M3_TABLE = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+E8M0_TABLE = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
+E2M1_TABLE = np.array([e2m1_value(n) for n in range(16)], dtype=np.float64)
+
+
+def _f32_from_bytes(b: np.ndarray) -> np.ndarray:
+    """Little-endian fp32 from a [..., 4] uint8 array."""
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    return b.view("<f4").reshape(b.shape[:-1]).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Page walk over the packed cache (page 1: a block is one contiguous row that
+# holds every DSA layer's latent page and index-key page; the block table plus
+# the slot give the page address of a token).
+# ---------------------------------------------------------------------------
+
+class Layout:
+    """Plain view of the row layout numbers: block_size, index_fmt, row_bytes,
+    lat_off[layer], idx_off[layer]. Accepts any object or dict carrying them."""
+
+    def __init__(self, src):
+        get = (lambda k: src[k]) if isinstance(src, dict) else (lambda k: getattr(src, k))
+        self.block_size = int(get("block_size"))
+        self.index_fmt = str(get("index_fmt"))
+        self.row_bytes = int(get("row_bytes"))
+        self.lat_off = [int(v) for v in get("lat_off")]
+        self.idx_off = [int(v) for v in get("idx_off")]
+
+
+def token_pages(bt_row: np.ndarray, tokens: np.ndarray, block_size: int):
+    """Token t lives in physical block bt_row[t // block_size], slot t % block_size."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    blk = np.asarray(bt_row, dtype=np.int64)[tokens // block_size]
+    slot = tokens % block_size
+    return blk, slot
+
+
+def read_index_keys(pool: np.ndarray, lay: Layout, layer: int, bt_row, tokens) -> np.ndarray:
+    """Dequantised index keys [n, 128] (float64) for the given token positions."""
+    pool = pool.reshape(-1, lay.row_bytes)
+    blk, slot = token_pages(bt_row, tokens, lay.block_size)
+    base = lay.idx_off[layer]
+    bs = lay.block_size
+    if lay.index_fmt == "fp8":
+        codes = pool[blk[:, None], base + slot[:, None] * D_IDX + np.arange(D_IDX)]
+        sc = _f32_from_bytes(pool[blk[:, None], base + bs * D_IDX + slot[:, None] * 4 + np.arange(4)])
+        return E4M3_TABLE[codes] * sc[:, None]
+    if lay.index_fmt == "mxfp4":
+        half = D_IDX // 2
+        packed = pool[blk[:, None], base + slot[:, None] * half + np.arange(half)]
+        e8 = pool[blk[:, None], base + bs * half + slot[:, None] * 4 + np.arange(4)]
+        return mxfp4_decode(packed, e8)
+    raise ValueError(lay.index_fmt)
+
+
+def mxfp4_decode(packed: np.ndarray, e8: np.ndarray) -> np.ndarray:
+    """[..., 64] packed e2m1 (element 2i in the low nibble of byte i) and
+    [..., 4] E8M0 (one per 32 elements) -> float64 [..., 128]."""
+    lo = packed & 0xF
+    hi = packed >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    vals = E2M1_TABLE[nib]
+    scale = np.repeat(E8M0_TABLE[e8], MX_GROUP, axis=-1)
+    return vals * scale
+
+
+def read_latents(pool: np.ndarray, lay: Layout, layer: int, bt_row, tokens) -> np.ndarray:
+    """Dequantised latents c_t [n, 576] (float64): code value times the token's fp32 scale."""
+    pool = pool.reshape(-1, lay.row_bytes)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    if tokens.size == 0:
+        return np.zeros((0, D_LAT))
+    blk, slot = token_pages(bt_row, tokens, lay.block_size)
+    base = lay.lat_off[layer]
+    codes = pool[blk[:, None], base + slot[:, None] * D_LAT + np.arange(D_LAT)]
+    sc = _f32_from_bytes(pool[blk[:, None], base + lay.block_size * D_LAT + slot[:, None] * 4 + np.arange(4)])
+    return E4M3_TABLE[codes] * sc[:, None]
+
+
+def index_query(q_codes: np.ndarray, q_scale: np.ndarray, index_fmt: str) -> np.ndarray:
+    """Dequantised indexer query [32, 128]: FP8 codes times one fp32 scale per head,
+    or MXFP4 codes with one E8M0 per 32 elements."""
+    if index_fmt == "fp8":
+        return E4M3_TABLE[np.asarray(q_codes)] * np.asarray(q_scale, dtype=np.float32).astype(np.float64)[:, None]
+    return mxfp4_decode(np.asarray(q_codes), np.asarray(q_scale))
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64 (exact)."""
+    u = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# The three steps.
+# ---------------------------------------------------------------------------
+
+def indexer_scores(q: np.ndarray, w: np.ndarray, keys: np.ndarray, chunk: int = 65536) -> np.ndarray:
+    """s_t = sum_h w_h * max(0, q_h . k_t), float64 [n]."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    out = np.empty(keys.shape[0], dtype=np.float64)
+    for a in range(0, keys.shape[0], chunk):
+        dots = keys[a:a + chunk] @ q.T                 # [m, 32]
+        out[a:a + chunk] = np.maximum(dots, 0.0) @ w
+    return out
+
+
+def indexer_magnitude(q: np.ndarray, w: np.ndarray, keys: np.ndarray, chunk: int = 65536) -> np.ndarray:
+    """sum_h |w_h| * sum_d |q_hd * k_td|: the size of the terms a score adds up
+    (used only to state rounding tolerances)."""
+    w = np.abs(np.asarray(w, dtype=np.float32).astype(np.float64))
+    out = np.empty(keys.shape[0], dtype=np.float64)
+    for a in range(0, keys.shape[0], chunk):
+        out[a:a + chunk] = (np.abs(keys[a:a + chunk]) @ np.abs(q).T) @ w
+    return out
+
+
+def select_topk(scores32: np.ndarray, k: int) -> np.ndarray:
+    """The min(k, n) largest scores, equal scores ordered by lower token index;
+    returned as ascending token positions (int64)."""
+    s = np.asarray(scores32, dtype=np.float32)
+    n = s.shape[0]
+    if n == 0 or k <= 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((np.arange(n), -s.astype(np.float64)))
+    return np.sort(order[:min(k, n)])
+
+
+def sparse_mla(q_lat: np.ndarray, lat: np.ndarray, sm_scale: float):
+    """Exact attention of every latent-query head over the given latents.
+
+    logits[h, t] = (q_h . c_t) * sm_scale over all 576 dims; p = softmax over t;
+    out[h] = sum_t p[h, t] * c_t[:512]; lse[h] = ln sum_t exp(logits[h, t]).
+    No tokens -> out = 0, lse = -inf.
+    """
+    if lat.shape[0] == 0:
+        return np.zeros((q_lat.shape[0], D_V)), np.full(q_lat.shape[0], -np.inf)
+    logits = (q_lat @ lat.T) * sm_scale                  # [96, m]
+    m = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - m)
+    l = p.sum(axis=1, keepdims=True)
+    out = (p @ lat[:, :D_V]) / l
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# One query row of the decode step, and the byte accounting quoted on the pages.
+# ---------------------------------------------------------------------------
+
+def decode_row(pool, layout, layer, bt_row, ctx, q_codes, q_scale, w, q_lat_bits, k, sm_scale,
+               idx_override=None, want_magnitude=False):
+    """Indexer over tokens [0, ctx), top-k, sparse MLA over the selected tokens.
+
+    ``idx_override`` (token positions) replaces the oracle's own selection in the
+    attention step, so attention can be checked on another implementation's set.
+    Returns dict(scores=float64 [ctx], scores32, idx (ascending, int64), out, lse[, mag]).
+    """
+    lay = layout if isinstance(layout, Layout) else Layout(layout)
+    ctx = max(0, int(ctx))
+    toks = np.arange(ctx)
+    keys = read_index_keys(pool, lay, layer, bt_row, toks)
+    q = index_query(q_codes, q_scale, lay.index_fmt)
+    s = indexer_scores(q, w, keys)
+    s32 = s.astype(np.float32)
+    idx = select_topk(s32, k)
+    use = idx if idx_override is None else np.asarray(idx_override, dtype=np.int64)
+    lat = read_latents(pool, lay, layer, bt_row, use)
+    out, lse = sparse_mla(bf16_to_f64(q_lat_bits), lat, sm_scale)
+    res = dict(scores=s, scores32=s32, idx=idx, out=out, lse=lse)
+    if want_magnitude:
+        res["mag"] = indexer_magnitude(q, w, keys)
+    return res
+
+
+def index_key_bytes(index_fmt: str) -> int:
+    """Per-token index-key bytes: FP8 128 codes + fp32 scale; MXFP4 64 B of e2m1
+    pairs + 4 E8M0 (page 1, KV-cache section; page 1, AMD section)."""
+    return D_IDX + 4 if index_fmt == "fp8" else D_IDX // 2 + D_IDX // MX_GROUP
+
+
+def latent_bytes(latent_fmt: str) -> int:
+    """Per-token latent bytes: 576 one-byte e4m3 codes in FP8; the page quotes
+    352 for NVFP4 (page 1, section on the KV cache serving three kinds of state)."""
+    return {"fp8": D_LAT, "nvfp4": 352}[latent_fmt]
+
+
+def dsa_layer_bytes(ctx: int, k: int, index_fmt: str = "fp8", latent_fmt: str = "fp8") -> int:
+    """Bytes one decode step reads per layer: every index key, then the latent of
+    min(k, ctx) tokens (page 1, "Sparse attention in K3.1 Pro")."""
+    return ctx * index_key_bytes(index_fmt) + min(k, ctx) * latent_bytes(latent_fmt)
+
+
+def dense_mla_layer_bytes(ctx: int, latent_fmt: str = "fp8") -> int:
+    return ctx * latent_bytes(latent_fmt)
+
+
+def kv_bytes_per_token(layers: int, latent_fmt: str, index_fmt) -> int:
+    """Per-GPU per-token cache bytes over ``layers`` DSA layers (TP replicates both caches)."""
+    return layers * (latent_bytes(latent_fmt) + (index_key_bytes(index_fmt) if index_fmt else 0))

@@ -1,0 +1,322 @@
+"""Pins for the CPU oracle, against facts that do not come from the oracle itself:
+library conversions, closed forms, brute force on tiny inputs, invariants of
+the definitions, and the byte figures the pages print (tests/golden)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+# ------------------------------------------------------------------ dequant tables
+def test_e4m3_table_matches_torch_exhaustive():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(ref) & np.isnan(O.E4M3_TABLE)
+    assert np.array_equal(np.isnan(ref), np.isnan(O.E4M3_TABLE))
+    assert np.all((ref == O.E4M3_TABLE) | both_nan)
+    assert O.E4M3_TABLE[0x7E] == 448.0 and O.E4M3_TABLE[0x01] == 2.0 ** -9
+
+
+def test_e8m0_table_matches_torch_exhaustive():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ref), np.isnan(O.E8M0_TABLE))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], O.E8M0_TABLE[ok])
+    assert O.E8M0_TABLE[127] == 1.0
+
+
+def test_e2m1_table_matches_spec_listing():
+    # OCP MX v1.0 FP4 (E2M1) value listing, codes 0..15.
+    spec = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    assert list(O.E2M1_TABLE) == spec
+
+
+def test_mxfp4_decode_nibble_order_and_group_scale():
+    packed = np.zeros((1, 64), np.uint8)
+    packed[0, 0] = 0x2 | (0x7 << 4)       # element 0 = 1.0 (low nibble), element 1 = 6.0
+    packed[0, 16] = 0xB                    # element 32 = -1.5
+    e8 = np.array([[127, 129, 0, 254]], np.uint8)
+    v = O.mxfp4_decode(packed, e8)[0]
+    assert v[0] == 1.0 and v[1] == 6.0
+    assert v[32] == -1.5 * 4.0
+    assert np.count_nonzero(v) == 3
+
+
+# ------------------------------------------------------------------ page walk
+def _struct_pool(bs, n_blocks, layers, fmt):
+    """A pool built through numpy structured dtypes (a different route from the
+    oracle's offset arithmetic): per layer a latent page {codes[bs][576], scales[bs]}
+    followed by an index page."""
+    fields = []
+    for l in range(layers):
+        fields.append((f"lat{l}", [("c", "u1", (bs, 576)), ("s", "<f4", (bs,))]))
+        if fmt == "fp8":
+            fields.append((f"idx{l}", [("c", "u1", (bs, 128)), ("s", "<f4", (bs,))]))
+        else:
+            fields.append((f"idx{l}", [("c", "u1", (bs, 64)), ("e", "u1", (bs, 4))]))
+    dt = np.dtype(fields)
+    rows = np.zeros(n_blocks, dtype=dt)
+    lat_off = [dt.fields[f"lat{l}"][1] for l in range(layers)]
+    idx_off = [dt.fields[f"idx{l}"][1] for l in range(layers)]
+    lay = dict(block_size=bs, index_fmt=fmt, row_bytes=dt.itemsize, lat_off=lat_off, idx_off=idx_off)
+    return rows, lay
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_page_walk_against_structured_pool(fmt):
+    bs, nb, L = 16, 7, 2
+    rows, lay = _struct_pool(bs, nb, L, fmt)
+    bt = np.array([5, 2, 6, 0, 3], np.int32)          # logical block j -> physical row
+    n_tok = 70
+    code = rng.integers(0, 0x7E, size=(L, n_tok, 576), dtype=np.uint8)     # no NaN codes
+    scale = rng.uniform(0.5, 2.0, size=(L, n_tok)).astype(np.float32)
+    kcode = rng.integers(0, 0x7E, size=(L, n_tok, 128), dtype=np.uint8)
+    kscale = rng.uniform(0.5, 2.0, size=(L, n_tok)).astype(np.float32)
+    kpack = rng.integers(0, 256, size=(L, n_tok, 64), dtype=np.uint8)
+    ke8 = rng.integers(120, 135, size=(L, n_tok, 4), dtype=np.uint8)
+    for l in range(L):
+        for t in range(n_tok):
+            r, s = bt[t // bs], t % bs
+            rows[r][f"lat{l}"]["c"][s] = code[l, t]
+            rows[r][f"lat{l}"]["s"][s] = scale[l, t]
+            if fmt == "fp8":
+                rows[r][f"idx{l}"]["c"][s] = kcode[l, t]
+                rows[r][f"idx{l}"]["s"][s] = kscale[l, t]
+            else:
+                rows[r][f"idx{l}"]["c"][s] = kpack[l, t]
+                rows[r][f"idx{l}"]["e"][s] = ke8[l, t]
+    pool = rows.view(np.uint8).reshape(nb, -1)
+    layout = O.Layout(lay)
+    toks = np.arange(n_tok)
+    for l in range(L):
+        lat = O.read_latents(pool, layout, l, bt, toks)
+        ref = torch.from_numpy(code[l]).view(torch.float8_e4m3fn).double().numpy() * scale[l, :, None].astype(np.float64)
+        assert np.array_equal(lat, ref)
+        keys = O.read_index_keys(pool, layout, l, bt, toks)
+        if fmt == "fp8":
+            refk = torch.from_numpy(kcode[l]).view(torch.float8_e4m3fn).double().numpy() * kscale[l, :, None].astype(np.float64)
+        else:
+            lo, hi = kpack[l] & 15, kpack[l] >> 4
+            nib = np.empty((n_tok, 128), np.uint8)
+            nib[:, 0::2], nib[:, 1::2] = lo, hi
+            spec = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+            mag = spec[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+            refk = mag * np.repeat(2.0 ** (ke8[l].astype(np.float64) - 127), 32, axis=1)
+        assert np.array_equal(keys, refk)
+
+
+def test_decode_row_paging_invariance():
+    from synth import make_case
+    c = make_case([700], block_size=16, seed=3)
+    pool = c.pool.numpy()
+    bt = c.block_table.numpy()[0]
+    nb = pool.shape[0]
+    perm = np.random.default_rng(1).permutation(nb)
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool                                   # physical row i moves to perm[i]
+    bt2 = perm[bt[bt >= 0]]
+    args = (c.q_idx[0, 0].numpy(), c.q_idx_scale[0, 0].numpy(), c.w[0, 0].numpy(),
+            c.q_lat[0, 0].view(torch.int16).numpy().view(np.uint16), 64, c.sm_scale)
+    a = O.decode_row(pool, c.layout, 0, bt, 700, *args)
+    b = O.decode_row(pool2, c.layout, 0, bt2, 700, *args)
+    assert np.array_equal(a["scores"], b["scores"])
+    assert np.array_equal(a["idx"], b["idx"])
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+
+
+def test_generated_cache_statistics():
+    """The generator draws N(0,1) keys and latents: the dequantised cache read
+    back through the page walk must have mean ~0, variance ~1, and each token's
+    largest code is exactly +-448 (scale = amax / 448)."""
+    from synth import make_case
+    c = make_case([4096], block_size=64, num_layers=2, seed=5)
+    pool = c.pool.numpy()
+    bt = c.block_table.numpy()[0]
+    lay = O.Layout(c.layout)
+    for l in range(2):
+        k = O.read_index_keys(pool, lay, l, bt, np.arange(4096))
+        v = O.read_latents(pool, lay, l, bt, np.arange(4096))
+        for x in (k, v):
+            assert abs(x.mean()) < 0.01 and abs(x.var() - 1.0) < 0.02
+        base = lay.idx_off[l]
+        codes = pool[:, base:base + 64 * 128].reshape(-1, 128)
+        assert np.all(np.abs(O.E4M3_TABLE[codes]).max(axis=1) == 448.0)
+    k0 = O.read_index_keys(pool, lay, 0, bt, np.arange(64))
+    k1 = O.read_index_keys(pool, lay, 1, bt, np.arange(64))
+    assert not np.array_equal(k0, k1)
+
+
+# ------------------------------------------------------------------ scores
+def _brute_scores(q, w, keys):
+    out = []
+    for t in range(keys.shape[0]):
+        s = 0.0
+        for h in range(q.shape[0]):
+            d = 0.0
+            for j in range(q.shape[1]):
+                d += q[h, j] * keys[t, j]
+            s += float(np.float32(w[h])) * (d if d > 0 else 0.0)
+        out.append(s)
+    return np.array(out)
+
+
+def test_scores_brute_force_tiny():
+    q = rng.standard_normal((32, 128))
+    w = (rng.standard_normal(32) / math.sqrt(32)).astype(np.float32)
+    keys = rng.standard_normal((12, 128))
+    got = O.indexer_scores(q, w, keys)
+    ref = _brute_scores(q, w, keys)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_scores_closed_forms():
+    keys = rng.standard_normal((50, 128))
+    d = rng.integers(0, 128, size=32)
+    q = np.zeros((32, 128))
+    q[np.arange(32), d] = 1.0
+    w = np.ones(32, np.float32)
+    assert np.allclose(O.indexer_scores(q, w, keys), np.maximum(keys[:, d], 0).sum(axis=1), rtol=0, atol=1e-12)
+    # ReLU before the weights: negative dots contribute nothing, whatever the sign of w
+    wneg = -np.abs(rng.standard_normal(32)).astype(np.float32)
+    assert np.all(O.indexer_scores(-np.abs(q), wneg, np.abs(keys)) == 0.0)
+    assert np.all(O.indexer_scores(q, w, np.zeros((5, 128))) == 0.0)
+    # one live head: s = w_h * (q_h . k)
+    q1 = np.zeros((32, 128)); q1[3] = rng.standard_normal(128)
+    w1 = np.zeros(32, np.float32); w1[3] = 2.5
+    dots = keys @ q1[3]
+    assert np.allclose(O.indexer_scores(q1, w1, keys), 2.5 * np.maximum(dots, 0), atol=1e-12)
+
+
+def test_mxfp4_query_and_score_brute_force():
+    packed = rng.integers(0, 256, size=(32, 64), dtype=np.uint8)
+    e8 = rng.integers(124, 131, size=(32, 4), dtype=np.uint8)
+    q = O.index_query(packed, e8, "mxfp4")
+    kp = rng.integers(0, 256, size=(9, 64), dtype=np.uint8)
+    ke = rng.integers(124, 131, size=(9, 4), dtype=np.uint8)
+    keys = O.mxfp4_decode(kp, ke)
+    w = rng.standard_normal(32).astype(np.float32)
+    assert np.allclose(O.indexer_scores(q, w, keys), _brute_scores(q, w, keys), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ selection
+def _brute_select(s, k):
+    """t is kept iff fewer than k tokens beat it (higher score, or equal score
+    and lower index)."""
+    n = len(s)
+    keep = []
+    for t in range(n):
+        beat = sum(1 for u in range(n) if s[u] > s[t] or (s[u] == s[t] and u < t))
+        if beat < k:
+            keep.append(t)
+    return np.array(keep, dtype=np.int64)
+
+
+@pytest.mark.parametrize("n,k", [(10, 3), (12, 12), (9, 20), (11, 1)])
+def test_select_brute_force(n, k):
+    for trial in range(20):
+        s = rng.integers(-3, 4, size=n).astype(np.float32)   # many ties
+        assert np.array_equal(O.select_topk(s, k), _brute_select(s, k))
+
+
+def test_select_matches_stable_argsort():
+    s = rng.standard_normal(5000).astype(np.float32)
+    s[::7] = s[3]                                            # plant equal scores
+    ref = np.sort(np.argsort(-s, kind="stable")[:2048])
+    assert np.array_equal(O.select_topk(s, 2048), ref)
+
+
+def test_select_constant_and_signed_zero():
+    assert np.array_equal(O.select_topk(np.zeros(5000, np.float32), 2048), np.arange(2048))
+    s = np.zeros(10, np.float32); s[::2] = -0.0
+    assert np.array_equal(O.select_topk(s, 4), np.arange(4))
+    assert O.select_topk(np.zeros(0, np.float32), 2048).size == 0
+
+
+# ------------------------------------------------------------------ attention
+def _sdpa_f64(q, lat, scale):
+    qt = torch.from_numpy(q)[None, :, None, :]                 # [1, 96, 1, 576]
+    kt = torch.from_numpy(lat)[None, None].expand(1, q.shape[0], -1, -1)
+    vt = torch.from_numpy(np.ascontiguousarray(lat[:, :512]))[None, None].expand(1, q.shape[0], -1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, :, 0].numpy()
+
+
+def test_attention_matches_sdpa():
+    q = rng.standard_normal((96, 576))
+    lat = rng.standard_normal((300, 576)) * 0.5
+    out, lse = O.sparse_mla(q, lat, 1 / 24)
+    assert np.allclose(out, _sdpa_f64(q, lat, 1 / 24), rtol=1e-10, atol=1e-12)
+    from scipy.special import logsumexp
+    assert np.allclose(lse, logsumexp((q @ lat.T) / 24, axis=1), rtol=1e-12)
+
+
+def test_attention_invariants():
+    q = rng.standard_normal((96, 576))
+    lat = rng.standard_normal((257, 576))
+    out, lse = O.sparse_mla(q, lat, 1 / 24)
+    logits = (q @ lat.T) / 24
+    assert np.allclose(np.exp(logits - lse[:, None]).sum(axis=1), 1.0, atol=1e-12)
+    perm = rng.permutation(257)
+    out2, lse2 = O.sparse_mla(q, lat[perm], 1 / 24)
+    assert np.allclose(out, out2, atol=1e-12) and np.allclose(lse, lse2, atol=1e-12)
+    one, l1 = O.sparse_mla(q, lat[5:6], 1 / 24)
+    assert np.array_equal(one, np.broadcast_to(lat[5, :512], (96, 512)))
+    assert np.allclose(l1, logits[:, 5])
+    same = np.repeat(lat[7:8], 40, axis=0)
+    o3, _ = O.sparse_mla(q, same, 1 / 24)
+    assert np.allclose(o3, lat[7, :512], atol=1e-12)
+    oe, le = O.sparse_mla(q, np.zeros((0, 576)), 1 / 24)
+    assert np.all(oe == 0) and np.all(np.isneginf(le))
+
+
+def test_decode_row_short_context_is_dense_mla():
+    from synth import make_case
+    c = make_case([1000], block_size=64, seed=9)
+    pool = c.pool.numpy(); bt = c.block_table.numpy()[0]
+    ql = c.q_lat[0, 0].view(torch.int16).numpy().view(np.uint16)
+    r = O.decode_row(pool, c.layout, 0, bt, 1000, c.q_idx[0, 0].numpy(), c.q_idx_scale[0, 0].numpy(),
+                     c.w[0, 0].numpy(), ql, 2048, c.sm_scale)
+    assert np.array_equal(r["idx"], np.arange(1000))
+    lat = O.read_latents(pool, O.Layout(c.layout), 0, bt, np.arange(1000))
+    ref = _sdpa_f64(O.bf16_to_f64(ql), lat, c.sm_scale)
+    assert np.allclose(r["out"], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_planted_tokens_dominate_selection():
+    """Keys shifted by +3 sigma along every head (sign of w) must outrank the rest."""
+    from synth import make_case
+    c = make_case([20000], block_size=64, seed=4, plant=256)
+    pool = c.pool.numpy(); bt = c.block_table.numpy()[0]
+    r = O.decode_row(pool, c.layout, 0, bt, 20000, c.q_idx[0, 0].numpy(), c.q_idx_scale[0, 0].numpy(),
+                     c.w[0, 0].numpy(), c.q_lat[0, 0].view(torch.int16).numpy().view(np.uint16), 256, c.sm_scale)
+    planted = set(c.planted[(0, 0)])
+    assert len(planted & set(r["idx"].tolist())) >= 0.95 * 256
+
+
+# ------------------------------------------------------------------ byte accounting (pages)
+def test_byte_accounting_golden():
+    g = json.load(open(os.path.join(GOLDEN, "page_byte_accounting.json")))
+    assert O.latent_bytes("fp8") == g["fp8_latent_bytes_per_token"]["value"]
+    assert O.latent_bytes("nvfp4") == g["nvfp4_latent_bytes_per_token"]["value"]
+    assert O.index_key_bytes("fp8") == g["fp8_index_key_bytes_per_token"]["value"]
+    assert O.index_key_bytes("mxfp4") == g["mxfp4_index_key_bytes_per_token"]["value"]
+    red = 100.0 * (1 - O.index_key_bytes("mxfp4") / O.index_key_bytes("fp8"))
+    e = g["mxfp4_index_storage_reduction_pct"]
+    assert abs(red - e["value"]) <= e["tol"]
+    e = g["dsa_over_dense_mla_bytes_long_context_pct"]
+    frac = 100.0 * O.dsa_layer_bytes(e["ctx"], e["k"]) / O.dense_mla_layer_bytes(e["ctx"])
+    assert abs(frac - e["value"]) <= e["tol"]
+    for key in ("kv_bytes_per_token_24_layers_k3_fp8", "kv_bytes_per_token_24_layers_fp8_fp8",
+                "kv_bytes_per_token_24_layers_nvfp4_mxfp4"):
+        e = g[key]
+        assert O.kv_bytes_per_token(e["layers"], e["latent"], e["index"]) == e["value"], key
+    assert (O.H_IDX, O.D_IDX, O.H_Q) == (g["indexer_heads"]["value"], g["indexer_head_dim"]["value"],
+                                          g["attention_heads"]["value"])
