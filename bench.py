@@ -1,0 +1,222 @@
+"""Benchmark: DSA decode layer-steps per second and achieved HBM bandwidth at 256K context.
+
+One step = one dsa_decode_step call (indexer -> exact top-2048 -> sparse MLA ->
+split merge) for a decode batch of one query row with a 262,144-token context,
+on one DSA layer. Steps rotate over 24 independent layers of one packed cache
+(186.6 MB of cache per layer, 4.48 GB in all) so that the working set is far
+larger than the GPU's 256 MB last-level cache. Inputs are seeded synthetic data
+already resident in HBM when timing starts.
+
+Prints one JSON line. `roofline` is for the dominant kernel (the indexer): its
+algorithmic bytes per launch divided by its average launch duration, timed with
+HIP events around each launch on the stream it runs on. `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload (rank 0, one GPU only).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode layer-steps/sec + achieved HBM GB/s (% of peak) at 256K ctx"
+PEAK_HBM_GBPS = 8000.0
+CTX = 262144
+LAYERS = 24
+K = 2048
+BS = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+INDEXER_SRC = os.path.join(ROOT, "sparse_attention_decode_paged_amd", "csrc", "indexer.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--ctx", type=int, default=CTX)
+    p.add_argument("--layers", type=int, default=LAYERS)
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-layers", type=int, default=4, help="layer-steps the CPU oracle runs for cpu_baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a 1 GiB device copy (for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    return p.parse_args()
+
+
+def src_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_src):
+    """HBM bytes per launch from committed counter summaries, if taken on this source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get("indexer_fp8")
+    if not e or e.get("source_sha") != src_sha(kernel_src):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, layers, k):
+    """Time the CPU oracle on `layers` full layer-steps of the same workload."""
+    import numpy as np
+    import torch
+    from oracle import dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    lay = case.layout
+    bt = case.block_table.cpu().numpy()
+    q_idx = case.q_idx.cpu().numpy()
+    q_sc = case.q_idx_scale.cpu().numpy()
+    w = case.w.cpu().numpy()
+    q_lat = case.q_lat.cpu().view(torch.int16).numpy().view(np.uint16)
+    R = case.num_rows
+    ctxs = case.row_ctx.cpu().numpy()
+    t_total = 0.0
+    n = 0
+    for l in range(layers):
+        # only this layer's pages travel to the host: the row bytes [lat_off, idx_off + page)
+        lo = lay.lat_off[l]
+        hi = lay.idx_off[l] + lay.index_page_bytes
+        pool = case.pool[:, lo:hi].cpu().numpy()
+        sub = dict(block_size=lay.block_size, index_fmt=lay.index_fmt, row_bytes=hi - lo,
+                   lat_off=[0], idx_off=[lay.idx_off[l] - lo])
+        t0 = time.perf_counter()
+        for r in range(R):
+            O.decode_row(pool, sub, 0, bt[r], int(ctxs[r]), q_idx[l, r], q_sc[l, r], w[l, r], q_lat[l, r], k,
+                         case.sm_scale)
+        t_total += time.perf_counter() - t0
+        n += 1
+    return dict(value=n / t_total, unit="layer-steps/s", cores=int(threads), kind="oracle",
+                sample=f"{n} of the {case.layout.num_layers} layers, {R} row(s) x {int(ctxs.max())} tokens each, "
+                       f"full indexer + top-{k} + sparse MLA per layer (float64 numpy, BLAS threads={threads})")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (the path is single-GPU, "
+              f"multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_attention_decode_paged_amd as dsa
+    from sparse_attention_decode_paged_amd import accounting as A
+    from synth import make_case
+
+    dev = torch.device("cuda:0")
+    dsa.load_library()
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 5}))
+        return
+
+    t0 = time.time()
+    case = make_case([a.ctx] * a.batch, block_size=BS, num_layers=a.layers, seed=a.seed, device=dev, k=K,
+                     name="decode_b%d_ctx%d_x%dlayers" % (a.batch, a.ctx, a.layers))
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    R, max_ctx = case.num_rows, case.max_ctx
+    ws = torch.empty(dsa.dsa_workspace_bytes(dsa.DSA_OP_DECODE_STEP, R, max_ctx, K), dtype=torch.uint8, device=dev)
+    idx = torch.empty((R, K), dtype=torch.int32, device=dev)
+    out = torch.empty((R, 96, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, 96), dtype=torch.float32, device=dev)
+
+    def step(i):
+        l = i % a.layers
+        dsa.dsa_decode_step(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l], case.q_lat[l],
+                            case.block_table, case.row_seq, case.row_ctx, max_ctx, K, case.sm_scale,
+                            idx=idx, out=out, lse=lse, workspace=ws)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+
+    # dominant kernel: the indexer alone, one event pair per launch, same rotation
+    scores = torch.empty((R, max_ctx), dtype=torch.float32, device=dev)
+    n_ix = min(a.steps, 500)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ix)]
+    for i in range(20):
+        l = i % a.layers
+        dsa.dsa_indexer_score(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l],
+                              case.block_table, case.row_seq, case.row_ctx, max_ctx, scores=scores)
+    torch.cuda.synchronize()
+    for i in range(n_ix):
+        l = i % a.layers
+        evs[i][0].record(stream)
+        dsa.dsa_indexer_score(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l],
+                              case.block_table, case.row_seq, case.row_ctx, max_ctx, scores=scores)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ix_us = 1000.0 * sum(s.elapsed_time(e) for s, e in evs) / n_ix
+
+    ctxs = [int(c) for c in case.row_ctx.tolist()]
+    step_bytes = A.layer_step_bytes(ctxs, K)
+    ix_bytes = sum(A.indexer_bytes(c) for c in ctxs)
+    ix_gbps = ix_bytes / (ix_us * 1e-6) / 1e9
+    step_gbps = step_bytes / (ms * 1e-3) / 1e9
+    traffic = traffic_for(INDEXER_SRC)
+
+    res = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms, 1),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"DSA decode, batch {R}, context {a.ctx} tokens, top-{K}, block size {BS}, FP8 index keys "
+                        f"(132 B/token) and FP8 latents (576 B + fp32 scale), {a.layers} independent layers rotated",
+            "batch": R, "ctx": a.ctx, "k": K, "block_size": BS, "layers_rotated": a.layers, "index_fmt": "fp8",
+        },
+        "step_hbm_gbps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {
+            "kernel": "indexer_fp8_kernel",
+            "bound": "hbm",
+            "achieved": round(ix_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(ix_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ix_bytes,
+            "avg_launch_us": round(ix_us, 3),
+        },
+        "gen_seconds": round(gen_s, 1),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, min(a.cpu_layers, a.layers), K)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * dsa.h - C ABI of a DeepSeek-style sparse attention (DSA) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (vLLM "Day-0 support for Kimi K3.1 Pro", section "Sparse attention
+ * in K3.1 Pro"): a small indexer scores every earlier token of a query with 32
+ * light heads, the 2,048 best tokens are kept, and MLA attention then runs
+ * exactly, but over those tokens only. All cache reads go through a block table
+ * into a packed per-block cache row (same page, section on the KV cache that
+ * serves three kinds of state: one contiguous row per block holds every DSA
+ * layer's latent page and index-key page; block and slot are turned into page
+ * addresses before each step).
+ *
+ * Definitions used by every entry point (R query rows, layer l):
+ *   score[r][t] = sum_{h<32} w[r][h] * ReLU(q_h . k_t),  t in [0, ctx[r])
+ *   idx[r]      = the min(k, ctx[r]) tokens with the largest fp32 score, equal
+ *                 scores ordered by lower token index; written in ascending token
+ *                 order, the rest of the k slots set to -1
+ *   out[r][h]   = sum_t softmax_t(sm_scale * q_lat[r][h] . c_t) * c_t[0:512]
+ *                 over t in idx[r] (c_t = latent scale * e4m3 codes, 576 wide)
+ *   lse[r][h]   = natural log of sum_t exp(sm_scale * q_lat[r][h] . c_t)
+ *
+ * Memory: every pointer argument except `cache` itself is a DEVICE pointer,
+ * except where marked (host). The caller owns every buffer. The library never
+ * allocates, frees or synchronises; all work is enqueued on `stream` (a
+ * hipStream_t; NULL = the default stream). Calls are stateless and may be made
+ * from several host threads on different streams with different workspaces.
+ *
+ * Errors: a non-zero dsa_status is returned before anything is enqueued when an
+ * argument is invalid; dsa_last_error_detail() then holds a message for the
+ * calling thread. DSA_ERR_HIP is returned when a launch fails. Data-dependent
+ * problems found on the device never fault: a row's ctx above the block-table
+ * capacity or max_ctx is clamped, ctx <= 0 gives an empty row (idx all -1, out 0,
+ * lse -inf), and a block id outside [0, num_blocks) is clamped into the pool
+ * (that token's values are then unspecified).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+#define DSA_H_IDX 32      /* indexer heads */
+#define DSA_D_IDX 128     /* indexer head dim */
+#define DSA_H_Q 96        /* latent-query heads */
+#define DSA_D_LAT 576     /* latent width (attention keys) */
+#define DSA_D_V 512       /* value width (first 512 latent dims) */
+#define DSA_MAX_K 2048    /* largest supported top-k */
+#define DSA_MAX_LAYERS 64
+
+typedef int32_t dsa_status;
+#define DSA_OK 0
+#define DSA_ERR_NULL 1          /* a required pointer is NULL */
+#define DSA_ERR_ARG 2           /* a size / count / index is out of range */
+#define DSA_ERR_LAYOUT 3        /* cache descriptor is inconsistent */
+#define DSA_ERR_WORKSPACE 4     /* workspace smaller than dsa_workspace_bytes() */
+#define DSA_ERR_ALIGN 5         /* a pointer or offset is not 16-byte aligned */
+#define DSA_ERR_HIP 6           /* a HIP launch failed */
+#define DSA_ERR_UNSUPPORTED 7   /* format or shape not supported */
+
+/* Index-key page formats (page 1, KV-cache section: FP8 keys are 132 B/token,
+ * MXFP4 keys 68 B/token). */
+#define DSA_INDEX_FP8 0    /* 128 e4m3 codes + fp32 scale per token */
+#define DSA_INDEX_MXFP4 1  /* 64 B packed e2m1 (element 2i = low nibble) + 4 E8M0 per token */
+
+/*
+ * Packed cache descriptor (host struct; `pool` is a device pointer).
+ * Block row b starts at pool + b * row_bytes. Inside a row, layer l holds
+ *   latent page at lat_off[l]: block_size * 576 e4m3 codes (slot s at s*576),
+ *                              then block_size fp32 scales;
+ *   index page  at idx_off[l]: FP8   block_size * 128 e4m3 codes, then block_size fp32 scales;
+ *                              MXFP4 block_size * 64 packed bytes, then block_size * 4 E8M0.
+ * Token t of a sequence lives in block block_table[seq][t / block_size], slot
+ * t % block_size. block_size must be a power of two; pool, row_bytes and every
+ * offset must be multiples of 16.
+ */
+typedef struct dsa_cache_desc {
+  void* pool;
+  int64_t row_bytes;
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t num_layers;
+  int32_t index_fmt;
+  int32_t reserved;
+  int64_t lat_off[DSA_MAX_LAYERS];
+  int64_t idx_off[DSA_MAX_LAYERS];
+} dsa_cache_desc;
+
+/* Operation ids for dsa_workspace_bytes. */
+#define DSA_OP_TOPK 1
+#define DSA_OP_SPARSE_MLA 2
+#define DSA_OP_DECODE_STEP 3
+
+int32_t dsa_abi_version(void);
+const char* dsa_status_string(dsa_status status);
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* dsa_last_error_detail(void);
+
+/* Bytes of device workspace an operation needs for R rows, max_ctx tokens and
+ * top-k k. 0 for an unknown op. The workspace needs no initial contents. */
+size_t dsa_workspace_bytes(int32_t op, int32_t R, int32_t max_ctx, int32_t k);
+/* Row stride (floats) of the score array a decode step keeps at the start of
+ * its workspace: scores of row r, token t are at ((float*)workspace)[r*ld + t]. */
+int64_t dsa_decode_scores_ld(int32_t max_ctx);
+
+/*
+ * Indexer (page 1, "Sparse attention in K3.1 Pro": 32 light heads score every
+ * earlier token; page 3, model table: 32 heads x 128 dims, FP8 keys; page 1,
+ * AMD section: MXFP4 keys scored with native FP4 matrix instructions and fp32
+ * accumulation, then a weighted reduction across heads).
+ *   q_idx        FP8:   R x 32 x 128 e4m3 codes;   MXFP4: R x 32 x 64 packed e2m1
+ *   q_idx_scale  FP8:   R x 32 fp32 (one positive scale per head);
+ *                MXFP4: R x 32 x 4 E8M0 bytes (one per 32 elements)
+ *   w            R x 32 fp32 head weights (any sign)
+ *   block_table  int32 [num_seqs][bt_stride]; row_seq[r] selects the row of query r
+ *   row_ctx      int32 [R]: query r scores tokens [0, row_ctx[r])
+ *   max_ctx      host bound: row_ctx[r] <= max_ctx <= bt_stride * block_size
+ *   scores       fp32 [R][ld_scores], ld_scores >= max_ctx; entries t >= ctx[r]
+ *                are left untouched.
+ * Key and query scales must be positive (the kernel factors them out of ReLU).
+ */
+dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer,
+                             const void* q_idx, const void* q_idx_scale, const float* w,
+                             const int32_t* block_table, int32_t bt_stride,
+                             const int32_t* row_seq, const int32_t* row_ctx,
+                             int32_t R, int32_t max_ctx,
+                             float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * Exact top-k (page 1, fused decode path: an exact top-k selection emits the KV
+ * rows attention reads; page 1, zero-mismatch RL: batch-invariant top-k).
+ * Selection is per row, exact in fp32, ties -> lower token index, -0.0 == +0.0.
+ *   scores  fp32 [R][ld_scores]; row_ctx as above; k in [1, 2048]
+ *   idx     int32 [R][k] output, ascending tokens then -1 padding.
+ *   workspace >= dsa_workspace_bytes(DSA_OP_TOPK, R, max_ctx, k)
+ */
+dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_ctx,
+                    int32_t R, int32_t max_ctx, int32_t k, int32_t* idx,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse MLA over the selected tokens (page 1, "Sparse attention in K3.1 Pro":
+ * MLA runs exactly over the 2,048 kept tokens; page 1 AMD section: the selected
+ * tokens are read directly from the FP8 cache; page 3 model table: NoPE).
+ *   q_lat   bf16 bit patterns, R x 96 x 576 (absorbed query in latent space)
+ *   idx     int32 [R][k]; entries < 0 are skipped, others must be < the row's
+ *           block-table capacity
+ *   out     fp32 [R][96][512]; lse fp32 [R][96] (may be NULL)
+ *   workspace >= dsa_workspace_bytes(DSA_OP_SPARSE_MLA, R, 0, k)
+ */
+dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer,
+                          const uint16_t* q_lat, const int32_t* block_table, int32_t bt_stride,
+                          const int32_t* row_seq, const int32_t* idx, int32_t R, int32_t k,
+                          float sm_scale, float* out, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The whole decode step for one layer: indexer -> exact top-k -> sparse MLA ->
+ * split merge, enqueued back to back on one stream (page 1, fused DSA decode
+ * path: a scorer and an exact top-k in two kernels, then sparse attention).
+ * Arguments as in the three calls above. Scores stay in the workspace (see
+ * dsa_decode_scores_ld); idx [R][k], out [R][96][512] and lse [R][96] (nullable)
+ * are written. Rows may share a sequence (prefill-append: row r of an append of
+ * T tokens on a P-token prefix uses row_ctx[r] = P + r + 1).
+ *   workspace >= dsa_workspace_bytes(DSA_OP_DECODE_STEP, R, max_ctx, k)
+ */
+dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer,
+                           const void* q_idx, const void* q_idx_scale, const float* w,
+                           const uint16_t* q_lat,
+                           const int32_t* block_table, int32_t bt_stride,
+                           const int32_t* row_seq, const int32_t* row_ctx,
+                           int32_t R, int32_t max_ctx, int32_t k, float sm_scale,
+                           int32_t* idx, float* out, float* lse,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -228,10 +228,15 @@ def decode_row(pool, layout, layer, bt_row, ctx, q_codes, q_scale, w, q_lat_bits
     """
     lay = layout if isinstance(layout, Layout) else Layout(layout)
     ctx = max(0, int(ctx))
-    toks = np.arange(ctx)
-    keys = read_index_keys(pool, lay, layer, bt_row, toks)
     q = index_query(q_codes, q_scale, lay.index_fmt)
-    s = indexer_scores(q, w, keys)
+    s = np.empty(ctx, dtype=np.float64)
+    mag = np.empty(ctx, dtype=np.float64) if want_magnitude else None
+    for a in range(0, ctx, 65536):                       # keys are read 64K tokens at a time
+        toks = np.arange(a, min(a + 65536, ctx))
+        keys = read_index_keys(pool, lay, layer, bt_row, toks)
+        s[a:a + toks.size] = indexer_scores(q, w, keys)
+        if want_magnitude:
+            mag[a:a + toks.size] = indexer_magnitude(q, w, keys)
     s32 = s.astype(np.float32)
     idx = select_topk(s32, k)
     use = idx if idx_override is None else np.asarray(idx_override, dtype=np.int64)
@@ -239,7 +244,7 @@ def decode_row(pool, layout, layer, bt_row, ctx, q_codes, q_scale, w, q_lat_bits
     out, lse = sparse_mla(bf16_to_f64(q_lat_bits), lat, sm_scale)
     res = dict(scores=s, scores32=s32, idx=idx, out=out, lse=lse)
     if want_magnitude:
-        res["mag"] = indexer_magnitude(q, w, keys)
+        res["mag"] = mag
     return res
 
 

@@ -1,0 +1,238 @@
+"""ctypes binding of libdsa.so: same names as the C ABI in include/dsa.h.
+
+Argument marshalling only. Torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels. There is
+no fallback: if libdsa.so is missing or a tensor is not on the GPU, the call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_INDEX_FP8 = 0
+DSA_INDEX_MXFP4 = 1
+DSA_OP_TOPK = 1
+DSA_OP_SPARSE_MLA = 2
+DSA_OP_DECODE_STEP = 3
+DSA_MAX_LAYERS = 64
+H_IDX, D_IDX, H_Q, D_LAT, D_V = 32, 128, 96, 576, 512
+
+EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_last_error_detail", "dsa_workspace_bytes",
+            "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step")
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn} failed: status {status}: {detail}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("pool", ctypes.c_void_p),
+        ("row_bytes", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int64),
+        ("block_size", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("index_fmt", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("lat_off", ctypes.c_int64 * DSA_MAX_LAYERS),
+        ("idx_off", ctypes.c_int64 * DSA_MAX_LAYERS),
+    ]
+
+
+_lib = None
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdsa.so and declare every exported signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
+    L.dsa_abi_version.restype = _i32
+    L.dsa_abi_version.argtypes = []
+    L.dsa_status_string.restype = ctypes.c_char_p
+    L.dsa_status_string.argtypes = [_i32]
+    L.dsa_last_error_detail.restype = ctypes.c_char_p
+    L.dsa_last_error_detail.argtypes = []
+    L.dsa_workspace_bytes.restype = _sz
+    L.dsa_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    L.dsa_decode_scores_ld.restype = _i64
+    L.dsa_decode_scores_ld.argtypes = [_i32]
+    P = ctypes.POINTER(CacheDesc)
+    L.dsa_indexer_score.restype = _i32
+    L.dsa_indexer_score.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _i64, _vp]
+    L.dsa_topk.restype = _i32
+    L.dsa_topk.argtypes = [_vp, _i64, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]
+    L.dsa_sparse_mla.restype = _i32
+    L.dsa_sparse_mla.argtypes = [P, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+    L.dsa_decode_step.restype = _i32
+    L.dsa_decode_step.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
+                                  _vp, _vp, _vp, _vp, _sz, _vp]
+    _lib = L
+    return L
+
+
+def _check(st: int, fn: str):
+    if st != 0:
+        L = load_library()
+        raise DSAError(st, fn, L.dsa_last_error_detail().decode())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_cache_desc(pool: torch.Tensor, layout) -> CacheDesc:
+    """Descriptor for a pool tensor uint8 [num_blocks, row_bytes] and a layout object
+    or dict with block_size, num_layers, index_fmt ('fp8'|'mxfp4'), row_bytes, lat_off, idx_off."""
+    get = (lambda k: layout[k]) if isinstance(layout, dict) else (lambda k: getattr(layout, k))
+    d = CacheDesc()
+    d.pool = _dev(pool, "pool", torch.uint8)
+    d.row_bytes = int(get("row_bytes"))
+    d.num_blocks = pool.numel() // d.row_bytes
+    d.block_size = int(get("block_size"))
+    d.num_layers = int(get("num_layers"))
+    fmt = get("index_fmt")
+    d.index_fmt = {"fp8": DSA_INDEX_FP8, "mxfp4": DSA_INDEX_MXFP4}.get(fmt, fmt if isinstance(fmt, int) else -1)
+    for i, v in enumerate(get("lat_off")):
+        d.lat_off[i] = int(v)
+    for i, v in enumerate(get("idx_off")):
+        d.idx_off[i] = int(v)
+    return d
+
+
+def dsa_abi_version() -> int:
+    return load_library().dsa_abi_version()
+
+
+def dsa_status_string(status: int) -> str:
+    return load_library().dsa_status_string(status).decode()
+
+
+def dsa_workspace_bytes(op: int, R: int, max_ctx: int, k: int) -> int:
+    return load_library().dsa_workspace_bytes(op, R, max_ctx, k)
+
+
+def dsa_decode_scores_ld(max_ctx: int) -> int:
+    return load_library().dsa_decode_scores_ld(max_ctx)
+
+
+def _bt_stride(block_table: torch.Tensor) -> int:
+    return block_table.shape[-1]
+
+
+def dsa_indexer_score(pool, layout, layer, q_idx, q_idx_scale, w, block_table, row_seq, row_ctx, max_ctx,
+                      scores=None, ld_scores=None):
+    """Scores fp32 [R][ld_scores] of every token t < row_ctx[r]."""
+    L = load_library()
+    R = row_seq.shape[0]
+    if ld_scores is None:
+        ld_scores = max(int(max_ctx), 1)
+    if scores is None:
+        scores = torch.empty((R, ld_scores), dtype=torch.float32, device=pool.device)
+    d = make_cache_desc(pool, layout)
+    st = L.dsa_indexer_score(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+                             _dev(w, "w", torch.float32), _dev(block_table, "block_table", torch.int32),
+                             _bt_stride(block_table), _dev(row_seq, "row_seq", torch.int32),
+                             _dev(row_ctx, "row_ctx", torch.int32), R, int(max_ctx), _dev(scores, "scores", torch.float32),
+                             int(ld_scores), _stream(pool.device))
+    _check(st, "dsa_indexer_score")
+    return scores
+
+
+def dsa_topk(scores, row_ctx, max_ctx, k, idx=None, workspace=None, ld_scores=None):
+    """Exact top-k token indices int32 [R][k] (ascending, -1 padded)."""
+    L = load_library()
+    R = row_ctx.shape[0]
+    if ld_scores is None:
+        ld_scores = scores.shape[-1]
+    if idx is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=scores.device)
+    need = L.dsa_workspace_bytes(DSA_OP_TOPK, R, int(max_ctx), int(k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=scores.device)
+    st = L.dsa_topk(_dev(scores, "scores", torch.float32), int(ld_scores), _dev(row_ctx, "row_ctx", torch.int32), R,
+                    int(max_ctx), int(k), _dev(idx, "idx", torch.int32), _dev(workspace, "workspace"),
+                    workspace.numel() * workspace.element_size(), _stream(scores.device))
+    _check(st, "dsa_topk")
+    return idx
+
+
+def dsa_sparse_mla(pool, layout, layer, q_lat, block_table, row_seq, idx, k, sm_scale, out=None, lse=None,
+                   workspace=None):
+    """Sparse MLA over idx: out fp32 [R][96][512], lse fp32 [R][96]."""
+    L = load_library()
+    R = row_seq.shape[0]
+    dev = pool.device
+    if out is None:
+        out = torch.empty((R, H_Q, D_V), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((R, H_Q), dtype=torch.float32, device=dev)
+    need = L.dsa_workspace_bytes(DSA_OP_SPARSE_MLA, R, 0, int(k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    d = make_cache_desc(pool, layout)
+    st = L.dsa_sparse_mla(ctypes.byref(d), layer, _dev(q_lat, "q_lat", torch.bfloat16),
+                          _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
+                          _dev(row_seq, "row_seq", torch.int32), _dev(idx, "idx", torch.int32), R, int(k),
+                          float(sm_scale), _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32),
+                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "dsa_sparse_mla")
+    return out, lse
+
+
+def dsa_decode_step(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_table, row_seq, row_ctx, max_ctx, k,
+                    sm_scale, idx=None, out=None, lse=None, workspace=None):
+    """Indexer -> exact top-k -> sparse MLA -> merge. Returns (idx, out, lse, workspace);
+    the scores sit at the start of the workspace with row stride dsa_decode_scores_ld(max_ctx)."""
+    L = load_library()
+    R = row_seq.shape[0]
+    dev = pool.device
+    if idx is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((R, H_Q, D_V), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((R, H_Q), dtype=torch.float32, device=dev)
+    need = L.dsa_workspace_bytes(DSA_OP_DECODE_STEP, R, int(max_ctx), int(k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    d = make_cache_desc(pool, layout)
+    st = L.dsa_decode_step(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+                           _dev(w, "w", torch.float32), _dev(q_lat, "q_lat", torch.bfloat16),
+                           _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
+                           _dev(row_seq, "row_seq", torch.int32), _dev(row_ctx, "row_ctx", torch.int32), R,
+                           int(max_ctx), int(k), float(sm_scale), _dev(idx, "idx", torch.int32),
+                           _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32),
+                           _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "dsa_decode_step")
+    return idx, out, lse, workspace
+
+
+def decode_scores_view(workspace: torch.Tensor, R: int, max_ctx: int) -> torch.Tensor:
+    """The fp32 score array [R][ld] kept at the start of a decode-step workspace."""
+    ld = dsa_decode_scores_ld(max_ctx)
+    return workspace[:R * ld * 4].view(torch.float32).view(R, ld)

@@ -1,0 +1,240 @@
+// C ABI entry points: argument checks, workspace carving, kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "internal.h"
+
+using namespace dsa;
+
+namespace {
+
+thread_local std::string g_detail;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_detail.clear();
+  return DSA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ilog2(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+dsa_status check_cache(const dsa_cache_desc* c, int32_t layer, CacheView* cv) {
+  if (c == nullptr) return fail(DSA_ERR_NULL, "cache descriptor is NULL");
+  if (c->pool == nullptr) return fail(DSA_ERR_NULL, "cache pool is NULL");
+  if (c->block_size <= 0 || (c->block_size & (c->block_size - 1)) != 0 || c->block_size > 65536)
+    return fail(DSA_ERR_LAYOUT, "block_size %d is not a power of two in [1, 65536]", c->block_size);
+  if (c->num_layers < 1 || c->num_layers > DSA_MAX_LAYERS)
+    return fail(DSA_ERR_LAYOUT, "num_layers %d out of [1, %d]", c->num_layers, DSA_MAX_LAYERS);
+  if (layer < 0 || layer >= c->num_layers) return fail(DSA_ERR_ARG, "layer %d out of [0, %d)", layer, c->num_layers);
+  if (c->num_blocks < 1) return fail(DSA_ERR_LAYOUT, "num_blocks %lld < 1", (long long)c->num_blocks);
+  if (c->row_bytes <= 0 || (c->row_bytes & 15)) return fail(DSA_ERR_ALIGN, "row_bytes %lld is not a positive multiple of 16", (long long)c->row_bytes);
+  if (!aligned16(c->pool)) return fail(DSA_ERR_ALIGN, "pool is not 16-byte aligned");
+  if (c->index_fmt != DSA_INDEX_FP8 && c->index_fmt != DSA_INDEX_MXFP4)
+    return fail(DSA_ERR_UNSUPPORTED, "index_fmt %d", c->index_fmt);
+  const int64_t bs = c->block_size;
+  const int64_t lat_page = bs * (DSA_D_LAT + 4);
+  const int64_t idx_page = c->index_fmt == DSA_INDEX_FP8 ? bs * (DSA_D_IDX + 4) : bs * (DSA_D_IDX / 2 + 4);
+  for (int l = 0; l < c->num_layers; ++l) {
+    if (c->lat_off[l] < 0 || (c->lat_off[l] & 15) || c->lat_off[l] + lat_page > c->row_bytes)
+      return fail(DSA_ERR_LAYOUT, "layer %d latent page [%lld, +%lld) does not fit a %lld-byte row or is misaligned", l,
+                  (long long)c->lat_off[l], (long long)lat_page, (long long)c->row_bytes);
+    if (c->idx_off[l] < 0 || (c->idx_off[l] & 15) || c->idx_off[l] + idx_page > c->row_bytes)
+      return fail(DSA_ERR_LAYOUT, "layer %d index page [%lld, +%lld) does not fit a %lld-byte row or is misaligned", l,
+                  (long long)c->idx_off[l], (long long)idx_page, (long long)c->row_bytes);
+  }
+  cv->pool = static_cast<const uint8_t*>(c->pool);
+  cv->row_bytes = c->row_bytes;
+  cv->num_blocks = c->num_blocks;
+  cv->lat_off = c->lat_off[layer];
+  cv->idx_off = c->idx_off[layer];
+  cv->block_size = c->block_size;
+  cv->log2_bs = ilog2(c->block_size);
+  return DSA_OK;
+}
+
+dsa_status check_rows(const dsa_cache_desc* c, const int32_t* bt, int32_t bt_stride, const int32_t* row_seq,
+                      const int32_t* row_ctx, int32_t R, int32_t max_ctx, bool need_ctx, RowMap* rm) {
+  if (R < 0 || R > 65535) return fail(DSA_ERR_ARG, "R %d out of [0, 65535]", R);
+  if (bt == nullptr || row_seq == nullptr) return fail(DSA_ERR_NULL, "block_table / row_seq is NULL");
+  if (need_ctx && row_ctx == nullptr) return fail(DSA_ERR_NULL, "row_ctx is NULL");
+  if (bt_stride < 1) return fail(DSA_ERR_ARG, "bt_stride %d < 1", bt_stride);
+  if (max_ctx < 0 || max_ctx > kMaxCtx) return fail(DSA_ERR_ARG, "max_ctx %d out of [0, %d]", max_ctx, kMaxCtx);
+  if ((int64_t)max_ctx > (int64_t)bt_stride * c->block_size)
+    return fail(DSA_ERR_ARG, "max_ctx %d exceeds block-table capacity %lld", max_ctx,
+                (long long)bt_stride * c->block_size);
+  rm->block_table = bt;
+  rm->row_seq = row_seq;
+  rm->row_ctx = row_ctx;
+  rm->bt_stride = bt_stride;
+  rm->max_ctx = max_ctx;
+  return DSA_OK;
+}
+
+int64_t scores_ld(int32_t max_ctx) {
+  int64_t ld = ((int64_t)max_ctx + 63) / 64 * 64;
+  return ld < 64 ? 64 : ld;
+}
+
+size_t decode_ws(int32_t R, int32_t max_ctx, int32_t k) {
+  return align_up((size_t)R * scores_ld(max_ctx) * 4, 256) + topk_ws_bytes(R, max_ctx) + mla_ws_bytes(R, k);
+}
+
+dsa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "null pointer";
+    case DSA_ERR_ARG: return "argument out of range";
+    case DSA_ERR_LAYOUT: return "inconsistent cache layout";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_ALIGN: return "misaligned pointer or offset";
+    case DSA_ERR_HIP: return "HIP launch failed";
+    case DSA_ERR_UNSUPPORTED: return "unsupported format or shape";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error_detail(void) { return g_detail.c_str(); }
+
+int64_t dsa_decode_scores_ld(int32_t max_ctx) { return scores_ld(max_ctx); }
+
+size_t dsa_workspace_bytes(int32_t op, int32_t R, int32_t max_ctx, int32_t k) {
+  if (R < 0 || max_ctx < 0 || k < 1 || k > DSA_MAX_K) return 0;
+  switch (op) {
+    case DSA_OP_TOPK: return topk_ws_bytes(R, max_ctx);
+    case DSA_OP_SPARSE_MLA: return mla_ws_bytes(R, k);
+    case DSA_OP_DECODE_STEP: return decode_ws(R, max_ctx, k);
+    default: return 0;
+  }
+}
+
+dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer, const void* q_idx, const void* q_idx_scale,
+                             const float* w, const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
+                             const int32_t* row_ctx, int32_t R, int32_t max_ctx, float* scores, int64_t ld_scores,
+                             void* stream) {
+  CacheView cv;
+  RowMap rm;
+  dsa_status st = check_cache(cache, layer, &cv);
+  if (st) return st;
+  if ((st = check_rows(cache, block_table, bt_stride, row_seq, row_ctx, R, max_ctx, true, &rm))) return st;
+  if (q_idx == nullptr || q_idx_scale == nullptr || w == nullptr || scores == nullptr)
+    return fail(DSA_ERR_NULL, "q_idx / q_idx_scale / w / scores is NULL");
+  if (ld_scores < max_ctx) return fail(DSA_ERR_ARG, "ld_scores %lld < max_ctx %d", (long long)ld_scores, max_ctx);
+  if (!aligned16(q_idx)) return fail(DSA_ERR_ALIGN, "q_idx is not 16-byte aligned");
+  if (cache->index_fmt != DSA_INDEX_FP8) return fail(DSA_ERR_UNSUPPORTED, "MXFP4 index keys are not built yet");
+  if (R == 0) return ok();
+  return hip_status(launch_indexer_fp8(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
+                                       w, R, scores, ld_scores, nullptr, 0, static_cast<hipStream_t>(stream)),
+                    "indexer");
+}
+
+dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_ctx, int32_t R, int32_t max_ctx,
+                    int32_t k, int32_t* idx, void* workspace, size_t ws_bytes, void* stream) {
+  if (scores == nullptr || row_ctx == nullptr || idx == nullptr) return fail(DSA_ERR_NULL, "scores / row_ctx / idx is NULL");
+  if (R < 0 || R > 65535) return fail(DSA_ERR_ARG, "R %d out of [0, 65535]", R);
+  if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
+  if (max_ctx < 0 || max_ctx > kMaxCtx) return fail(DSA_ERR_ARG, "max_ctx %d out of [0, %d]", max_ctx, kMaxCtx);
+  if (ld_scores < max_ctx) return fail(DSA_ERR_ARG, "ld_scores %lld < max_ctx %d", (long long)ld_scores, max_ctx);
+  const size_t need = topk_ws_bytes(R, max_ctx);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(workspace)) return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (R == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TopkWs tw = topk_ws_carve(workspace, R, max_ctx);
+  hipError_t e = launch_clear(tw.hist, tw.clear_words, s);
+  if (e == hipSuccess) e = launch_topk(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, s);
+  return hip_status(e, "topk");
+}
+
+dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer, const uint16_t* q_lat, const int32_t* block_table,
+                          int32_t bt_stride, const int32_t* row_seq, const int32_t* idx, int32_t R, int32_t k,
+                          float sm_scale, float* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  CacheView cv;
+  RowMap rm;
+  dsa_status st = check_cache(cache, layer, &cv);
+  if (st) return st;
+  // idx entries must lie inside the block-table row: allow the full row capacity
+  const int32_t cap = (int32_t)((int64_t)bt_stride * cache->block_size > kMaxCtx ? kMaxCtx : (int64_t)bt_stride * cache->block_size);
+  if ((st = check_rows(cache, block_table, bt_stride, row_seq, nullptr, R, cap, false, &rm))) return st;
+  if (q_lat == nullptr || idx == nullptr || out == nullptr) return fail(DSA_ERR_NULL, "q_lat / idx / out is NULL");
+  if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
+  if (!aligned16(q_lat)) return fail(DSA_ERR_ALIGN, "q_lat is not 16-byte aligned");
+  const size_t need = mla_ws_bytes(R, k);
+  if (mla_splits(R, k) > 1 && (workspace == nullptr || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (R == 0) return ok();
+  return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, R, k, sm_scale, out, lse, workspace,
+                                      static_cast<hipStream_t>(stream)),
+                    "sparse_mla");
+}
+
+dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const void* q_idx, const void* q_idx_scale,
+                           const float* w, const uint16_t* q_lat, const int32_t* block_table, int32_t bt_stride,
+                           const int32_t* row_seq, const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k,
+                           float sm_scale, int32_t* idx, float* out, float* lse, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  CacheView cv;
+  RowMap rm;
+  dsa_status st = check_cache(cache, layer, &cv);
+  if (st) return st;
+  if ((st = check_rows(cache, block_table, bt_stride, row_seq, row_ctx, R, max_ctx, true, &rm))) return st;
+  if (q_idx == nullptr || q_idx_scale == nullptr || w == nullptr || q_lat == nullptr || idx == nullptr || out == nullptr)
+    return fail(DSA_ERR_NULL, "q_idx / q_idx_scale / w / q_lat / idx / out is NULL");
+  if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
+  if (!aligned16(q_idx) || !aligned16(q_lat)) return fail(DSA_ERR_ALIGN, "q_idx / q_lat is not 16-byte aligned");
+  if (cache->index_fmt != DSA_INDEX_FP8) return fail(DSA_ERR_UNSUPPORTED, "MXFP4 index keys are not built yet");
+  const size_t need = decode_ws(R, max_ctx, k);
+  if (workspace == nullptr || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(workspace)) return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (R == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* p = static_cast<uint8_t*>(workspace);
+  const int64_t ld = scores_ld(max_ctx);
+  float* scores = reinterpret_cast<float*>(p);
+  p += align_up((size_t)R * ld * 4, 256);
+  TopkWs tw = topk_ws_carve(p, R, max_ctx);
+  p += topk_ws_bytes(R, max_ctx);
+  void* mla_ws = p;
+  hipError_t e = launch_indexer_fp8(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
+                                    w, R, scores, ld, tw.hist, (int64_t)tw.clear_words, s);
+  if (e == hipSuccess) e = launch_topk(scores, ld, row_ctx, R, max_ctx, k, idx, tw, s);
+  if (e == hipSuccess) {
+    // the selected tokens lie below max_ctx, so the row map's bound is unchanged
+    e = launch_sparse_mla(cv, rm, q_lat, idx, R, k, sm_scale, out, lse, mla_ws, s);
+  }
+  return hip_status(e, "decode_step");
+}
+
+}  // extern "C"
