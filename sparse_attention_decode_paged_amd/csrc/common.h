@@ -89,6 +89,99 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(uint32_t a, uint32_t b) {
   return r;
 }
 
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8hf __attribute__((ext_vector_type(8)));
+
+// Eight e4m3 codes -> v8 fp16 (exact: every e4m3 value is an fp16 value).
+__device__ __forceinline__ v8hf e4m3x8_to_f16(uint32_t a, uint32_t b) {
+  v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false);
+  v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true);
+  v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+  v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true);
+  v8hf r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// ---- cross-lane exchange without the LDS path --------------------------------------
+// x ^ J partner within the 64-lane wave: DPP quad permutes / row mirrors for J < 16,
+// permlane swaps for 16 and 32 (lane semantics checked on gfx950).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+}
+template <int J>
+__device__ __forceinline__ uint32_t xshfl(uint32_t v) {
+  if constexpr (J == 1) return dpp_mov<0xB1>(v);                   // quad_perm [1,0,3,2]
+  else if constexpr (J == 2) return dpp_mov<0x4E>(v);              // quad_perm [2,3,0,1]
+  else if constexpr (J == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(v));  // half mirror, then quad reverse
+  else if constexpr (J == 8) return dpp_mov<0x141>(dpp_mov<0x140>(v)); // row mirror, then half mirror
+  else if constexpr (J == 16) {
+    auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((threadIdx.x >> 4) & 1) ? p[0] : p[1];
+  } else {
+    static_assert(J == 32, "xor distance");
+    auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return ((threadIdx.x >> 5) & 1) ? p[0] : p[1];
+  }
+}
+template <int J>
+__device__ __forceinline__ float xshflf(float v) {
+  return __uint_as_float(xshfl<J>(__float_as_uint(v)));
+}
+template <int J>
+__device__ __forceinline__ uint64_t xshfl64(uint64_t v) {
+  return ((uint64_t)xshfl<J>((uint32_t)(v >> 32)) << 32) | xshfl<J>((uint32_t)v);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += xshfl<1>(v); v += xshfl<2>(v); v += xshfl<4>(v);
+  v += xshfl<8>(v); v += xshfl<16>(v); v += xshfl<32>(v);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  uint64_t o;
+  o = xshfl64<1>(v); v = o < v ? o : v;
+  o = xshfl64<2>(v); v = o < v ? o : v;
+  o = xshfl64<4>(v); v = o < v ? o : v;
+  o = xshfl64<8>(v); v = o < v ? o : v;
+  o = xshfl64<16>(v); v = o < v ? o : v;
+  o = xshfl64<32>(v); v = o < v ? o : v;
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = xshfl64<1>(v); v = o > v ? o : v;
+  o = xshfl64<2>(v); v = o > v ? o : v;
+  o = xshfl64<4>(v); v = o > v ? o : v;
+  o = xshfl64<8>(v); v = o > v ? o : v;
+  o = xshfl64<16>(v); v = o > v ? o : v;
+  o = xshfl64<32>(v); v = o > v ? o : v;
+  return v;
+}
+
+// One compare-exchange stage of a descending bitonic network across the wave.
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic_desc_step(uint32_t v, int lane) {
+  const uint32_t o = xshfl<J>(v);
+  const bool take_max = ((lane & K) == 0) == ((lane & J) == 0);
+  return take_max ? (v > o ? v : o) : (v < o ? v : o);
+}
+// Sort 64 values (one per lane) in descending lane order.
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v, int lane) {
+  v = bitonic_desc_step<2, 1>(v, lane);
+  v = bitonic_desc_step<4, 2>(v, lane);  v = bitonic_desc_step<4, 1>(v, lane);
+  v = bitonic_desc_step<8, 4>(v, lane);  v = bitonic_desc_step<8, 2>(v, lane);  v = bitonic_desc_step<8, 1>(v, lane);
+  v = bitonic_desc_step<16, 8>(v, lane); v = bitonic_desc_step<16, 4>(v, lane);
+  v = bitonic_desc_step<16, 2>(v, lane); v = bitonic_desc_step<16, 1>(v, lane);
+  v = bitonic_desc_step<32, 16>(v, lane); v = bitonic_desc_step<32, 8>(v, lane); v = bitonic_desc_step<32, 4>(v, lane);
+  v = bitonic_desc_step<32, 2>(v, lane);  v = bitonic_desc_step<32, 1>(v, lane);
+  v = bitonic_desc_step<64, 32>(v, lane); v = bitonic_desc_step<64, 16>(v, lane); v = bitonic_desc_step<64, 8>(v, lane);
+  v = bitonic_desc_step<64, 4>(v, lane);  v = bitonic_desc_step<64, 2>(v, lane);  v = bitonic_desc_step<64, 1>(v, lane);
+  return v;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

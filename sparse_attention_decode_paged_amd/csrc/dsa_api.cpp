@@ -6,7 +6,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "internal.h"
 
 using namespace dsa;
@@ -63,6 +63,8 @@ dsa_status check_cache(const dsa_cache_desc* c, int32_t layer, CacheView* cv) {
       return fail(DSA_ERR_LAYOUT, "layer %d index page [%lld, +%lld) does not fit a %lld-byte row or is misaligned", l,
                   (long long)c->idx_off[l], (long long)idx_page, (long long)c->row_bytes);
   }
+  if (c->num_blocks * (int64_t)c->block_size > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "num_blocks * block_size exceeds 2^31 token slots");
   cv->pool = static_cast<const uint8_t*>(c->pool);
   cv->row_bytes = c->row_bytes;
   cv->num_blocks = c->num_blocks;
@@ -97,7 +99,8 @@ int64_t scores_ld(int32_t max_ctx) {
 }
 
 size_t decode_ws(int32_t R, int32_t max_ctx, int32_t k) {
-  return align_up((size_t)R * scores_ld(max_ctx) * 4, 256) + topk_ws_bytes(R, max_ctx) + mla_ws_bytes(R, k);
+  return align_up((size_t)R * scores_ld(max_ctx) * 4, 256) + topk_ws_bytes(R, max_ctx) +
+         align_up((size_t)R * k * 4, 256) + mla_ws_bytes(R, k);
 }
 
 dsa_status hip_status(hipError_t e, const char* what) {
@@ -155,7 +158,7 @@ dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer, const v
   if (cache->index_fmt != DSA_INDEX_FP8) return fail(DSA_ERR_UNSUPPORTED, "MXFP4 index keys are not built yet");
   if (R == 0) return ok();
   return hip_status(launch_indexer_fp8(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
-                                       w, R, scores, ld_scores, nullptr, 0, static_cast<hipStream_t>(stream)),
+                                       w, R, scores, ld_scores, nullptr, static_cast<hipStream_t>(stream)),
                     "indexer");
 }
 
@@ -173,8 +176,8 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_c
   if (R == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   TopkWs tw = topk_ws_carve(workspace, R, max_ctx);
-  hipError_t e = launch_clear(tw.hist, tw.clear_words, s);
-  if (e == hipSuccess) e = launch_topk(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, s);
+  hipError_t e = launch_topk_send(scores, ld_scores, row_ctx, R, max_ctx, tw, s);
+  if (e == hipSuccess) e = launch_topk_select(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, nullptr, nullptr, nullptr, nullptr, s);
   return hip_status(e, "topk");
 }
 
@@ -195,7 +198,7 @@ dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer, const uint
   if (mla_splits(R, k) > 1 && (workspace == nullptr || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (R == 0) return ok();
-  return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, R, k, sm_scale, out, lse, workspace,
+  return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, nullptr, nullptr, R, k, sm_scale, out, lse, workspace,
                                       static_cast<hipStream_t>(stream)),
                     "sparse_mla");
 }
@@ -226,13 +229,15 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const voi
   p += align_up((size_t)R * ld * 4, 256);
   TopkWs tw = topk_ws_carve(p, R, max_ctx);
   p += topk_ws_bytes(R, max_ctx);
+  int32_t* phys = reinterpret_cast<int32_t*>(p);
+  p += align_up((size_t)R * k * 4, 256);
   void* mla_ws = p;
   hipError_t e = launch_indexer_fp8(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
-                                    w, R, scores, ld, tw.hist, (int64_t)tw.clear_words, s);
-  if (e == hipSuccess) e = launch_topk(scores, ld, row_ctx, R, max_ctx, k, idx, tw, s);
+                                    w, R, scores, ld, &tw, s);
+  if (e == hipSuccess) e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, idx, tw, phys, nullptr, &cv, &rm, s);
   if (e == hipSuccess) {
     // the selected tokens lie below max_ctx, so the row map's bound is unchanged
-    e = launch_sparse_mla(cv, rm, q_lat, idx, R, k, sm_scale, out, lse, mla_ws, s);
+    e = launch_sparse_mla(cv, rm, q_lat, idx, phys, nullptr, R, k, sm_scale, out, lse, mla_ws, s);
   }
   return hip_status(e, "decode_step");
 }

@@ -10,56 +10,33 @@
 namespace dsa {
 
 // ---- top-k workspace -------------------------------------------------------------
-constexpr int kTopkChunk = 4096;    // tokens per workgroup in the select passes
-constexpr int kTopkBins = 4096;     // first-level histogram: top 12 bits of the score key
-constexpr int kTopkCtrl = 16;       // control words per row
-constexpr int kCandCap = 16384;     // per-row candidate list (beyond it, passes rescan scores)
-constexpr int kMaxCtx = 1 << 22;    // largest supported context
-
-// control word indices
-enum : int { CT_DONE1 = 0, CT_DONE2 = 1, CT_NCAND = 2, CT_B1 = 3, CT_NEED1 = 4, CT_NEQ = 5,
-             CT_CSTAR_HI = 6, CT_CSTAR_LO = 7 };
+constexpr int kTopkFullRow = 16384;   // rows up to this length are selected from all their scores
+constexpr int kCandUnit = 64;         // tokens per candidate-sending unit (one indexer wave)
+constexpr int kCandRowCap = 16384;    // candidates a row sends in total (select stage registers)
+constexpr int kCandPerUnitMax = 16;   // candidates a unit sends, at most
+constexpr int kMaxCtx = 1 << 20;      // largest supported context (16384 units x >= 1 candidate)
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-inline int topk_chunks(int max_ctx) { int c = (max_ctx + kTopkChunk - 1) / kTopkChunk; return c < 1 ? 1 : c; }
+inline int cand_units(int max_ctx) { int c = (max_ctx + kCandUnit - 1) / kCandUnit; return c < 1 ? 1 : c; }
 
 struct TopkWs {
-  uint32_t* hist;   // [R][kTopkBins]   (cleared before each call)
-  uint32_t* ctrl;   // [R][kTopkCtrl]   (cleared before each call, contiguous after hist)
-  uint32_t* gtc;    // [R][nch]
-  uint32_t* base;   // [R][nch]
-  uint32_t* cand;   // [R][kCandCap]
-  int nch;
-  size_t clear_words;  // words from hist to the end of ctrl
+  uint64_t* cand;    // [R][kCandRowCap] keys sent by the row's units (unit u at u*m .. u*m+m)
+  uint64_t* floors;  // [R][nunits] upper bound of the keys a unit did not send (0: sent all)
+  int nunits;
 };
 
 inline size_t topk_ws_bytes(int R, int max_ctx) {
-  size_t nch = (size_t)topk_chunks(max_ctx);
-  size_t b = 0;
-  b += align_up((size_t)R * kTopkBins * 4, 256);
-  b += align_up((size_t)R * kTopkCtrl * 4, 256);
-  b += align_up((size_t)R * nch * 4, 256);
-  b += align_up((size_t)R * nch * 4, 256);
-  b += align_up((size_t)R * kCandCap * 4, 256);
-  return b;
+  const size_t nu = (size_t)cand_units(max_ctx);
+  return align_up((size_t)R * kCandRowCap * 8, 256) + align_up((size_t)R * nu * 8, 256);
 }
 
 inline TopkWs topk_ws_carve(void* ws, int R, int max_ctx) {
   TopkWs t;
   uint8_t* p = static_cast<uint8_t*>(ws);
-  t.nch = topk_chunks(max_ctx);
-  t.hist = reinterpret_cast<uint32_t*>(p);
-  size_t hb = (size_t)R * kTopkBins * 4;
-  // ctrl directly after hist so that one clear covers both
-  t.ctrl = reinterpret_cast<uint32_t*>(p + hb);
-  t.clear_words = (size_t)R * (kTopkBins + kTopkCtrl);
-  p += align_up(hb, 256) + align_up((size_t)R * kTopkCtrl * 4, 256);
-  // hb is a multiple of 256 (kTopkBins * 4 = 16 KiB per row), so ctrl sits right after hist
-  t.gtc = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)R * t.nch * 4, 256);
-  t.base = reinterpret_cast<uint32_t*>(p);
-  p += align_up((size_t)R * t.nch * 4, 256);
-  t.cand = reinterpret_cast<uint32_t*>(p);
+  t.nunits = cand_units(max_ctx);
+  t.cand = reinterpret_cast<uint64_t*>(p);
+  p += align_up((size_t)R * kCandRowCap * 8, 256);
+  t.floors = reinterpret_cast<uint64_t*>(p);
   return t;
 }
 
@@ -88,16 +65,25 @@ inline size_t mla_ws_bytes(int R, int k) {
 }
 
 // ---- launches -------------------------------------------------------------------------
+// Indexer; when `ws` is non-null the epilogue also sends each block's top-k candidates.
 hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const float* q_scale,
-                              const float* w, int R, float* scores, int64_t ld, uint32_t* clear_ptr,
-                              int64_t clear_words, hipStream_t stream);
+                              const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
+                              hipStream_t stream);
 
-hipError_t launch_clear(uint32_t* p, size_t words, hipStream_t stream);
+// Candidate sending over an existing score array (standalone top-k).
+hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx,
+                            const TopkWs& ws, hipStream_t stream);
+// Selection; when `phys` is non-null it also receives, per selected token, its page
+// slot (physical block * block_size + slot) and `pscale` the token's latent scale,
+// for the attention kernel.
+hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
+                              int32_t* idx, const TopkWs& ws, int32_t* phys, float* pscale, const CacheView* cv,
+                              const RowMap* rm, hipStream_t stream);
 
-hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
-                       int32_t* idx, const TopkWs& ws, hipStream_t stream);
-
+// Sparse MLA over idx; when `phys` / `pscale` (page slots and latent scales from the
+// selection) are non-null they replace the block-table lookups and scale loads.
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
-                             int R, int k, float sm_scale, float* out, float* lse, void* ws, hipStream_t stream);
+                             const int32_t* phys, const float* pscale, int R, int k, float sm_scale, float* out,
+                             float* lse, void* ws, hipStream_t stream);
 
 }  // namespace dsa

@@ -9,13 +9,15 @@
 //
 // Grid (split, row, head group of 32). A workgroup walks its split's slice of the
 // row's index list 64 tokens at a time:
-//   gather 64 latents (576 e4m3 bytes + fp32 scale) into LDS;
+//   translate the 64 token ids to latent row offsets once (block table lookups),
+//   then gather the 64 latents (576 e4m3 bytes each) into LDS;
 //   S = Q . C^T on 16x16x32 bf16 MFMAs (each wave: 16 tokens x 32 heads);
 //   online softmax in the log2 domain (running max / sum per head);
-//   P' = p * scale_t split into bf16 high and low parts in LDS;
-//   O += P'_hi . codes + P'_lo . codes on 32x32x16 bf16 MFMAs (each wave: 128 of
-//   the 512 value columns). The two-part P' keeps ~16 significant bits, so rows
-//   dominated by a handful of tokens lose nothing visible to bf16 rounding.
+//   P'' = p * scale_t / (largest scale in the chunk), in [0, 1], as fp16 in LDS;
+//   O += P'' . codes on 32x32x16 fp16 MFMAs (each wave: 128 of the 512 value
+//   columns); e4m3 codes are exact in fp16, and fp16 P keeps 11 significant bits
+//   (bf16's 8 were visibly too few on rows dominated by a handful of tokens).
+//   The chunk's scale factor joins the per-head softmax rescale.
 // e4m3 codes convert to bf16 exactly; the per-token scale is applied to the
 // logit and folded into P'. With one split the workgroup writes out / lse; with
 // several it writes unnormalised partials (O, m, l) that the merge kernel
@@ -26,9 +28,12 @@
 namespace dsa {
 
 namespace {
+using v8h = v8hf;
 constexpr int NT = 256;
 constexpr int CH = kMlaChunk;           // 64 tokens per iteration
 constexpr int PIECES = kDLat / 16;      // 36 16-byte pieces per latent
+constexpr int QROW = kDLat + 8;         // LDS row strides padded by 16 bytes so that the
+constexpr int LROW = kDLat + 16;        // 16 rows an MFMA fragment reads fall in distinct banks
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
@@ -38,35 +43,22 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
 }  // namespace
 
 __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm, const uint16_t* __restrict__ q_lat,
-                                                        const int32_t* __restrict__ idx, int k, int ts, float c2,
+                                                        const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ phys, int k, int ts, float c2,
                                                         float* __restrict__ out, float* __restrict__ lse,
                                                         float* __restrict__ part_o, float* __restrict__ part_ml,
                                                         int nsplit) {
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[kMlaGroup * kDLat];
-  __shared__ __attribute__((aligned(16))) uint8_t lat_s[CH * kDLat];
-  __shared__ __attribute__((aligned(16))) uint16_t p_s[kMlaGroup * CH];
-  __shared__ __attribute__((aligned(16))) uint16_t pl_s[kMlaGroup * CH];
+  __shared__ __attribute__((aligned(16))) uint16_t q_s[kMlaGroup * QROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lat_s[CH * LROW];
+  __shared__ __attribute__((aligned(16))) _Float16 p_s[kMlaGroup * CH];
+  __shared__ int64_t addr_s[CH];
   __shared__ float sc_s[CH];
   __shared__ float red_s[4][kMlaGroup];
   __shared__ float m_s[kMlaGroup], l_s[kMlaGroup], alpha_s[kMlaGroup];
-
-  {
-    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * kMlaGroup) * kDLat);
-    v4i* qd = reinterpret_cast<v4i*>(q_s);
-    for (int i = tid; i < kMlaGroup * kDLat / 8; i += NT) qd[i] = qg[i];
-  }
-  if (tid < kMlaGroup) {
-    m_s[tid] = kNegInf;
-    l_s[tid] = 0.f;
-  }
-  __syncthreads();
-
-  v16f acc[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] = v16f{};
+  __shared__ float smax_s;
 
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
@@ -74,34 +66,74 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
   const int seq = rm.row_seq[r];
   const int bs_mask = cv.block_size - 1;
 
-  for (int c0 = j0; c0 < j1; c0 += CH) {
-    // ---- gather 64 latents ----
-#pragma unroll
-    for (int q = 0; q < (CH * PIECES) / NT; ++q) {
-      int p = tid + NT * q;
-      int tt = p / PIECES, pc = p - tt * PIECES;
-      int j = c0 + tt;
-      int t = j < j1 ? irow[j] : -1;
-      t = t < rm.max_ctx ? t : -1;  // indices beyond the row bound are treated as empty
-      v4i v = {0, 0, 0, 0};
-      if (t >= 0) {
-        int64_t blk = token_block(cv, rm, seq, t);
-        const uint8_t* lp = row_base(cv, blk) + cv.lat_off + (int64_t)(t & bs_mask) * kDLat + pc * 16;
-        v = *reinterpret_cast<const v4i*>(lp);
-      }
-      reinterpret_cast<v4i*>(lat_s)[p] = v;
+  // Q fragment rows for this head group, straight to LDS.
+  {
+    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * kMlaGroup) * kDLat);
+    constexpr int QP = kDLat / 8;  // 72 16-byte pieces per head row
+    for (int i = tid; i < kMlaGroup * QP; i += NT) {
+      const int h = i / QP, pc = i - h * QP;
+      *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qg[i];
     }
+  }
+  if (tid < kMlaGroup) {
+    m_s[tid] = kNegInf;
+    l_s[tid] = 0.f;
+  }
+
+  v16f acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = v16f{};
+  float s_run = 1.f;  // acc holds O / s_run (token scales folded into P per chunk)
+
+  for (int c0 = j0; c0 < j1; c0 += CH) {
+    // ---- translate the chunk's 64 token ids into latent row offsets (one lookup each) ----
     if (tid < CH) {
-      int j = c0 + tid;
+      const int j = c0 + tid;
       int t = j < j1 ? irow[j] : -1;
       t = t < rm.max_ctx ? t : -1;
-      float s = 0.f;
-      if (t >= 0) {
-        int64_t blk = token_block(cv, rm, seq, t);
-        s = *reinterpret_cast<const float*>(row_base(cv, blk) + cv.lat_off + (int64_t)cv.block_size * kDLat +
-                                            (int64_t)(t & bs_mask) * 4);
+      const int tc = t >= 0 ? t : 0;  // every load below stays in the pool; empty slots are masked
+      int64_t blk;
+      if (phys != nullptr) {
+        const int ps = j < j1 ? phys[(int64_t)r * k + j] : 0;
+        blk = (int64_t)(ps >= 0 ? ps : 0) >> cv.log2_bs;
+        blk = blk < cv.num_blocks ? blk : cv.num_blocks - 1;
+      } else {
+        blk = token_block(cv, rm, seq, tc);
       }
+      const int64_t base = blk * cv.row_bytes + cv.lat_off;
+      const float s = *reinterpret_cast<const float*>(cv.pool + base + (int64_t)cv.block_size * kDLat +
+                                                      (int64_t)(tc & bs_mask) * 4);
+      addr_s[tid] = t >= 0 ? base + (int64_t)(tc & bs_mask) * kDLat : -1;
       sc_s[tid] = t >= 0 ? s : kNegInf;  // -inf marks an empty slot
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float v = sc_s[tid];
+      v = fmaxf(v, xshflf<1>(v));
+      v = fmaxf(v, xshflf<2>(v));
+      v = fmaxf(v, xshflf<4>(v));
+      v = fmaxf(v, xshflf<8>(v));
+      v = fmaxf(v, xshflf<16>(v));
+      v = fmaxf(v, xshflf<32>(v));
+      if (tid == 0) smax_s = v > 0.f ? v : 1.f;
+    }
+    // ---- gather 64 latents: 9 independent 16-byte loads per thread, then the LDS stores ----
+    {
+      v4i v[(CH * PIECES) / NT];
+#pragma unroll
+      for (int q = 0; q < (CH * PIECES) / NT; ++q) {
+        const int p = tid + NT * q;
+        const int tt = p / PIECES, pc = p - tt * PIECES;
+        const int64_t off = addr_s[tt];
+        v[q] = *reinterpret_cast<const v4i*>(cv.pool + (off >= 0 ? off : 0) + pc * 16);
+        if (off < 0) v[q] = v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int q = 0; q < (CH * PIECES) / NT; ++q) {
+        const int p = tid + NT * q;
+        const int tt = p / PIECES, pc = p - tt * PIECES;
+        *reinterpret_cast<v4i*>(lat_s + tt * LROW + pc * 16) = v[q];
+      }
     }
     __syncthreads();
 
@@ -109,9 +141,9 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     {
       const int hrow = lane & 15, kq = 8 * (lane >> 4);
-      const uint8_t* lrow = lat_s + (16 * wid + hrow) * kDLat + kq;
-      const uint16_t* qa0 = q_s + hrow * kDLat + kq;
-      const uint16_t* qa1 = q_s + (16 + hrow) * kDLat + kq;
+      const uint8_t* lrow = lat_s + (16 * wid + hrow) * LROW + kq;
+      const uint16_t* qa0 = q_s + hrow * QROW + kq;
+      const uint16_t* qa1 = q_s + (16 + hrow) * QROW + kq;
 #pragma unroll 6
       for (int kk = 0; kk < kDLat / 32; ++kk) {
         v8bf a0 = *reinterpret_cast<const v8bf*>(qa0 + 32 * kk);
@@ -122,10 +154,10 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, s1, 0, 0, 0);
       }
     }
-    // s0[i]: head 4*(lane>>4)+i, s1[i]: head 16+4*(lane>>4)+i, token tt
     const int tt = 16 * wid + (lane & 15);
     const float sct = sc_s[tt];
     const bool ok = sct != kNegInf;
+    const float smax = smax_s;
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -136,8 +168,10 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float v = x[i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+      v = fmaxf(v, xshflf<1>(v));
+      v = fmaxf(v, xshflf<2>(v));
+      v = fmaxf(v, xshflf<4>(v));
+      v = fmaxf(v, xshflf<8>(v));
       mx[i] = v;
     }
     const int hb = 4 * (lane >> 4);
@@ -157,23 +191,23 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       m_s[tid] = mn;
     }
     __syncthreads();
+    // p = 2^(x - m); P'' = p * scale_t / smax in [0, 1] goes to the fp16 MFMA
     float ps[8];
+    const float sfac = ok ? sct / smax : 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       int h = (i < 4) ? hb + i : 16 + hb + (i - 4);
-      float mn = m_s[h];
-      float p = (x[i] == kNegInf) ? 0.f : exp2f(x[i] - mn);
+      float p = (x[i] == kNegInf) ? 0.f : exp2f(x[i] - m_s[h]);
       ps[i] = p;
-      const float pv = ok ? p * sct : 0.f;
-      const __bf16 hi = (__bf16)pv;
-      p_s[h * CH + tt] = __builtin_bit_cast(uint16_t, hi);
-      pl_s[h * CH + tt] = bf16_bits(pv - (float)hi);
+      p_s[h * CH + tt] = (_Float16)(p * sfac);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float v = ps[i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+      v += xshflf<1>(v);
+      v += xshflf<2>(v);
+      v += xshflf<4>(v);
+      v += xshflf<8>(v);
       ps[i] = v;
     }
     if ((lane & 15) == 0) {
@@ -188,44 +222,45 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       l_s[tid] = l_s[tid] * alpha_s[tid] + (red_s[0][tid] + red_s[1][tid] + red_s[2][tid] + red_s[3][tid]);
     }
 
-    // ---- O = alpha * O + P' . codes : wave w -> value columns [128w, 128w+128) ----
+    // ---- acc = acc * alpha * (s_run / smax) + P'' . codes : wave w -> columns [128w, 128w+128) ----
+    const float rescale = s_run / smax;
+    s_run = smax;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      float a = alpha_s[8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3)];
+      float a = alpha_s[8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3)] * rescale;
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[c][rr] *= a;
     }
 #pragma unroll
     for (int ks = 0; ks < CH / 16; ++ks) {
       const int tk = 16 * ks + 8 * (lane >> 5);
-      v8bf a = *reinterpret_cast<const v8bf*>(p_s + (lane & 31) * CH + tk);
-      v8bf al = *reinterpret_cast<const v8bf*>(pl_s + (lane & 31) * CH + tk);
+      v8h a = *reinterpret_cast<const v8h*>(p_s + (lane & 31) * CH + tk);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int col = 128 * wid + 32 * c + (lane & 31);
-        const uint8_t* vp = lat_s + tk * kDLat + col;
-        uint32_t w0 = (uint32_t)vp[0] | ((uint32_t)vp[kDLat] << 8) | ((uint32_t)vp[2 * kDLat] << 16) |
-                      ((uint32_t)vp[3 * kDLat] << 24);
-        uint32_t w1 = (uint32_t)vp[4 * kDLat] | ((uint32_t)vp[5 * kDLat] << 8) | ((uint32_t)vp[6 * kDLat] << 16) |
-                      ((uint32_t)vp[7 * kDLat] << 24);
-        v8bf b = e4m3x8_to_bf16(w0, w1);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[c], 0, 0, 0);
+        const uint8_t* vp = lat_s + tk * LROW + col;
+        uint32_t w0 = (uint32_t)vp[0] | ((uint32_t)vp[LROW] << 8) | ((uint32_t)vp[2 * LROW] << 16) |
+                      ((uint32_t)vp[3 * LROW] << 24);
+        uint32_t w1 = (uint32_t)vp[4 * LROW] | ((uint32_t)vp[5 * LROW] << 8) | ((uint32_t)vp[6 * LROW] << 16) |
+                      ((uint32_t)vp[7 * LROW] << 24);
+        v8h b = e4m3x8_to_f16(w0, w1);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[c], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
+  __syncthreads();
   // ---- epilogue ----
   if (nsplit == 1) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int h = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
       const float lv = l_s[h];
-      const float inv = lv > 0.f ? 1.f / lv : 0.f;
+      const float f = lv > 0.f ? s_run / lv : 0.f;
       float* orow = out + ((int64_t)r * kHQ + hg * kMlaGroup + h) * kDV + 128 * wid + (lane & 31);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][rr] * inv;
+      for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][rr] * f;
     }
     if (lse != nullptr && tid < kMlaGroup) {
       float lv = l_s[tid];
@@ -238,7 +273,7 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       const int h = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
       float* orow = part_o + (pbase + h) * kDV + 128 * wid + (lane & 31);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][rr];
+      for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][rr] * s_run;
     }
     if (tid < kMlaGroup) {
       part_ml[(pbase + tid) * 2 + 0] = m_s[tid];
@@ -252,17 +287,20 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
                                                        const float* __restrict__ part_ml, int nsplit,
                                                        float* __restrict__ out, float* __restrict__ lse) {
   const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + (int64_t)r * nsplit * kHQ + h;
   float M = kNegInf;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(((int64_t)r * nsplit + s) * kHQ + h) * 2]);
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[(int64_t)s * kHQ].x);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
+  const float* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + tid;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
-    const int64_t base = ((int64_t)r * nsplit + s) * kHQ + h;
-    float m = part_ml[base * 2];
-    if (m == kNegInf) continue;
-    float wgt = exp2f(m - M);
-    L += wgt * part_ml[base * 2 + 1];
-    o0 += wgt * part_o[base * kDV + tid];
-    o1 += wgt * part_o[base * kDV + tid + NT];
+    const float2 e = ml[(int64_t)s * kHQ];
+    const float x0 = po[(int64_t)s * kHQ * kDV], x1 = po[(int64_t)s * kHQ * kDV + NT];
+    const float wgt = (e.x == kNegInf) ? 0.f : exp2f(e.x - M);
+    L = fmaf(wgt, e.y, L);
+    o0 = fmaf(wgt, x0, o0);
+    o1 = fmaf(wgt, x1, o1);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float* orow = out + ((int64_t)r * kHQ + h) * kDV;
@@ -272,7 +310,9 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
 }
 
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
-                             int R, int k, float sm_scale, float* out, float* lse, void* ws, hipStream_t stream) {
+                             const int32_t* phys, const float* pscale, int R, int k, float sm_scale, float* out,
+                             float* lse, void* ws, hipStream_t stream) {
+  (void)pscale;
   if (R <= 0) return hipSuccess;
   const int nsplit = mla_splits(R, k);
   const int ts = mla_split_tokens(k, nsplit);
@@ -283,8 +323,8 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     part_o = static_cast<float*>(ws);
     part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 4, 256));
   }
-  hipLaunchKernelGGL(sparse_mla_kernel, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NT), 0, stream, cv, rm, q_lat, idx, k,
-                     ts, c2, out, lse, part_o, part_ml, nsplit);
+  hipLaunchKernelGGL(sparse_mla_kernel, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NT), 0, stream, cv, rm, q_lat, idx, phys,
+                     k, ts, c2, out, lse, part_o, part_ml, nsplit);
   if (nsplit > 1)
     hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
   return hipGetLastError();

@@ -1,33 +1,44 @@
 // Exact per-row top-k over fp32 scores (ties -> lower token index).
 //
 // vLLM "Day-0 support for Kimi K3.1 Pro": the fused decode path ends the indexer
-// with an exact top-k selection that emits the rows attention reads, and the
-// zero-mismatch RL section wants top-k to be batch invariant. Here each row's
-// selection is a pure function of that row's scores.
+// with an exact top-k selection that emits the rows attention reads; the
+// zero-mismatch RL section wants top-k to be batch invariant; and the DCP
+// section's exact one-round merge sends only a bounded number of best candidates
+// per shard, detects when a shard held more of the true top-k than it sent, and
+// has that shard resend. The same scheme runs here between the 64-token units of
+// one row instead of between GPUs.
 //
 // Every (score, token) pair maps to a 64-bit composite key
 //   (order-preserving bits of the score) << 32 | (0xFFFFFFFF - token)
-// so "larger score, then lower index" is plain integer order and all composites
-// are distinct. The k selected tokens are exactly those whose composite is >= c*,
-// the k-th largest composite. Three passes over the row, each split over
-// workgroups of 4096 tokens:
-//   1. histogram of the top 12 key bits; the last workgroup of the row finds the
-//      bin b1 holding the k-th element and how many of that bin are still needed;
-//   2. tokens of bin b1 are appended to a candidate list and tokens above it are
-//      counted per chunk; the last workgroup resolves c* with 8-bit radix digits
-//      over the remaining 52 composite bits (reading the candidate list, or the
-//      scores again if the list overflowed) and turns per-chunk counts into
-//      output offsets;
-//   3. each workgroup writes its chunk's selected tokens in ascending order.
+// so "larger score, then lower index" is plain integer order, the keys of a row
+// are distinct, and the selection is the k largest keys. Key 0 never comes from a
+// real token and marks an empty slot.
+//
+// Stage 1 (topk_send.h: the indexer epilogue or topk_send_kernel): every unit
+// sends its m best keys in token order plus a floor bounding the keys it kept.
+// Stage 2 (topk_select_kernel, one 1024-thread workgroup per row). Every thread
+// holds 16 keys in registers, a contiguous run in token order:
+//   ctx <= k      every token;
+//   ctx <= 16384  the row's own keys;
+//   otherwise     the candidates (whole units per thread); c_u = their k-th
+//                 largest key; a unit whose floor reaches c_u may hold unsent keys
+//                 >= c_u and is rescanned from the scores (the "resend"), giving a
+//                 set U in token order whose k largest keys are the row's top k.
+// The k-th largest key is found two bits at a time over 32-bit words (score bits,
+// then token bits for exact ties), counting with ballots; the result is written by
+// an ordered compaction, ascending, with no sort.
 #include "common.h"
 #include "internal.h"
+#include "topk_send.h"
 
 namespace dsa {
 
 namespace {
 
-constexpr int NT = 256;
-constexpr int PER_T = kTopkChunk / NT;  // 16 tokens per thread per pass
+constexpr int SEL_NT = 1024;
+constexpr int NW = SEL_NT / 64;
+constexpr int PER = 16;  // keys per thread
+static_assert(PER * SEL_NT == kCandRowCap && PER * SEL_NT == kTopkFullRow, "register tiling");
 
 __device__ __forceinline__ int clamp_ctx(const int32_t* row_ctx, int r, int max_ctx) {
   int c = row_ctx[r];
@@ -35,294 +46,428 @@ __device__ __forceinline__ int clamp_ctx(const int32_t* row_ctx, int r, int max_
   return c > max_ctx ? max_ctx : c;
 }
 
-__device__ __forceinline__ uint32_t ld_acquire(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+struct SelShared {
+  uint64_t buf[kCandRowCap];  // U on the resend path
+  union {
+    uint32_t hist[NW * 256];  // whole-row fallback histograms
+    uint32_t sel[kMaxK];      // whole-row fallback selection before its sort
+  };
+  uint32_t red[2][NW][4];     // per-wave partial results, double buffered
+  uint64_t mred[NW];
+  uint32_t scan[NW + 1];
+  uint32_t res[4];
+  uint32_t cnt[2];
+};
+
+__device__ __forceinline__ uint64_t block_min64(uint64_t v, SelShared& S) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_min_u64(v);
+  __syncthreads();
+  if (lane == 0) S.mred[wid] = v;
+  __syncthreads();
+  uint64_t t = ~0ull;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t = S.mred[w] < t ? S.mred[w] : t;
+  return t;
 }
 
-// Returns true in every thread of the workgroup that arrives last for this row.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (prev == expected - 1) ? 1 : 0;
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  uint32_t o;
+  o = xshfl<1>(v); v = o < v ? o : v;
+  o = xshfl<2>(v); v = o < v ? o : v;
+  o = xshfl<4>(v); v = o < v ? o : v;
+  o = xshfl<8>(v); v = o < v ? o : v;
+  o = xshfl<16>(v); v = o < v ? o : v;
+  o = xshfl<32>(v); v = o < v ? o : v;
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t o;
+  o = xshfl<1>(v); v = o > v ? o : v;
+  o = xshfl<2>(v); v = o > v ? o : v;
+  o = xshfl<4>(v); v = o > v ? o : v;
+  o = xshfl<8>(v); v = o > v ? o : v;
+  o = xshfl<16>(v); v = o > v ? o : v;
+  o = xshfl<32>(v); v = o > v ? o : v;
+  return v;
+}
+
+// need-th largest (1 <= need <= number of valid keys) of the nonzero 64-bit keys e[].
+// Resolves the 32-bit score word, then (only if scores tie at the threshold) the
+// token word, 8 bits per pass with one LDS histogram per wave; the leading bits all
+// live words share are skipped, and a pass ends the search once every key left in
+// the current bucket is selected.
+__device__ uint64_t select_kth(const uint64_t (&e)[PER], uint32_t need, SelShared& S) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int parity = 0;
+  uint32_t wv[PER];
+  bool live[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    wv[i] = (uint32_t)(e[i] >> 32);
+    live[i] = e[i] != 0;
   }
+  uint32_t* wh = S.hist + wid * 256;
+  for (int word = 0; word < 2; ++word) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0, n = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (live[i]) {
+        lo = wv[i] < lo ? wv[i] : lo;
+        hi = wv[i] > hi ? wv[i] : hi;
+        ++n;
+      }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    n = wave_sum_u32(n);
+    if (lane == 0) { S.red[parity][wid][0] = lo; S.red[parity][wid][1] = hi; S.red[parity][wid][2] = n; }
+    __syncthreads();
+    lo = 0xFFFFFFFFu; hi = 0; n = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      lo = S.red[parity][w][0] < lo ? S.red[parity][w][0] : lo;
+      hi = S.red[parity][w][1] > hi ? S.red[parity][w][1] : hi;
+      n += S.red[parity][w][2];
+    }
+    parity ^= 1;
+    uint32_t bucket = n;
+    bool done = need == bucket;
+    uint32_t prefix = hi, mask = 0xFFFFFFFFu;
+    if (!done && lo != hi) {
+      const int common = __clz(lo ^ hi);
+      mask = common ? (0xFFFFFFFFu << (32 - common)) : 0u;
+      prefix = hi & mask;
+      int top = 31 - common;  // highest unresolved bit
+      while (top >= 0) {
+        const int width = top >= 7 ? 8 : top + 1;
+        const int sh = top + 1 - width;
+        const uint32_t dm = (1u << width) - 1u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wh[lane + 64 * j] = 0u;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (live[i] && (wv[i] & mask) == prefix) atomicAdd(&wh[(wv[i] >> sh) & dm], 1u);
+        __syncthreads();
+        // digit d (thread 255 - d) total, suffix position from the top
+        uint32_t v = 0;
+        if (tid < 256) {
+#pragma unroll
+          for (int w = 0; w < NW; ++w) v += S.hist[w * 256 + 255 - tid];
+        }
+        const uint32_t inc = wave_incl_scan(v);
+        if (wid < 4 && lane == 63) S.red[parity][wid][3] = inc;
+        __syncthreads();
+        if (tid < 256) {
+          uint32_t before = 0;
+          for (int w = 0; w < wid; ++w) before += S.red[parity][w][3];
+          const uint32_t above = before + inc - v;
+          if (above < need && above + v >= need) { S.res[0] = 255u - tid; S.res[1] = above; S.res[2] = v; }
+        }
+        __syncthreads();
+        const uint32_t dig = S.res[0], above = S.res[1], cnt = S.res[2];
+        parity ^= 1;
+        need -= above;
+        prefix |= dig << sh;
+        mask |= dm << sh;
+        bucket = cnt;
+        top = sh - 1;
+        if (need == bucket) { done = true; break; }
+      }
+    }
+    if (done || word == 1) {
+      // the need keys left in the bucket are selected: the threshold is the smallest
+      uint64_t m = ~0ull;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (live[i] && (wv[i] & mask) == prefix && e[i] < m) m = e[i];
+      return block_min64(m, S);
+    }
+    // scores tie at the threshold: continue on the token word of the tied keys
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      live[i] = live[i] && wv[i] == prefix;
+      wv[i] = (uint32_t)e[i];
+    }
+  }
+  return 0;  // not reached
+}
+
+__device__ __forceinline__ int32_t page_slot(const CacheView& cv, const RowMap& rm, int seq, int t) {
+  return (int32_t)(token_block(cv, rm, seq, t) * cv.block_size + (t & (cv.block_size - 1)));
+}
+
+// Writes, in element order (token order), the tokens whose key is >= cstar, then
+// -1 up to k. `slot` holds the page slots of the elements when `prow` is set.
+__device__ void ordered_write(const uint64_t (&e)[PER], const int32_t (&slot)[PER], uint64_t cstar, int k,
+                              int32_t* __restrict__ orow, int32_t* __restrict__ prow, SelShared& S) {
+  uint32_t bits = 0, cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (e[i] != 0 && e[i] >= cstar) { bits |= 1u << i; ++cnt; }
+  uint32_t total;
+  uint32_t off = block_excl_scan<SEL_NT>(cnt, S.scan, &total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if ((bits >> i) & 1u) {
+      if (off < (uint32_t)k) {
+        orow[off] = (int32_t)(0xFFFFFFFFu - (uint32_t)e[i]);
+        if (prow) prow[off] = slot[i];
+      }
+      ++off;
+    }
+  }
+  for (int i = (int)total + threadIdx.x; i < k; i += SEL_NT) {
+    orow[i] = -1;
+    if (prow) prow[i] = -1;
+  }
+}
+
+// Exact selection over the whole row straight from global memory (8-bit digits,
+// per-wave LDS histograms), then a sort of the k tokens. Only reached when a
+// resend set outgrows LDS (e.g. scores tied across far more than k tokens).
+__device__ void select_row_global(const float* __restrict__ srow, int ctx, int k, SelShared& S,
+                                  int32_t* __restrict__ orow, int32_t* __restrict__ prow, const CacheView& cv,
+                                  const RowMap& rm, int seq) {
+  const int tid = threadIdx.x, wid = tid >> 6;
+  uint64_t prefix = 0, mask = 0;
+  uint32_t need = (uint32_t)k;
+  for (int sh = 56; sh >= 0; sh -= 8) {
+    for (int i = tid; i < NW * 256; i += SEL_NT) S.hist[i] = 0u;
+    __syncthreads();
+    for (int t = tid; t < ctx; t += SEL_NT) {
+      const uint64_t c = composite_key(srow[t], t);
+      if ((c & mask) == prefix) atomicAdd(&S.hist[wid * 256 + ((c >> sh) & 0xFF)], 1u);
+    }
+    __syncthreads();
+    uint32_t v = 0;
+    if (tid < 256)
+      for (int w = 0; w < NW; ++w) v += S.hist[w * 256 + tid];
+    __syncthreads();
+    if (tid < 256) S.hist[tid] = v;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t above = 0;
+      for (int d = 255; d >= 0; --d) {
+        const uint32_t x = S.hist[d];
+        if (above + x >= need) { S.res[0] = (uint32_t)d; S.res[1] = above; break; }
+        above += x;
+      }
+    }
+    __syncthreads();
+    const uint32_t dig = S.res[0], above = S.res[1];
+    __syncthreads();
+    need -= above;
+    prefix |= (uint64_t)dig << sh;
+    mask |= 0xFFull << sh;
+  }
+  if (tid == 0) S.cnt[0] = 0;
   __syncthreads();
-  bool last = *flag != 0;
-  if (last) __threadfence();
-  return last;
+  for (int t = tid; t < ctx; t += SEL_NT)
+    if (composite_key(srow[t], t) >= prefix) {
+      const uint32_t pos = atomicAdd(&S.cnt[0], 1u);
+      if (pos < (uint32_t)kMaxK) S.sel[pos] = (uint32_t)t;
+    }
+  __syncthreads();
+  int P = 1;
+  while (P < k) P <<= 1;
+  for (int i = k + tid; i < P; i += SEL_NT) S.sel[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += SEL_NT) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint32_t a = S.sel[i], b = S.sel[p];
+          if ((a > b) == ((i & kk) == 0)) { S.sel[i] = b; S.sel[p] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += SEL_NT) {
+    const int t = (int)S.sel[i];
+    orow[i] = t;
+    if (prow) prow[i] = page_slot(cv, rm, seq, t);
+  }
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(NT) void topk_clear_kernel(uint32_t* p, size_t words) {
-  for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < words; i += (size_t)gridDim.x * NT) p[i] = 0u;
-}
-
-__global__ __launch_bounds__(NT) void topk_hist_kernel(const float* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ row_ctx, int max_ctx, int k,
-                                                       TopkWs ws) {
-  const int r = blockIdx.y, ch = blockIdx.x;
+// Stage 1 over an existing score array (the standalone top-k entry point).
+__global__ __launch_bounds__(256) void topk_send_kernel(const float* __restrict__ scores, int64_t ld,
+                                                        const int32_t* __restrict__ row_ctx, int max_ctx,
+                                                        TopkWs ws) {
+  const int r = blockIdx.y;
   const int ctx = clamp_ctx(row_ctx, r, max_ctx);
-  if (ctx <= k) return;
-  const int nchr = (ctx + kTopkChunk - 1) / kTopkChunk;
-  if (ch >= nchr) return;
-
-  __shared__ uint32_t lh[kTopkBins];
-  __shared__ uint32_t tmp[NT / 64 + 1];
-  __shared__ int flag;
-  for (int b = threadIdx.x; b < kTopkBins; b += NT) lh[b] = 0u;
-  __syncthreads();
-  const float* srow = scores + (int64_t)r * ld;
-#pragma unroll 4
-  for (int i = 0; i < PER_T; ++i) {
-    int t = ch * kTopkChunk + i * NT + threadIdx.x;
-    if (t < ctx) atomicAdd(&lh[float_key(srow[t]) >> 20], 1u);
-  }
-  __syncthreads();
-  uint32_t* gh = ws.hist + (int64_t)r * kTopkBins;
-  for (int b = threadIdx.x; b < kTopkBins; b += NT) {
-    uint32_t c = lh[b];
-    if (c) atomicAdd(&gh[b], c);
-  }
-  uint32_t* ctrl = ws.ctrl + (int64_t)r * kTopkCtrl;
-  if (!arrive_last(&ctrl[CT_DONE1], (uint32_t)nchr, &flag)) return;
-
-  // Thread i owns bins [16*(255-i), 16*(255-i)+16): exclusive scan = count above its segment.
-  const int seg = NT - 1 - threadIdx.x;
-  uint32_t c[16];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    c[j] = ld_acquire(&gh[seg * 16 + j]);
-    sum += c[j];
-  }
-  uint32_t total;
-  uint32_t above = block_excl_scan<NT>(sum, tmp, &total);
-  if (above < (uint32_t)k && above + sum >= (uint32_t)k) {
-#pragma unroll
-    for (int j = 15; j >= 0; --j) {
-      if (above + c[j] >= (uint32_t)k) {
-        ctrl[CT_B1] = (uint32_t)(seg * 16 + j);
-        ctrl[CT_NEED1] = (uint32_t)k - above;
-        ctrl[CT_NEQ] = c[j];
-        break;
-      }
-      above += c[j];
-    }
-  }
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int base = unit * kCandUnit;
+  if (base >= ctx || cand_per_unit(ctx) == 0) return;  // wave-uniform
+  const int t = base + (threadIdx.x & 63);
+  const bool valid = t < ctx;
+  const float s = valid ? scores[(int64_t)r * ld + t] : 0.f;
+  wave_send_candidates(s, valid, ctx, base, r, unit, ws);
 }
 
-// Resolve c*: the need-th largest composite among elements whose top 12 key bits
-// equal b1. Elements are read from the candidate list when it holds them all,
-// otherwise by rescanning the row's scores.
-__device__ uint64_t refine_threshold(const float* __restrict__ srow, int ctx, const uint32_t* __restrict__ cand,
-                                     bool use_cand, uint32_t n_src, uint32_t b1, uint32_t need,
-                                     uint32_t* dh /*256*/, uint32_t* tmp, uint64_t* s_min, uint32_t* s_res) {
-  uint64_t prefix = (uint64_t)b1 << 52;
-  uint64_t mask = 0xFFFull << 52;
-  const int shifts[7] = {44, 36, 28, 20, 12, 4, 0};
-  const int widths[7] = {8, 8, 8, 8, 8, 8, 4};
-  for (int p = 0; p < 7; ++p) {
-    const int sh = shifts[p];
-    const uint64_t dm = (1ull << widths[p]) - 1;
-    dh[threadIdx.x] = 0u;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n_src; i += NT) {
-      int t = use_cand ? (int)cand[i] : (int)i;
-      if (t >= ctx) continue;
-      uint64_t cc = composite_key(srow[t], t);
-      if ((cc & mask) == prefix) atomicAdd(&dh[(cc >> sh) & dm], 1u);
-    }
-    __syncthreads();
-    const int d = NT - 1 - threadIdx.x;
-    uint32_t v = dh[d];
-    uint32_t tot;
-    uint32_t above = block_excl_scan<NT>(v, tmp, &tot);
-    if (above < need && above + v >= need) {
-      s_res[0] = (uint32_t)d;
-      s_res[1] = above;
-      s_res[2] = v;
-    }
-    __syncthreads();
-    const uint32_t dig = s_res[0], ab = s_res[1], cnt = s_res[2];
-    __syncthreads();
-    need -= ab;
-    prefix |= (uint64_t)dig << sh;
-    mask |= dm << sh;
-    if (need == cnt) {
-      // every remaining match is selected: c* is the smallest of them
-      if (threadIdx.x == 0) *s_min = ~0ull;
-      __syncthreads();
-      for (uint32_t i = threadIdx.x; i < n_src; i += NT) {
-        int t = use_cand ? (int)cand[i] : (int)i;
-        if (t >= ctx) continue;
-        uint64_t cc = composite_key(srow[t], t);
-        if ((cc & mask) == prefix) atomicMin(reinterpret_cast<unsigned long long*>(s_min), (unsigned long long)cc);
-      }
-      __syncthreads();
-      uint64_t m = *s_min;
-      __syncthreads();
-      return m;
-    }
-  }
-  return prefix;
-}
-
-__global__ __launch_bounds__(NT) void topk_cand_kernel(const float* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ row_ctx, int max_ctx, int k,
-                                                       TopkWs ws) {
-  const int r = blockIdx.y, ch = blockIdx.x;
+__global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
+                                                             const int32_t* __restrict__ row_ctx, int max_ctx, int k,
+                                                             TopkWs ws, int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ phys, CacheView cv, RowMap rm) {
+  __shared__ SelShared S;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int ctx = clamp_ctx(row_ctx, r, max_ctx);
-  if (ctx <= k) return;
-  const int nchr = (ctx + kTopkChunk - 1) / kTopkChunk;
-  if (ch >= nchr) return;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-
-  __shared__ uint32_t tmp[NT / 64 + 1];
-  __shared__ uint32_t dh[256];
-  __shared__ uint64_t s_min;
-  __shared__ uint32_t s_res[4];
-  __shared__ uint32_t cnt[kMaxCtx / kTopkChunk];
-  __shared__ int flag;
-
-  uint32_t* ctrl = ws.ctrl + (int64_t)r * kTopkCtrl;
-  const uint32_t b1 = ctrl[CT_B1];
-  const float* srow = scores + (int64_t)r * ld;
-  uint32_t* cand = ws.cand + (int64_t)r * kCandCap;
-  uint32_t gt = 0;
-#pragma unroll 4
-  for (int i = 0; i < PER_T; ++i) {
-    int t = ch * kTopkChunk + i * NT + threadIdx.x;
-    bool eq = false;
-    if (t < ctx) {
-      uint32_t bin = float_key(srow[t]) >> 20;
-      gt += bin > b1 ? 1u : 0u;
-      eq = bin == b1;
-    }
-    uint64_t m = __ballot(eq);
-    if (m) {
-      int leader = __ffsll((unsigned long long)m) - 1;
-      uint32_t basep = 0;
-      if (lane == leader) basep = atomicAdd(&ctrl[CT_NCAND], (uint32_t)__popcll(m));
-      basep = __shfl(basep, leader, 64);
-      uint32_t pos = basep + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-      if (eq && pos < (uint32_t)kCandCap) cand[pos] = (uint32_t)t;
-    }
-  }
-  gt = wave_sum(gt);
-  if (lane == 0) tmp[wid] = gt;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t s = 0;
-    for (int i = 0; i < NT / 64; ++i) s += tmp[i];
-    ws.gtc[(int64_t)r * ws.nch + ch] = s;
-  }
-  if (!arrive_last(&ctrl[CT_DONE2], (uint32_t)nchr, &flag)) return;
-
-  const uint32_t n_eq = ctrl[CT_NEQ];
-  const uint32_t need1 = ctrl[CT_NEED1];
-  const bool use_cand = n_eq <= (uint32_t)kCandCap;
-  const uint32_t n_src = use_cand ? n_eq : (uint32_t)ctx;
-  const uint64_t cstar = refine_threshold(srow, ctx, cand, use_cand, n_src, b1, need1, dh, tmp, &s_min, s_res);
-
-  // Per-chunk selected counts -> exclusive offsets.
-  for (int c = threadIdx.x; c < nchr; c += NT) cnt[c] = ws.gtc[(int64_t)r * ws.nch + c];
-  __syncthreads();
-  const uint64_t bin_mask = 0xFFFull << 52, bin_val = (uint64_t)b1 << 52;
-  for (uint32_t i = threadIdx.x; i < n_src; i += NT) {
-    int t = use_cand ? (int)cand[i] : (int)i;
-    if (t >= ctx) continue;
-    uint64_t cc = composite_key(srow[t], t);
-    if ((cc & bin_mask) == bin_val && cc >= cstar) atomicAdd(&cnt[t / kTopkChunk], 1u);
-  }
-  __syncthreads();
-  constexpr int PER = (kMaxCtx / kTopkChunk + NT - 1) / NT;
-  uint32_t loc[PER];
-  uint32_t s = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    int c = threadIdx.x * PER + j;
-    loc[j] = c < nchr ? cnt[c] : 0u;
-    s += loc[j];
-  }
-  uint32_t tot;
-  uint32_t off = block_excl_scan<NT>(s, tmp, &tot);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    int c = threadIdx.x * PER + j;
-    if (c < nchr) ws.base[(int64_t)r * ws.nch + c] = off;
-    off += loc[j];
-  }
-  if (threadIdx.x == 0) {
-    ctrl[CT_CSTAR_HI] = (uint32_t)(cstar >> 32);
-    ctrl[CT_CSTAR_LO] = (uint32_t)cstar;
-  }
-}
-
-__global__ __launch_bounds__(NT) void topk_write_kernel(const float* __restrict__ scores, int64_t ld,
-                                                        const int32_t* __restrict__ row_ctx, int max_ctx, int k,
-                                                        TopkWs ws, int32_t* __restrict__ idx) {
-  const int r = blockIdx.y, ch = blockIdx.x;
-  const int ctx = clamp_ctx(row_ctx, r, max_ctx);
-  const int total = ctx < k ? ctx : k;
   int32_t* orow = idx + (int64_t)r * k;
-  if (ch == 0)
-    for (int j = total + threadIdx.x; j < k; j += NT) orow[j] = -1;
-  const int nchr = (ctx + kTopkChunk - 1) / kTopkChunk;
-  if (ch >= nchr) return;
-  const bool all = ctx <= k;
-  const uint32_t* ctrl = ws.ctrl + (int64_t)r * kTopkCtrl;
-  const uint64_t cstar = all ? 0ull : (((uint64_t)ctrl[CT_CSTAR_HI] << 32) | ctrl[CT_CSTAR_LO]);
-  const uint32_t basech = all ? (uint32_t)(ch * kTopkChunk) : ws.base[(int64_t)r * ws.nch + ch];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int32_t* prow = phys ? phys + (int64_t)r * k : nullptr;
+  const int seq = phys ? rm.row_seq[r] : 0;
   const float* srow = scores + (int64_t)r * ld;
 
-  __shared__ uint32_t wc[PER_T][NT / 64];
-  uint64_t masks[PER_T];
+  if (ctx <= k) {
+    for (int i = tid; i < k; i += SEL_NT) {
+      orow[i] = i < ctx ? i : -1;
+      if (prow) prow[i] = i < ctx ? page_slot(cv, rm, seq, i) : -1;
+    }
+    return;
+  }
+
+  uint64_t e[PER];
+  int32_t slot[PER];
+  if (ctx <= kTopkFullRow) {
+    // ---- the row's own keys: thread owns tokens [16 tid, 16 tid + 16) ----
 #pragma unroll
-  for (int i = 0; i < PER_T; ++i) {
-    int t = ch * kTopkChunk + i * NT + threadIdx.x;
-    bool sel = false;
-    if (t < ctx) sel = all || composite_key(srow[t], t) >= cstar;
-    masks[i] = __ballot(sel);
-    if (lane == 0) wc[i][wid] = (uint32_t)__popcll(masks[i]);
+    for (int i = 0; i < PER; ++i) {
+      const int t = tid * PER + i;
+      e[i] = t < ctx ? composite_key(srow[t], t) : 0ull;
+      slot[i] = (prow && t < ctx) ? page_slot(cv, rm, seq, t) : -1;
+    }
+    const uint64_t cstar = select_kth(e, (uint32_t)k, S);
+    ordered_write(e, slot, cstar, k, orow, prow, S);
+    return;
+  }
+
+  // ---- candidates: thread owns candidates [16 tid, 16 tid + 16), whole units ----
+  const int nu = (ctx + kCandUnit - 1) / kCandUnit;
+  const int m = cand_per_unit(ctx);
+  const int n = nu * m;
+  {
+    const v4i* src = reinterpret_cast<const v4i*>(ws.cand + (int64_t)r * kCandRowCap + tid * PER);
+    v4i raw[PER / 2];
+#pragma unroll
+    for (int q = 0; q < PER / 2; ++q) raw[q] = src[q];
+#pragma unroll
+    for (int q = 0; q < PER / 2; ++q) {
+      e[2 * q] = ((uint64_t)(uint32_t)raw[q][1] << 32) | (uint32_t)raw[q][0];
+      e[2 * q + 1] = ((uint64_t)(uint32_t)raw[q][3] << 32) | (uint32_t)raw[q][2];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (tid * PER + i >= n) e[i] = 0ull;
+    // block-table lookups issued now, consumed after the search
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      slot[i] = (prow && e[i] != 0) ? page_slot(cv, rm, seq, (int)(0xFFFFFFFFu - (uint32_t)e[i])) : -1;
+  }
+  const uint64_t cu = select_kth(e, (uint32_t)k, S);
+
+  // units (whole ones per thread) whose kept-back keys may reach cu
+  const int upt = PER / m;                 // units per thread
+  const int u0 = tid * upt;
+  const uint64_t* rf = ws.floors + (int64_t)r * ws.nunits;
+  uint32_t fmask = 0;
+  for (int j = 0; j < upt; ++j)
+    if (u0 + j < nu && rf[u0 + j] >= cu) fmask |= 1u << j;
+  const uint32_t nflag = wave_sum_u32((uint32_t)__popc(fmask));
+  if (tid % 64 == 0) S.red[0][tid >> 6][3] = nflag;
+  __syncthreads();
+  uint32_t nflag_all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) nflag_all += S.red[0][w][3];
+  if (nflag_all == 0) {
+    ordered_write(e, slot, cu, k, orow, prow, S);
+    return;
+  }
+
+  // ---- resend: U in token order = per unit, (flagged ? its keys >= cu : its candidates >= cu) ----
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0);
+  auto unit_keys = [&](int u, auto&& fn) {
+    // visits the keys of unit u's tokens in token order, 16 at a time
+    const int tb = u * kCandUnit;
+#pragma unroll 1
+    for (int q = 0; q < kCandUnit / 16; ++q) {
+      float f[16];
+      const int t0 = tb + q * 16;
+      if (vec_ok && t0 + 16 <= ctx) {
+        const float4* p4 = reinterpret_cast<const float4*>(srow + t0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float4 v = p4[x];
+          f[4 * x] = v.x; f[4 * x + 1] = v.y; f[4 * x + 2] = v.z; f[4 * x + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) f[x] = (t0 + x < ctx) ? srow[t0 + x] : 0.f;
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x)
+        if (t0 + x < ctx) fn(composite_key(f[x], t0 + x));
+    }
+  };
+  uint32_t cnt = 0;
+  for (int j = 0; j < upt; ++j) {
+    if ((fmask >> j) & 1u) {
+      unit_keys(u0 + j, [&](uint64_t c) { cnt += c >= cu ? 1u : 0u; });
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i / m == j && e[i] != 0 && e[i] >= cu) ++cnt;
+    }
+  }
+  uint32_t nuall;
+  uint32_t off = block_excl_scan<SEL_NT>(cnt, S.scan, &nuall);
+  if (nuall > (uint32_t)kCandRowCap) {
+    select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+    return;
+  }
+  for (int j = 0; j < upt; ++j) {
+    if ((fmask >> j) & 1u) {
+      unit_keys(u0 + j, [&](uint64_t c) { if (c >= cu) S.buf[off++] = c; });
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i / m == j && e[i] != 0 && e[i] >= cu) S.buf[off++] = e[i];
+    }
   }
   __syncthreads();
-  const uint64_t lt = (1ull << lane) - 1ull;
-  uint32_t run = basech;
+  uint64_t u[PER];
+  int32_t uslot[PER];
 #pragma unroll
-  for (int i = 0; i < PER_T; ++i) {
-    uint32_t off = run, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-      uint32_t x = wc[i][w];
-      off += w < wid ? x : 0u;
-      tot += x;
-    }
-    if ((masks[i] >> lane) & 1ull) {
-      uint32_t pos = off + (uint32_t)__popcll(masks[i] & lt);
-      if (pos < (uint32_t)k) orow[pos] = ch * kTopkChunk + i * NT + threadIdx.x;
-    }
-    run += tot;
+  for (int i = 0; i < PER; ++i) {
+    u[i] = (uint32_t)(tid * PER + i) < nuall ? S.buf[tid * PER + i] : 0ull;
+    uslot[i] = (prow && u[i] != 0) ? page_slot(cv, rm, seq, (int)(0xFFFFFFFFu - (uint32_t)u[i])) : -1;
   }
+  const uint64_t cstar = select_kth(u, (uint32_t)k, S);
+  ordered_write(u, uslot, cstar, k, orow, prow, S);
 }
 
-hipError_t launch_clear(uint32_t* p, size_t words, hipStream_t stream) {
-  if (words == 0) return hipSuccess;
-  size_t blocks = (words + NT - 1) / NT;
-  if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(topk_clear_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, p, words);
+hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx,
+                            const TopkWs& ws, hipStream_t stream) {
+  if (R <= 0 || max_ctx <= kTopkFullRow) return hipSuccess;
+  dim3 grid((cand_units(max_ctx) + 3) / 4, R);
+  hipLaunchKernelGGL(topk_send_kernel, grid, dim3(256), 0, stream, scores, ld, row_ctx, max_ctx, ws);
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
-                       int32_t* idx, const TopkWs& ws, hipStream_t stream) {
+hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
+                              int32_t* idx, const TopkWs& ws, int32_t* phys, float* pscale, const CacheView* cv,
+                              const RowMap* rm, hipStream_t stream) {
+  (void)pscale;
   if (R <= 0) return hipSuccess;
-  dim3 grid(ws.nch, R);
-  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws);
-  hipLaunchKernelGGL(topk_cand_kernel, grid, dim3(NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws);
-  hipLaunchKernelGGL(topk_write_kernel, grid, dim3(NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws, idx);
+  CacheView c{};
+  RowMap m{};
+  if (phys) {
+    c = *cv;
+    m = *rm;
+  }
+  hipLaunchKernelGGL(topk_select_kernel, dim3(R), dim3(SEL_NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws, idx,
+                     phys, c, m);
   return hipGetLastError();
 }
 

@@ -256,3 +256,32 @@ def test_out_of_range_block_ids_do_not_fault(dev):
                  c.sm_scale)
     scores, idx, out, lse = run_step(c2, dev)
     assert np.all(np.isfinite(scores[0, :3000])) and np.all(np.isfinite(out))
+
+
+def test_select_paths_mixed_batch(dev):
+    """One batch whose rows take every selection path: ctx <= k, whole row in LDS
+    (<= 16384), and block candidates with rescans (> 16384)."""
+    say("case: select paths mixed batch")
+    c = make_case([1500, 3000, 16384, 16385, 20000, 33000, 70000], block_size=64, seed=44, k=2048)
+    full_check(c, dev)
+
+
+def test_workspace_reuse_across_inputs(dev):
+    """The workspace carries nothing from one call to the next."""
+    say("case: workspace reuse")
+    a = make_case([50000, 9000], block_size=64, seed=51, k=2048).to(dev)
+    b = make_case([70000, 30000], block_size=64, seed=52, k=2048).to(dev)
+    ws = torch.empty(dsa.dsa_workspace_bytes(dsa.DSA_OP_DECODE_STEP, 2, 70000, 2048), dtype=torch.uint8, device=dev)
+    ws.fill_(0xA5)
+
+    def go(c, w):
+        idx, out, lse, _ = dsa.dsa_decode_step(c.pool, c.layout, 0, c.q_idx[0], c.q_idx_scale[0], c.w[0], c.q_lat[0],
+                                               c.block_table, c.row_seq, c.row_ctx, c.max_ctx, 2048, c.sm_scale,
+                                               workspace=w)
+        torch.cuda.synchronize()
+        return idx.cpu().numpy(), out.cpu().numpy()
+
+    go(a, ws)
+    i1, o1 = go(b, ws)
+    i2, o2 = go(b, None)
+    assert np.array_equal(i1, i2) and np.array_equal(o1, o2)
