@@ -11,32 +11,31 @@ namespace dsa {
 
 // ---- top-k workspace -------------------------------------------------------------
 constexpr int kTopkFullRow = 16384;   // rows up to this length are selected from all their scores
-constexpr int kCandUnit = 64;         // tokens per candidate-sending unit (one indexer wave)
-constexpr int kCandRowCap = 16384;    // candidates a row sends in total (select stage registers)
-constexpr int kCandPerUnitMax = 16;   // candidates a unit sends, at most
-constexpr int kMaxCtx = 1 << 20;      // largest supported context (16384 units x >= 1 candidate)
+constexpr int kCandRowCap = 16384;    // candidate keys a row sends in total (select stage registers)
+constexpr int kCandPerUnitMax = 16;   // candidate keys a unit sends, at most
+constexpr int kMaxCtx = 1 << 20;      // largest supported context
+constexpr int kFloorRowCap = kMaxCtx / 256;  // units of a row, at most
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-inline int cand_units(int max_ctx) { int c = (max_ctx + kCandUnit - 1) / kCandUnit; return c < 1 ? 1 : c; }
 
 struct TopkWs {
-  uint64_t* cand;    // [R][kCandRowCap] keys sent by the row's units (unit u at u*m .. u*m+m)
-  uint64_t* floors;  // [R][nunits] upper bound of the keys a unit did not send (0: sent all)
-  int nunits;
+  uint64_t* cand;    // [R][kCandRowCap]: key of rank q of unit u at q * nu + u
+  uint32_t* floors;  // [R][kFloorRowCap]: score word bounding the keys a unit did not send (0: sent all)
 };
 
+// Rows of at most kTopkFullRow tokens send no candidates: no candidate space then.
 inline size_t topk_ws_bytes(int R, int max_ctx) {
-  const size_t nu = (size_t)cand_units(max_ctx);
-  return align_up((size_t)R * kCandRowCap * 8, 256) + align_up((size_t)R * nu * 8, 256);
+  if (max_ctx <= kTopkFullRow) return 256;
+  return align_up((size_t)R * kCandRowCap * 8, 256) + align_up((size_t)R * kFloorRowCap * 4, 256);
 }
 
 inline TopkWs topk_ws_carve(void* ws, int R, int max_ctx) {
   TopkWs t;
+  if (max_ctx <= kTopkFullRow) return TopkWs{nullptr, nullptr};
   uint8_t* p = static_cast<uint8_t*>(ws);
-  t.nunits = cand_units(max_ctx);
   t.cand = reinterpret_cast<uint64_t*>(p);
   p += align_up((size_t)R * kCandRowCap * 8, 256);
-  t.floors = reinterpret_cast<uint64_t*>(p);
+  t.floors = reinterpret_cast<uint32_t*>(p);
   return t;
 }
 

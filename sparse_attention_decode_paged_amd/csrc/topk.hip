@@ -15,18 +15,25 @@
 // real token and marks an empty slot.
 //
 // Stage 1 (topk_send.h: the indexer epilogue or topk_send_kernel): every unit
-// sends its m best keys in token order plus a floor bounding the keys it kept.
+// sends its m best keys plus a floor bounding the keys it kept.
 // Stage 2 (topk_select_kernel, one 1024-thread workgroup per row). Every thread
-// holds 16 keys in registers, a contiguous run in token order:
+// holds up to 16 keys in registers:
 //   ctx <= k      every token;
-//   ctx <= 16384  the row's own keys;
-//   otherwise     the candidates (whole units per thread); c_u = their k-th
-//                 largest key; a unit whose floor reaches c_u may hold unsent keys
-//                 >= c_u and is rescanned from the scores (the "resend"), giving a
-//                 set U in token order whose k largest keys are the row's top k.
-// The k-th largest key is found two bits at a time over 32-bit words (score bits,
-// then token bits for exact ties), counting with ballots; the result is written by
-// an ordered compaction, ascending, with no sort.
+//   ctx <= 16384  the row's own keys, tokens [16 t, 16 t + 16) on thread t;
+//   otherwise     the candidates of units t + 1024 j (j < units per thread), read
+//                 rank-major so that each load instruction covers 64 consecutive
+//                 units. c_u = their k-th largest key. A unit whose floor reaches
+//                 c_u may hold unsent keys >= c_u: waves rescan such units' scores
+//                 (the "resend") into a compact LDS list, the unit's candidates leave
+//                 the register set, and the k-th largest of the union is the answer.
+// The k-th largest key: the score words of the live keys share their bits above
+// the highest bit in which they differ; an 11-bit digit histogram over the next
+// bits (8 copies, lane l adding into copy l % 8, so at most 8 lanes of one
+// instruction hit one LDS word) fixes the bucket of the k-th key. A bucket of at
+// most 64 keys is gathered into LDS and one wave sorts it (64-bit keys, so equal
+// scores order by token); a larger one takes another pass over lower bits. The
+// selection is written in token order: per-unit counts, one block prefix sum over
+// units, then each thread writes its units' selected keys.
 #include "common.h"
 #include "internal.h"
 #include "topk_send.h"
@@ -37,8 +44,15 @@ namespace {
 
 constexpr int SEL_NT = 1024;
 constexpr int NW = SEL_NT / 64;
-constexpr int PER = 16;  // keys per thread
+constexpr int PER = 16;              // keys per thread
+constexpr int HBITS = 11;            // digit width of one histogram pass
+constexpr int NBIN = 1 << HBITS;     // two bins per thread
+constexpr int NREP = 8;              // histogram copies
+constexpr int XPER = 8;              // rescanned keys per thread
+constexpr int ECAP = XPER * SEL_NT;  // rescanned keys a row may hold in LDS
+constexpr int FCAP = 512;            // rescanned units a row may hold in LDS
 static_assert(PER * SEL_NT == kCandRowCap && PER * SEL_NT == kTopkFullRow, "register tiling");
+static_assert(NBIN == 2 * SEL_NT, "two histogram bins per thread");
 
 __device__ __forceinline__ int clamp_ctx(const int32_t* row_ctx, int r, int max_ctx) {
   int c = row_ctx[r];
@@ -47,171 +61,325 @@ __device__ __forceinline__ int clamp_ctx(const int32_t* row_ctx, int r, int max_
 }
 
 struct SelShared {
-  uint64_t buf[kCandRowCap];  // U on the resend path
   union {
-    uint32_t hist[NW * 256];  // whole-row fallback histograms
-    uint32_t sel[kMaxK];      // whole-row fallback selection before its sort
+    struct {
+      uint32_t hist[NBIN * NREP];  // bin b, copy c at b * NREP + c
+      uint64_t ext[ECAP];          // keys >= c_u of the rescanned units, one segment per unit
+    } a;
+    struct {
+      uint32_t hist[NW * 256];  // whole-row fallback: per-wave 8-bit histograms
+      uint32_t sel[kMaxK];      // whole-row fallback: selection before its sort
+    } g;
   };
-  uint32_t red[2][NW][4];     // per-wave partial results, double buffered
-  uint64_t mred[NW];
-  uint32_t scan[NW + 1];
+  uint32_t funit[FCAP];   // rescanned unit of each slot, in unit order
+  uint32_t fstart[FCAP];  // its segment in ext
+  uint32_t flen[FCAP];
+  uint32_t fcnt[FCAP];    // selected keys of the segment
+  uint32_t foff[FCAP];    // their first output position
+  uint64_t bucket[64];    // keys of the last histogram bucket
+  uint64_t res64;
+  uint32_t r32[2][2][NW];  // block min / max partials, double buffered
+  uint32_t scan[2][NW];    // block prefix partials, double buffered
+  uint32_t scan4[NW][4];   // per-wave totals of four prefix sums
   uint32_t res[4];
-  uint32_t cnt[2];
+  uint32_t ecount, bcount;
 };
 
-__device__ __forceinline__ uint64_t block_min64(uint64_t v, SelShared& S) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  v = wave_min_u64(v);
-  __syncthreads();
-  if (lane == 0) S.mred[wid] = v;
-  __syncthreads();
-  uint64_t t = ~0ull;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) t = S.mred[w] < t ? S.mred[w] : t;
-  return t;
-}
-
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  uint32_t o;
-  o = xshfl<1>(v); v = o < v ? o : v;
-  o = xshfl<2>(v); v = o < v ? o : v;
-  o = xshfl<4>(v); v = o < v ? o : v;
-  o = xshfl<8>(v); v = o < v ? o : v;
-  o = xshfl<16>(v); v = o < v ? o : v;
-  o = xshfl<32>(v); v = o < v ? o : v;
+  v = min(v, xshfl<1>(v));
+  v = min(v, xshfl<2>(v));
+  v = min(v, xshfl<4>(v));
+  v = min(v, xshfl<8>(v));
+  v = min(v, xshfl<16>(v));
+  v = min(v, xshfl<32>(v));
   return v;
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  uint32_t o;
-  o = xshfl<1>(v); v = o > v ? o : v;
-  o = xshfl<2>(v); v = o > v ? o : v;
-  o = xshfl<4>(v); v = o > v ? o : v;
-  o = xshfl<8>(v); v = o > v ? o : v;
-  o = xshfl<16>(v); v = o > v ? o : v;
-  o = xshfl<32>(v); v = o > v ? o : v;
+  v = max(v, xshfl<1>(v));
+  v = max(v, xshfl<2>(v));
+  v = max(v, xshfl<4>(v));
+  v = max(v, xshfl<8>(v));
+  v = max(v, xshfl<16>(v));
+  v = max(v, xshfl<32>(v));
   return v;
 }
 
-// need-th largest (1 <= need <= number of valid keys) of the nonzero 64-bit keys e[].
-// Resolves the 32-bit score word, then (only if scores tie at the threshold) the
-// token word, 8 bits per pass with one LDS histogram per wave; the leading bits all
-// live words share are skipped, and a pass ends the search once every key left in
-// the current bucket is selected.
-__device__ uint64_t select_kth(const uint64_t (&e)[PER], uint32_t need, SelShared& S) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int parity = 0;
-  uint32_t wv[PER];
-  bool live[PER];
+// Exclusive prefix sum over the threads in thread order; `total` gets the sum.
+__device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t& total, SelShared& S, int& par) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) S.scan[par][wid] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    wv[i] = (uint32_t)(e[i] >> 32);
-    live[i] = e[i] != 0;
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = S.scan[par][w];
+    before += w < wid ? x : 0u;
+    tot += x;
   }
-  uint32_t* wh = S.hist + wid * 256;
-  for (int word = 0; word < 2; ++word) {
-    uint32_t lo = 0xFFFFFFFFu, hi = 0, n = 0;
+  par ^= 1;
+  total = tot;
+  return before + inc - v;
+}
+
+// Four exclusive prefix sums over the threads at once (one barrier). The caller
+// keeps a barrier between two calls.
+__device__ __forceinline__ void excl_scan4(const uint32_t (&v)[4], uint32_t (&off)[4], uint32_t (&total)[4], int nj,
+                                           SelShared& S) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t inc[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (live[i]) {
-        lo = wv[i] < lo ? wv[i] : lo;
-        hi = wv[i] > hi ? wv[i] : hi;
-        ++n;
-      }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    n = wave_sum_u32(n);
-    if (lane == 0) { S.red[parity][wid][0] = lo; S.red[parity][wid][1] = hi; S.red[parity][wid][2] = n; }
-    __syncthreads();
-    lo = 0xFFFFFFFFu; hi = 0; n = 0;
+  for (int j = 0; j < 4; ++j) {
+    if (j < nj) inc[j] = wave_incl_scan(v[j]);  // nj is block-uniform
+    if (lane == 63) S.scan4[wid][j] = inc[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      lo = S.red[parity][w][0] < lo ? S.red[parity][w][0] : lo;
-      hi = S.red[parity][w][1] > hi ? S.red[parity][w][1] : hi;
-      n += S.red[parity][w][2];
+      const uint32_t x = S.scan4[w][j];
+      before += w < wid ? x : 0u;
+      tot += x;
     }
-    parity ^= 1;
-    uint32_t bucket = n;
-    bool done = need == bucket;
-    uint32_t prefix = hi, mask = 0xFFFFFFFFu;
-    if (!done && lo != hi) {
-      const int common = __clz(lo ^ hi);
-      mask = common ? (0xFFFFFFFFu << (32 - common)) : 0u;
-      prefix = hi & mask;
-      int top = 31 - common;  // highest unresolved bit
-      while (top >= 0) {
-        const int width = top >= 7 ? 8 : top + 1;
-        const int sh = top + 1 - width;
-        const uint32_t dm = (1u << width) - 1u;
+    off[j] = before + inc[j] - v[j];
+    total[j] = tot;
+  }
+}
+
+// Block-wide min and max of 32-bit values.
+__device__ __forceinline__ void block_minmax32(uint32_t& lo, uint32_t& hi, SelShared& S, int& par) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    S.r32[par][0][wid] = lo;
+    S.r32[par][1][wid] = hi;
+  }
+  __syncthreads();
+  lo = 0xFFFFFFFFu;
+  hi = 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wh[lane + 64 * j] = 0u;
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, S.r32[par][0][w]);
+    hi = max(hi, S.r32[par][1][w]);
+  }
+  par ^= 1;
+}
+
+// Sorts up to 64 keys (one per lane, 0 = empty) in descending order across the wave.
+__device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-          if (live[i] && (wv[i] & mask) == prefix) atomicAdd(&wh[(wv[i] >> sh) & dm], 1u);
-        __syncthreads();
-        // digit d (thread 255 - d) total, suffix position from the top
-        uint32_t v = 0;
-        if (tid < 256) {
+  for (int kk = 2; kk <= 64; kk <<= 1) {
 #pragma unroll
-          for (int w = 0; w < NW; ++w) v += S.hist[w * 256 + 255 - tid];
-        }
-        const uint32_t inc = wave_incl_scan(v);
-        if (wid < 4 && lane == 63) S.red[parity][wid][3] = inc;
-        __syncthreads();
-        if (tid < 256) {
-          uint32_t before = 0;
-          for (int w = 0; w < wid; ++w) before += S.red[parity][w][3];
-          const uint32_t above = before + inc - v;
-          if (above < need && above + v >= need) { S.res[0] = 255u - tid; S.res[1] = above; S.res[2] = v; }
-        }
-        __syncthreads();
-        const uint32_t dig = S.res[0], above = S.res[1], cnt = S.res[2];
-        parity ^= 1;
-        need -= above;
-        prefix |= dig << sh;
-        mask |= dm << sh;
-        bucket = cnt;
-        top = sh - 1;
-        if (need == bucket) { done = true; break; }
-      }
-    }
-    if (done || word == 1) {
-      // the need keys left in the bucket are selected: the threshold is the smallest
-      uint64_t m = ~0ull;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (live[i] && (wv[i] & mask) == prefix && e[i] < m) m = e[i];
-      return block_min64(m, S);
-    }
-    // scores tie at the threshold: continue on the token word of the tied keys
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      live[i] = live[i] && wv[i] == prefix;
-      wv[i] = (uint32_t)e[i];
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      uint64_t o;
+      if (j == 32) o = xshfl64<32>(v);
+      else if (j == 16) o = xshfl64<16>(v);
+      else if (j == 8) o = xshfl64<8>(v);
+      else if (j == 4) o = xshfl64<4>(v);
+      else if (j == 2) o = xshfl64<2>(v);
+      else o = xshfl64<1>(v);
+      const bool take_max = ((lane & kk) == 0) == ((lane & j) == 0);
+      v = take_max ? (v > o ? v : o) : (v < o ? v : o);
     }
   }
-  return 0;  // not reached
+  return v;
+}
+
+// The need-th largest (1 <= need <= number of live keys) of the nonzero keys in
+// e[] and, with EXTRA, in xs[0, nx) (LDS, thread t reading xs[t + SEL_NT j]), held
+// across the workgroup. Keys are distinct.
+__device__ __forceinline__ void clear_hist(SelShared& S) {
+  v4i* hz = reinterpret_cast<v4i*>(S.a.hist) + threadIdx.x * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) hz[q] = v4i{0, 0, 0, 0};
+}
+
+template <int N, bool EXTRA>
+__device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const uint64_t* xs, uint32_t nx, uint32_t need,
+                                SelShared& S, int& par) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  auto key = [&](int i) -> uint64_t {
+    if (i < N) return e[i];
+    const uint32_t p = (uint32_t)tid + (uint32_t)(i - N) * SEL_NT;
+    return p < nx ? xs[p] : 0ull;
+  };
+  constexpr int NK = N + (EXTRA ? XPER : 0);
+  clear_hist(S);  // ordered before the first pass by the min / max barrier
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const uint64_t v = key(i);
+    const uint32_t w = (uint32_t)(v >> 32);
+    if (v != 0ull) {
+      lo = min(lo, w);
+      hi = max(hi, w);
+    }
+  }
+  block_minmax32(lo, hi, S, par);
+  // score-word bits fixed so far: (w & mask) == prefix
+  // bits above `top` are common to every live score word; (w & mask) == prefix
+  // selects the keys still in play. 64-bit shifts keep every shift count defined.
+  int top = -1;  // -1: every live key has the same score word
+  if (lo != hi) top = 31 - __clz(lo ^ hi);
+  uint32_t mask = (uint32_t)(~0ull << (top + 1));
+  uint32_t prefix = hi & mask;
+  uint32_t cnt = 0;
+  bool first = true;
+  while (top >= 0) {
+    const int width = top + 1 < HBITS ? top + 1 : HBITS;
+    const int sh = top + 1 - width;
+    const uint32_t dm = (1u << width) - 1u;
+    if (!first) {
+      clear_hist(S);
+      __syncthreads();
+    }
+    first = false;
+    const uint32_t rep = (uint32_t)tid & (NREP - 1);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const uint64_t v = key(i);
+      const uint32_t w = (uint32_t)(v >> 32);
+      if (v != 0ull && (w & mask) == prefix) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
+    }
+    __syncthreads();
+    // thread t holds bins NBIN-1-2t (upper) and NBIN-2-2t: thread order = descending digits
+    uint32_t h0, h1;
+    {
+      const v4i* hb = reinterpret_cast<const v4i*>(S.a.hist) + (NBIN - 2 - 2 * tid) * (NREP / 4);
+      const v4i a0 = hb[0], a1 = hb[1], b0 = hb[2], b1 = hb[3];
+      h1 = (uint32_t)(a0[0] + a0[1] + a0[2] + a0[3] + a1[0] + a1[1] + a1[2] + a1[3]);
+      h0 = (uint32_t)(b0[0] + b0[1] + b0[2] + b0[3] + b1[0] + b1[1] + b1[2] + b1[3]);
+    }
+    uint32_t tot;
+    const uint32_t above = excl_scan(h0 + h1, tot, S, par);
+    if (above < need && above + h0 + h1 >= need) {
+      if (above + h0 >= need) {
+        S.res[0] = NBIN - 1 - 2 * tid;
+        S.res[1] = above;
+        S.res[2] = h0;
+      } else {
+        S.res[0] = NBIN - 2 - 2 * tid;
+        S.res[1] = above + h0;
+        S.res[2] = h1;
+      }
+    }
+    __syncthreads();
+    const uint32_t d = S.res[0], ab = S.res[1];
+    cnt = S.res[2];
+    need -= ab;
+    prefix |= d << sh;
+    mask |= dm << sh;
+    top = sh - 1;
+    if (cnt <= 64u) break;
+  }
+  // the bucket: live keys whose score word matches; need-th largest among them
+  if (top < 0 && cnt == 0u) {
+    // no pass ran (one score word): count the bucket
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) c += key(i) != 0ull ? 1u : 0u;
+    uint32_t unused;
+    excl_scan(c, unused, S, par);
+    cnt = unused;
+  }
+  if (cnt <= 64u) {
+    if (tid == 0) S.bcount = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const uint64_t v = key(i);
+      if (v != 0ull && ((uint32_t)(v >> 32) & mask) == prefix) S.bucket[atomicAdd(&S.bcount, 1u) & 63u] = v;
+    }
+    __syncthreads();
+    if (wid == 0) {
+      const uint64_t v = (uint32_t)lane < cnt ? S.bucket[lane] : 0ull;
+      if (need == cnt) {
+        // every bucket key is selected: the threshold is the smallest
+        const uint64_t mn = wave_min_u64((uint32_t)lane < cnt ? v : ~0ull);
+        if (lane == 0) S.res64 = mn;
+      } else {
+        const uint64_t sorted = wave_sort_desc_u64(v);
+        if (lane == (int)need - 1) S.res64 = sorted;
+      }
+    }
+    __syncthreads();
+    return S.res64;
+  }
+  // more than 64 keys share the whole score word: resolve the token bits by radix
+  uint32_t lmask = 0u, lprefix = 0u;
+  for (int sh = 32 - HBITS; sh > -HBITS; sh -= HBITS) {
+    const int s0 = sh < 0 ? 0 : sh;
+    const int width = sh < 0 ? HBITS + sh : HBITS;
+    const uint32_t dm = (1u << width) - 1u;
+    clear_hist(S);
+    __syncthreads();
+    const uint32_t rep = (uint32_t)tid & (NREP - 1);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const uint64_t v = key(i);
+      const uint32_t lw = (uint32_t)v;
+      if (v != 0ull && ((uint32_t)(v >> 32) & mask) == prefix && (lw & lmask) == lprefix)
+        atomicAdd(&S.a.hist[((lw >> s0) & dm) * NREP + rep], 1u);
+    }
+    __syncthreads();
+    uint32_t h0, h1;
+    {
+      const v4i* hb = reinterpret_cast<const v4i*>(S.a.hist) + (NBIN - 2 - 2 * tid) * (NREP / 4);
+      const v4i a0 = hb[0], a1 = hb[1], b0 = hb[2], b1 = hb[3];
+      h1 = (uint32_t)(a0[0] + a0[1] + a0[2] + a0[3] + a1[0] + a1[1] + a1[2] + a1[3]);
+      h0 = (uint32_t)(b0[0] + b0[1] + b0[2] + b0[3] + b1[0] + b1[1] + b1[2] + b1[3]);
+    }
+    uint32_t tot;
+    const uint32_t above = excl_scan(h0 + h1, tot, S, par);
+    if (above < need && above + h0 + h1 >= need) {
+      if (above + h0 >= need) {
+        S.res[0] = NBIN - 1 - 2 * tid;
+        S.res[1] = above;
+      } else {
+        S.res[0] = NBIN - 2 - 2 * tid;
+        S.res[1] = above + h0;
+      }
+    }
+    __syncthreads();
+    need -= S.res[1];
+    lprefix |= S.res[0] << s0;
+    lmask |= dm << s0;
+    __syncthreads();
+  }
+  return ((uint64_t)prefix << 32) | lprefix;
 }
 
 __device__ __forceinline__ int32_t page_slot(const CacheView& cv, const RowMap& rm, int seq, int t) {
   return (int32_t)(token_block(cv, rm, seq, t) * cv.block_size + (t & (cv.block_size - 1)));
 }
 
+__device__ __forceinline__ int key_token(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
+
 // Writes, in element order (token order), the tokens whose key is >= cstar, then
-// -1 up to k. `slot` holds the page slots of the elements when `prow` is set.
-__device__ void ordered_write(const uint64_t (&e)[PER], const int32_t (&slot)[PER], uint64_t cstar, int k,
-                              int32_t* __restrict__ orow, int32_t* __restrict__ prow, SelShared& S) {
+// -1 up to k; with `prow` also their page slots.
+__device__ __forceinline__ void ordered_write(const uint64_t (&e)[PER], uint64_t cstar, int k, int32_t* __restrict__ orow,
+                              int32_t* __restrict__ prow, const CacheView& cv, const RowMap& rm, int seq,
+                              SelShared& S, int& par) {
   uint32_t bits = 0, cnt = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i)
-    if (e[i] != 0 && e[i] >= cstar) { bits |= 1u << i; ++cnt; }
+    if (e[i] != 0ull && e[i] >= cstar) {
+      bits |= 1u << i;
+      ++cnt;
+    }
   uint32_t total;
-  uint32_t off = block_excl_scan<SEL_NT>(cnt, S.scan, &total);
+  uint32_t off = excl_scan(cnt, total, S, par);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if ((bits >> i) & 1u) {
       if (off < (uint32_t)k) {
-        orow[off] = (int32_t)(0xFFFFFFFFu - (uint32_t)e[i]);
-        if (prow) prow[off] = slot[i];
+        const int t = key_token(e[i]);
+        orow[off] = t;
+        if (prow) prow[off] = page_slot(cv, rm, seq, t);
       }
       ++off;
     }
@@ -223,33 +391,38 @@ __device__ void ordered_write(const uint64_t (&e)[PER], const int32_t (&slot)[PE
 }
 
 // Exact selection over the whole row straight from global memory (8-bit digits,
-// per-wave LDS histograms), then a sort of the k tokens. Only reached when a
-// resend set outgrows LDS (e.g. scores tied across far more than k tokens).
-__device__ void select_row_global(const float* __restrict__ srow, int ctx, int k, SelShared& S,
-                                  int32_t* __restrict__ orow, int32_t* __restrict__ prow, const CacheView& cv,
-                                  const RowMap& rm, int seq) {
+// per-wave LDS histograms), then a sort of the k tokens. Only reached when the
+// rescans outgrow LDS (e.g. scores tied across far more than k tokens).
+__device__ __forceinline__ void select_row_global(const float* __restrict__ srow, int ctx, int k, SelShared& S,
+                                               int32_t* __restrict__ orow, int32_t* __restrict__ prow, CacheView cv,
+                                               RowMap rm, int seq) {
   const int tid = threadIdx.x, wid = tid >> 6;
   uint64_t prefix = 0, mask = 0;
   uint32_t need = (uint32_t)k;
+  __syncthreads();
   for (int sh = 56; sh >= 0; sh -= 8) {
-    for (int i = tid; i < NW * 256; i += SEL_NT) S.hist[i] = 0u;
+    for (int i = tid; i < NW * 256; i += SEL_NT) S.g.hist[i] = 0u;
     __syncthreads();
     for (int t = tid; t < ctx; t += SEL_NT) {
       const uint64_t c = composite_key(srow[t], t);
-      if ((c & mask) == prefix) atomicAdd(&S.hist[wid * 256 + ((c >> sh) & 0xFF)], 1u);
+      if ((c & mask) == prefix) atomicAdd(&S.g.hist[wid * 256 + ((c >> sh) & 0xFF)], 1u);
     }
     __syncthreads();
     uint32_t v = 0;
     if (tid < 256)
-      for (int w = 0; w < NW; ++w) v += S.hist[w * 256 + tid];
+      for (int w = 0; w < NW; ++w) v += S.g.hist[w * 256 + tid];
     __syncthreads();
-    if (tid < 256) S.hist[tid] = v;
+    if (tid < 256) S.g.hist[tid] = v;
     __syncthreads();
     if (tid == 0) {
       uint32_t above = 0;
       for (int d = 255; d >= 0; --d) {
-        const uint32_t x = S.hist[d];
-        if (above + x >= need) { S.res[0] = (uint32_t)d; S.res[1] = above; break; }
+        const uint32_t x = S.g.hist[d];
+        if (above + x >= need) {
+          S.res[0] = (uint32_t)d;
+          S.res[1] = above;
+          break;
+        }
         above += x;
       }
     }
@@ -260,32 +433,35 @@ __device__ void select_row_global(const float* __restrict__ srow, int ctx, int k
     prefix |= (uint64_t)dig << sh;
     mask |= 0xFFull << sh;
   }
-  if (tid == 0) S.cnt[0] = 0;
+  if (tid == 0) S.ecount = 0;
   __syncthreads();
   for (int t = tid; t < ctx; t += SEL_NT)
     if (composite_key(srow[t], t) >= prefix) {
-      const uint32_t pos = atomicAdd(&S.cnt[0], 1u);
-      if (pos < (uint32_t)kMaxK) S.sel[pos] = (uint32_t)t;
+      const uint32_t pos = atomicAdd(&S.ecount, 1u);
+      if (pos < (uint32_t)kMaxK) S.g.sel[pos] = (uint32_t)t;
     }
   __syncthreads();
   int P = 1;
   while (P < k) P <<= 1;
-  for (int i = k + tid; i < P; i += SEL_NT) S.sel[i] = 0xFFFFFFFFu;
+  for (int i = k + tid; i < P; i += SEL_NT) S.g.sel[i] = 0xFFFFFFFFu;
   __syncthreads();
   for (int kk = 2; kk <= P; kk <<= 1) {
     for (int j = kk >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < P; i += SEL_NT) {
         const int p = i ^ j;
         if (p > i) {
-          const uint32_t a = S.sel[i], b = S.sel[p];
-          if ((a > b) == ((i & kk) == 0)) { S.sel[i] = b; S.sel[p] = a; }
+          const uint32_t a = S.g.sel[i], b = S.g.sel[p];
+          if ((a > b) == ((i & kk) == 0)) {
+            S.g.sel[i] = b;
+            S.g.sel[p] = a;
+          }
         }
       }
       __syncthreads();
     }
   }
   for (int i = tid; i < k; i += SEL_NT) {
-    const int t = (int)S.sel[i];
+    const int t = (int)S.g.sel[i];
     orow[i] = t;
     if (prow) prow[i] = page_slot(cv, rm, seq, t);
   }
@@ -293,19 +469,20 @@ __device__ void select_row_global(const float* __restrict__ srow, int ctx, int k
 
 }  // namespace
 
-// Stage 1 over an existing score array (the standalone top-k entry point).
+// Stage 1 over an existing score array (the standalone top-k entry point): one
+// workgroup per 256 tokens of a row, all threads reaching the send.
 __global__ __launch_bounds__(256) void topk_send_kernel(const float* __restrict__ scores, int64_t ld,
                                                         const int32_t* __restrict__ row_ctx, int max_ctx,
                                                         TopkWs ws) {
+  __shared__ uint32_t send_lds[68];
   const int r = blockIdx.y;
   const int ctx = clamp_ctx(row_ctx, r, max_ctx);
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int base = unit * kCandUnit;
-  if (base >= ctx || cand_per_unit(ctx) == 0) return;  // wave-uniform
-  const int t = base + (threadIdx.x & 63);
+  const int base = blockIdx.x * 256;
+  if (base >= ctx || cand_plan(ctx).unit == 0) return;  // whole workgroup
+  const int t = base + threadIdx.x;
   const bool valid = t < ctx;
   const float s = valid ? scores[(int64_t)r * ld + t] : 0.f;
-  wave_send_candidates(s, valid, ctx, base, r, unit, ws);
+  send_candidates(s, valid, ctx, base, r, ws, send_lds);
 }
 
 __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
@@ -313,12 +490,13 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
                                                              TopkWs ws, int32_t* __restrict__ idx,
                                                              int32_t* __restrict__ phys, CacheView cv, RowMap rm) {
   __shared__ SelShared S;
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int ctx = clamp_ctx(row_ctx, r, max_ctx);
   int32_t* orow = idx + (int64_t)r * k;
   int32_t* prow = phys ? phys + (int64_t)r * k : nullptr;
   const int seq = phys ? rm.row_seq[r] : 0;
   const float* srow = scores + (int64_t)r * ld;
+  int par = 0;
 
   if (ctx <= k) {
     for (int i = tid; i < k; i += SEL_NT) {
@@ -329,128 +507,209 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
   }
 
   uint64_t e[PER];
-  int32_t slot[PER];
-  if (ctx <= kTopkFullRow) {
+  const CandPlan p = cand_plan(ctx);
+  if (p.unit == 0) {
     // ---- the row's own keys: thread owns tokens [16 tid, 16 tid + 16) ----
+    const int t0 = tid * PER;
+    float f[PER];
+    if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0 && t0 + PER <= ctx) {
+      const float4* p4 = reinterpret_cast<const float4*>(srow + t0);
+#pragma unroll
+      for (int x = 0; x < PER / 4; ++x) {
+        const float4 v = p4[x];
+        f[4 * x] = v.x;
+        f[4 * x + 1] = v.y;
+        f[4 * x + 2] = v.z;
+        f[4 * x + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) f[i] = t0 + i < ctx ? srow[t0 + i] : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int t = tid * PER + i;
-      e[i] = t < ctx ? composite_key(srow[t], t) : 0ull;
-      slot[i] = (prow && t < ctx) ? page_slot(cv, rm, seq, t) : -1;
+      const int t = t0 + i;
+      e[i] = t < ctx ? composite_key(f[i], t) : 0ull;
     }
-    const uint64_t cstar = select_kth(e, (uint32_t)k, S);
-    ordered_write(e, slot, cstar, k, orow, prow, S);
+    const uint64_t cstar = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
+    ordered_write(e, cstar, k, orow, prow, cv, rm, seq, S, par);
     return;
   }
 
-  // ---- candidates: thread owns candidates [16 tid, 16 tid + 16), whole units ----
-  const int nu = (ctx + kCandUnit - 1) / kCandUnit;
-  const int m = cand_per_unit(ctx);
-  const int n = nu * m;
-  {
-    const v4i* src = reinterpret_cast<const v4i*>(ws.cand + (int64_t)r * kCandRowCap + tid * PER);
-    v4i raw[PER / 2];
-#pragma unroll
-    for (int q = 0; q < PER / 2; ++q) raw[q] = src[q];
-#pragma unroll
-    for (int q = 0; q < PER / 2; ++q) {
-      e[2 * q] = ((uint64_t)(uint32_t)raw[q][1] << 32) | (uint32_t)raw[q][0];
-      e[2 * q + 1] = ((uint64_t)(uint32_t)raw[q][3] << 32) | (uint32_t)raw[q][2];
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (tid * PER + i >= n) e[i] = 0ull;
-    // block-table lookups issued now, consumed after the search
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      slot[i] = (prow && e[i] != 0) ? page_slot(cv, rm, seq, (int)(0xFFFFFFFFu - (uint32_t)e[i])) : -1;
-  }
-  const uint64_t cu = select_kth(e, (uint32_t)k, S);
-
-  // units (whole ones per thread) whose kept-back keys may reach cu
-  const int upt = PER / m;                 // units per thread
-  const int u0 = tid * upt;
-  const uint64_t* rf = ws.floors + (int64_t)r * ws.nunits;
-  uint32_t fmask = 0;
-  for (int j = 0; j < upt; ++j)
-    if (u0 + j < nu && rf[u0 + j] >= cu) fmask |= 1u << j;
-  const uint32_t nflag = wave_sum_u32((uint32_t)__popc(fmask));
-  if (tid % 64 == 0) S.red[0][tid >> 6][3] = nflag;
-  __syncthreads();
-  uint32_t nflag_all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) nflag_all += S.red[0][w][3];
-  if (nflag_all == 0) {
-    ordered_write(e, slot, cu, k, orow, prow, S);
-    return;
-  }
-
-  // ---- resend: U in token order = per unit, (flagged ? its keys >= cu : its candidates >= cu) ----
-  const bool vec_ok = ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0);
-  auto unit_keys = [&](int u, auto&& fn) {
-    // visits the keys of unit u's tokens in token order, 16 at a time
-    const int tb = u * kCandUnit;
-#pragma unroll 1
-    for (int q = 0; q < kCandUnit / 16; ++q) {
-      float f[16];
-      const int t0 = tb + q * 16;
-      if (vec_ok && t0 + 16 <= ctx) {
-        const float4* p4 = reinterpret_cast<const float4*>(srow + t0);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float4 v = p4[x];
-          f[4 * x] = v.x; f[4 * x + 1] = v.y; f[4 * x + 2] = v.z; f[4 * x + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) f[x] = (t0 + x < ctx) ? srow[t0 + x] : 0.f;
-      }
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        if (t0 + x < ctx) fn(composite_key(f[x], t0 + x));
-    }
-  };
-  uint32_t cnt = 0;
-  for (int j = 0; j < upt; ++j) {
-    if ((fmask >> j) & 1u) {
-      unit_keys(u0 + j, [&](uint64_t c) { cnt += c >= cu ? 1u : 0u; });
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (i / m == j && e[i] != 0 && e[i] >= cu) ++cnt;
-    }
-  }
-  uint32_t nuall;
-  uint32_t off = block_excl_scan<SEL_NT>(cnt, S.scan, &nuall);
-  if (nuall > (uint32_t)kCandRowCap) {
-    select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
-    return;
-  }
-  for (int j = 0; j < upt; ++j) {
-    if ((fmask >> j) & 1u) {
-      unit_keys(u0 + j, [&](uint64_t c) { if (c >= cu) S.buf[off++] = c; });
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (i / m == j && e[i] != 0 && e[i] >= cu) S.buf[off++] = e[i];
-    }
-  }
-  __syncthreads();
-  uint64_t u[PER];
-  int32_t uslot[PER];
+  // ---- candidates: e[q + m j] = rank q of unit t + 1024 j (j < upt) ----
+  const int m = p.m, nu = p.nu;
+  const int lm = 31 - __clz(m);
+  const int upt = (nu + SEL_NT - 1) / SEL_NT;  // 1, 2 or 4; upt * m <= 16
+  const uint64_t* crow = ws.cand + (int64_t)r * kCandRowCap;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    u[i] = (uint32_t)(tid * PER + i) < nuall ? S.buf[tid * PER + i] : 0ull;
-    uslot[i] = (prow && u[i] != 0) ? page_slot(cv, rm, seq, (int)(0xFFFFFFFFu - (uint32_t)u[i])) : -1;
+    const int q = i & (m - 1), j = i >> lm;
+    const int u = tid + SEL_NT * j;
+    e[i] = (j < upt && u < nu) ? crow[(int64_t)q * nu + u] : 0ull;
   }
-  const uint64_t cstar = select_kth(u, (uint32_t)k, S);
-  ordered_write(u, uslot, cstar, k, orow, prow, S);
+  // floors of this thread's units, fetched before the search needs them
+  uint32_t fl[4];
+  const uint32_t* rf = ws.floors + (int64_t)r * kFloorRowCap;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int u = tid + SEL_NT * j;
+    fl[j] = (j < upt && u < nu) ? rf[u] : 0u;
+  }
+  const uint64_t cu = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
+
+  // units whose kept-back keys may reach cu
+  const uint32_t cu_hi = (uint32_t)(cu >> 32);
+  uint32_t fmask = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (fl[j] != 0u && fl[j] >= cu_hi) fmask |= 1u << j;
+  uint32_t nflag;
+  const uint32_t fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
+  uint64_t cstar = cu;
+  uint32_t ne = 0;
+  if (nflag > 0) {
+    if (nflag > (uint32_t)FCAP) {
+      select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+      return;
+    }
+    // ---- resend: each flagged unit's keys >= cu, rescanned by one wave per unit ----
+    {
+      uint32_t fm = fmask, sl = fbase;
+      while (fm) {
+        const int j = __ffs(fm) - 1;
+        fm &= fm - 1u;
+        S.funit[sl++] = (uint32_t)(tid + SEL_NT * j);
+      }
+    }
+    if (tid == 0) S.ecount = 0u;
+    __syncthreads();
+    const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1 or 4
+    for (uint32_t sl = wid; sl < nflag; sl += NW) {
+      const int t0 = (int)S.funit[sl] * p.unit;
+      float f[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int t = t0 + 64 * c + lane;
+        f[c] = (c < chunks && t < ctx) ? srow[t] : 0.f;
+      }
+      uint64_t bal[4];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int t = t0 + 64 * c + lane;
+        const bool keep = c < chunks && t < ctx && composite_key(f[c], t) >= cu;
+        bal[c] = __ballot(keep);
+        tot += (uint32_t)__popcll(bal[c]);
+      }
+      uint32_t st = 0;
+      if (lane == 0) st = atomicAdd(&S.ecount, tot);
+      st = (uint32_t)__shfl((int)st, 0, 64);
+      uint32_t run = st;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int t = t0 + 64 * c + lane;
+        const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
+        if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
+        run += (uint32_t)__popcll(bal[c]);
+      }
+      if (lane == 0) {
+        S.fstart[sl] = st;
+        S.flen[sl] = tot;
+      }
+    }
+    __syncthreads();
+    ne = S.ecount;
+    if (ne > (uint32_t)ECAP) {
+      select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+      return;
+    }
+    // union: unflagged candidates >= cu in registers, rescanned keys from LDS
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool flagged = (fmask >> (i >> lm)) & 1u;
+      if (flagged || e[i] < cu) e[i] = 0ull;
+    }
+    cstar = kth_largest<PER, true>(e, S.a.ext, ne, (uint32_t)k, S, par);
+    // selected keys of each rescanned unit
+    for (uint32_t sl = wid; sl < nflag; sl += NW) {
+      const uint32_t st = S.fstart[sl], len = S.flen[sl];
+      uint32_t c = 0;
+      for (uint32_t q0 = 0; q0 < len; q0 += 64) {
+        const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
+        c += (uint32_t)__popcll(__ballot(sel));
+      }
+      if (lane == 0) S.fcnt[sl] = c;
+    }
+    __syncthreads();
+  }
+
+  // ---- ordered write: unit counts, prefix sums over units (unit u = tid + 1024 j) ----
+  uint32_t bits = 0;  // selected register keys
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (e[i] != 0ull && e[i] >= cstar) bits |= 1u << i;
+  const uint32_t umask = m >= 16 ? 0xFFFFu : ((1u << m) - 1u);  // keys of one unit
+  uint32_t cnt[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t mj = j < upt ? (umask << (m * j)) & 0xFFFFu : 0u;
+    cnt[j] = (fmask >> j) & 1u ? S.fcnt[fbase + (uint32_t)__popc(fmask & ((1u << j) - 1u))]
+                               : (uint32_t)__popc(bits & mj);
+  }
+  uint32_t off[4], tot[4];
+  excl_scan4(cnt, off, tot, upt, S);
+  uint32_t base = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    off[j] += base;
+    base += tot[j];
+  }
+  const uint32_t total = base;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if ((fmask >> j) & 1u) S.foff[fbase + (uint32_t)__popc(fmask & ((1u << j) - 1u))] = off[j];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if ((bits >> i) & 1u) {
+      const int j = i >> lm;
+      const uint32_t oj = j == 0 ? off[0] : j == 1 ? off[1] : j == 2 ? off[2] : off[3];
+      const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
+      if (o < (uint32_t)k) {
+        const int t = key_token(e[i]);
+        orow[o] = t;
+        if (prow) prow[o] = page_slot(cv, rm, seq, t);
+      }
+    }
+  }
+  if (nflag > 0) {
+    __syncthreads();
+    for (uint32_t sl = wid; sl < nflag; sl += NW) {
+      const uint32_t st = S.fstart[sl], len = S.flen[sl];
+      uint32_t o = S.foff[sl];
+      for (uint32_t q0 = 0; q0 < len; q0 += 64) {
+        const uint64_t c = q0 + (uint32_t)lane < len ? S.a.ext[st + q0 + lane] : 0ull;
+        const bool sel = c != 0ull && c >= cstar;
+        const uint64_t bal = __ballot(sel);
+        const uint32_t pos = o + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        if (sel && pos < (uint32_t)k) {
+          const int t = key_token(c);
+          orow[pos] = t;
+          if (prow) prow[pos] = page_slot(cv, rm, seq, t);
+        }
+        o += (uint32_t)__popcll(bal);
+      }
+    }
+  }
+  for (int i = (int)total + tid; i < k; i += SEL_NT) {
+    orow[i] = -1;
+    if (prow) prow[i] = -1;
+  }
 }
 
 hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx,
                             const TopkWs& ws, hipStream_t stream) {
   if (R <= 0 || max_ctx <= kTopkFullRow) return hipSuccess;
-  dim3 grid((cand_units(max_ctx) + 3) / 4, R);
+  dim3 grid((max_ctx + 255) / 256, R);
   hipLaunchKernelGGL(topk_send_kernel, grid, dim3(256), 0, stream, scores, ld, row_ctx, max_ctx, ws);
   return hipGetLastError();
 }

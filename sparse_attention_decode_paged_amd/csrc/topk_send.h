@@ -1,14 +1,24 @@
-// Stage 1 of the exact top-k: every 64-token unit of a row (one wave of the
-// indexer) sends its m best keys, in token order, and a floor. Shared by the
-// indexer epilogue and the standalone top-k kernel.
+// Stage 1 of the exact top-k: every unit of a row (a run of consecutive tokens)
+// sends its m best keys, in token order, and a floor. Shared by the indexer
+// epilogue and the standalone top-k kernel, which both hand it one workgroup of
+// 4 waves covering 256 consecutive tokens (wave w: tokens 64 w .. 64 w + 63, lane =
+// token).
 //
-// Ranking inside a wave uses a 32-bit packed key per token: the score's
-// order-preserving bits with the low 6 bits replaced by (63 - lane). Packed keys
-// are distinct within the wave and ordered like the scores up to those 6 bits. The
-// wave's m largest packed keys are sent with their full 64-bit composite keys; the
-// floor bounds the composite key of every token not sent:
-// ((packed key of rank m) | 63) << 32 | 0xFFFFFFFF, or 0 when the unit sent all of
-// its valid tokens. The sort runs on DPP / permlane exchanges: no LDS, no barrier.
+// Unit size and m depend only on the row length (see cand_plan): 64-token units
+// (one wave, m = 16) up to 65,536 tokens, 256-token units (the workgroup, m = 16, 8
+// or 4) above. A unit of 256 tokens holds on average 2 of the top 2048 of a
+// 262,144-token row, so 16 sent keys leave it short only when it holds 17 or more.
+//
+// Ranking uses a 32-bit packed key per token: the score's order-preserving bits with
+// the low 8 bits replaced by (255 - position in the workgroup). Packed keys are
+// distinct within the workgroup and ordered like the scores up to those 8 bits. The
+// m largest packed keys of a unit are sent with their full 64-bit composite keys at
+// cand[q * nu + u] (q = rank in token order, u = unit, nu = units of the row). The
+// floor is a score word f such that every unsent token's composite key is below
+// (f << 32) | 0xFFFFFFFF, so an unsent key can reach a threshold c only if
+// f >= c >> 32; f = 0 when the unit sent all of its valid tokens. Sorting uses DPP /
+// permlane exchanges inside a wave; 256-token units merge the four waves' best 16
+// through LDS with one barrier.
 #pragma once
 
 #include "common.h"
@@ -16,38 +26,78 @@
 
 namespace dsa {
 
-// Keys a 64-token unit sends for a row of length ctx: the largest power of two
-// (at most 16) that keeps the row within kCandRowCap; 0 when the row is short
-// enough for the select stage to read every score.
-__device__ __forceinline__ int cand_per_unit(int ctx) {
-  if (ctx <= kTopkFullRow) return 0;
-  const int nu = (ctx + kCandUnit - 1) / kCandUnit;
-  int m = kCandPerUnitMax;
-  while (m > 1 && nu * m > kCandRowCap) m >>= 1;
-  return m;
+struct CandPlan {
+  int unit;  // tokens per unit: 0 (no candidates: the select reads the whole row), 64 or 256
+  int m;     // keys sent per unit
+  int nu;    // units of the row
+};
+
+__host__ __device__ inline CandPlan cand_plan(int ctx) {
+  CandPlan p{0, 0, 0};
+  if (ctx <= kTopkFullRow) return p;
+  if (ctx <= 4 * kTopkFullRow) {
+    p.unit = 64;
+    p.m = kCandPerUnitMax;
+  } else {
+    p.unit = 256;
+    const int nu = (ctx + 255) / 256;
+    int m = kCandPerUnitMax;
+    while (m > 1 && nu * m > kCandRowCap) m >>= 1;
+    p.m = m;
+  }
+  p.nu = (ctx + p.unit - 1) / p.unit;
+  return p;
 }
 
-// Called by a whole wave; lane l carries token unit_base + l.
-__device__ __forceinline__ void wave_send_candidates(float score, bool valid, int ctx, int unit_base, int row,
-                                                     int unit, const TopkWs& tw) {
-  const int m = cand_per_unit(ctx);
-  if (m == 0) return;  // uniform over the row
-  const int lane = threadIdx.x & 63;
-  const uint32_t packed = valid ? ((float_key(score) & ~63u) | (63u - (uint32_t)lane)) : 0u;
+// Called by all 256 threads of a workgroup (no thread may have returned): thread
+// 64 w + l holds the score of token base + 64 w + l. `lds` is 68 words of LDS.
+__device__ __forceinline__ void send_candidates(float score, bool valid, int ctx, int base, int row,
+                                                const TopkWs& tw, uint32_t* lds) {
+  const CandPlan p = cand_plan(ctx);
+  if (p.unit == 0) return;  // uniform over the row
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int pos = threadIdx.x;  // position in the workgroup
+  const uint32_t packed = valid ? ((float_key(score) & ~255u) | (255u - (uint32_t)pos)) : 0u;
   const uint32_t sorted = wave_sort_desc_u32(packed, lane);
-  const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)sorted, m - 1);
+  uint64_t* cand = tw.cand + (int64_t)row * kCandRowCap;
+  uint32_t* floors = tw.floors + (int64_t)row * kFloorRowCap;
+  const uint64_t key = valid ? composite_key(score, base + pos) : 0ull;
+
+  if (p.unit == 64) {
+    // one unit per wave
+    const int u = (base >> 6) + wid;
+    if (u >= p.nu) return;  // wave-uniform, past the row
+    const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)sorted, p.m - 1);
+    const uint32_t nxt = (uint32_t)__builtin_amdgcn_readlane((int)sorted, p.m);
+    const bool sent = packed != 0u && packed >= thr;
+    const uint64_t bal = __ballot(sent);
+    const uint32_t nsent = (uint32_t)__popcll(bal);
+    const uint32_t q = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+    if (sent) cand[(int64_t)q * p.nu + u] = key;
+    if ((uint32_t)lane >= nsent && lane < p.m) cand[(int64_t)lane * p.nu + u] = 0ull;  // unused ranks
+    if (lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
+    return;
+  }
+
+  // one unit per workgroup: merge the waves' best 16 (and each wave's 17th) in LDS
+  if (lane < 16) lds[wid * 16 + lane] = sorted;
+  if (lane == 16) lds[64 + wid] = sorted;
+  __syncthreads();
+  const uint32_t all = lds[lane];
+  const uint32_t w17 = max(max(lds[64], lds[65]), max(lds[66], lds[67]));
+  const uint32_t msort = wave_sort_desc_u32(all, lane);
+  const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)msort, p.m - 1);
+  const uint32_t nxt = max((uint32_t)__builtin_amdgcn_readlane((int)msort, p.m), w17);
+  // keys this wave sends, and how many lower waves send (all within their best 16)
   const bool sent = packed != 0u && packed >= thr;
   const uint64_t bal = __ballot(sent);
-  const uint32_t nsent = (uint32_t)__popcll(bal);
-  const uint32_t pos = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-  uint64_t* dst = tw.cand + (int64_t)row * kCandRowCap + (int64_t)unit * m;
-  if (sent) dst[pos] = composite_key(score, unit_base + lane);
-  if ((uint32_t)lane >= nsent && lane < m) dst[lane] = 0ull;  // unused slots of a short unit
-  int valid_n = ctx - unit_base;
-  valid_n = valid_n > kCandUnit ? kCandUnit : valid_n;
-  const uint32_t next = (uint32_t)__builtin_amdgcn_readlane((int)sorted, m < kCandUnit ? m : kCandUnit - 1);
-  if (lane == 0)
-    tw.floors[(int64_t)row * tw.nunits + unit] = valid_n > m ? (((uint64_t)(next | 63u) << 32) | 0xFFFFFFFFull) : 0ull;
+  const uint32_t before = (uint32_t)__popcll(__ballot(all != 0u && all >= thr && lane < 16 * wid));
+  const uint32_t q = before + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+  const int u = base >> 8;
+  if (sent) cand[(int64_t)q * p.nu + u] = key;
+  const uint32_t ntot = (uint32_t)__popcll(__ballot(all != 0u && all >= thr));
+  if (wid == 0 && (uint32_t)lane >= ntot && lane < p.m) cand[(int64_t)lane * p.nu + u] = 0ull;  // unused ranks
+  if (wid == 0 && lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
 }
 
 }  // namespace dsa
