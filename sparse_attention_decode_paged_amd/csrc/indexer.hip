@@ -44,12 +44,12 @@ __device__ __forceinline__ int swz(int tn, int c) { return tn * kDIdx + 16 * (c 
 // One workgroup = 4 waves = 256 consecutive tokens of one row; wave w owns tokens
 // [64w, 64w + 64) of it. PAGED32: block size >= 32, so a tile lies inside one page.
 // Waves past the row's end stay to the epilogue, whose 256-token units take a
-// workgroup barrier.
-template <bool PAGED32>
+// workgroup barrier. SEND: also run stage 1 of the top-k on the fresh scores.
+template <bool PAGED32, bool SEND>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(CacheView cv, RowMap rm, const uint8_t* __restrict__ q_idx,
                                                           const float* __restrict__ q_scale,
                                                           const float* __restrict__ w, float* __restrict__ scores,
-                                                          int64_t ld, TopkWs tw, int send) {
+                                                          int64_t ld, TopkWs tw) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kTileBytes];
   __shared__ uint32_t send_lds[68];
   const int r = blockIdx.y;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(CacheView cv, RowMap r
   const int t = tok0 + lane;
   const float sc = (g ? res[1] : res[0]) * ksc;
   if (t < ctx) scores[(int64_t)r * ld + t] = sc;
-  if (send) send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds);
+  if (SEND) send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds);
 }
 
 hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const float* q_scale,
@@ -155,12 +155,15 @@ hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8
   TopkWs tw = ws ? *ws : TopkWs{nullptr, nullptr};
   const int send = (ws != nullptr && rm.max_ctx > kTopkFullRow) ? 1 : 0;
   dim3 grid(nx, R);
-  if (cv.block_size >= kTileTok)
-    hipLaunchKernelGGL(indexer_fp8_kernel<true>, grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw,
-                       send);
+  const bool p32 = cv.block_size >= kTileTok;
+  if (send && p32)
+    hipLaunchKernelGGL((indexer_fp8_kernel<true, true>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
+  else if (send)
+    hipLaunchKernelGGL((indexer_fp8_kernel<false, true>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
+  else if (p32)
+    hipLaunchKernelGGL((indexer_fp8_kernel<true, false>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
   else
-    hipLaunchKernelGGL(indexer_fp8_kernel<false>, grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw,
-                       send);
+    hipLaunchKernelGGL((indexer_fp8_kernel<false, false>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
   return hipGetLastError();
 }
 
