@@ -18,7 +18,8 @@
 // least 32. Each of the wave's four 16-byte loads per tile reads 1 KB of whole
 // 128-byte lines (lane l takes byte 16 l of the kilobyte), which keeps the number
 // of vector memory instructions and cache-line requests per byte minimal; per-lane
-// gathers of one token's half key measured 2.3x slower at 256K tokens. The tile
+// gathers of one token's half key measured 2.3x slower at 256K tokens. Key loads
+// are nontemporal: the keys are read once per step. The tile
 // then passes through a wave-private LDS buffer, written with an XOR swizzle of the
 // 16-byte chunks so that the MFMA operand reads (lane = token, 64 bytes of its key)
 // are bank-conflict free. Block-table entries, head weights and query scales are
@@ -71,14 +72,15 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(CacheView cv, RowMap r
       if (PAGED32) {
         const uint8_t* tile = row_base(cv, token_block(cv, rm, seq, tb)) + cv.idx_off + (int64_t)(tb & bs_mask) * kDIdx;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kv[j][i] = *reinterpret_cast<const v4i*>(tile + 1024 * i + 16 * lane);
+        for (int i = 0; i < 4; ++i)
+          kv[j][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(tile + 1024 * i + 16 * lane));
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           int t = tb + 8 * i + (lane >> 3);
           t = t < ctx ? t : ctx - 1;
           const uint8_t* key = row_base(cv, token_block(cv, rm, seq, t)) + cv.idx_off + (int64_t)(t & bs_mask) * kDIdx;
-          kv[j][i] = *reinterpret_cast<const v4i*>(key + 16 * (lane & 7));
+          kv[j][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(key + 16 * (lane & 7)));
         }
       }
     } else {

@@ -54,11 +54,9 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
   __shared__ __attribute__((aligned(16))) uint16_t q_s[kMlaGroup * QROW];
   __shared__ __attribute__((aligned(16))) uint8_t lat_s[CH * LROW];
   __shared__ __attribute__((aligned(16))) _Float16 p_s[kMlaGroup * CH];
-  __shared__ int64_t addr_s[CH];
   __shared__ float sc_s[CH];
   __shared__ float red_s[4][kMlaGroup];
   __shared__ float m_s[kMlaGroup], l_s[kMlaGroup], alpha_s[kMlaGroup];
-  __shared__ float smax_s;
 
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
@@ -66,13 +64,19 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
   const int seq = rm.row_seq[r];
   const int bs_mask = cv.block_size - 1;
 
-  // Q fragment rows for this head group, straight to LDS.
+  // Q fragment rows for this head group, straight to LDS (all loads issued first).
   {
     const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * kMlaGroup) * kDLat);
     constexpr int QP = kDLat / 8;  // 72 16-byte pieces per head row
-    for (int i = tid; i < kMlaGroup * QP; i += NT) {
-      const int h = i / QP, pc = i - h * QP;
-      *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qg[i];
+    constexpr int QN = kMlaGroup * QP / NT;
+    static_assert(QN * NT == kMlaGroup * QP, "Q pieces per thread");
+    v4i qv[QN];
+#pragma unroll
+    for (int q = 0; q < QN; ++q) qv[q] = qg[tid + NT * q];
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const int i = tid + NT * q, h = i / QP, pc = i - h * QP;
+      *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
     }
   }
   if (tid < kMlaGroup) {
@@ -86,56 +90,52 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
   float s_run = 1.f;  // acc holds O / s_run (token scales folded into P per chunk)
 
   for (int c0 = j0; c0 < j1; c0 += CH) {
-    // ---- translate the chunk's 64 token ids into latent row offsets (one lookup each) ----
-    if (tid < CH) {
-      const int j = c0 + tid;
+    // ---- gather: 4 threads per token; each looks up its token's latent row and
+    // issues its 9 of the 36 16-byte pieces (and the scale) right away ----
+    {
+      const int tt = tid >> 2, qtr = tid & 3;
+      const int j = c0 + tt;
       int t = j < j1 ? irow[j] : -1;
       t = t < rm.max_ctx ? t : -1;
       const int tc = t >= 0 ? t : 0;  // every load below stays in the pool; empty slots are masked
       int64_t blk;
+      int slot;
       if (phys != nullptr) {
-        const int ps = j < j1 ? phys[(int64_t)r * k + j] : 0;
-        blk = (int64_t)(ps >= 0 ? ps : 0) >> cv.log2_bs;
+        int ps = j < j1 ? phys[(int64_t)r * k + j] : 0;
+        ps = ps >= 0 ? ps : 0;
+        blk = (int64_t)ps >> cv.log2_bs;
         blk = blk < cv.num_blocks ? blk : cv.num_blocks - 1;
+        slot = ps & bs_mask;
       } else {
         blk = token_block(cv, rm, seq, tc);
+        slot = tc & bs_mask;
       }
-      const int64_t base = blk * cv.row_bytes + cv.lat_off;
-      const float s = *reinterpret_cast<const float*>(cv.pool + base + (int64_t)cv.block_size * kDLat +
-                                                      (int64_t)(tc & bs_mask) * 4);
-      addr_s[tid] = t >= 0 ? base + (int64_t)(tc & bs_mask) * kDLat : -1;
-      sc_s[tid] = t >= 0 ? s : kNegInf;  // -inf marks an empty slot
+      const uint8_t* page = cv.pool + blk * cv.row_bytes + cv.lat_off;
+      const uint8_t* lrow = page + (int64_t)slot * kDLat;
+      float sv = 0.f;
+      if (qtr == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
+      constexpr int PN = PIECES / 4;  // 9 pieces per thread
+      v4i v[PN];
+#pragma unroll
+      for (int q = 0; q < PN; ++q) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (qtr + 4 * q));
+#pragma unroll
+      for (int q = 0; q < PN; ++q)
+        *reinterpret_cast<v4i*>(lat_s + tt * LROW + 16 * (qtr + 4 * q)) = t >= 0 ? v[q] : v4i{0, 0, 0, 0};
+      if (qtr == 0) sc_s[tt] = t >= 0 ? sv : kNegInf;  // -inf marks an empty slot
     }
     __syncthreads();
-    if (tid < 64) {
-      float v = sc_s[tid];
+    // largest token scale of the chunk, computed by every wave (no extra barrier)
+    float smax;
+    {
+      float v = sc_s[lane];
       v = fmaxf(v, xshflf<1>(v));
       v = fmaxf(v, xshflf<2>(v));
       v = fmaxf(v, xshflf<4>(v));
       v = fmaxf(v, xshflf<8>(v));
       v = fmaxf(v, xshflf<16>(v));
       v = fmaxf(v, xshflf<32>(v));
-      if (tid == 0) smax_s = v > 0.f ? v : 1.f;
+      smax = v > 0.f ? v : 1.f;
     }
-    // ---- gather 64 latents: 9 independent 16-byte loads per thread, then the LDS stores ----
-    {
-      v4i v[(CH * PIECES) / NT];
-#pragma unroll
-      for (int q = 0; q < (CH * PIECES) / NT; ++q) {
-        const int p = tid + NT * q;
-        const int tt = p / PIECES, pc = p - tt * PIECES;
-        const int64_t off = addr_s[tt];
-        v[q] = *reinterpret_cast<const v4i*>(cv.pool + (off >= 0 ? off : 0) + pc * 16);
-        if (off < 0) v[q] = v4i{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int q = 0; q < (CH * PIECES) / NT; ++q) {
-        const int p = tid + NT * q;
-        const int tt = p / PIECES, pc = p - tt * PIECES;
-        *reinterpret_cast<v4i*>(lat_s + tt * LROW + pc * 16) = v[q];
-      }
-    }
-    __syncthreads();
 
     // ---- S = Q . C^T : wave w -> tokens [16w, 16w+16), heads 0..31 ----
     v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -157,7 +157,6 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
     const int tt = 16 * wid + (lane & 15);
     const float sct = sc_s[tt];
     const bool ok = sct != kNegInf;
-    const float smax = smax_s;
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
