@@ -56,69 +56,92 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(CacheView cv, RowMap r
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ctx = row_len(rm, r);
-  if (blockIdx.x * 256 >= ctx) return;  // whole workgroup
-  const int tok0 = blockIdx.x * 256 + wid * 64;
-  const bool active = tok0 < ctx;       // wave-uniform
+  // the row's length and block-table row are read together; a workgroup past the
+  // row's end still issues its (clamped, valid) loads and leaves after them
   const int seq = rm.row_seq[r];
+  int ctx = row_len(rm, r);
+  const bool past = blockIdx.x * 256 >= ctx;  // whole workgroup
+  ctx = ctx > 0 ? ctx : 1;
+  const int tok0 = blockIdx.x * 256 + wid * 64;
   const int bs_mask = cv.block_size - 1;
 
-  // ---- key loads for both tiles: 4 x 1 KB of whole lines each ----
+  // ---- key loads for both tiles: 4 x 1 KB of whole lines each. No branches: a tile
+  // start past the row's end is clamped to the row's last tile, so every load reads
+  // valid keys; results for tokens >= ctx are never stored ----
   v4i kv[2][4];
+  int64_t toff[2];  // byte offset of each tile's index page in the pool (PAGED32)
+  const int last_tile = (ctx - 1) & ~(kTileTok - 1);
+  const int tb1 = tok0 + kTileTok < last_tile ? tok0 + kTileTok : last_tile;
+  const int tb0 = tok0 < last_tile ? tok0 : last_tile;
+  if (PAGED32) {  // both block-table entries are loaded before either is used
+    const int32_t* btrow = rm.block_table + (int64_t)seq * rm.bt_stride;
+    // read as unsigned (no sign extension between the two loads), so both are in
+    // flight together; ids outside [0, num_blocks) are clamped like token_block does
+    const uint32_t e0 = (uint32_t)btrow[tb0 >> cv.log2_bs], e1 = (uint32_t)btrow[tb1 >> cv.log2_bs];
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t nb = (uint32_t)cv.num_blocks;
+    const uint32_t b0 = e0 < nb ? e0 : ((int32_t)e0 < 0 ? 0u : nb - 1u);
+    const uint32_t b1 = e1 < nb ? e1 : ((int32_t)e1 < 0 ? 0u : nb - 1u);
+    toff[0] = (int64_t)b0 * cv.row_bytes + cv.idx_off;
+    toff[1] = (int64_t)b1 * cv.row_bytes + cv.idx_off;
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int tb = tok0 + kTileTok * j;
-    if (active && tb < ctx) {
-      if (PAGED32) {
-        const uint8_t* tile = row_base(cv, token_block(cv, rm, seq, tb)) + cv.idx_off + (int64_t)(tb & bs_mask) * kDIdx;
+    const int tb = j ? tb1 : tb0;
+    if (PAGED32) {
+      const uint8_t* tile = cv.pool + toff[j] + (int64_t)(tb & bs_mask) * kDIdx;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          kv[j][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(tile + 1024 * i + 16 * lane));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int t = tb + 8 * i + (lane >> 3);
-          t = t < ctx ? t : ctx - 1;
-          const uint8_t* key = row_base(cv, token_block(cv, rm, seq, t)) + cv.idx_off + (int64_t)(t & bs_mask) * kDIdx;
-          kv[j][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(key + 16 * (lane & 7)));
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        kv[j][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(tile + 1024 * i + 16 * lane));
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kv[j][i] = v4i{0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) {
+        int t = tb + 8 * i + (lane >> 3);
+        t = t < ctx ? t : ctx - 1;
+        const uint8_t* key = row_base(cv, token_block(cv, rm, seq, t)) + cv.idx_off + (int64_t)(t & bs_mask) * kDIdx;
+        kv[j][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(key + 16 * (lane & 7)));
+      }
     }
   }
-  // key scale of token tok0 + lane
-  float ksc = 0.f;
-  if (active) {
+  // key scale of token tok0 + lane (clamped into the row); with PAGED32 the token's
+  // page is one of the two tiles' pages (uniform addresses), so the load does not
+  // wait behind the key loads
+  float ksc;
+  {
     int t = tok0 + lane;
     t = t < ctx ? t : ctx - 1;
-    const uint8_t* page = row_base(cv, token_block(cv, rm, seq, t)) + cv.idx_off;
-    ksc = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDIdx + (int64_t)(t & bs_mask) * 4);
+    const int64_t off = PAGED32 ? ((t & ~(kTileTok - 1)) == tb1 ? toff[1] : toff[0])
+                                : token_block(cv, rm, seq, t) * cv.row_bytes + cv.idx_off;
+    ksc = *reinterpret_cast<const float*>(cv.pool + off + (int64_t)cv.block_size * kDIdx + (int64_t)(t & bs_mask) * 4);
   }
 
-  // ---- query fragment (head n, bytes [64g, 64g+64)) and folded head weights ----
-  v8bf qa[8];
+  // ---- query fragment (head n, bytes [64g, 64g+64)) and folded head weights, issued
+  // behind the key stream (needed only once keys are in) ----
+  v4i qr[4];
   {
     const v4i* qp = reinterpret_cast<const v4i*>(q_idx + ((int64_t)r * kHIdx + n) * kDIdx + 64 * g);
-    v4i qr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) qr[i] = qp[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qa[2 * i] = e4m3x8_to_bf16((uint32_t)qr[i][0], (uint32_t)qr[i][1]);
-      qa[2 * i + 1] = e4m3x8_to_bf16((uint32_t)qr[i][2], (uint32_t)qr[i][3]);
-    }
   }
+  float W[kHIdx];
+#pragma unroll
+  for (int h = 0; h < kHIdx; ++h)  // uniform: scalar loads, kept in scalar registers
+    W[h] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w[r * kHIdx + h] * q_scale[r * kHIdx + h])));
+
+  // every load of the wave is in flight before anything waits on one
+  __builtin_amdgcn_sched_barrier(0);
+  if (past) return;  // whole workgroup, no barrier reached
+
+  v8bf qa[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qa[2 * i] = e4m3x8_to_bf16((uint32_t)qr[i][0], (uint32_t)qr[i][1]);
+    qa[2 * i + 1] = e4m3x8_to_bf16((uint32_t)qr[i][2], (uint32_t)qr[i][3]);
+  }
+  // accumulator element rr of lane (n, g) is head 8 (rr >> 2) + 4 g + (rr & 3)
   float wq[16];
-  {
-    float W[kHIdx];
 #pragma unroll
-    for (int h = 0; h < kHIdx; ++h) W[h] = w[r * kHIdx + h] * q_scale[r * kHIdx + h];  // uniform loads
-    // accumulator element rr of lane (n, g) is head 8 (rr >> 2) + 4 g + (rr & 3)
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) wq[rr] = g ? W[8 * (rr >> 2) + 4 + (rr & 3)] : W[8 * (rr >> 2) + (rr & 3)];
-  }
+  for (int rr = 0; rr < 16; ++rr) wq[rr] = g ? W[8 * (rr >> 2) + 4 + (rr & 3)] : W[8 * (rr >> 2) + (rr & 3)];
 
   // ---- per tile: swizzled LDS transpose, 8 bf16 MFMAs, ReLU + weighted head sum ----
   const int wpos = swz(lane >> 3, lane & 7);  // where this lane's chunk of each kilobyte goes
