@@ -9,11 +9,16 @@
 //
 // Grid (split, row, head group of 32). A workgroup walks its split's slice of the
 // row's index list 64 tokens at a time:
-//   translate the 64 token ids to latent row offsets once (block table lookups),
-//   then gather the 64 latents (576 e4m3 bytes each) into LDS;
-//   S = Q . C^T on 16x16x32 bf16 MFMAs (each wave: 16 tokens x 32 heads);
-//   online softmax in the log2 domain (running max / sum per head);
-//   P'' = p * scale_t / (largest scale in the chunk), in [0, 1], as fp16 in LDS;
+//   the chunk's token ids / page slots are the head of a load chain (ids -> latent
+//   rows), so they are fetched first (the next chunk's behind the current latents);
+//   gather the 64 latents (576 e4m3 bytes each) into LDS;
+//   S = Q . C^T on 16x16x32 bf16 MFMAs (each wave: 16 tokens x 32 heads), scaled
+//   logits (log2 domain) to LDS;
+//   every wave then runs the online softmax of the whole chunk for the 32 heads
+//   itself (running max / sum per head, identical in every wave), so one barrier
+//   separates S from P . V;
+//   P'' = p * scale_t / (largest scale in the chunk), in [0, 1], as fp16 straight
+//   into the MFMA operand registers;
 //   O += P'' . codes on 32x32x16 fp16 MFMAs (each wave: 128 of the 512 value
 //   columns); e4m3 codes are exact in fp16, and fp16 P keeps 11 significant bits
 //   (bf16's 8 were visibly too few on rows dominated by a handful of tokens).
@@ -34,6 +39,7 @@ constexpr int CH = kMlaChunk;           // 64 tokens per iteration
 constexpr int PIECES = kDLat / 16;      // 36 16-byte pieces per latent
 constexpr int QROW = kDLat + 8;         // LDS row strides padded by 16 bytes so that the
 constexpr int LROW = kDLat + 16;        // 16 rows an MFMA fragment reads fall in distinct banks
+constexpr int XROW = CH + 16;           // logit rows: the four 16-lane groups of a store hit distinct banks
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
@@ -50,59 +56,59 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
                                                         int nsplit) {
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 5;  // half of the wave
 
   __shared__ __attribute__((aligned(16))) uint16_t q_s[kMlaGroup * QROW];
   __shared__ __attribute__((aligned(16))) uint8_t lat_s[CH * LROW];
-  __shared__ __attribute__((aligned(16))) _Float16 p_s[kMlaGroup * CH];
-  __shared__ float sc_s[CH];
-  __shared__ float red_s[4][kMlaGroup];
-  __shared__ float m_s[kMlaGroup], l_s[kMlaGroup], alpha_s[kMlaGroup];
+  __shared__ __attribute__((aligned(16))) float x_s[kMlaGroup * XROW];  // scaled logits, head-major
+  __shared__ __attribute__((aligned(16))) float sc_s[CH];
+  __shared__ __attribute__((aligned(16))) float hv_s[4][kMlaGroup];  // per-wave exchange of per-head values
 
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
   const int j1 = (j0 + ts < k) ? j0 + ts : k;
   const int seq = rm.row_seq[r];
   const int bs_mask = cv.block_size - 1;
+  const int tt_g = tid >> 2, qtr = tid & 3;  // gather: 4 threads per token, 9 pieces each
 
-  // Q fragment rows for this head group, straight to LDS (all loads issued first).
+  // token id and page slot of this thread's gather token: the head of the load chain,
+  // issued before anything else
+  int t_n = -1, ps_n = 0;
   {
-    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * kMlaGroup) * kDLat);
-    constexpr int QP = kDLat / 8;  // 72 16-byte pieces per head row
-    constexpr int QN = kMlaGroup * QP / NT;
-    static_assert(QN * NT == kMlaGroup * QP, "Q pieces per thread");
-    v4i qv[QN];
-#pragma unroll
-    for (int q = 0; q < QN; ++q) qv[q] = qg[tid + NT * q];
-#pragma unroll
-    for (int q = 0; q < QN; ++q) {
-      const int i = tid + NT * q, h = i / QP, pc = i - h * QP;
-      *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
+    const int j = j0 + tt_g;
+    if (j < j1) {
+      t_n = irow[j];
+      if (phys != nullptr) ps_n = phys[(int64_t)r * k + j];
     }
   }
-  if (tid < kMlaGroup) {
-    m_s[tid] = kNegInf;
-    l_s[tid] = 0.f;
+  // Q fragment rows for this head group (to LDS once the first latents are in flight)
+  constexpr int QP = kDLat / 8;  // 72 16-byte pieces per head row
+  constexpr int QN = kMlaGroup * QP / NT;
+  static_assert(QN * NT == kMlaGroup * QP, "Q pieces per thread");
+  v4i qv[QN];
+  {
+    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * kMlaGroup) * kDLat);
+#pragma unroll
+    for (int q = 0; q < QN; ++q) qv[q] = qg[tid + NT * q];
   }
 
+  // running softmax state of head (lane & 31); every wave keeps an identical copy
+  float m_run = kNegInf, l_run = 0.f;
   v16f acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = v16f{};
   float s_run = 1.f;  // acc holds O / s_run (token scales folded into P per chunk)
 
   for (int c0 = j0; c0 < j1; c0 += CH) {
-    // ---- gather: 4 threads per token; each looks up its token's latent row and
-    // issues its 9 of the 36 16-byte pieces (and the scale) right away ----
+    // ---- gather: each thread issues its 9 of the token's 36 16-byte pieces (and the
+    // scale); the next chunk's ids are fetched behind them ----
     {
-      const int tt = tid >> 2, qtr = tid & 3;
-      const int j = c0 + tt;
-      int t = j < j1 ? irow[j] : -1;
-      t = t < rm.max_ctx ? t : -1;
+      int t = t_n < rm.max_ctx ? t_n : -1;
       const int tc = t >= 0 ? t : 0;  // every load below stays in the pool; empty slots are masked
       int64_t blk;
       int slot;
       if (phys != nullptr) {
-        int ps = j < j1 ? phys[(int64_t)r * k + j] : 0;
-        ps = ps >= 0 ? ps : 0;
+        const int ps = ps_n >= 0 ? ps_n : 0;
         blk = (int64_t)ps >> cv.log2_bs;
         blk = blk < cv.num_blocks ? blk : cv.num_blocks - 1;
         slot = ps & bs_mask;
@@ -118,13 +124,28 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       v4i v[PN];
 #pragma unroll
       for (int q = 0; q < PN; ++q) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (qtr + 4 * q));
+      if (c0 == j0) {
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+          const int i = tid + NT * q, h = i / QP, pc = i - h * QP;
+          *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
+        }
+      }
+      {
+        const int j = c0 + CH + tt_g;
+        t_n = -1;
+        if (j < j1) {
+          t_n = irow[j];
+          if (phys != nullptr) ps_n = phys[(int64_t)r * k + j];
+        }
+      }
 #pragma unroll
       for (int q = 0; q < PN; ++q)
-        *reinterpret_cast<v4i*>(lat_s + tt * LROW + 16 * (qtr + 4 * q)) = t >= 0 ? v[q] : v4i{0, 0, 0, 0};
-      if (qtr == 0) sc_s[tt] = t >= 0 ? sv : kNegInf;  // -inf marks an empty slot
+        *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (qtr + 4 * q)) = t >= 0 ? v[q] : v4i{0, 0, 0, 0};
+      if (qtr == 0) sc_s[tt_g] = t >= 0 ? sv : kNegInf;  // -inf marks an empty slot
     }
     __syncthreads();
-    // largest token scale of the chunk, computed by every wave (no extra barrier)
+    // largest token scale of the chunk, computed by every wave
     float smax;
     {
       float v = sc_s[lane];
@@ -137,9 +158,10 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       smax = v > 0.f ? v : 1.f;
     }
 
-    // ---- S = Q . C^T : wave w -> tokens [16w, 16w+16), heads 0..31 ----
-    v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- S = Q . C^T : wave w -> tokens [16w, 16w+16), heads 0..31; scaled logits
+    // (log2 domain) go to LDS ----
     {
+      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
       const int hrow = lane & 15, kq = 8 * (lane >> 4);
       const uint8_t* lrow = lat_s + (16 * wid + hrow) * LROW + kq;
       const uint16_t* qa0 = q_s + hrow * QROW + kq;
@@ -153,87 +175,77 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, s1, 0, 0, 0);
       }
-    }
-    const int tt = 16 * wid + (lane & 15);
-    const float sct = sc_s[tt];
-    const bool ok = sct != kNegInf;
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = ok ? s0[i] * (sct * c2) : kNegInf;
-      x[4 + i] = ok ? s1[i] * (sct * c2) : kNegInf;
-    }
-    float mx[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = x[i];
-      v = fmaxf(v, xshflf<1>(v));
-      v = fmaxf(v, xshflf<2>(v));
-      v = fmaxf(v, xshflf<4>(v));
-      v = fmaxf(v, xshflf<8>(v));
-      mx[i] = v;
-    }
-    const int hb = 4 * (lane >> 4);
-    if ((lane & 15) == 0) {
+      const int tt = 16 * wid + hrow;
+      const float sct = sc_s[tt];
+      const bool ok = sct != kNegInf;
+      const int hb = 4 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        red_s[wid][hb + i] = mx[i];
-        red_s[wid][16 + hb + i] = mx[4 + i];
+        x_s[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
+        x_s[(16 + hb + i) * XROW + tt] = ok ? s1[i] * (sct * c2) : kNegInf;
       }
     }
     __syncthreads();
-    if (tid < kMlaGroup) {
-      float cm = fmaxf(fmaxf(red_s[0][tid], red_s[1][tid]), fmaxf(red_s[2][tid], red_s[3][tid]));
-      float mo = m_s[tid];
-      float mn = fmaxf(mo, cm);
-      alpha_s[tid] = (mn == kNegInf) ? 1.f : exp2f(mo - mn);
-      m_s[tid] = mn;
-    }
-    __syncthreads();
-    // p = 2^(x - m); P'' = p * scale_t / smax in [0, 1] goes to the fp16 MFMA
-    float ps[8];
-    const float sfac = ok ? sct / smax : 0.f;
+
+    // ---- softmax of head h = lane & 31 over the chunk, by every wave: this lane's
+    // 32 tokens are the ones its P fragments cover (16 ks + 8 g + e) ----
+    v8h pa[4];
+    float alpha;
+    {
+      const int h = lane & 31;
+      float xv[4][8], sv[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int h = (i < 4) ? hb + i : 16 + hb + (i - 4);
-      float p = (x[i] == kNegInf) ? 0.f : exp2f(x[i] - m_s[h]);
-      ps[i] = p;
-      p_s[h * CH + tt] = (_Float16)(p * sfac);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = ps[i];
-      v += xshflf<1>(v);
-      v += xshflf<2>(v);
-      v += xshflf<4>(v);
-      v += xshflf<8>(v);
-      ps[i] = v;
-    }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        red_s[wid][hb + i] = ps[i];
-        red_s[wid][16 + hb + i] = ps[4 + i];
+      for (int ks = 0; ks < 4; ++ks) {
+        const float4* xp = reinterpret_cast<const float4*>(x_s + h * XROW + 16 * ks + 8 * g);
+        const float4* sp = reinterpret_cast<const float4*>(sc_s + 16 * ks + 8 * g);
+        const float4 x0 = xp[0], x1 = xp[1], q0 = sp[0], q1 = sp[1];
+        xv[ks][0] = x0.x; xv[ks][1] = x0.y; xv[ks][2] = x0.z; xv[ks][3] = x0.w;
+        xv[ks][4] = x1.x; xv[ks][5] = x1.y; xv[ks][6] = x1.z; xv[ks][7] = x1.w;
+        sv[ks][0] = q0.x; sv[ks][1] = q0.y; sv[ks][2] = q0.z; sv[ks][3] = q0.w;
+        sv[ks][4] = q1.x; sv[ks][5] = q1.y; sv[ks][6] = q1.z; sv[ks][7] = q1.w;
       }
-    }
-    __syncthreads();
-    if (tid < kMlaGroup) {
-      l_s[tid] = l_s[tid] * alpha_s[tid] + (red_s[0][tid] + red_s[1][tid] + red_s[2][tid] + red_s[3][tid]);
+      float cm = kNegInf;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cm = fmaxf(cm, xv[ks][e]);
+      cm = fmaxf(cm, xshflf<32>(cm));
+      const float mn = fmaxf(m_run, cm);
+      alpha = (mn == kNegInf) ? 1.f : exp2f(m_run - mn);
+      const float inv_smax = 1.f / smax;
+      float psum = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = (xv[ks][e] == kNegInf) ? 0.f : exp2f(xv[ks][e] - mn);
+          psum += p;
+          const float sfac = sv[ks][e] != kNegInf ? sv[ks][e] * inv_smax : 0.f;
+          pa[ks][e] = (_Float16)(p * sfac);
+        }
+      }
+      psum += xshflf<32>(psum);
+      l_run = l_run * alpha + psum;
+      m_run = mn;
     }
 
     // ---- acc = acc * alpha * (s_run / smax) + P'' . codes : wave w -> columns [128w, 128w+128) ----
+    // accumulator row rr of this lane is head 8 (rr >> 2) + 4 g + (rr & 3)
+    if (lane < kMlaGroup) hv_s[wid][lane] = alpha;  // read back by this wave only
     const float rescale = s_run / smax;
     s_run = smax;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      float a = alpha_s[8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3)] * rescale;
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&hv_s[wid][8 * jj + 4 * g]);
+      const float a[4] = {a4.x * rescale, a4.y * rescale, a4.z * rescale, a4.w * rescale};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c][rr] *= a;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c][4 * jj + i] *= a[i];
     }
 #pragma unroll
     for (int ks = 0; ks < CH / 16; ++ks) {
-      const int tk = 16 * ks + 8 * (lane >> 5);
-      v8h a = *reinterpret_cast<const v8h*>(p_s + (lane & 31) * CH + tk);
+      const int tk = 16 * ks + 8 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int col = 128 * wid + 32 * c + (lane & 31);
@@ -243,63 +255,87 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
         uint32_t w1 = (uint32_t)vp[4 * LROW] | ((uint32_t)vp[5 * LROW] << 8) | ((uint32_t)vp[6 * LROW] << 16) |
                       ((uint32_t)vp[7 * LROW] << 24);
         v8h b = e4m3x8_to_f16(w0, w1);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, acc[c], 0, 0, 0);
       }
     }
-    __syncthreads();
+    __syncthreads();  // lat_s, x_s, sc_s and hv_s are rewritten by the next chunk
   }
 
-  __syncthreads();
   // ---- epilogue ----
   if (nsplit == 1) {
+    if (lane < kMlaGroup) hv_s[wid][lane] = l_run;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int h = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-      const float lv = l_s[h];
-      const float f = lv > 0.f ? s_run / lv : 0.f;
-      float* orow = out + ((int64_t)r * kHQ + hg * kMlaGroup + h) * kDV + 128 * wid + (lane & 31);
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&hv_s[wid][8 * jj + 4 * g]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][rr] * f;
+      for (int i = 0; i < 4; ++i) {
+        const int h = 8 * jj + 4 * g + i;
+        const float f = lv[i] > 0.f ? s_run / lv[i] : 0.f;
+        float* orow = out + ((int64_t)r * kHQ + hg * kMlaGroup + h) * kDV + 128 * wid + (lane & 31);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][4 * jj + i] * f;
+      }
     }
-    if (lse != nullptr && tid < kMlaGroup) {
-      float lv = l_s[tid];
-      lse[(int64_t)r * kHQ + hg * kMlaGroup + tid] = lv > 0.f ? (m_s[tid] + log2f(lv)) * 0.69314718055994531f : kNegInf;
-    }
+    if (lse != nullptr && tid < kMlaGroup)
+      lse[(int64_t)r * kHQ + hg * kMlaGroup + tid] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : kNegInf;
   } else {
     const int64_t pbase = ((int64_t)r * nsplit + split) * kHQ + hg * kMlaGroup;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int h = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+      const int h = 8 * (rr >> 2) + 4 * g + (rr & 3);
       float* orow = part_o + (pbase + h) * kDV + 128 * wid + (lane & 31);
 #pragma unroll
       for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][rr] * s_run;
     }
     if (tid < kMlaGroup) {
-      part_ml[(pbase + tid) * 2 + 0] = m_s[tid];
-      part_ml[(pbase + tid) * 2 + 1] = l_s[tid];
+      part_ml[(pbase + tid) * 2 + 0] = m_run;
+      part_ml[(pbase + tid) * 2 + 1] = l_run;
     }
   }
 }
 
-// out[r][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s ; empty splits (m = -inf) weigh 0.
+// out[r][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s ; empty splits (m = -inf)
+// weigh 0. Lane s of every wave reads split s's (m, l); each thread then loads its two
+// value columns of every split at once (splits past nsplit repeat the last one with
+// weight 0), so the whole merge is one round of loads.
 __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml, int nsplit,
                                                        float* __restrict__ out, float* __restrict__ lse) {
-  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  constexpr int MS = kMaxK / kMlaChunk;  // most splits a row can have
+  static_assert(MS <= 64, "one split per lane");
+  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (int64_t)r * nsplit * kHQ + h;
-  float M = kNegInf;
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[(int64_t)s * kHQ].x);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  const float2 e = lane < nsplit ? ml[(int64_t)lane * kHQ] : float2{kNegInf, 0.f};
   const float* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + tid;
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 e = ml[(int64_t)s * kHQ];
-    const float x0 = po[(int64_t)s * kHQ * kDV], x1 = po[(int64_t)s * kHQ * kDV + NT];
-    const float wgt = (e.x == kNegInf) ? 0.f : exp2f(e.x - M);
-    L = fmaf(wgt, e.y, L);
-    o0 = fmaf(wgt, x0, o0);
-    o1 = fmaf(wgt, x1, o1);
+  float x0[MS], x1[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const int sc = s < nsplit ? s : nsplit - 1;
+    x0[s] = po[(int64_t)sc * kHQ * kDV];
+    x1[s] = po[(int64_t)sc * kHQ * kDV + NT];
+  }
+  float M = e.x;
+  M = fmaxf(M, xshflf<1>(M));
+  M = fmaxf(M, xshflf<2>(M));
+  M = fmaxf(M, xshflf<4>(M));
+  M = fmaxf(M, xshflf<8>(M));
+  M = fmaxf(M, xshflf<16>(M));
+  M = fmaxf(M, xshflf<32>(M));
+  const float wgt = (e.x == kNegInf) ? 0.f : exp2f(e.x - M);
+  float L = wgt * e.y;
+  L += xshflf<1>(L);
+  L += xshflf<2>(L);
+  L += xshflf<4>(L);
+  L += xshflf<8>(L);
+  L += xshflf<16>(L);
+  L += xshflf<32>(L);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s));
+    o0 = fmaf(ws, x0[s], o0);
+    o1 = fmaf(ws, x1[s], o1);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float* orow = out + ((int64_t)r * kHQ + h) * kDV;
