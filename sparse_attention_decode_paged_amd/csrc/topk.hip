@@ -51,6 +51,7 @@ constexpr int NREP = 8;              // histogram copies
 constexpr int XPER = 8;              // rescanned keys per thread
 constexpr int ECAP = XPER * SEL_NT;  // rescanned keys a row may hold in LDS
 constexpr int FCAP = 512;            // rescanned units a row may hold in LDS
+constexpr int BTCAP = 4096;          // block-table entries of a row staged in LDS (16 KB)
 static_assert(PER * SEL_NT == kCandRowCap && PER * SEL_NT == kTopkFullRow, "register tiling");
 static_assert(NBIN == 2 * SEL_NT, "two histogram bins per thread");
 
@@ -80,9 +81,10 @@ struct SelShared {
   uint64_t res64;
   uint32_t r32[2][2][NW];  // block min / max partials, double buffered
   uint32_t scan[2][NW];    // block prefix partials, double buffered
-  uint32_t scan4[NW][4];   // per-wave totals of four prefix sums
+  uint32_t scan4[4][NW];   // per-wave totals of four prefix sums
   uint32_t res[4];
   uint32_t ecount, bcount;
+  int32_t bt[BTCAP];  // the row's block-table entries (clamped into the pool) when they fit
 };
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -104,21 +106,30 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Combines the NW per-wave totals p[0..NW) (LDS): lane w of every wave reads p[w], a
+// 16-lane DPP scan runs over them, and two lane reads give the sum over the waves
+// below this one (`before`) and the total.
+__device__ __forceinline__ uint32_t wave_totals(const uint32_t* p, uint32_t& before) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = lane < NW ? p[lane] : 0u;
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  before = wid > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)x, wid - 1) : 0u;
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, NW - 1);
+}
+
 // Exclusive prefix sum over the threads in thread order; `total` gets the sum.
 __device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t& total, SelShared& S, int& par) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v);
   if (lane == 63) S.scan[par][wid] = inc;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t x = S.scan[par][w];
-    before += w < wid ? x : 0u;
-    tot += x;
-  }
+  uint32_t before;
+  total = wave_totals(S.scan[par], before);
   par ^= 1;
-  total = tot;
   return before + inc - v;
 }
 
@@ -131,18 +142,13 @@ __device__ __forceinline__ void excl_scan4(const uint32_t (&v)[4], uint32_t (&of
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (j < nj) inc[j] = wave_incl_scan(v[j]);  // nj is block-uniform
-    if (lane == 63) S.scan4[wid][j] = inc[j];
+    if (lane == 63) S.scan4[j][wid] = inc[j];
   }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t x = S.scan4[w][j];
-      before += w < wid ? x : 0u;
-      tot += x;
-    }
+    if (j < nj) tot = wave_totals(S.scan4[j], before);
     off[j] = before + inc[j] - v[j];
     total[j] = tot;
   }
@@ -359,10 +365,35 @@ __device__ __forceinline__ int32_t page_slot(const CacheView& cv, const RowMap& 
 
 __device__ __forceinline__ int key_token(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
 
+// Page slot of token t, from the staged block-table row when `btl`.
+__device__ __forceinline__ int32_t slot_of(const SelShared& S, bool btl, const CacheView& cv, const RowMap& rm, int seq,
+                                           int t) {
+  if (btl) return S.bt[t >> cv.log2_bs] * cv.block_size + (t & (cv.block_size - 1));
+  return page_slot(cv, rm, seq, t);
+}
+
+// Second half of the output write: S.a.hist (free once the search is done) holds the
+// `total` selected tokens in output order; every thread writes positions tid and
+// tid + 1024 of the index row (and of the page-slot row), -1 past the selection.
+__device__ __forceinline__ void flush_selection(uint32_t total, int k, int32_t* __restrict__ orow,
+                                                int32_t* __restrict__ prow, const CacheView& cv, const RowMap& rm,
+                                                int seq, bool btl, const SelShared& S) {
+  const uint32_t nout = total < (uint32_t)k ? total : (uint32_t)k;
+#pragma unroll
+  for (int q = 0; q < kMaxK / SEL_NT; ++q) {
+    const int i = (int)threadIdx.x + SEL_NT * q;
+    if (i < k) {
+      const int t = (uint32_t)i < nout ? (int)S.a.hist[i] : -1;
+      orow[i] = t;
+      if (prow) prow[i] = t >= 0 ? slot_of(S, btl, cv, rm, seq, t) : -1;
+    }
+  }
+}
+
 // Writes, in element order (token order), the tokens whose key is >= cstar, then
 // -1 up to k; with `prow` also their page slots.
 __device__ __forceinline__ void ordered_write(const uint64_t (&e)[PER], uint64_t cstar, int k, int32_t* __restrict__ orow,
-                              int32_t* __restrict__ prow, const CacheView& cv, const RowMap& rm, int seq,
+                              int32_t* __restrict__ prow, const CacheView& cv, const RowMap& rm, int seq, bool btl,
                               SelShared& S, int& par) {
   uint32_t bits = 0, cnt = 0;
 #pragma unroll
@@ -372,22 +403,14 @@ __device__ __forceinline__ void ordered_write(const uint64_t (&e)[PER], uint64_t
       ++cnt;
     }
   uint32_t total;
-  uint32_t off = excl_scan(cnt, total, S, par);
+  const uint32_t off = excl_scan(cnt, total, S, par);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    if ((bits >> i) & 1u) {
-      if (off < (uint32_t)k) {
-        const int t = key_token(e[i]);
-        orow[off] = t;
-        if (prow) prow[off] = page_slot(cv, rm, seq, t);
-      }
-      ++off;
-    }
+    const uint32_t o = off + (uint32_t)__popc(bits & ((1u << i) - 1u));
+    if (((bits >> i) & 1u) && o < (uint32_t)k) S.a.hist[o] = (uint32_t)key_token(e[i]);
   }
-  for (int i = (int)total + threadIdx.x; i < k; i += SEL_NT) {
-    orow[i] = -1;
-    if (prow) prow[i] = -1;
-  }
+  __syncthreads();
+  flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
 }
 
 // Exact selection over the whole row straight from global memory (8-bit digits,
@@ -506,6 +529,32 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
     return;
   }
 
+  // the row's block-table entries for the page slots of the output, loaded now and
+  // staged in LDS (visible after the search's first barrier); one dependent global
+  // load per written token would otherwise sit on the write path
+  const int nblk = (ctx + cv.block_size - 1) >> cv.log2_bs;
+  const bool btl = prow != nullptr && nblk <= BTCAP;
+  int32_t bv[BTCAP / SEL_NT];
+  if (btl) {
+    const int32_t* btr = rm.block_table + (int64_t)seq * rm.bt_stride;
+#pragma unroll
+    for (int q = 0; q < BTCAP / SEL_NT; ++q) {
+      const int i = tid + SEL_NT * q;
+      bv[q] = i < nblk ? btr[i] : 0;
+    }
+  }
+  auto stage_bt = [&]() {
+    if (!btl) return;
+    const int64_t nb = cv.num_blocks;
+#pragma unroll
+    for (int q = 0; q < BTCAP / SEL_NT; ++q) {
+      const int i = tid + SEL_NT * q;
+      int64_t b = bv[q];
+      if ((uint64_t)b >= (uint64_t)nb) b = b < 0 ? 0 : nb - 1;
+      if (i < nblk) S.bt[i] = (int32_t)b;
+    }
+  };
+
   uint64_t e[PER];
   const CandPlan p = cand_plan(ctx);
   if (p.unit == 0) {
@@ -531,8 +580,9 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
       const int t = t0 + i;
       e[i] = t < ctx ? composite_key(f[i], t) : 0ull;
     }
+    stage_bt();
     const uint64_t cstar = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
-    ordered_write(e, cstar, k, orow, prow, cv, rm, seq, S, par);
+    ordered_write(e, cstar, k, orow, prow, cv, rm, seq, btl, S, par);
     return;
   }
 
@@ -555,6 +605,7 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
     const int u = tid + SEL_NT * j;
     fl[j] = (j < upt && u < nu) ? rf[u] : 0u;
   }
+  stage_bt();
   const uint64_t cu = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
 
   // units whose kept-back keys may reach cu
@@ -668,18 +719,15 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     if ((fmask >> j) & 1u) S.foff[fbase + (uint32_t)__popc(fmask & ((1u << j) - 1u))] = off[j];
+  // selected tokens go to their output positions in an LDS list first (the histogram
+  // is free now), then one coalesced pass writes the index and page-slot rows
+  uint32_t* list = S.a.hist;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    if ((bits >> i) & 1u) {
-      const int j = i >> lm;
-      const uint32_t oj = j == 0 ? off[0] : j == 1 ? off[1] : j == 2 ? off[2] : off[3];
-      const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
-      if (o < (uint32_t)k) {
-        const int t = key_token(e[i]);
-        orow[o] = t;
-        if (prow) prow[o] = page_slot(cv, rm, seq, t);
-      }
-    }
+    const int j = i >> lm;
+    const uint32_t oj = j == 0 ? off[0] : j == 1 ? off[1] : j == 2 ? off[2] : off[3];
+    const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
+    if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = (uint32_t)key_token(e[i]);
   }
   if (nflag > 0) {
     __syncthreads();
@@ -691,19 +739,13 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
         const bool sel = c != 0ull && c >= cstar;
         const uint64_t bal = __ballot(sel);
         const uint32_t pos = o + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        if (sel && pos < (uint32_t)k) {
-          const int t = key_token(c);
-          orow[pos] = t;
-          if (prow) prow[pos] = page_slot(cv, rm, seq, t);
-        }
+        if (sel && pos < (uint32_t)k) list[pos] = (uint32_t)key_token(c);
         o += (uint32_t)__popcll(bal);
       }
     }
   }
-  for (int i = (int)total + tid; i < k; i += SEL_NT) {
-    orow[i] = -1;
-    if (prow) prow[i] = -1;
-  }
+  __syncthreads();
+  flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
 }
 
 hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx,
