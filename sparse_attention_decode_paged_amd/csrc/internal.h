@@ -19,7 +19,7 @@ constexpr int kFloorRowCap = kMaxCtx / 256;  // units of a row, at most
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct TopkWs {
-  uint64_t* cand;    // [R][kCandRowCap]: key of rank q of unit u at q * nu + u
+  uint64_t* cand;    // [R][kCandRowCap]: key of rank q of unit u at cand_slot(q, u, m)
   uint32_t* floors;  // [R][kFloorRowCap]: score word bounding the keys a unit did not send (0: sent all)
 };
 

@@ -19,21 +19,25 @@
 // Stage 2 (topk_select_kernel, one 1024-thread workgroup per row). Every thread
 // holds up to 16 keys in registers:
 //   ctx <= k      every token;
-//   ctx <= 16384  the row's own keys, tokens [16 t, 16 t + 16) on thread t;
+//   launches whose row-length bound is at most 16384: the row's own keys, tokens
+//                 [16 t, 16 t + 16) on thread t;
 //   otherwise     the candidates of units t + 1024 j (j < units per thread), read
-//                 rank-major so that each load instruction covers 64 consecutive
-//                 units. c_u = their k-th largest key. A unit whose floor reaches
-//                 c_u may hold unsent keys >= c_u: waves rescan such units' scores
-//                 (the "resend") into a compact LDS list, the unit's candidates leave
-//                 the register set, and the k-th largest of the union is the answer.
+//                 slot-major so that each load instruction covers 64 consecutive
+//                 units and no address depends on the row length (the loads start
+//                 with the kernel). c_u = their k-th largest key. A unit whose floor
+//                 reaches c_u may hold unsent keys >= c_u: waves rescan such units'
+//                 scores (the "resend") into a compact LDS list, the unit's
+//                 candidates leave the register set, and the k-th largest of the
+//                 union is the answer.
 // The k-th largest key: the score words of the live keys share their bits above
 // the highest bit in which they differ; an 11-bit digit histogram over the next
 // bits (8 copies, lane l adding into copy l % 8, so at most 8 lanes of one
 // instruction hit one LDS word) fixes the bucket of the k-th key. A bucket of at
 // most 64 keys is gathered into LDS and one wave sorts it (64-bit keys, so equal
 // scores order by token); a larger one takes another pass over lower bits. The
-// selection is written in token order: per-unit counts, one block prefix sum over
-// units, then each thread writes its units' selected keys.
+// selection is written in token order: per-unit counts and one block prefix sum over
+// units place every selected token in an LDS list, which one coalesced pass then
+// writes out with the tokens' page slots (block-table row staged in LDS).
 #include "common.h"
 #include "internal.h"
 #include "topk_send.h"
@@ -208,23 +212,28 @@ template <int N, bool EXTRA>
 __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const uint64_t* xs, uint32_t nx, uint32_t need,
                                 SelShared& S, int& par) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  auto key = [&](int i) -> uint64_t {
-    if (i < N) return e[i];
-    const uint32_t p = (uint32_t)tid + (uint32_t)(i - N) * SEL_NT;
-    return p < nx ? xs[p] : 0ull;
+  // fn(key) over the register keys, then (only when the LDS list is not empty, a
+  // uniform branch) over xs[tid + SEL_NT x], x < XPER
+  auto for_keys = [&](auto&& fn) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) fn(e[i]);
+    if (EXTRA && nx > 0) {
+#pragma unroll
+      for (int x = 0; x < XPER; ++x) {
+        const uint32_t p = (uint32_t)tid + (uint32_t)x * SEL_NT;
+        fn(p < nx ? xs[p] : 0ull);
+      }
+    }
   };
-  constexpr int NK = N + (EXTRA ? XPER : 0);
   clear_hist(S);  // ordered before the first pass by the min / max barrier
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const uint64_t v = key(i);
+  for_keys([&](uint64_t v) {
     const uint32_t w = (uint32_t)(v >> 32);
     if (v != 0ull) {
       lo = min(lo, w);
       hi = max(hi, w);
     }
-  }
+  });
   block_minmax32(lo, hi, S, par);
   // score-word bits fixed so far: (w & mask) == prefix
   // bits above `top` are common to every live score word; (w & mask) == prefix
@@ -245,12 +254,10 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const ui
     }
     first = false;
     const uint32_t rep = (uint32_t)tid & (NREP - 1);
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const uint64_t v = key(i);
+    for_keys([&](uint64_t v) {
       const uint32_t w = (uint32_t)(v >> 32);
       if (v != 0ull && (w & mask) == prefix) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
-    }
+    });
     __syncthreads();
     // thread t holds bins NBIN-1-2t (upper) and NBIN-2-2t: thread order = descending digits
     uint32_t h0, h1;
@@ -286,8 +293,7 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const ui
   if (top < 0 && cnt == 0u) {
     // no pass ran (one score word): count the bucket
     uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < NK; ++i) c += key(i) != 0ull ? 1u : 0u;
+    for_keys([&](uint64_t v) { c += v != 0ull ? 1u : 0u; });
     uint32_t unused;
     excl_scan(c, unused, S, par);
     cnt = unused;
@@ -295,11 +301,9 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const ui
   if (cnt <= 64u) {
     if (tid == 0) S.bcount = 0u;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const uint64_t v = key(i);
+    for_keys([&](uint64_t v) {
       if (v != 0ull && ((uint32_t)(v >> 32) & mask) == prefix) S.bucket[atomicAdd(&S.bcount, 1u) & 63u] = v;
-    }
+    });
     __syncthreads();
     if (wid == 0) {
       const uint64_t v = (uint32_t)lane < cnt ? S.bucket[lane] : 0ull;
@@ -324,13 +328,11 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const ui
     clear_hist(S);
     __syncthreads();
     const uint32_t rep = (uint32_t)tid & (NREP - 1);
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const uint64_t v = key(i);
+    for_keys([&](uint64_t v) {
       const uint32_t lw = (uint32_t)v;
       if (v != 0ull && ((uint32_t)(v >> 32) & mask) == prefix && (lw & lmask) == lprefix)
         atomicAdd(&S.a.hist[((lw >> s0) & dm) * NREP + rep], 1u);
-    }
+    });
     __syncthreads();
     uint32_t h0, h1;
     {
@@ -388,29 +390,6 @@ __device__ __forceinline__ void flush_selection(uint32_t total, int k, int32_t* 
       if (prow) prow[i] = t >= 0 ? slot_of(S, btl, cv, rm, seq, t) : -1;
     }
   }
-}
-
-// Writes, in element order (token order), the tokens whose key is >= cstar, then
-// -1 up to k; with `prow` also their page slots.
-__device__ __forceinline__ void ordered_write(const uint64_t (&e)[PER], uint64_t cstar, int k, int32_t* __restrict__ orow,
-                              int32_t* __restrict__ prow, const CacheView& cv, const RowMap& rm, int seq, bool btl,
-                              SelShared& S, int& par) {
-  uint32_t bits = 0, cnt = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (e[i] != 0ull && e[i] >= cstar) {
-      bits |= 1u << i;
-      ++cnt;
-    }
-  uint32_t total;
-  const uint32_t off = excl_scan(cnt, total, S, par);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const uint32_t o = off + (uint32_t)__popc(bits & ((1u << i) - 1u));
-    if (((bits >> i) & 1u) && o < (uint32_t)k) S.a.hist[o] = (uint32_t)key_token(e[i]);
-  }
-  __syncthreads();
-  flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
 }
 
 // Exact selection over the whole row straight from global memory (8-bit digits,
@@ -501,50 +480,63 @@ __global__ __launch_bounds__(256) void topk_send_kernel(const float* __restrict_
   const int r = blockIdx.y;
   const int ctx = clamp_ctx(row_ctx, r, max_ctx);
   const int base = blockIdx.x * 256;
-  if (base >= ctx || cand_plan(ctx).unit == 0) return;  // whole workgroup
+  if (base >= ctx) return;  // whole workgroup
   const int t = base + threadIdx.x;
   const bool valid = t < ctx;
   const float s = valid ? scores[(int64_t)r * ld + t] : 0.f;
   send_candidates(s, valid, ctx, base, r, ws, send_lds);
 }
 
+// CAND: rows may be longer than kTopkFullRow, so candidates were sent.
+template <bool CAND>
 __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
                                                              const int32_t* __restrict__ row_ctx, int max_ctx, int k,
                                                              TopkWs ws, int32_t* __restrict__ idx,
                                                              int32_t* __restrict__ phys, CacheView cv, RowMap rm) {
   __shared__ SelShared S;
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // candidate slots and unit floors first: their addresses need only the kernel
+  // arguments, so they load alongside the row's length (slots the row's plan does not
+  // use are cleared once the length is known)
+  uint64_t e[PER];
+  uint32_t fl[4] = {0u, 0u, 0u, 0u};
+  if (CAND) {
+    const uint64_t* crow = ws.cand + (int64_t)r * kCandRowCap;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) e[i] = crow[i * SEL_NT + tid];
+    const uint32_t* rf = ws.floors + (int64_t)r * kFloorRowCap;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fl[j] = rf[tid + SEL_NT * j];
+  }
   const int ctx = clamp_ctx(row_ctx, r, max_ctx);
+  const int seq = rm.row_seq[r];  // the launch points row_seq at row_ctx when there are no page slots
   int32_t* orow = idx + (int64_t)r * k;
   int32_t* prow = phys ? phys + (int64_t)r * k : nullptr;
-  const int seq = phys ? rm.row_seq[r] : 0;
   const float* srow = scores + (int64_t)r * ld;
   int par = 0;
-
-  if (ctx <= k) {
+  auto write_all = [&]() {  // ctx <= k: every token, in order
     for (int i = tid; i < k; i += SEL_NT) {
       orow[i] = i < ctx ? i : -1;
       if (prow) prow[i] = i < ctx ? page_slot(cv, rm, seq, i) : -1;
     }
+  };
+  if (!CAND && ctx <= k) {
+    write_all();
     return;
   }
 
-  // the row's block-table entries for the page slots of the output, loaded now and
-  // staged in LDS (visible after the search's first barrier); one dependent global
-  // load per written token would otherwise sit on the write path
+  // the row's block-table entries for the page slots of the output, staged in LDS;
+  // one dependent global load per written token would otherwise sit on the write path
   const int nblk = (ctx + cv.block_size - 1) >> cv.log2_bs;
   const bool btl = prow != nullptr && nblk <= BTCAP;
-  int32_t bv[BTCAP / SEL_NT];
-  if (btl) {
+  if (btl) {  // S.bt is read only after the search's barriers
     const int32_t* btr = rm.block_table + (int64_t)seq * rm.bt_stride;
+    int32_t bv[BTCAP / SEL_NT];
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
       const int i = tid + SEL_NT * q;
       bv[q] = i < nblk ? btr[i] : 0;
     }
-  }
-  auto stage_bt = [&]() {
-    if (!btl) return;
     const int64_t nb = cv.num_blocks;
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
@@ -553,12 +545,11 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
       if ((uint64_t)b >= (uint64_t)nb) b = b < 0 ? 0 : nb - 1;
       if (i < nblk) S.bt[i] = (int32_t)b;
     }
-  };
+  }
 
-  uint64_t e[PER];
-  const CandPlan p = cand_plan(ctx);
-  if (p.unit == 0) {
-    // ---- the row's own keys: thread owns tokens [16 tid, 16 tid + 16) ----
+  // The row's own keys (rows of at most kTopkFullRow tokens): thread t holds tokens
+  // [16 t, 16 t + 16), one 16-key unit per thread.
+  auto load_own = [&]() {
     const int t0 = tid * PER;
     float f[PER];
     if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0 && t0 + PER <= ctx) {
@@ -580,118 +571,122 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
       const int t = t0 + i;
       e[i] = t < ctx ? composite_key(f[i], t) : 0ull;
     }
-    stage_bt();
-    const uint64_t cstar = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
-    ordered_write(e, cstar, k, orow, prow, cv, rm, seq, btl, S, par);
-    return;
-  }
+  };
 
-  // ---- candidates: e[q + m j] = rank q of unit t + 1024 j (j < upt) ----
-  const int m = p.m, nu = p.nu;
-  const int lm = 31 - __clz(m);
-  const int upt = (nu + SEL_NT - 1) / SEL_NT;  // 1, 2 or 4; upt * m <= 16
-  const uint64_t* crow = ws.cand + (int64_t)r * kCandRowCap;
+  // Unit layout of the register keys: thread t holds units t + 1024 j (j < upt) with m
+  // keys each, unit j in slots [m j, m j + m). Candidates: e[q + m j] = rank q of unit
+  // t + 1024 j. Own keys: m = 16, upt = 1.
+  int m = PER, lm = 4, upt = 1;
+  uint32_t fmask = 0, fbase = 0, nflag = 0;
+  uint64_t cstar;
+  if (!CAND) {
+    load_own();
+    cstar = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
+  } else {
+    const CandPlan p = cand_plan(ctx);
+    m = p.m;
+    lm = 31 - __clz(m);
+    upt = (p.nu + SEL_NT - 1) / SEL_NT;  // 1, 2 or 4; upt * m <= 16
+    uint32_t umine = 0;                  // this thread's units that exist
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int q = i & (m - 1), j = i >> lm;
-    const int u = tid + SEL_NT * j;
-    e[i] = (j < upt && u < nu) ? crow[(int64_t)q * nu + u] : 0ull;
-  }
-  // floors of this thread's units, fetched before the search needs them
-  uint32_t fl[4];
-  const uint32_t* rf = ws.floors + (int64_t)r * kFloorRowCap;
+    for (int j = 0; j < 4; ++j)
+      if (j < upt && tid + SEL_NT * j < p.nu) umine |= 1u << j;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int u = tid + SEL_NT * j;
-    fl[j] = (j < upt && u < nu) ? rf[u] : 0u;
-  }
-  stage_bt();
-  const uint64_t cu = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
-
-  // units whose kept-back keys may reach cu
-  const uint32_t cu_hi = (uint32_t)(cu >> 32);
-  uint32_t fmask = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (fl[j] != 0u && fl[j] >= cu_hi) fmask |= 1u << j;
-  uint32_t nflag;
-  const uint32_t fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
-  uint64_t cstar = cu;
-  uint32_t ne = 0;
-  if (nflag > 0) {
-    if (nflag > (uint32_t)FCAP) {
-      select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+    for (int i = 0; i < PER; ++i)
+      if (!((umine >> (i >> lm)) & 1u)) e[i] = 0ull;
+    // The first search comes before the short-row exits so that nothing between the
+    // kernel's start and the first use of the candidates is a branch (a branch lets
+    // the compiler sink the loads behind the row-length round trip).
+    const uint64_t c1 = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
+    if (ctx <= k) {
+      write_all();
       return;
     }
-    // ---- resend: each flagged unit's keys >= cu, rescanned by one wave per unit ----
-    {
-      uint32_t fm = fmask, sl = fbase;
-      while (fm) {
-        const int j = __ffs(fm) - 1;
-        fm &= fm - 1u;
-        S.funit[sl++] = (uint32_t)(tid + SEL_NT * j);
-      }
-    }
-    if (tid == 0) S.ecount = 0u;
-    __syncthreads();
-    const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1 or 4
-    for (uint32_t sl = wid; sl < nflag; sl += NW) {
-      const int t0 = (int)S.funit[sl] * p.unit;
-      float f[4];
+    // A row of at most 4k tokens may have sent fewer than k candidates (a 64-token unit
+    // sends at least a quarter of its tokens): every unit is rescanned whole.
+    const bool all = ctx <= 4 * k;
+    const uint64_t cu = all ? 1ull : c1;  // every real key is >= 1
+    const uint32_t cu_hi = (uint32_t)(cu >> 32);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = t0 + 64 * c + lane;
-        f[c] = (c < chunks && t < ctx) ? srow[t] : 0.f;
+    for (int j = 0; j < 4; ++j)
+      if (((umine >> j) & 1u) && (all || (fl[j] != 0u && fl[j] >= cu_hi))) fmask |= 1u << j;
+    fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
+    cstar = c1;
+    if (nflag > 0) {
+      if (nflag > (uint32_t)FCAP) {
+        select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+        return;
       }
-      uint64_t bal[4];
-      uint32_t tot = 0;
+      // ---- resend: each flagged unit's keys >= c_u, rescanned by one wave per unit ----
+      {
+        uint32_t fm = fmask, sl = fbase;
+        while (fm) {
+          const int j = __ffs(fm) - 1;
+          fm &= fm - 1u;
+          S.funit[sl++] = (uint32_t)(tid + SEL_NT * j);
+        }
+      }
+      if (tid == 0) S.ecount = 0u;
+      __syncthreads();
+      const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1 or 4
+      for (uint32_t sl = wid; sl < nflag; sl += NW) {
+        const int t0 = (int)S.funit[sl] * p.unit;
+        float f[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = t0 + 64 * c + lane;
-        const bool keep = c < chunks && t < ctx && composite_key(f[c], t) >= cu;
-        bal[c] = __ballot(keep);
-        tot += (uint32_t)__popcll(bal[c]);
-      }
-      uint32_t st = 0;
-      if (lane == 0) st = atomicAdd(&S.ecount, tot);
-      st = (uint32_t)__shfl((int)st, 0, 64);
-      uint32_t run = st;
+        for (int c = 0; c < 4; ++c) {
+          const int t = t0 + 64 * c + lane;
+          f[c] = (c < chunks && t < ctx) ? srow[t] : 0.f;
+        }
+        uint64_t bal[4];
+        uint32_t tot = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t = t0 + 64 * c + lane;
-        const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
-        if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
-        run += (uint32_t)__popcll(bal[c]);
-      }
-      if (lane == 0) {
-        S.fstart[sl] = st;
-        S.flen[sl] = tot;
-      }
-    }
-    __syncthreads();
-    ne = S.ecount;
-    if (ne > (uint32_t)ECAP) {
-      select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
-      return;
-    }
-    // union: unflagged candidates >= cu in registers, rescanned keys from LDS
+        for (int c = 0; c < 4; ++c) {
+          const int t = t0 + 64 * c + lane;
+          const bool keep = c < chunks && t < ctx && composite_key(f[c], t) >= cu;
+          bal[c] = __ballot(keep);
+          tot += (uint32_t)__popcll(bal[c]);
+        }
+        uint32_t st = 0;
+        if (lane == 0) st = atomicAdd(&S.ecount, tot);
+        st = (uint32_t)__shfl((int)st, 0, 64);
+        uint32_t run = st;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const bool flagged = (fmask >> (i >> lm)) & 1u;
-      if (flagged || e[i] < cu) e[i] = 0ull;
-    }
-    cstar = kth_largest<PER, true>(e, S.a.ext, ne, (uint32_t)k, S, par);
-    // selected keys of each rescanned unit
-    for (uint32_t sl = wid; sl < nflag; sl += NW) {
-      const uint32_t st = S.fstart[sl], len = S.flen[sl];
-      uint32_t c = 0;
-      for (uint32_t q0 = 0; q0 < len; q0 += 64) {
-        const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
-        c += (uint32_t)__popcll(__ballot(sel));
+        for (int c = 0; c < 4; ++c) {
+          const int t = t0 + 64 * c + lane;
+          const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
+          if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
+          run += (uint32_t)__popcll(bal[c]);
+        }
+        if (lane == 0) {
+          S.fstart[sl] = st;
+          S.flen[sl] = tot;
+        }
       }
-      if (lane == 0) S.fcnt[sl] = c;
+      __syncthreads();
+      const uint32_t ne = S.ecount;
+      if (ne > (uint32_t)ECAP) {
+        select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+        return;
+      }
+      // union: unflagged candidates >= c_u in registers, rescanned keys from LDS
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const bool flagged = (fmask >> (i >> lm)) & 1u;
+        if (flagged || e[i] < cu) e[i] = 0ull;
+      }
+      cstar = kth_largest<PER, true>(e, S.a.ext, ne, (uint32_t)k, S, par);
+      // selected keys of each rescanned unit
+      for (uint32_t sl = wid; sl < nflag; sl += NW) {
+        const uint32_t st = S.fstart[sl], len = S.flen[sl];
+        uint32_t c = 0;
+        for (uint32_t q0 = 0; q0 < len; q0 += 64) {
+          const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
+          c += (uint32_t)__popcll(__ballot(sel));
+        }
+        if (lane == 0) S.fcnt[sl] = c;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---- ordered write: unit counts, prefix sums over units (unit u = tid + 1024 j) ----
@@ -767,8 +762,13 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* ro
     c = *cv;
     m = *rm;
   }
-  hipLaunchKernelGGL(topk_select_kernel, dim3(R), dim3(SEL_NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws, idx,
-                     phys, c, m);
+  if (!phys) m.row_seq = row_ctx;  // read, never used
+  if (max_ctx > kTopkFullRow)
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(R), dim3(SEL_NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws,
+                       idx, phys, c, m);
+  else
+    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(R), dim3(SEL_NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws,
+                       idx, phys, c, m);
   return hipGetLastError();
 }
 

@@ -13,7 +13,9 @@
 // the low 8 bits replaced by (255 - position in the workgroup). Packed keys are
 // distinct within the workgroup and ordered like the scores up to those 8 bits. The
 // m largest packed keys of a unit are sent with their full 64-bit composite keys at
-// cand[q * nu + u] (q = rank in token order, u = unit, nu = units of the row). The
+// cand[cand_slot(q, u, m)] (q = rank in token order, u = unit): slot i = q + m (u / 1024)
+// of lane u % 1024, at i * 1024 + u % 1024. The select's thread t then reads
+// cand[i * 1024 + t] for i < 16, addresses that do not depend on the row length. The
 // floor is a score word f such that every unsent token's composite key is below
 // (f << 32) | 0xFFFFFFFF, so an unsent key can reach a threshold c only if
 // f >= c >> 32; f = 0 when the unit sent all of its valid tokens. Sorting uses DPP /
@@ -27,34 +29,37 @@
 namespace dsa {
 
 struct CandPlan {
-  int unit;  // tokens per unit: 0 (no candidates: the select reads the whole row), 64 or 256
+  int unit;  // tokens per unit: 64 or 256
   int m;     // keys sent per unit
   int nu;    // units of the row
 };
 
+// Every row of a launch whose row-length bound exceeds kTopkFullRow sends; launches
+// with a smaller bound send nothing (their select reads the rows whole).
 __host__ __device__ inline CandPlan cand_plan(int ctx) {
   CandPlan p{0, 0, 0};
-  if (ctx <= kTopkFullRow) return p;
   if (ctx <= 4 * kTopkFullRow) {
     p.unit = 64;
     p.m = kCandPerUnitMax;
   } else {
     p.unit = 256;
+    // largest power of two m <= 16 with nu * m <= kCandRowCap
     const int nu = (ctx + 255) / 256;
-    int m = kCandPerUnitMax;
-    while (m > 1 && nu * m > kCandRowCap) m >>= 1;
-    p.m = m;
+    p.m = nu <= 1024 ? 16 : nu <= 2048 ? 8 : nu <= 4096 ? 4 : nu <= 8192 ? 2 : 1;
   }
   p.nu = (ctx + p.unit - 1) / p.unit;
   return p;
 }
+static_assert(kCandPerUnitMax == 16 && kCandRowCap == 16 * 1024, "candidate slot layout");
+
+// Position of rank q of unit u in a row's candidate array (m keys per unit).
+__host__ __device__ inline int cand_slot(int q, int u, int m) { return (q + m * (u >> 10)) * 1024 + (u & 1023); }
 
 // Called by all 256 threads of a workgroup (no thread may have returned): thread
 // 64 w + l holds the score of token base + 64 w + l. `lds` is 68 words of LDS.
 __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx, int base, int row,
                                                 const TopkWs& tw, uint32_t* lds) {
   const CandPlan p = cand_plan(ctx);
-  if (p.unit == 0) return;  // uniform over the row
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int pos = threadIdx.x;  // position in the workgroup
   const uint32_t packed = valid ? ((float_key(score) & ~255u) | (255u - (uint32_t)pos)) : 0u;
@@ -73,8 +78,8 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
     const uint64_t bal = __ballot(sent);
     const uint32_t nsent = (uint32_t)__popcll(bal);
     const uint32_t q = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-    if (sent) cand[(int64_t)q * p.nu + u] = key;
-    if ((uint32_t)lane >= nsent && lane < p.m) cand[(int64_t)lane * p.nu + u] = 0ull;  // unused ranks
+    if (sent) cand[cand_slot((int)q, u, p.m)] = key;
+    if ((uint32_t)lane >= nsent && lane < p.m) cand[cand_slot(lane, u, p.m)] = 0ull;  // unused ranks
     if (lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
     return;
   }
@@ -94,9 +99,9 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
   const uint32_t before = (uint32_t)__popcll(__ballot(all != 0u && all >= thr && lane < 16 * wid));
   const uint32_t q = before + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
   const int u = base >> 8;
-  if (sent) cand[(int64_t)q * p.nu + u] = key;
+  if (sent) cand[cand_slot((int)q, u, p.m)] = key;
   const uint32_t ntot = (uint32_t)__popcll(__ballot(all != 0u && all >= thr));
-  if (wid == 0 && (uint32_t)lane >= ntot && lane < p.m) cand[(int64_t)lane * p.nu + u] = 0ull;  // unused ranks
+  if (wid == 0 && (uint32_t)lane >= ntot && lane < p.m) cand[cand_slot(lane, u, p.m)] = 0ull;  // unused ranks
   if (wid == 0 && lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
 }
 
