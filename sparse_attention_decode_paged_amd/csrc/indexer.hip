@@ -177,7 +177,7 @@ hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8
                               hipStream_t stream) {
   int nx = (rm.max_ctx + 255) / 256;
   if (nx < 1) nx = 1;
-  TopkWs tw = ws ? *ws : TopkWs{nullptr, nullptr};
+  TopkWs tw = ws ? *ws : TopkWs{nullptr, nullptr, nullptr};
   const int send = (ws != nullptr && rm.max_ctx > kTopkFullRow) ? 1 : 0;
   dim3 grid(nx, R);
   const bool p32 = cv.block_size >= kTileTok;

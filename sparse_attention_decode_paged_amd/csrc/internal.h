@@ -18,23 +18,28 @@ constexpr int kFloorRowCap = kMaxCtx / 256;  // units of a row, at most
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// A candidate key is kept as two words at the same slot of two arrays, so that the
+// select can load the score words (all its search passes need) ahead of the tokens.
 struct TopkWs {
-  uint64_t* cand;    // [R][kCandRowCap]: key of rank q of unit u at cand_slot(q, u, m)
-  uint32_t* floors;  // [R][kFloorRowCap]: score word bounding the keys a unit did not send (0: sent all)
+  uint32_t* cand_hi;  // [R][kCandRowCap]: score word of rank q of unit u at cand_slot(q, u, m); 0 = empty
+  uint32_t* cand_lo;  // [R][kCandRowCap]: its token word (0xFFFFFFFF - token)
+  uint32_t* floors;   // [R][kFloorRowCap]: score word bounding the keys a unit did not send (0: sent all)
 };
 
 // Rows of at most kTopkFullRow tokens send no candidates: no candidate space then.
 inline size_t topk_ws_bytes(int R, int max_ctx) {
   if (max_ctx <= kTopkFullRow) return 256;
-  return align_up((size_t)R * kCandRowCap * 8, 256) + align_up((size_t)R * kFloorRowCap * 4, 256);
+  return 2 * align_up((size_t)R * kCandRowCap * 4, 256) + align_up((size_t)R * kFloorRowCap * 4, 256);
 }
 
 inline TopkWs topk_ws_carve(void* ws, int R, int max_ctx) {
-  TopkWs t;
-  if (max_ctx <= kTopkFullRow) return TopkWs{nullptr, nullptr};
+  TopkWs t{nullptr, nullptr, nullptr};
+  if (max_ctx <= kTopkFullRow) return t;
   uint8_t* p = static_cast<uint8_t*>(ws);
-  t.cand = reinterpret_cast<uint64_t*>(p);
-  p += align_up((size_t)R * kCandRowCap * 8, 256);
+  t.cand_hi = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)R * kCandRowCap * 4, 256);
+  t.cand_lo = reinterpret_cast<uint32_t*>(p);
+  p += align_up((size_t)R * kCandRowCap * 4, 256);
   t.floors = reinterpret_cast<uint32_t*>(p);
   return t;
 }

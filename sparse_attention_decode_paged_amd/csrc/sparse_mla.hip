@@ -286,7 +286,7 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       const int h = 8 * (rr >> 2) + 4 * g + (rr & 3);
       float* orow = part_o + (pbase + h) * kDV + 128 * wid + (lane & 31);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][rr] * s_run;
+      for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(acc[c][rr] * s_run, orow + 32 * c);
     }
     if (tid < kMlaGroup) {
       part_ml[(pbase + tid) * 2 + 0] = m_run;

@@ -200,7 +200,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
 }
 
 // The need-th largest (1 <= need <= number of live keys) of the nonzero keys in
-// e[] and, with EXTRA, in xs[0, nx) (LDS, thread t reading xs[t + SEL_NT j]), held
+// kh[]/kl[] and, with EXTRA, in xs[0, nx) (LDS, thread t reading xs[t + SEL_NT j]), held
 // across the workgroup. Keys are distinct.
 __device__ __forceinline__ void clear_hist(SelShared& S) {
   v4i* hz = reinterpret_cast<v4i*>(S.a.hist) + threadIdx.x * 4;
@@ -208,28 +208,32 @@ __device__ __forceinline__ void clear_hist(SelShared& S) {
   for (int q = 0; q < 4; ++q) hz[q] = v4i{0, 0, 0, 0};
 }
 
+// Register keys come as score words kh[] and token words kl[] (key = kh << 32 | kl;
+// kh == 0 marks an empty slot: no finite score maps to 0). The passes read only the
+// score words, so the token words may still be in flight until the bucket stage.
 template <int N, bool EXTRA>
-__device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const uint64_t* xs, uint32_t nx, uint32_t need,
-                                SelShared& S, int& par) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  // fn(key) over the register keys, then (only when the LDS list is not empty, a
-  // uniform branch) over xs[tid + SEL_NT x], x < XPER
+__device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const uint32_t (&kl)[N], const uint64_t* xs,
+                                                uint32_t nx, uint32_t need, SelShared& S, int& par) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // fn(score word, token word) over the register keys, then (only when the LDS list
+  // is not empty, a uniform branch) over xs[tid + SEL_NT x], x < XPER
   auto for_keys = [&](auto&& fn) {
 #pragma unroll
-    for (int i = 0; i < N; ++i) fn(e[i]);
+    for (int i = 0; i < N; ++i) fn(kh[i], kl[i]);
     if (EXTRA && nx > 0) {
 #pragma unroll
       for (int x = 0; x < XPER; ++x) {
         const uint32_t p = (uint32_t)tid + (uint32_t)x * SEL_NT;
-        fn(p < nx ? xs[p] : 0ull);
+        const uint64_t v = p < nx ? xs[p] : 0ull;
+        fn((uint32_t)(v >> 32), (uint32_t)v);
       }
     }
   };
-  clear_hist(S);  // ordered before the first pass by the min / max barrier
+  if (tid == 0) S.bcount = 0u;  // the bucket gather is ordered after this by the barriers below
+  clear_hist(S);                // ordered before the first pass by the min / max barrier
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for_keys([&](uint64_t v) {
-    const uint32_t w = (uint32_t)(v >> 32);
-    if (v != 0ull) {
+  for_keys([&](uint32_t w, uint32_t) {
+    if (w != 0u) {
       lo = min(lo, w);
       hi = max(hi, w);
     }
@@ -254,9 +258,8 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const ui
     }
     first = false;
     const uint32_t rep = (uint32_t)tid & (NREP - 1);
-    for_keys([&](uint64_t v) {
-      const uint32_t w = (uint32_t)(v >> 32);
-      if (v != 0ull && (w & mask) == prefix) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
+    for_keys([&](uint32_t w, uint32_t) {
+      if (w != 0u && (w & mask) == prefix) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
     });
     __syncthreads();
     // thread t holds bins NBIN-1-2t (upper) and NBIN-2-2t: thread order = descending digits
@@ -293,22 +296,19 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const ui
   if (top < 0 && cnt == 0u) {
     // no pass ran (one score word): count the bucket
     uint32_t c = 0;
-    for_keys([&](uint64_t v) { c += v != 0ull ? 1u : 0u; });
+    for_keys([&](uint32_t w, uint32_t) { c += w != 0u ? 1u : 0u; });
     uint32_t unused;
     excl_scan(c, unused, S, par);
     cnt = unused;
   }
   if (cnt <= 64u) {
-    if (tid == 0) S.bcount = 0u;
-    __syncthreads();
-    for_keys([&](uint64_t v) {
-      if (v != 0ull && ((uint32_t)(v >> 32) & mask) == prefix) S.bucket[atomicAdd(&S.bcount, 1u) & 63u] = v;
+    for_keys([&](uint32_t w, uint32_t l) {
+      if (w != 0u && (w & mask) == prefix) S.bucket[atomicAdd(&S.bcount, 1u) & 63u] = ((uint64_t)w << 32) | l;
     });
     __syncthreads();
-    if (wid == 0) {
+    if (tid < 64) {  // one wave resolves the bucket
       const uint64_t v = (uint32_t)lane < cnt ? S.bucket[lane] : 0ull;
-      if (need == cnt) {
-        // every bucket key is selected: the threshold is the smallest
+      if (need == cnt) {  // every bucket key is selected: the threshold is the smallest
         const uint64_t mn = wave_min_u64((uint32_t)lane < cnt ? v : ~0ull);
         if (lane == 0) S.res64 = mn;
       } else {
@@ -328,9 +328,8 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&e)[N], const ui
     clear_hist(S);
     __syncthreads();
     const uint32_t rep = (uint32_t)tid & (NREP - 1);
-    for_keys([&](uint64_t v) {
-      const uint32_t lw = (uint32_t)v;
-      if (v != 0ull && ((uint32_t)(v >> 32) & mask) == prefix && (lw & lmask) == lprefix)
+    for_keys([&](uint32_t w, uint32_t lw) {
+      if (w != 0u && (w & mask) == prefix && (lw & lmask) == lprefix)
         atomicAdd(&S.a.hist[((lw >> s0) & dm) * NREP + rep], 1u);
     });
     __syncthreads();
@@ -498,12 +497,16 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
   // candidate slots and unit floors first: their addresses need only the kernel
   // arguments, so they load alongside the row's length (slots the row's plan does not
   // use are cleared once the length is known)
-  uint64_t e[PER];
+  // score words first (the passes need only them), then token words and floors
+  uint32_t kh[PER], kl[PER];
   uint32_t fl[4] = {0u, 0u, 0u, 0u};
   if (CAND) {
-    const uint64_t* crow = ws.cand + (int64_t)r * kCandRowCap;
+    const uint32_t* ch = ws.cand_hi + (int64_t)r * kCandRowCap;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) e[i] = crow[i * SEL_NT + tid];
+    for (int i = 0; i < PER; ++i) kh[i] = ch[i * SEL_NT + tid];
+    const uint32_t* cl = ws.cand_lo + (int64_t)r * kCandRowCap;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) kl[i] = cl[i * SEL_NT + tid];
     const uint32_t* rf = ws.floors + (int64_t)r * kFloorRowCap;
 #pragma unroll
     for (int j = 0; j < 4; ++j) fl[j] = rf[tid + SEL_NT * j];
@@ -529,14 +532,20 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
   // one dependent global load per written token would otherwise sit on the write path
   const int nblk = (ctx + cv.block_size - 1) >> cv.log2_bs;
   const bool btl = prow != nullptr && nblk <= BTCAP;
-  if (btl) {  // S.bt is read only after the search's barriers
+  int32_t bv[BTCAP / SEL_NT];
+  if (btl) {
     const int32_t* btr = rm.block_table + (int64_t)seq * rm.bt_stride;
-    int32_t bv[BTCAP / SEL_NT];
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
       const int i = tid + SEL_NT * q;
       bv[q] = i < nblk ? btr[i] : 0;
     }
+  }
+  // The entries reach LDS after the first search: they sit one scalar round trip
+  // further down the load chain than the candidates, and a store waiting for them
+  // ahead of the search's first barrier would hold every wave.
+  auto stage_bt = [&]() {
+    if (!btl) return;
     const int64_t nb = cv.num_blocks;
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
@@ -545,7 +554,7 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
       if ((uint64_t)b >= (uint64_t)nb) b = b < 0 ? 0 : nb - 1;
       if (i < nblk) S.bt[i] = (int32_t)b;
     }
-  }
+  };
 
   // The row's own keys (rows of at most kTopkFullRow tokens): thread t holds tokens
   // [16 t, 16 t + 16), one 16-key unit per thread.
@@ -569,19 +578,22 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int t = t0 + i;
-      e[i] = t < ctx ? composite_key(f[i], t) : 0ull;
+      const uint64_t key = t < ctx ? composite_key(f[i], t) : 0ull;
+      kh[i] = (uint32_t)(key >> 32);
+      kl[i] = (uint32_t)key;
     }
   };
 
   // Unit layout of the register keys: thread t holds units t + 1024 j (j < upt) with m
-  // keys each, unit j in slots [m j, m j + m). Candidates: e[q + m j] = rank q of unit
+  // keys each, unit j in slots [m j, m j + m). Candidates: slot q + m j = rank q of unit
   // t + 1024 j. Own keys: m = 16, upt = 1.
   int m = PER, lm = 4, upt = 1;
   uint32_t fmask = 0, fbase = 0, nflag = 0;
   uint64_t cstar;
   if (!CAND) {
     load_own();
-    cstar = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
+    cstar = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par);
+    stage_bt();
   } else {
     const CandPlan p = cand_plan(ctx);
     m = p.m;
@@ -593,15 +605,16 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
       if (j < upt && tid + SEL_NT * j < p.nu) umine |= 1u << j;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
-      if (!((umine >> (i >> lm)) & 1u)) e[i] = 0ull;
+      if (!((umine >> (i >> lm)) & 1u)) kh[i] = 0u;
     // The first search comes before the short-row exits so that nothing between the
     // kernel's start and the first use of the candidates is a branch (a branch lets
     // the compiler sink the loads behind the row-length round trip).
-    const uint64_t c1 = kth_largest<PER, false>(e, nullptr, 0u, (uint32_t)k, S, par);
+    const uint64_t c1 = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par);
     if (ctx <= k) {
       write_all();
       return;
     }
+    stage_bt();
     // A row of at most 4k tokens may have sent fewer than k candidates (a 64-token unit
     // sends at least a quarter of its tokens): every unit is rescanned whole.
     const bool all = ctx <= 4 * k;
@@ -672,9 +685,9 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const bool flagged = (fmask >> (i >> lm)) & 1u;
-        if (flagged || e[i] < cu) e[i] = 0ull;
+        if (flagged || (((uint64_t)kh[i] << 32) | kl[i]) < cu) kh[i] = 0u;
       }
-      cstar = kth_largest<PER, true>(e, S.a.ext, ne, (uint32_t)k, S, par);
+      cstar = kth_largest<PER, true>(kh, kl, S.a.ext, ne, (uint32_t)k, S, par);
       // selected keys of each rescanned unit
       for (uint32_t sl = wid; sl < nflag; sl += NW) {
         const uint32_t st = S.fstart[sl], len = S.flen[sl];
@@ -693,7 +706,7 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
   uint32_t bits = 0;  // selected register keys
 #pragma unroll
   for (int i = 0; i < PER; ++i)
-    if (e[i] != 0ull && e[i] >= cstar) bits |= 1u << i;
+    if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
   const uint32_t umask = m >= 16 ? 0xFFFFu : ((1u << m) - 1u);  // keys of one unit
   uint32_t cnt[4];
 #pragma unroll
@@ -722,7 +735,7 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
     const int j = i >> lm;
     const uint32_t oj = j == 0 ? off[0] : j == 1 ? off[1] : j == 2 ? off[2] : off[3];
     const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
-    if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = (uint32_t)key_token(e[i]);
+    if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = 0xFFFFFFFFu - kl[i];
   }
   if (nflag > 0) {
     __syncthreads();

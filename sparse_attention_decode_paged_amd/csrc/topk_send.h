@@ -12,11 +12,11 @@
 // Ranking uses a 32-bit packed key per token: the score's order-preserving bits with
 // the low 8 bits replaced by (255 - position in the workgroup). Packed keys are
 // distinct within the workgroup and ordered like the scores up to those 8 bits. The
-// m largest packed keys of a unit are sent with their full 64-bit composite keys at
-// cand[cand_slot(q, u, m)] (q = rank in token order, u = unit): slot i = q + m (u / 1024)
-// of lane u % 1024, at i * 1024 + u % 1024. The select's thread t then reads
-// cand[i * 1024 + t] for i < 16, addresses that do not depend on the row length. The
-// floor is a score word f such that every unsent token's composite key is below
+// m largest packed keys of a unit are sent with their full 64-bit composite keys
+// (score word and token word, in two arrays) at slot cand_slot(q, u, m), q = rank in
+// token order, u = unit: slot row i = q + m (u / 1024), lane u % 1024, at
+// i * 1024 + u % 1024. The select's thread t then reads slots i * 1024 + t for
+// i < 16, addresses that do not depend on the row length. The floor is a score word f such that every unsent token's composite key is below
 // (f << 32) | 0xFFFFFFFF, so an unsent key can reach a threshold c only if
 // f >= c >> 32; f = 0 when the unit sent all of its valid tokens. Sorting uses DPP /
 // permlane exchanges inside a wave; 256-token units merge the four waves' best 16
@@ -64,7 +64,8 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
   const int pos = threadIdx.x;  // position in the workgroup
   const uint32_t packed = valid ? ((float_key(score) & ~255u) | (255u - (uint32_t)pos)) : 0u;
   const uint32_t sorted = wave_sort_desc_u32(packed, lane);
-  uint64_t* cand = tw.cand + (int64_t)row * kCandRowCap;
+  uint32_t* cand_hi = tw.cand_hi + (int64_t)row * kCandRowCap;
+  uint32_t* cand_lo = tw.cand_lo + (int64_t)row * kCandRowCap;
   uint32_t* floors = tw.floors + (int64_t)row * kFloorRowCap;
   const uint64_t key = valid ? composite_key(score, base + pos) : 0ull;
 
@@ -78,8 +79,11 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
     const uint64_t bal = __ballot(sent);
     const uint32_t nsent = (uint32_t)__popcll(bal);
     const uint32_t q = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-    if (sent) cand[cand_slot((int)q, u, p.m)] = key;
-    if ((uint32_t)lane >= nsent && lane < p.m) cand[cand_slot(lane, u, p.m)] = 0ull;  // unused ranks
+    if (sent) {
+      cand_hi[cand_slot((int)q, u, p.m)] = (uint32_t)(key >> 32);
+      cand_lo[cand_slot((int)q, u, p.m)] = (uint32_t)key;
+    }
+    if ((uint32_t)lane >= nsent && lane < p.m) cand_hi[cand_slot(lane, u, p.m)] = 0u;  // unused ranks
     if (lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
     return;
   }
@@ -99,9 +103,12 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
   const uint32_t before = (uint32_t)__popcll(__ballot(all != 0u && all >= thr && lane < 16 * wid));
   const uint32_t q = before + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
   const int u = base >> 8;
-  if (sent) cand[cand_slot((int)q, u, p.m)] = key;
+  if (sent) {
+    cand_hi[cand_slot((int)q, u, p.m)] = (uint32_t)(key >> 32);
+    cand_lo[cand_slot((int)q, u, p.m)] = (uint32_t)key;
+  }
   const uint32_t ntot = (uint32_t)__popcll(__ballot(all != 0u && all >= thr));
-  if (wid == 0 && (uint32_t)lane >= ntot && lane < p.m) cand[cand_slot(lane, u, p.m)] = 0ull;  // unused ranks
+  if (wid == 0 && (uint32_t)lane >= ntot && lane < p.m) cand_hi[cand_slot(lane, u, p.m)] = 0u;  // unused ranks
   if (wid == 0 && lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
 }
 
