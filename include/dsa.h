@@ -124,6 +124,7 @@ int64_t dsa_decode_scores_ld(int32_t max_ctx);
  *   scores       fp32 [R][ld_scores], ld_scores >= max_ctx; entries t >= ctx[r]
  *                are left untouched.
  * Key and query scales must be positive (the kernel factors them out of ReLU).
+ * q_idx must be 16-byte and q_idx_scale 4-byte aligned (DSA_ERR_ALIGN otherwise).
  */
 dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer,
                              const void* q_idx, const void* q_idx_scale, const float* w,

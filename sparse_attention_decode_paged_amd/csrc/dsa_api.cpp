@@ -103,6 +103,18 @@ size_t decode_ws(int32_t R, int32_t max_ctx, int32_t k) {
          align_up((size_t)R * k * 4, 256) + mla_ws_bytes(R, k);
 }
 
+// The indexer for the cache's key format: FP8 (q_idx_scale = R x 32 fp32) or MXFP4
+// (q_idx_scale = R x 32 x 4 E8M0 bytes).
+hipError_t launch_indexer(int32_t index_fmt, const CacheView& cv, const RowMap& rm, const void* q_idx,
+                          const void* q_idx_scale, const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
+                          hipStream_t s) {
+  if (index_fmt == DSA_INDEX_MXFP4)
+    return launch_indexer_mxfp4(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(q_idx_scale), w,
+                                R, scores, ld, ws, s);
+  return launch_indexer_fp8(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale), w, R,
+                            scores, ld, ws, s);
+}
+
 dsa_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -155,10 +167,10 @@ dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer, const v
     return fail(DSA_ERR_NULL, "q_idx / q_idx_scale / w / scores is NULL");
   if (ld_scores < max_ctx) return fail(DSA_ERR_ARG, "ld_scores %lld < max_ctx %d", (long long)ld_scores, max_ctx);
   if (!aligned16(q_idx)) return fail(DSA_ERR_ALIGN, "q_idx is not 16-byte aligned");
-  if (cache->index_fmt != DSA_INDEX_FP8) return fail(DSA_ERR_UNSUPPORTED, "MXFP4 index keys are not built yet");
+  if (reinterpret_cast<uintptr_t>(q_idx_scale) & 3u) return fail(DSA_ERR_ALIGN, "q_idx_scale is not 4-byte aligned");
   if (R == 0) return ok();
-  return hip_status(launch_indexer_fp8(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
-                                       w, R, scores, ld_scores, nullptr, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, scores, ld_scores, nullptr,
+                                   static_cast<hipStream_t>(stream)),
                     "indexer");
 }
 
@@ -217,7 +229,7 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const voi
     return fail(DSA_ERR_NULL, "q_idx / q_idx_scale / w / q_lat / idx / out is NULL");
   if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
   if (!aligned16(q_idx) || !aligned16(q_lat)) return fail(DSA_ERR_ALIGN, "q_idx / q_lat is not 16-byte aligned");
-  if (cache->index_fmt != DSA_INDEX_FP8) return fail(DSA_ERR_UNSUPPORTED, "MXFP4 index keys are not built yet");
+  if (reinterpret_cast<uintptr_t>(q_idx_scale) & 3u) return fail(DSA_ERR_ALIGN, "q_idx_scale is not 4-byte aligned");
   const size_t need = decode_ws(R, max_ctx, k);
   if (workspace == nullptr || ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (!aligned16(workspace)) return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -232,8 +244,7 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const voi
   int32_t* phys = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)R * k * 4, 256);
   void* mla_ws = p;
-  hipError_t e = launch_indexer_fp8(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
-                                    w, R, scores, ld, &tw, s);
+  hipError_t e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, scores, ld, &tw, s);
   if (e == hipSuccess) e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, idx, tw, phys, nullptr, &cv, &rm, s);
   if (e == hipSuccess) {
     // the selected tokens lie below max_ctx, so the row map's bound is unchanged

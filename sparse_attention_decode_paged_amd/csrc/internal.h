@@ -74,6 +74,11 @@ hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8
                               const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
                               hipStream_t stream);
 
+// Indexer over MXFP4 keys (q_idx: R x 32 x 64 packed e2m1, q_e8: R x 32 x 4 E8M0).
+hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const uint8_t* q_e8,
+                                const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
+                                hipStream_t stream);
+
 // Candidate sending over an existing score array (standalone top-k).
 hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx,
                             const TopkWs& ws, hipStream_t stream);

@@ -20,7 +20,7 @@ import torch
 
 from oracle import dsa_oracle as O
 from synth import (make_case, make_prefill_case, config_small, config_batch16, config_long_1m,
-                   config_prefill_append)
+                   config_prefill_append, config_mixed_mxfp4)
 
 pytestmark = pytest.mark.gpu
 
@@ -205,6 +205,23 @@ def test_batch16_mixed_lengths(dev):
     say("case: decode B=16 ctx U[16K,64K] shared shuffled pool")
     c = config_batch16(device=dev)
     full_check(c, dev)
+
+
+@pytest.mark.parametrize("bs", [16, 128])
+def test_mxfp4_keys_ragged(dev, bs):
+    """MXFP4 index keys (bs 16: per-token key gathers; bs 128: page-contiguous tiles); rows
+    below, at and above k, and two long enough for the candidate top-k."""
+    say(f"case: mxfp4 keys, bs {bs}")
+    c = make_case([1, 700, 2048, 2049, 9000, 20000, 70000], block_size=bs, seed=70 + bs, k=2048, index_fmt="mxfp4")
+    full_check(c, dev)
+
+
+def test_mxfp4_mixed_batch_layers(dev):
+    """The mixed-length MXFP4 workload at reduced size: B=8, lengths log-uniform in [4K, 256K],
+    3 layers in one packed row, bs 128; every row checked on the last layer."""
+    say("case: mxfp4 B=8 log-uniform [4K, 256K], 3 layers, bs 128")
+    c = config_mixed_mxfp4(device=dev, batch=8, num_layers=3)
+    full_check(c, dev, layer=2)
 
 
 def test_long_context_1m_planted(dev):
