@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--layers", type=int, default=LAYERS)
     p.add_argument("--batch", type=int, default=1)
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--index-fmt", choices=["fp8", "mxfp4"], default="fp8",
+                   help="index key format (the headline workload uses fp8)")
+    p.add_argument("--block-size", type=int, default=BS)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=4, help="layer-steps the CPU oracle runs for cpu_baseline")
     p.add_argument("--copy-calibration", action="store_true",
@@ -162,8 +165,8 @@ def main():
         return
 
     t0 = time.time()
-    case = make_case([a.ctx] * a.batch, block_size=BS, num_layers=a.layers, seed=a.seed, device=dev, k=K,
-                     name="decode_b%d_ctx%d_x%dlayers" % (a.batch, a.ctx, a.layers))
+    case = make_case([a.ctx] * a.batch, block_size=a.block_size, num_layers=a.layers, seed=a.seed, device=dev, k=K,
+                     index_fmt=a.index_fmt, name="decode_b%d_ctx%d_x%dlayers" % (a.batch, a.ctx, a.layers))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     R, max_ctx = case.num_rows, case.max_ctx
@@ -220,11 +223,12 @@ def main():
     ix_us = timed_indexer_us(dsa, case, a.layers, max_ctx, max(2, min(a.steps, 480) // a.layers))
 
     ctxs = [int(c) for c in case.row_ctx.tolist()]
-    step_bytes = A.layer_step_bytes(ctxs, K)
-    ix_bytes = sum(A.indexer_bytes(c) for c in ctxs)
+    step_bytes = A.layer_step_bytes(ctxs, K, a.index_fmt)
+    ix_bytes = sum(A.indexer_bytes(c, a.index_fmt) for c in ctxs)
     ix_gbps = ix_bytes / (ix_us * 1e-6) / 1e9
     step_gbps = step_bytes / (ms * 1e-3) / 1e9
-    traffic = traffic_for(INDEXER_SRC)
+    traffic = traffic_for(INDEXER_SRC) if a.index_fmt == "fp8" else None
+    key_desc = "FP8 index keys (132 B/token)" if a.index_fmt == "fp8" else "MXFP4 index keys (68 B/token)"
 
     res = {
         "metric": METRIC,
@@ -240,16 +244,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"DSA decode, batch {R}, context {a.ctx} tokens, top-{K}, block size {BS}, FP8 index keys "
-                        f"(132 B/token) and FP8 latents (576 B + fp32 scale), {a.layers} independent layers rotated",
-            "batch": R, "ctx": a.ctx, "k": K, "block_size": BS, "layers_rotated": a.layers, "index_fmt": "fp8",
+            "workload": f"DSA decode, batch {R}, context {a.ctx} tokens, top-{K}, block size {a.block_size}, {key_desc} "
+                        f"and FP8 latents (576 B + fp32 scale), {a.layers} independent layers rotated",
+            "batch": R, "ctx": a.ctx, "k": K, "block_size": a.block_size, "layers_rotated": a.layers,
+            "index_fmt": a.index_fmt,
             "launch": "HIP graph replay, one decode step per layer",
         },
         "step_hbm_gbps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "roofline": {
-            "kernel": "indexer_fp8_kernel (scoring only, as dsa_indexer_score launches it)",
+            "kernel": f"indexer_{a.index_fmt}_kernel (scoring only, as dsa_indexer_score launches it)",
             "bound": "hbm",
             "achieved": round(ix_gbps, 1),
             "peak": PEAK_HBM_GBPS,
