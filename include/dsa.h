@@ -180,6 +180,34 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer,
                            int32_t* idx, float* out, float* lse,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Several query rows per sequence (page 1: the 2K-token append on a 150K prefix,
+ * every appended token a query row; the AMD section: several speculative-verify
+ * tokens per sequence whose queries share one key scan). Same as dsa_indexer_score
+ * / dsa_decode_step, plus
+ *   rows_per_seq  >= 1: rows come in runs of this many consecutive rows that share
+ *                 a sequence (row_seq equal), e.g. T for a T-token append or the
+ *                 draft length + 1 for speculative verification; 1 = no sharing.
+ * With FP8 keys and rows_per_seq > 1 the indexer reads and converts each key once
+ * for up to 16 consecutive rows. It is a performance hint only: a row whose row_seq
+ * differs from the row before it reloads the keys, so results never depend on it.
+ * (MXFP4 keys are scored row by row.) DSA_ERR_ARG if rows_per_seq < 1.
+ */
+dsa_status dsa_indexer_score_multi(const dsa_cache_desc* cache, int32_t layer,
+                                   const void* q_idx, const void* q_idx_scale, const float* w,
+                                   const int32_t* block_table, int32_t bt_stride,
+                                   const int32_t* row_seq, const int32_t* row_ctx,
+                                   int32_t R, int32_t max_ctx, int32_t rows_per_seq,
+                                   float* scores, int64_t ld_scores, void* stream);
+dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer,
+                                 const void* q_idx, const void* q_idx_scale, const float* w,
+                                 const uint16_t* q_lat,
+                                 const int32_t* block_table, int32_t bt_stride,
+                                 const int32_t* row_seq, const int32_t* row_ctx,
+                                 int32_t R, int32_t max_ctx, int32_t k, int32_t rows_per_seq,
+                                 float sm_scale, int32_t* idx, float* out, float* lse,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

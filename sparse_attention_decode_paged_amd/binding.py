@@ -24,7 +24,8 @@ DSA_MAX_LAYERS = 64
 H_IDX, D_IDX, H_Q, D_LAT, D_V = 32, 128, 96, 576, 512
 
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_last_error_detail", "dsa_workspace_bytes",
-            "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step")
+            "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step",
+            "dsa_indexer_score_multi", "dsa_decode_step_multi")
 
 
 class DSAError(RuntimeError):
@@ -79,6 +80,12 @@ def load_library(path: str = LIB_PATH):
     L.dsa_decode_step.restype = _i32
     L.dsa_decode_step.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _f32,
                                   _vp, _vp, _vp, _vp, _sz, _vp]
+    L.dsa_indexer_score_multi.restype = _i32
+    L.dsa_indexer_score_multi.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _i64,
+                                          _vp]
+    L.dsa_decode_step_multi.restype = _i32
+    L.dsa_decode_step_multi.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _f32, _vp, _vp, _vp, _vp, _sz, _vp]
     _lib = L
     return L
 
@@ -145,8 +152,9 @@ def _bt_stride(block_table: torch.Tensor) -> int:
 
 
 def dsa_indexer_score(pool, layout, layer, q_idx, q_idx_scale, w, block_table, row_seq, row_ctx, max_ctx,
-                      scores=None, ld_scores=None):
-    """Scores fp32 [R][ld_scores] of every token t < row_ctx[r]."""
+                      scores=None, ld_scores=None, rows_per_seq=1):
+    """Scores fp32 [R][ld_scores] of every token t < row_ctx[r]. rows_per_seq > 1:
+    runs of that many consecutive rows share a sequence (dsa_indexer_score_multi)."""
     L = load_library()
     R = row_seq.shape[0]
     if ld_scores is None:
@@ -154,12 +162,12 @@ def dsa_indexer_score(pool, layout, layer, q_idx, q_idx_scale, w, block_table, r
     if scores is None:
         scores = torch.empty((R, ld_scores), dtype=torch.float32, device=pool.device)
     d = make_cache_desc(pool, layout)
-    st = L.dsa_indexer_score(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
-                             _dev(w, "w", torch.float32), _dev(block_table, "block_table", torch.int32),
-                             _bt_stride(block_table), _dev(row_seq, "row_seq", torch.int32),
-                             _dev(row_ctx, "row_ctx", torch.int32), R, int(max_ctx), _dev(scores, "scores", torch.float32),
-                             int(ld_scores), _stream(pool.device))
-    _check(st, "dsa_indexer_score")
+    st = L.dsa_indexer_score_multi(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+                                   _dev(w, "w", torch.float32), _dev(block_table, "block_table", torch.int32),
+                                   _bt_stride(block_table), _dev(row_seq, "row_seq", torch.int32),
+                                   _dev(row_ctx, "row_ctx", torch.int32), R, int(max_ctx), int(rows_per_seq),
+                                   _dev(scores, "scores", torch.float32), int(ld_scores), _stream(pool.device))
+    _check(st, "dsa_indexer_score_multi")
     return scores
 
 
@@ -205,9 +213,10 @@ def dsa_sparse_mla(pool, layout, layer, q_lat, block_table, row_seq, idx, k, sm_
 
 
 def dsa_decode_step(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_table, row_seq, row_ctx, max_ctx, k,
-                    sm_scale, idx=None, out=None, lse=None, workspace=None):
+                    sm_scale, idx=None, out=None, lse=None, workspace=None, rows_per_seq=1):
     """Indexer -> exact top-k -> sparse MLA -> merge. Returns (idx, out, lse, workspace);
-    the scores sit at the start of the workspace with row stride dsa_decode_scores_ld(max_ctx)."""
+    the scores sit at the start of the workspace with row stride dsa_decode_scores_ld(max_ctx).
+    rows_per_seq > 1: runs of that many consecutive rows share a sequence (dsa_decode_step_multi)."""
     L = load_library()
     R = row_seq.shape[0]
     dev = pool.device
@@ -221,14 +230,15 @@ def dsa_decode_step(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_tab
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     d = make_cache_desc(pool, layout)
-    st = L.dsa_decode_step(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
-                           _dev(w, "w", torch.float32), _dev(q_lat, "q_lat", torch.bfloat16),
-                           _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
-                           _dev(row_seq, "row_seq", torch.int32), _dev(row_ctx, "row_ctx", torch.int32), R,
-                           int(max_ctx), int(k), float(sm_scale), _dev(idx, "idx", torch.int32),
-                           _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32),
-                           _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(st, "dsa_decode_step")
+    st = L.dsa_decode_step_multi(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+                                 _dev(w, "w", torch.float32), _dev(q_lat, "q_lat", torch.bfloat16),
+                                 _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
+                                 _dev(row_seq, "row_seq", torch.int32), _dev(row_ctx, "row_ctx", torch.int32), R,
+                                 int(max_ctx), int(k), int(rows_per_seq), float(sm_scale),
+                                 _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
+                                 _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "dsa_decode_step_multi")
     return idx, out, lse, workspace
 
 

@@ -105,9 +105,16 @@ size_t decode_ws(int32_t R, int32_t max_ctx, int32_t k) {
 
 // The indexer for the cache's key format: FP8 (q_idx_scale = R x 32 fp32) or MXFP4
 // (q_idx_scale = R x 32 x 4 E8M0 bytes).
+// rows_per_seq > 1 (FP8): runs of that many consecutive rows share a sequence, so the
+// row-group kernel reads each key once per group of up to kRowsPerGroupMax rows.
 hipError_t launch_indexer(int32_t index_fmt, const CacheView& cv, const RowMap& rm, const void* q_idx,
-                          const void* q_idx_scale, const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
-                          hipStream_t s) {
+                          const void* q_idx_scale, const float* w, int R, int32_t rows_per_seq, float* scores,
+                          int64_t ld, const TopkWs* ws, hipStream_t s) {
+  if (index_fmt == DSA_INDEX_FP8 && rows_per_seq > 1) {
+    const int G = rows_per_seq < kRowsPerGroupMax ? rows_per_seq : kRowsPerGroupMax;
+    return launch_indexer_fp8_rows(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
+                                   w, R, G, scores, ld, ws, s);
+  }
   if (index_fmt == DSA_INDEX_MXFP4)
     return launch_indexer_mxfp4(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(q_idx_scale), w,
                                 R, scores, ld, ws, s);
@@ -154,10 +161,11 @@ size_t dsa_workspace_bytes(int32_t op, int32_t R, int32_t max_ctx, int32_t k) {
   }
 }
 
-dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer, const void* q_idx, const void* q_idx_scale,
-                             const float* w, const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
-                             const int32_t* row_ctx, int32_t R, int32_t max_ctx, float* scores, int64_t ld_scores,
-                             void* stream) {
+dsa_status dsa_indexer_score_multi(const dsa_cache_desc* cache, int32_t layer, const void* q_idx,
+                                   const void* q_idx_scale, const float* w, const int32_t* block_table,
+                                   int32_t bt_stride, const int32_t* row_seq, const int32_t* row_ctx, int32_t R,
+                                   int32_t max_ctx, int32_t rows_per_seq, float* scores, int64_t ld_scores,
+                                   void* stream) {
   CacheView cv;
   RowMap rm;
   dsa_status st = check_cache(cache, layer, &cv);
@@ -166,12 +174,21 @@ dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer, const v
   if (q_idx == nullptr || q_idx_scale == nullptr || w == nullptr || scores == nullptr)
     return fail(DSA_ERR_NULL, "q_idx / q_idx_scale / w / scores is NULL");
   if (ld_scores < max_ctx) return fail(DSA_ERR_ARG, "ld_scores %lld < max_ctx %d", (long long)ld_scores, max_ctx);
+  if (rows_per_seq < 1) return fail(DSA_ERR_ARG, "rows_per_seq %d < 1", rows_per_seq);
   if (!aligned16(q_idx)) return fail(DSA_ERR_ALIGN, "q_idx is not 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(q_idx_scale) & 3u) return fail(DSA_ERR_ALIGN, "q_idx_scale is not 4-byte aligned");
   if (R == 0) return ok();
-  return hip_status(launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, scores, ld_scores, nullptr,
-                                   static_cast<hipStream_t>(stream)),
+  return hip_status(launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld_scores,
+                                   nullptr, static_cast<hipStream_t>(stream)),
                     "indexer");
+}
+
+dsa_status dsa_indexer_score(const dsa_cache_desc* cache, int32_t layer, const void* q_idx, const void* q_idx_scale,
+                             const float* w, const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
+                             const int32_t* row_ctx, int32_t R, int32_t max_ctx, float* scores, int64_t ld_scores,
+                             void* stream) {
+  return dsa_indexer_score_multi(cache, layer, q_idx, q_idx_scale, w, block_table, bt_stride, row_seq, row_ctx, R,
+                                 max_ctx, 1, scores, ld_scores, stream);
 }
 
 dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_ctx, int32_t R, int32_t max_ctx,
@@ -215,11 +232,12 @@ dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer, const uint
                     "sparse_mla");
 }
 
-dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const void* q_idx, const void* q_idx_scale,
-                           const float* w, const uint16_t* q_lat, const int32_t* block_table, int32_t bt_stride,
-                           const int32_t* row_seq, const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k,
-                           float sm_scale, int32_t* idx, float* out, float* lse, void* workspace, size_t ws_bytes,
-                           void* stream) {
+dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, const void* q_idx,
+                                 const void* q_idx_scale, const float* w, const uint16_t* q_lat,
+                                 const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
+                                 const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k, int32_t rows_per_seq,
+                                 float sm_scale, int32_t* idx, float* out, float* lse, void* workspace,
+                                 size_t ws_bytes, void* stream) {
   CacheView cv;
   RowMap rm;
   dsa_status st = check_cache(cache, layer, &cv);
@@ -228,6 +246,7 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const voi
   if (q_idx == nullptr || q_idx_scale == nullptr || w == nullptr || q_lat == nullptr || idx == nullptr || out == nullptr)
     return fail(DSA_ERR_NULL, "q_idx / q_idx_scale / w / q_lat / idx / out is NULL");
   if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
+  if (rows_per_seq < 1) return fail(DSA_ERR_ARG, "rows_per_seq %d < 1", rows_per_seq);
   if (!aligned16(q_idx) || !aligned16(q_lat)) return fail(DSA_ERR_ALIGN, "q_idx / q_lat is not 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(q_idx_scale) & 3u) return fail(DSA_ERR_ALIGN, "q_idx_scale is not 4-byte aligned");
   const size_t need = decode_ws(R, max_ctx, k);
@@ -244,13 +263,22 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const voi
   int32_t* phys = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)R * k * 4, 256);
   void* mla_ws = p;
-  hipError_t e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, scores, ld, &tw, s);
+  hipError_t e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld, &tw, s);
   if (e == hipSuccess) e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, idx, tw, phys, nullptr, &cv, &rm, s);
   if (e == hipSuccess) {
     // the selected tokens lie below max_ctx, so the row map's bound is unchanged
     e = launch_sparse_mla(cv, rm, q_lat, idx, phys, nullptr, R, k, sm_scale, out, lse, mla_ws, s);
   }
   return hip_status(e, "decode_step");
+}
+
+dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const void* q_idx, const void* q_idx_scale,
+                           const float* w, const uint16_t* q_lat, const int32_t* block_table, int32_t bt_stride,
+                           const int32_t* row_seq, const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k,
+                           float sm_scale, int32_t* idx, float* out, float* lse, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  return dsa_decode_step_multi(cache, layer, q_idx, q_idx_scale, w, q_lat, block_table, bt_stride, row_seq, row_ctx, R,
+                               max_ctx, k, 1, sm_scale, idx, out, lse, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -74,6 +74,13 @@ hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8
                               const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
                               hipStream_t stream);
 
+// Indexer for G consecutive rows per workgroup that share one sequence (FP8 keys): each
+// key tile is read and converted once for all of them.
+hipError_t launch_indexer_fp8_rows(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const float* q_scale,
+                                   const float* w, int R, int G, float* scores, int64_t ld, const TopkWs* ws,
+                                   hipStream_t stream);
+constexpr int kRowsPerGroupMax = 16;  // rows one workgroup of the row-group indexer covers, at most
+
 // Indexer over MXFP4 keys (q_idx: R x 32 x 64 packed e2m1, q_e8: R x 32 x 4 E8M0).
 hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const uint8_t* q_e8,
                                 const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,

@@ -39,13 +39,13 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run_step(case, dev, layer=0, k=None):
+def run_step(case, dev, layer=0, k=None, rows_per_seq=1):
     g = case if case.pool.is_cuda else case.to(dev)
     k = case.k if k is None else k
     R = g.num_rows
     idx, out, lse, ws = dsa.dsa_decode_step(g.pool, g.layout, layer, g.q_idx[layer], g.q_idx_scale[layer], g.w[layer],
                                             g.q_lat[layer], g.block_table, g.row_seq, g.row_ctx, case.max_ctx, k,
-                                            case.sm_scale)
+                                            case.sm_scale, rows_per_seq=rows_per_seq)
     torch.cuda.synchronize()
     scores = dsa.decode_scores_view(ws, R, case.max_ctx).cpu().numpy().copy()
     return scores, idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
@@ -260,6 +260,55 @@ def test_prefill_append_150k(dev):
         check_scores(scores[r], ref, ctx)
         sel = check_selection(scores[r], idx[r], ref, ctx, c.k)
         check_attention(hc, r, sel, out[r], lse[r])
+
+
+def test_prefill_append_row_groups(dev):
+    """The row-group indexer (rows_per_seq = all rows) on a 300-row append to a 20,000-token
+    prefix: identical bytes to the row-by-row path, and oracle parity on sampled rows."""
+    say("case: prefill-append 300 rows on 20000 prefix, rows_per_seq 300 vs 1")
+    c = make_prefill_case(20000, 300, block_size=64, seed=81, device=dev)
+    hc = HostCase(c)
+    a = run_step(c, dev, rows_per_seq=1)
+    b = run_step(c, dev, rows_per_seq=c.num_rows)
+    for r in range(c.num_rows):
+        ctx = int(hc.row_ctx[r])
+        assert np.array_equal(a[0][r, :ctx], b[0][r, :ctx]), f"scores row {r}"
+    for x, y in zip(a[1:], b[1:]):
+        assert np.array_equal(x, y)
+    for r in [0, 1, 17, 150, 299]:
+        say(f"  oracle row {r}")
+        ref = hc.oracle(r)
+        ctx = int(hc.row_ctx[r])
+        check_scores(b[0][r], ref, ctx)
+        sel = check_selection(b[0][r], b[1][r], ref, ctx, c.k)
+        check_attention(hc, r, sel, b[2][r], b[3][r])
+
+
+@pytest.mark.parametrize("hint", [4, 3])
+def test_speculative_verify_rows(dev, hint):
+    """Speculative verification: 5 sequences x 4 verify tokens, row j of sequence b sees
+    t < L_b + j + 1. hint 4 matches the runs; hint 3 makes workgroups straddle sequences,
+    which reload keys: the result must not change. Every row against the oracle."""
+    say(f"case: speculative verify 5 x 4 rows, rows_per_seq {hint}")
+    lens = [3000, 17000, 40000, 9000, 70000]
+    T = 4
+    row_seq = [b for b in range(len(lens)) for _ in range(T)]
+    row_ctx = [lens[b] + j + 1 for b in range(len(lens)) for j in range(T)]
+    c = make_case(row_ctx, row_seq=row_seq, ctx_lens_are_rows=True, block_size=64, seed=90, k=2048, device=dev)
+    hc = HostCase(c)
+    base = run_step(c, dev, rows_per_seq=1)
+    got = run_step(c, dev, rows_per_seq=hint)
+    for r in range(c.num_rows):
+        ctx = int(hc.row_ctx[r])
+        assert np.array_equal(base[0][r, :ctx], got[0][r, :ctx]), f"scores row {r}"
+    for x, y in zip(base[1:], got[1:]):
+        assert np.array_equal(x, y)
+    for r in range(c.num_rows):
+        ctx = int(hc.row_ctx[r])
+        ref = hc.oracle(r)
+        check_scores(got[0][r], ref, ctx)
+        sel = check_selection(got[0][r], got[1][r], ref, ctx, c.k)
+        check_attention(hc, r, sel, got[2][r], got[3][r])
 
 
 def test_out_of_range_block_ids_do_not_fault(dev):
