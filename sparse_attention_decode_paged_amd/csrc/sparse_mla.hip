@@ -10,8 +10,9 @@
 // Grid (split, row, head group of 32). A workgroup walks its split's slice of the
 // row's index list 64 tokens at a time:
 //   the chunk's token ids / page slots are the head of a load chain (ids -> latent
-//   rows), so they are fetched first (the next chunk's behind the current latents);
-//   gather the 64 latents (576 e4m3 bytes each) into LDS;
+//   rows), so they are fetched first; the 64 latents (576 e4m3 bytes each) of chunk
+//   c + 1 are loaded into registers while chunk c is computed (the ids of c + 2
+//   behind them) and go to LDS once chunk c is done with it;
 //   S = Q . C^T on 16x16x32 bf16 MFMAs (each wave: 16 tokens x 32 heads), scaled
 //   logits (log2 domain) to LDS;
 //   every wave then runs the online softmax of the whole chunk for the 32 heads
@@ -99,52 +100,61 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
   for (int c = 0; c < 4; ++c) acc[c] = v16f{};
   float s_run = 1.f;  // acc holds O / s_run (token scales folded into P per chunk)
 
-  for (int c0 = j0; c0 < j1; c0 += CH) {
-    // ---- gather: each thread issues its 9 of the token's 36 16-byte pieces (and the
-    // scale); the next chunk's ids are fetched behind them ----
-    {
-      int t = t_n < rm.max_ctx ? t_n : -1;
-      const int tc = t >= 0 ? t : 0;  // every load below stays in the pool; empty slots are masked
-      int64_t blk;
-      int slot;
-      if (phys != nullptr) {
-        const int ps = ps_n >= 0 ? ps_n : 0;
-        blk = (int64_t)ps >> cv.log2_bs;
-        blk = blk < cv.num_blocks ? blk : cv.num_blocks - 1;
-        slot = ps & bs_mask;
-      } else {
-        blk = token_block(cv, rm, seq, tc);
-        slot = tc & bs_mask;
-      }
-      const uint8_t* page = cv.pool + blk * cv.row_bytes + cv.lat_off;
-      const uint8_t* lrow = page + (int64_t)slot * kDLat;
-      float sv = 0.f;
-      if (qtr == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
-      constexpr int PN = PIECES / 4;  // 9 pieces per thread
-      v4i v[PN];
-#pragma unroll
-      for (int q = 0; q < PN; ++q) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (qtr + 4 * q));
-      if (c0 == j0) {
-#pragma unroll
-        for (int q = 0; q < QN; ++q) {
-          const int i = tid + NT * q, h = i / QP, pc = i - h * QP;
-          *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
-        }
-      }
-      {
-        const int j = c0 + CH + tt_g;
-        t_n = -1;
-        if (j < j1) {
-          t_n = irow[j];
-          if (phys != nullptr) ps_n = phys[(int64_t)r * k + j];
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < PN; ++q)
-        *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (qtr + 4 * q)) = t >= 0 ? v[q] : v4i{0, 0, 0, 0};
-      if (qtr == 0) sc_s[tt_g] = t >= 0 ? sv : kNegInf;  // -inf marks an empty slot
+  // ---- gather, software-pipelined: the latents of chunk c + 1 are loaded into
+  // registers (each thread 9 of its token's 36 16-byte pieces, and the scale) while
+  // chunk c is computed, and the ids of chunk c + 2 behind them ----
+  constexpr int PN = PIECES / 4;  // 9 pieces per thread
+  v4i v[PN];
+  float sv = 0.f;
+  bool tv = false;  // the gathered slot holds a token
+  auto issue = [&]() {
+    const int t = t_n < rm.max_ctx ? t_n : -1;
+    const int tc = t >= 0 ? t : 0;  // every load below stays in the pool; empty slots are masked
+    int64_t blk;
+    int slot;
+    if (phys != nullptr) {
+      const int ps = ps_n >= 0 ? ps_n : 0;
+      blk = (int64_t)ps >> cv.log2_bs;
+      blk = blk < cv.num_blocks ? blk : cv.num_blocks - 1;
+      slot = ps & bs_mask;
+    } else {
+      blk = token_block(cv, rm, seq, tc);
+      slot = tc & bs_mask;
     }
+    const uint8_t* page = cv.pool + blk * cv.row_bytes + cv.lat_off;
+    const uint8_t* lrow = page + (int64_t)slot * kDLat;
+    if (qtr == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
+#pragma unroll
+    for (int q = 0; q < PN; ++q) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (qtr + 4 * q));
+    tv = t >= 0;
+  };
+  auto fetch_ids = [&](int c0) {
+    const int j = c0 + tt_g;
+    t_n = -1;
+    if (j < j1) {
+      t_n = irow[j];
+      if (phys != nullptr) ps_n = phys[(int64_t)r * k + j];
+    }
+  };
+  issue();
+  fetch_ids(j0 + CH);
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+    const int i = tid + NT * q, h = i / QP, pc = i - h * QP;
+    *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
+  }
+
+  for (int c0 = j0; c0 < j1; c0 += CH) {
+    // LDS is free here: the previous chunk ended with a barrier
+#pragma unroll
+    for (int q = 0; q < PN; ++q)
+      *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (qtr + 4 * q)) = tv ? v[q] : v4i{0, 0, 0, 0};
+    if (qtr == 0) sc_s[tt_g] = tv ? sv : kNegInf;  // -inf marks an empty slot
     __syncthreads();
+    if (c0 + CH < j1) {  // uniform
+      issue();
+      fetch_ids(c0 + 2 * CH);
+    }
     // largest token scale of the chunk, computed by every wave
     float smax;
     {
