@@ -14,6 +14,7 @@ constexpr int kDV = 512;     // value width
 constexpr int kMaxK = 2048;
 constexpr int kWave = 64;
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));

@@ -13,14 +13,14 @@
 //   rows), so they are fetched first; the 64 latents (576 e4m3 bytes each) of chunk
 //   c + 1 are loaded into registers while chunk c is computed (the ids of c + 2
 //   behind them) and go to LDS once chunk c is done with it;
-//   S = Q . C^T on 16x16x32 bf16 MFMAs (each wave: 16 tokens x 32 heads), scaled
+//   S = Q . C^T on 16x16x32 bf16 MFMAs (8 waves, each 16 tokens x 16 heads), scaled
 //   logits (log2 domain) to LDS;
 //   every wave then runs the online softmax of the whole chunk for the 32 heads
 //   itself (running max / sum per head, identical in every wave), so one barrier
 //   separates S from P . V;
 //   P'' = p * scale_t / (largest scale in the chunk), in [0, 1], as fp16 straight
 //   into the MFMA operand registers;
-//   O += P'' . codes on 32x32x16 fp16 MFMAs (each wave: 128 of the 512 value
+//   O += P'' . codes on 32x32x16 fp16 MFMAs (each wave: 64 of the 512 value
 //   columns); e4m3 codes are exact in fp16, and fp16 P keeps 11 significant bits
 //   (bf16's 8 were visibly too few on rows dominated by a handful of tokens).
 //   The chunk's scale factor joins the per-head softmax rescale.
@@ -35,11 +35,15 @@ namespace dsa {
 
 namespace {
 using v8h = v8hf;
-constexpr int NT = 256;
+constexpr int NT = 256;   // merge workgroup
+constexpr int NTM = 512;  // attention workgroup: 8 waves, two per SIMD
+constexpr int NWM = NTM / 64;
 constexpr int CH = kMlaChunk;           // 64 tokens per iteration
 constexpr int PIECES = kDLat / 16;      // 36 16-byte pieces per latent
-constexpr int QROW = kDLat + 8;         // LDS row strides padded by 16 bytes so that the
-constexpr int LROW = kDLat + 16;        // 16 rows an MFMA fragment reads fall in distinct banks
+constexpr int LROW = kDLat + 16;        // LDS row strides padded by 16 bytes so that the
+constexpr int QROW = kDLat + 8;         // 16 rows an MFMA fragment reads fall in distinct banks
+constexpr int LAT_LDS = CH * LROW;      // the latent tile; Q passes through the same bytes first
+static_assert(kMlaGroup * QROW * 2 <= LAT_LDS, "Q staging fits the latent tile");
 constexpr int XROW = CH + 16;           // logit rows: the four 16-lane groups of a store hit distinct banks
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -49,7 +53,7 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm, const uint16_t* __restrict__ q_lat,
+__global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm, const uint16_t* __restrict__ q_lat,
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ phys, int k, int ts, float c2,
                                                         float* __restrict__ out, float* __restrict__ lse,
@@ -59,18 +63,17 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 5;  // half of the wave
 
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[kMlaGroup * QROW];
-  __shared__ __attribute__((aligned(16))) uint8_t lat_s[CH * LROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lat_s[LAT_LDS];
   __shared__ __attribute__((aligned(16))) float x_s[kMlaGroup * XROW];  // scaled logits, head-major
   __shared__ __attribute__((aligned(16))) float sc_s[CH];
-  __shared__ __attribute__((aligned(16))) float hv_s[4][kMlaGroup];  // per-wave exchange of per-head values
+  __shared__ __attribute__((aligned(16))) float hv_s[NWM][kMlaGroup];  // per-wave exchange of per-head values
 
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
   const int j1 = (j0 + ts < k) ? j0 + ts : k;
   const int seq = rm.row_seq[r];
   const int bs_mask = cv.block_size - 1;
-  const int tt_g = tid >> 2, qtr = tid & 3;  // gather: 4 threads per token, 9 pieces each
+  const int tt_g = tid >> 3, q8 = tid & 7;  // gather: 8 threads per token, pieces q8 + 8 q (q < 5) of 36
 
   // token id and page slot of this thread's gather token: the head of the load chain,
   // issued before anything else
@@ -82,28 +85,37 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       if (phys != nullptr) ps_n = phys[(int64_t)r * k + j];
     }
   }
-  // Q fragment rows for this head group (to LDS once the first latents are in flight)
-  constexpr int QP = kDLat / 8;  // 72 16-byte pieces per head row
-  constexpr int QN = kMlaGroup * QP / NT;
-  static_assert(QN * NT == kMlaGroup * QP, "Q pieces per thread");
+  // Q stays in registers for the whole workgroup: wave w holds the MFMA A fragments of
+  // heads [16 (w >> 2), +16) over all 576 dims (lane: head lane & 15, dims 32 kk +
+  // 8 (lane >> 4) ..+8). Q is read from HBM coalesced (rows of this head group are
+  // contiguous) and passes through the latent tile's LDS bytes, which the first chunk's
+  // latents overwrite after a barrier.
+  const int hrow = lane & 15, kq = 8 * (lane >> 4);
+  const int tg = wid & 3, hh = wid >> 2;  // QK tile of this wave: tokens 16 tg.., heads 16 hh..
+  constexpr int KQ = kDLat / 32;          // 18 steps of 32 dims
+  constexpr int QP = kDLat / 8;           // 72 16-byte pieces per head row
+  constexpr int QALL = kMlaGroup * QP;
+  constexpr int QN = (QALL + NTM - 1) / NTM;
   v4i qv[QN];
   {
     const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * kMlaGroup) * kDLat);
 #pragma unroll
-    for (int q = 0; q < QN; ++q) qv[q] = qg[tid + NT * q];
+    for (int q = 0; q < QN; ++q)
+      if (tid + NTM * q < QALL) qv[q] = qg[tid + NTM * q];
   }
+  v8bf qa[KQ];
 
   // running softmax state of head (lane & 31); every wave keeps an identical copy
   float m_run = kNegInf, l_run = 0.f;
-  v16f acc[4];
+  v16f acc[2];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] = v16f{};
+  for (int c = 0; c < 2; ++c) acc[c] = v16f{};
   float s_run = 1.f;  // acc holds O / s_run (token scales folded into P per chunk)
 
   // ---- gather, software-pipelined: the latents of chunk c + 1 are loaded into
-  // registers (each thread 9 of its token's 36 16-byte pieces, and the scale) while
-  // chunk c is computed, and the ids of chunk c + 2 behind them ----
-  constexpr int PN = PIECES / 4;  // 9 pieces per thread
+  // registers (each thread up to 5 of its token's 36 16-byte pieces, and the scale)
+  // while chunk c is computed, and the ids of chunk c + 2 behind them ----
+  constexpr int PN = (PIECES + 7) / 8;  // 5 pieces per thread, the last on q8 < 4
   v4i v[PN];
   float sv = 0.f;
   bool tv = false;  // the gathered slot holds a token
@@ -123,9 +135,10 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
     }
     const uint8_t* page = cv.pool + blk * cv.row_bytes + cv.lat_off;
     const uint8_t* lrow = page + (int64_t)slot * kDLat;
-    if (qtr == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
+    if (q8 == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
 #pragma unroll
-    for (int q = 0; q < PN; ++q) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (qtr + 4 * q));
+    for (int q = 0; q < PN; ++q)
+      if (q8 + 8 * q < PIECES) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (q8 + 8 * q));
     tv = t >= 0;
   };
   auto fetch_ids = [&](int c0) {
@@ -138,18 +151,27 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
   };
   issue();
   fetch_ids(j0 + CH);
+  {
+    uint16_t* q_s = reinterpret_cast<uint16_t*>(lat_s);
 #pragma unroll
-  for (int q = 0; q < QN; ++q) {
-    const int i = tid + NT * q, h = i / QP, pc = i - h * QP;
-    *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
+    for (int q = 0; q < QN; ++q) {
+      const int i = tid + NTM * q, h = i / QP, pc = i - h * QP;
+      if (i < QALL) *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
+    }
+    __syncthreads();
+    const uint16_t* qrow = q_s + (16 * hh + hrow) * QROW + kq;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) qa[kk] = *reinterpret_cast<const v8bf*>(qrow + 32 * kk);
+    __syncthreads();  // every wave holds its fragments before the latents overwrite them
   }
 
   for (int c0 = j0; c0 < j1; c0 += CH) {
     // LDS is free here: the previous chunk ended with a barrier
 #pragma unroll
     for (int q = 0; q < PN; ++q)
-      *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (qtr + 4 * q)) = tv ? v[q] : v4i{0, 0, 0, 0};
-    if (qtr == 0) sc_s[tt_g] = tv ? sv : kNegInf;  // -inf marks an empty slot
+      if (q8 + 8 * q < PIECES)
+        *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (q8 + 8 * q)) = tv ? v[q] : v4i{0, 0, 0, 0};
+    if (q8 == 0) sc_s[tt_g] = tv ? sv : kNegInf;  // -inf marks an empty slot
     __syncthreads();
     if (c0 + CH < j1) {  // uniform
       issue();
@@ -168,32 +190,23 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       smax = v > 0.f ? v : 1.f;
     }
 
-    // ---- S = Q . C^T : wave w -> tokens [16w, 16w+16), heads 0..31; scaled logits
-    // (log2 domain) go to LDS ----
+    // ---- S = Q . C^T : wave w -> tokens [16 (w & 3), +16), heads [16 (w >> 2), +16);
+    // scaled logits (log2 domain) go to LDS ----
     {
-      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-      const int hrow = lane & 15, kq = 8 * (lane >> 4);
-      const uint8_t* lrow = lat_s + (16 * wid + hrow) * LROW + kq;
-      const uint16_t* qa0 = q_s + hrow * QROW + kq;
-      const uint16_t* qa1 = q_s + (16 + hrow) * QROW + kq;
-#pragma unroll 6
-      for (int kk = 0; kk < kDLat / 32; ++kk) {
-        v8bf a0 = *reinterpret_cast<const v8bf*>(qa0 + 32 * kk);
-        v8bf a1 = *reinterpret_cast<const v8bf*>(qa1 + 32 * kk);
+      v4f s0 = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW + kq;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) {
         uint2 raw = *reinterpret_cast<const uint2*>(lrow + 32 * kk);
         v8bf b = e4m3x8_to_bf16(raw.x, raw.y);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], b, s0, 0, 0, 0);
       }
-      const int tt = 16 * wid + hrow;
+      const int tt = 16 * tg + hrow;
       const float sct = sc_s[tt];
       const bool ok = sct != kNegInf;
-      const int hb = 4 * (lane >> 4);
+      const int hb = 16 * hh + 4 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x_s[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
-        x_s[(16 + hb + i) * XROW + tt] = ok ? s1[i] * (sct * c2) : kNegInf;
-      }
+      for (int i = 0; i < 4; ++i) x_s[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
     }
     __syncthreads();
 
@@ -239,7 +252,7 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       m_run = mn;
     }
 
-    // ---- acc = acc * alpha * (s_run / smax) + P'' . codes : wave w -> columns [128w, 128w+128) ----
+    // ---- acc = acc * alpha * (s_run / smax) + P'' . codes : wave w -> columns [64w, 64w+64) ----
     // accumulator row rr of this lane is head 8 (rr >> 2) + 4 g + (rr & 3)
     if (lane < kMlaGroup) hv_s[wid][lane] = alpha;  // read back by this wave only
     const float rescale = s_run / smax;
@@ -251,20 +264,20 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c][4 * jj + i] *= a[i];
+        for (int c = 0; c < 2; ++c) acc[c][4 * jj + i] *= a[i];
     }
+    // B operand (codes of tokens 16 ks + 8 g .. +8 at value column 64 w + 32 c + (lane & 31))
+    // by one transposing LDS read: within each 16-lane group, lane 8 a + c' receives byte c'
+    // of the 8-byte rows that lanes 2 j + a point at, j = 0..7 (in token order). So lane l
+    // points at token row 8 (l >> 5) + ((l & 15) >> 1), columns 16 ((l >> 4) & 1) + 8 (l & 1).
+    const int tr_off = (8 * (lane >> 5) + ((lane & 15) >> 1)) * LROW + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
 #pragma unroll
     for (int ks = 0; ks < CH / 16; ++ks) {
-      const int tk = 16 * ks + 8 * g;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int col = 128 * wid + 32 * c + (lane & 31);
-        const uint8_t* vp = lat_s + tk * LROW + col;
-        uint32_t w0 = (uint32_t)vp[0] | ((uint32_t)vp[LROW] << 8) | ((uint32_t)vp[2 * LROW] << 16) |
-                      ((uint32_t)vp[3 * LROW] << 24);
-        uint32_t w1 = (uint32_t)vp[4 * LROW] | ((uint32_t)vp[5 * LROW] << 8) | ((uint32_t)vp[6 * LROW] << 16) |
-                      ((uint32_t)vp[7 * LROW] << 24);
-        v8h b = e4m3x8_to_f16(w0, w1);
+      for (int c = 0; c < 2; ++c) {
+        const uint8_t* vp = lat_s + 16 * ks * LROW + 64 * wid + 32 * c + tr_off;
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(vp));
+        v8h b = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, acc[c], 0, 0, 0);
       }
     }
@@ -282,9 +295,9 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
       for (int i = 0; i < 4; ++i) {
         const int h = 8 * jj + 4 * g + i;
         const float f = lv[i] > 0.f ? s_run / lv[i] : 0.f;
-        float* orow = out + ((int64_t)r * kHQ + hg * kMlaGroup + h) * kDV + 128 * wid + (lane & 31);
+        float* orow = out + ((int64_t)r * kHQ + hg * kMlaGroup + h) * kDV + 64 * wid + (lane & 31);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) orow[32 * c] = acc[c][4 * jj + i] * f;
+        for (int c = 0; c < 2; ++c) orow[32 * c] = acc[c][4 * jj + i] * f;
       }
     }
     if (lse != nullptr && tid < kMlaGroup)
@@ -294,9 +307,9 @@ __global__ __launch_bounds__(NT) void sparse_mla_kernel(CacheView cv, RowMap rm,
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int h = 8 * (rr >> 2) + 4 * g + (rr & 3);
-      float* orow = part_o + (pbase + h) * kDV + 128 * wid + (lane & 31);
+      float* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 31);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) __builtin_nontemporal_store(acc[c][rr] * s_run, orow + 32 * c);
+      for (int c = 0; c < 2; ++c) __builtin_nontemporal_store(acc[c][rr] * s_run, orow + 32 * c);
     }
     if (tid < kMlaGroup) {
       part_ml[(pbase + tid) * 2 + 0] = m_run;
@@ -368,7 +381,7 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     part_o = static_cast<float*>(ws);
     part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 4, 256));
   }
-  hipLaunchKernelGGL(sparse_mla_kernel, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NT), 0, stream, cv, rm, q_lat, idx, phys,
+  hipLaunchKernelGGL(sparse_mla_kernel, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, cv, rm, q_lat, idx, phys,
                      k, ts, c2, out, lse, part_o, part_ml, nsplit);
   if (nsplit > 1)
     hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
