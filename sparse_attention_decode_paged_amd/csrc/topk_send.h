@@ -20,7 +20,7 @@
 // (f << 32) | 0xFFFFFFFF, so an unsent key can reach a threshold c only if
 // f >= c >> 32; f = 0 when the unit sent all of its valid tokens. Sorting uses DPP /
 // permlane exchanges inside a wave; 256-token units merge the four waves' best 16
-// through LDS with one barrier.
+// through LDS with one barrier (a bitonic merge of the four sorted lists).
 #pragma once
 
 #include "common.h"
@@ -88,13 +88,26 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
     return;
   }
 
-  // one unit per workgroup: merge the waves' best 16 (and each wave's 17th) in LDS
-  if (lane < 16) lds[wid * 16 + lane] = sorted;
+  // one unit per workgroup: merge the waves' best 16 (and each wave's 17th) in LDS.
+  // Odd waves store theirs reversed, so lanes [0, 32) and [32, 64) each hold a bitonic
+  // sequence and the last two phases of a bitonic sort (11 steps) order all 64.
+  if (lane < 16) lds[wid * 16 + ((wid & 1) ? 15 - lane : lane)] = sorted;
   if (lane == 16) lds[64 + wid] = sorted;
   __syncthreads();
   const uint32_t all = lds[lane];
   const uint32_t w17 = max(max(lds[64], lds[65]), max(lds[66], lds[67]));
-  const uint32_t msort = wave_sort_desc_u32(all, lane);
+  uint32_t msort = all;
+  msort = bitonic_desc_step<32, 16>(msort, lane);
+  msort = bitonic_desc_step<32, 8>(msort, lane);
+  msort = bitonic_desc_step<32, 4>(msort, lane);
+  msort = bitonic_desc_step<32, 2>(msort, lane);
+  msort = bitonic_desc_step<32, 1>(msort, lane);
+  msort = bitonic_desc_step<64, 32>(msort, lane);
+  msort = bitonic_desc_step<64, 16>(msort, lane);
+  msort = bitonic_desc_step<64, 8>(msort, lane);
+  msort = bitonic_desc_step<64, 4>(msort, lane);
+  msort = bitonic_desc_step<64, 2>(msort, lane);
+  msort = bitonic_desc_step<64, 1>(msort, lane);
   const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)msort, p.m - 1);
   const uint32_t nxt = max((uint32_t)__builtin_amdgcn_readlane((int)msort, p.m), w17);
   // keys this wave sends, and how many lower waves send (all within their best 16)
