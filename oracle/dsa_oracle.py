@@ -273,3 +273,110 @@ def dense_mla_layer_bytes(ctx: int, latent_fmt: str = "fp8") -> int:
 def kv_bytes_per_token(layers: int, latent_fmt: str, index_fmt) -> int:
     """Per-GPU per-token cache bytes over ``layers`` DSA layers (TP replicates both caches)."""
     return layers * (latent_bytes(latent_fmt) + (index_key_bytes(index_fmt) if index_fmt else 0))
+
+
+# ---------------------------------------------------------------------------
+# New-token cache append: the step just before the hot path (page 1, fused
+# front-end: the new token's index key is quantised and written, and its latent
+# is written into the cache, before scoring). The pages do not spell out the
+# quantiser; the reading used here, per vector:
+#   FP8   scale = amax / 448 in fp32 (1 when amax = 0); y = x / scale in fp32,
+#         clamped to +-448 and rounded to the nearest e4m3 value, ties to the
+#         even code; the sign bit follows the sign of y (so -0 gives 0x80).
+#   MXFP4 per 32 elements E = floor(log2 amax) - 2 clamped to [-127, 127] (0 when
+#         amax = 0), stored as the E8M0 byte E + 127; y = x / 2^E rounded to the
+#         nearest e2m1 magnitude, ties to the even code, 6 at most; no negative 0.
+# Rounding is done by searching the value tables above, not by formula.
+# ---------------------------------------------------------------------------
+
+_E4M3_POS = np.array([E4M3_TABLE[c] for c in range(0x7F)], dtype=np.float64)  # codes 0x00..0x7E
+_E2M1_POS = E2M1_TABLE[:8]                                                       # nibbles 0..7
+
+
+def _nearest_even(table: np.ndarray, mag: float) -> int:
+    """Index of the table value nearest to mag; on a tie the even index."""
+    d = np.abs(table - mag)
+    best = np.flatnonzero(d == d.min())
+    even = [int(i) for i in best if i % 2 == 0]
+    return even[0] if even else int(best[0])
+
+
+def e4m3_encode(y: float) -> int:
+    """e4m3 code of an fp32 value already inside [-448, 448]."""
+    y = float(np.float32(y))
+    code = _nearest_even(_E4M3_POS, abs(y))
+    return code | (0x80 if math.copysign(1.0, y) < 0 else 0)
+
+
+def e2m1_encode(y: float) -> int:
+    """e2m1 nibble of a value (magnitudes above 6 clamp to 6)."""
+    m = _nearest_even(_E2M1_POS, min(abs(y), 6.0))
+    return m | (0x8 if (y < 0 and m > 0) else 0)
+
+
+def quantize_fp8_vector(x) -> tuple:
+    """(codes uint8 [D], fp32 scale) of one vector, per the reading above."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    scale = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    y = np.clip((x / scale).astype(np.float32), np.float32(-448.0), np.float32(448.0))
+    return np.array([e4m3_encode(v) for v in y], dtype=np.uint8), scale
+
+
+def quantize_mxfp4_vector(x) -> tuple:
+    """(packed uint8 [D/2] with element 2i in the low nibble of byte i, E8M0 uint8 [D/32])."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    groups = x.reshape(-1, MX_GROUP)
+    nib = np.zeros(x.size, dtype=np.uint8)
+    e8 = np.zeros(groups.shape[0], dtype=np.uint8)
+    for gi, g in enumerate(groups):
+        amax = float(np.max(np.abs(g)))
+        if amax > 0:
+            _, ex = math.frexp(amax)          # amax = m * 2^ex, m in [0.5, 1)
+            E = min(max(ex - 1 - 2, -127), 127)
+        else:
+            E = 0
+        e8[gi] = E + 127
+        for j, v in enumerate(g):
+            nib[gi * MX_GROUP + j] = e2m1_encode(v / 2.0 ** E)
+    packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+    return packed, e8
+
+
+def append_tokens(pool: np.ndarray, lay: Layout, layer: int, bt: np.ndarray, row_seq, pos,
+                  idx_key=None, latent=None) -> np.ndarray:
+    """A copy of ``pool`` with row r's quantised index key (fp32 [R][128]) and
+    latent (fp32 [R][576]) written at token pos[r] of block-table row row_seq[r].
+    Rows whose position or block id falls outside the table or the pool are skipped."""
+    out = np.array(pool, dtype=np.uint8, copy=True).reshape(-1, lay.row_bytes)
+    nb = out.shape[0]
+    bs = lay.block_size
+    bt = np.asarray(bt)
+    for r in range(len(pos)):
+        p = int(pos[r])
+        row = bt[int(row_seq[r])]
+        if p < 0 or p >= row.size * bs:
+            continue
+        blk, slot = int(row[p // bs]), p % bs
+        if blk < 0 or blk >= nb:
+            continue
+        if latent is not None:
+            codes, sc = quantize_fp8_vector(latent[r])
+            o = lay.lat_off[layer]
+            out[blk, o + slot * D_LAT: o + (slot + 1) * D_LAT] = codes
+            out[blk, o + bs * D_LAT + 4 * slot: o + bs * D_LAT + 4 * slot + 4] = np.frombuffer(
+                np.float32(sc).tobytes(), dtype=np.uint8)
+        if idx_key is not None:
+            o = lay.idx_off[layer]
+            if lay.index_fmt == "fp8":
+                codes, sc = quantize_fp8_vector(idx_key[r])
+                out[blk, o + slot * D_IDX: o + (slot + 1) * D_IDX] = codes
+                out[blk, o + bs * D_IDX + 4 * slot: o + bs * D_IDX + 4 * slot + 4] = np.frombuffer(
+                    np.float32(sc).tobytes(), dtype=np.uint8)
+            else:
+                packed, e8 = quantize_mxfp4_vector(idx_key[r])
+                half = D_IDX // 2
+                out[blk, o + slot * half: o + (slot + 1) * half] = packed
+                ng = D_IDX // MX_GROUP
+                out[blk, o + bs * half + ng * slot: o + bs * half + ng * (slot + 1)] = e8
+    return out.reshape(pool.shape)

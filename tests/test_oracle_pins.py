@@ -320,3 +320,94 @@ def test_byte_accounting_golden():
         assert O.kv_bytes_per_token(e["layers"], e["latent"], e["index"]) == e["value"], key
     assert (O.H_IDX, O.D_IDX, O.H_Q) == (g["indexer_heads"]["value"], g["indexer_head_dim"]["value"],
                                           g["attention_heads"]["value"])
+
+
+# ----------------------------------------------------------------------------- cache append
+def test_e4m3_encode_matches_torch_cast_on_every_midpoint():
+    """The oracle's table-search rounding against torch's own float8_e4m3fn cast: every
+    code value, every midpoint between neighbouring codes (the ties), and random values."""
+    import torch
+    pos = O.E4M3_TABLE[:0x7F]
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([pos, mids, -pos, -mids, rng.uniform(-448, 448, 3000),
+                           rng.normal(0, 0.01, 1000)]).astype(np.float32)
+    want = torch.tensor(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([O.e4m3_encode(v) for v in vals], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_encode_round_trip_and_ties():
+    for c in range(256):
+        v = O.E4M3_TABLE[c]
+        if np.isnan(v):
+            continue
+        assert O.e4m3_encode(v) == c, hex(c)
+    assert O.e4m3_encode(1.0625) == 0x38      # 1.0 | 1.125: even code
+    assert O.e4m3_encode(1.1875) == 0x3A      # 1.125 | 1.25: even code
+    assert O.e4m3_encode(2.0 ** -10) == 0x00  # half the smallest subnormal: even (zero)
+
+
+def test_e2m1_encode_ties_clamp_and_round_trip():
+    for n in range(16):
+        if n == 8:
+            continue                          # -0 is never produced
+        assert O.e2m1_encode(O.E2M1_TABLE[n]) == n
+    ties = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for v, n in ties.items():
+        assert O.e2m1_encode(v) == n and O.e2m1_encode(-v) == (n | 8 if n else 0)
+    assert O.e2m1_encode(7.9) == 7 and O.e2m1_encode(-100.0) == 15
+
+
+def test_quantize_fp8_vector_error_bound():
+    """Every dequantised element is within half a code spacing (times the scale) of the input."""
+    rng = np.random.default_rng(4)
+    for x in [rng.normal(0, 1, 576), rng.normal(0, 1e-3, 128), np.zeros(128), np.r_[np.zeros(127), -5.0]]:
+        codes, sc = O.quantize_fp8_vector(x)
+        x32 = np.asarray(x, dtype=np.float32).astype(np.float64)
+        deq = O.E4M3_TABLE[codes] * float(sc)
+        amax = np.abs(x32).max()
+        assert float(sc) == (float(np.float32(amax / np.float32(448))) if amax > 0 else 1.0)
+        mag = np.abs(x32 / float(sc))
+        e = np.floor(np.log2(np.maximum(mag, 2.0 ** -6)))
+        half = 2.0 ** (e - 3) / 2 * float(sc)         # half the spacing at that binade (3 mantissa bits)
+        assert np.all(np.abs(deq - x32) <= half * (1 + 1e-6) + 1e-30)
+        if amax > 0:
+            assert np.max(np.abs(deq)) == pytest.approx(amax, rel=1e-6)
+
+
+def test_quantize_mxfp4_vector_exponent_and_bound():
+    rng = np.random.default_rng(5)
+    x = rng.normal(0, 1, 128) * np.repeat([1e-3, 1.0, 40.0, 0.0], 32)
+    packed, e8 = O.quantize_mxfp4_vector(x)
+    assert e8[3] == 127                                  # an all-zero group keeps scale 1
+    deq = O.mxfp4_decode(packed[None], e8[None])[0]
+    x32 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    for g in range(3):
+        s = slice(32 * g, 32 * g + 32)
+        amax = np.abs(x32[s]).max()
+        E = int(e8[g]) - 127
+        assert 2.0 ** (E + 2) <= amax < 2.0 ** (E + 3)   # amax / 2^E in [4, 8)
+        # nearest e2m1 step is at most 2 (between 4 and 6), and 6 caps values up to 8
+        assert np.all(np.abs(deq[s] - x32[s]) <= 2.0 * 2.0 ** E + 1e-30)
+
+
+def test_append_tokens_writes_only_the_token_slot():
+    from synth import make_case
+    c = make_case([200, 90], block_size=16, seed=8, k=64)
+    lay = O.Layout(c.layout)
+    pool = c.pool.numpy().copy()
+    bt = c.block_table.numpy()
+    rng = np.random.default_rng(6)
+    key = rng.normal(0, 1, (3, 128)).astype(np.float32)
+    lat = rng.normal(0, 2, (3, 576)).astype(np.float32)
+    row_seq, pos = [0, 1, 1], [150, 5, 10 ** 6]        # the last row is outside its table: skipped
+    out = O.append_tokens(pool, lay, 0, bt, row_seq, pos, idx_key=key, latent=lat)
+    diff = np.flatnonzero(out.reshape(-1) != pool.reshape(-1))
+    rows = set((diff // lay.row_bytes).tolist())
+    assert rows <= {int(bt[0][150 // 16]), int(bt[1][5 // 16])}
+    for r in range(2):
+        k_back = O.read_index_keys(out, lay, 0, bt[row_seq[r]], [pos[r]])[0]
+        l_back = O.read_latents(out, lay, 0, bt[row_seq[r]], [pos[r]])[0]
+        assert np.max(np.abs(k_back - key[r])) <= np.abs(key[r]).max() / 448 * 16 + 1e-12
+        assert np.max(np.abs(l_back - lat[r])) <= np.abs(lat[r]).max() / 448 * 16 + 1e-12
