@@ -208,6 +208,28 @@ dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer,
                                  float sm_scale, int32_t* idx, float* out, float* lse,
                                  void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * New-token cache append, the step just before the hot path (page 1, fused
+ * front-end: the new token's index key is quantised and written, and its latent is
+ * written into the packed cache, before scoring). For each row r, token pos[r] of
+ * block-table row row_seq[r] gets, for `layer`:
+ *   idx_key  R x 128 fp32 (nullable): FP8 pool: e4m3 codes of x / s with one fp32
+ *            scale s = amax / 448 (1 if amax = 0), values clamped to +-448, rounded to
+ *            nearest, ties to the even code; MXFP4 pool: per 32 elements the E8M0
+ *            exponent E + 127 with E = floor(log2 amax) - 2 (clamped to [-127, 127], 0
+ *            if amax = 0) and e2m1 codes of x / 2^E, nearest, ties to even, at most 6.
+ *   latent   R x 576 fp32 (nullable): e4m3 codes + fp32 scale as for an FP8 key.
+ * (The quantiser is this library's reading; the pages do not spell one out.)
+ * Rows whose pos is negative or past the table, or whose block id lies outside
+ * [0, num_blocks), write nothing. Rows must target distinct slots (writes of two
+ * rows to one slot race). DSA_ERR_NULL if both inputs are NULL.
+ */
+dsa_status dsa_cache_append(const dsa_cache_desc* cache, int32_t layer,
+                            const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* row_seq, const int32_t* pos,
+                            const float* idx_key, const float* latent,
+                            int32_t R, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,12 +1,13 @@
 """DSA decode over a packed paged cache on MI355X (gfx950): HIP kernels behind a C ABI.
 
 The Python functions are a thin ctypes layer over libdsa.so (include/dsa.h):
-dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step.
+dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step (each decode-step and
+indexer call takes an optional rows_per_seq), and dsa_cache_append.
 """
 from .binding import (  # noqa: F401
     DSAError, CacheDesc, load_library, make_cache_desc, decode_scores_view, EXPORTED, LIB_PATH,
     dsa_abi_version, dsa_status_string, dsa_workspace_bytes, dsa_decode_scores_ld,
-    dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step,
+    dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step, dsa_cache_append,
     DSA_INDEX_FP8, DSA_INDEX_MXFP4, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP,
 )
 from . import accounting  # noqa: F401

@@ -25,7 +25,7 @@ H_IDX, D_IDX, H_Q, D_LAT, D_V = 32, 128, 96, 576, 512
 
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_last_error_detail", "dsa_workspace_bytes",
             "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step",
-            "dsa_indexer_score_multi", "dsa_decode_step_multi")
+            "dsa_indexer_score_multi", "dsa_decode_step_multi", "dsa_cache_append")
 
 
 class DSAError(RuntimeError):
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     L.dsa_indexer_score_multi.restype = _i32
     L.dsa_indexer_score_multi.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _i64,
                                           _vp]
+    L.dsa_cache_append.restype = _i32
+    L.dsa_cache_append.argtypes = [P, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]
     L.dsa_decode_step_multi.restype = _i32
     L.dsa_decode_step_multi.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _f32, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -240,6 +242,22 @@ def dsa_decode_step(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_tab
                                  workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st, "dsa_decode_step_multi")
     return idx, out, lse, workspace
+
+
+def dsa_cache_append(pool, layout, layer, block_table, row_seq, pos, idx_key=None, latent=None):
+    """Quantise and write each row's new index key (fp32 [R][128]) and / or latent
+    (fp32 [R][576]) at token pos[r] of block-table row row_seq[r] (in place)."""
+    L = load_library()
+    R = row_seq.shape[0]
+    d = make_cache_desc(pool, layout)
+    st = L.dsa_cache_append(ctypes.byref(d), layer, _dev(block_table, "block_table", torch.int32),
+                            _bt_stride(block_table), _dev(row_seq, "row_seq", torch.int32),
+                            _dev(pos, "pos", torch.int32),
+                            _dev(idx_key, "idx_key", torch.float32) if idx_key is not None else None,
+                            _dev(latent, "latent", torch.float32) if latent is not None else None,
+                            R, _stream(pool.device))
+    _check(st, "dsa_cache_append")
+    return pool
 
 
 def decode_scores_view(workspace: torch.Tensor, R: int, max_ctx: int) -> torch.Tensor:

@@ -7,7 +7,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["dsa_api.cpp", "indexer.hip", "indexer_rows.hip", "indexer_mxfp4.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["dsa_api.cpp", "indexer.hip", "indexer_rows.hip", "indexer_mxfp4.hip", "topk.hip", "sparse_mla.hip",
+           "cache_append.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -232,6 +232,25 @@ dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer, const uint
                     "sparse_mla");
 }
 
+dsa_status dsa_cache_append(const dsa_cache_desc* cache, int32_t layer, const int32_t* block_table, int32_t bt_stride,
+                            const int32_t* row_seq, const int32_t* pos, const float* idx_key, const float* latent,
+                            int32_t R, void* stream) {
+  CacheView cv;
+  dsa_status st = check_cache(cache, layer, &cv);
+  if (st) return st;
+  if (R < 0 || R > 65535) return fail(DSA_ERR_ARG, "R %d out of [0, 65535]", R);
+  if (R == 0) return ok();
+  if (block_table == nullptr || row_seq == nullptr || pos == nullptr)
+    return fail(DSA_ERR_NULL, "block_table / row_seq / pos is NULL");
+  if (idx_key == nullptr && latent == nullptr) return fail(DSA_ERR_NULL, "both idx_key and latent are NULL");
+  if (bt_stride < 1) return fail(DSA_ERR_ARG, "bt_stride %d < 1", bt_stride);
+  if ((reinterpret_cast<uintptr_t>(idx_key) | reinterpret_cast<uintptr_t>(latent)) & 3u)
+    return fail(DSA_ERR_ALIGN, "idx_key / latent is not 4-byte aligned");
+  return hip_status(launch_cache_append(cv, cache->index_fmt, block_table, bt_stride, row_seq, pos, idx_key, latent, R,
+                                        static_cast<hipStream_t>(stream)),
+                    "cache_append");
+}
+
 dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, const void* q_idx,
                                  const void* q_idx_scale, const float* w, const uint16_t* q_lat,
                                  const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,

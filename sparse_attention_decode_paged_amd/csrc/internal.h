@@ -81,6 +81,11 @@ hipError_t launch_indexer_fp8_rows(const CacheView& cv, const RowMap& rm, const 
                                    hipStream_t stream);
 constexpr int kRowsPerGroupMax = 16;  // rows one workgroup of the row-group indexer covers, at most
 
+// New-token cache append (quantise and write index key and latent of one token per row).
+hipError_t launch_cache_append(const CacheView& cv, int32_t index_fmt, const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* row_seq, const int32_t* pos, const float* idx_key,
+                               const float* latent, int R, hipStream_t stream);
+
 // Indexer over MXFP4 keys (q_idx: R x 32 x 64 packed e2m1, q_e8: R x 32 x 4 E8M0).
 hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const uint8_t* q_e8,
                                 const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,

@@ -126,6 +126,22 @@ def test_topk_and_mla_reject_bad_arguments(lib):
                                0.04, FAKE, FAKE, FAKE, FAKE, dws, None) == 2
 
 
+def test_multi_and_append_reject_bad_arguments(lib):
+    d = _desc()
+    dws = dsa.dsa_workspace_bytes(dsa.DSA_OP_DECODE_STEP, 1, 8192, 2048)
+    assert lib.dsa_decode_step_multi(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1, 8192,
+                                     2048, 0, 0.04, FAKE, FAKE, FAKE, FAKE, dws, None) == 2   # rows_per_seq 0
+    assert lib.dsa_indexer_score_multi(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, 128, FAKE, FAKE, 1, 8192, 0,
+                                       FAKE, 8192, None) == 2
+    assert lib.dsa_cache_append(ctypes.byref(d), 0, FAKE, 128, FAKE, FAKE, None, None, 1, None) == 1  # no input
+    assert lib.dsa_cache_append(ctypes.byref(d), 0, None, 128, FAKE, FAKE, FAKE, None, 1, None) == 1
+    assert lib.dsa_cache_append(ctypes.byref(d), 0, FAKE, 128, FAKE, FAKE, FAKE + 2, None, 1, None) == 5
+    assert lib.dsa_cache_append(ctypes.byref(d), 0, FAKE, 0, FAKE, FAKE, FAKE, None, 1, None) == 2
+    assert lib.dsa_cache_append(ctypes.byref(d), 0, FAKE, 128, FAKE, FAKE, FAKE, None, -1, None) == 2
+    assert lib.dsa_cache_append(ctypes.byref(d), 0, FAKE, 128, FAKE, FAKE, FAKE, None, 0, None) == 0   # nothing to do
+    assert lib.dsa_cache_append(ctypes.byref(d), 5, FAKE, 128, FAKE, FAKE, FAKE, None, 1, None) != 0   # no layer 5
+
+
 def test_binding_refuses_cpu_tensors(lib):
     import torch
     pool = torch.zeros((4, 45568), dtype=torch.uint8)

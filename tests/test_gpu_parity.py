@@ -351,3 +351,66 @@ def test_workspace_reuse_across_inputs(dev):
     i1, o1 = go(b, ws)
     i2, o2 = go(b, None)
     assert np.array_equal(i1, i2) and np.array_equal(o1, o2)
+
+
+# ----------------------------------------------------------------------------- cache append
+def _append_inputs(R, seed):
+    """fp32 keys / latents with the cases that decide rounding: exact ties of the e4m3
+    grid (amax 448 makes the scale 1), e2m1 midpoints, zero vectors, tiny values, signs."""
+    rng = np.random.default_rng(seed)
+    key = rng.normal(0, 1, (R, 128)).astype(np.float32)
+    lat = rng.normal(0, 3, (R, 576)).astype(np.float32)
+    mids = np.array([1.0625, 1.1875, 3.25, -5.5, 0.0068359375, 448.0], dtype=np.float32)  # e4m3 midpoints (+ amax)
+    lat[0, :6] = mids
+    lat[0, 6:] = 0.5
+    key[0, :6] = mids
+    key[0, 6:] = 0.25
+    key[1] = 0.0                                                  # all-zero key: scale 1
+    lat[1] = 0.0
+    key[2, :32] = np.array([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 4, dtype=np.float32)  # e2m1 ties, E = 0
+    key[2, 32:64] = np.float32(1e-30)                             # tiny group
+    key[3] *= -1e5                                                # large values
+    return key, lat
+
+
+@pytest.mark.parametrize("fmt,bs", [("fp8", 64), ("fp8", 16), ("mxfp4", 128), ("mxfp4", 16)])
+def test_cache_append_bit_exact(dev, fmt, bs):
+    """New-token append: the whole pool after the GPU append equals the oracle's append of
+    the same inputs byte for byte; rows outside their table or on an unmapped block write nothing."""
+    say(f"case: cache append {fmt} bs {bs}")
+    c = make_case([300, 1000, 64, 2000, 5], block_size=bs, seed=95, k=64, index_fmt=fmt, num_layers=2,
+                  spare_blocks=2).to(dev)
+    R = 9
+    key, lat = _append_inputs(R, 96)
+    # rows 5, 6, 8 write nothing: a negative position, one past the table, one on an unmapped (-1) block
+    row_seq = np.array([0, 1, 2, 3, 4, 0, 1, 3, 4], dtype=np.int32)
+    pos = np.array([299, 1000, 10, 1999, 4, -1, 10 ** 7, 300, 200], dtype=np.int32)
+    bt = c.block_table.cpu().numpy()
+    assert bt[4][200 // bs] == -1
+    pool0 = c.pool.cpu().numpy()
+    want = O.append_tokens(pool0, O.Layout(c.layout), 1, bt, row_seq, pos, idx_key=key, latent=lat)
+    dsa.dsa_cache_append(c.pool, c.layout, 1, c.block_table, torch.tensor(row_seq, device=dev),
+                         torch.tensor(pos, device=dev), idx_key=torch.tensor(key, device=dev),
+                         latent=torch.tensor(lat, device=dev))
+    torch.cuda.synchronize()
+    got = c.pool.cpu().numpy()
+    bad = np.flatnonzero(got.reshape(-1) != want.reshape(-1))
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+    assert np.any(got != pool0), "nothing was written"
+
+
+def test_append_then_decode(dev):
+    """Append a token's key and latent at position ctx, then decode over ctx + 1 tokens:
+    the new token is scored and attended like any other (oracle on the appended bytes)."""
+    say("case: append then decode")
+    c = make_case([5000, 30000], block_size=64, seed=97, k=2048, spare_blocks=2).to(dev)
+    rng = np.random.default_rng(98)
+    key = (rng.normal(0, 1, (2, 128)) * 4).astype(np.float32)
+    lat = rng.normal(0, 1, (2, 576)).astype(np.float32)
+    pos = c.row_ctx.clone()                                        # the next token of each sequence
+    dsa.dsa_cache_append(c.pool, c.layout, 0, c.block_table, c.row_seq, pos,
+                         idx_key=torch.tensor(key, device=dev), latent=torch.tensor(lat, device=dev))
+    c.row_ctx += 1
+    scores, idx, out, lse = full_check(c, dev)
+    for r in range(2):
+        assert int(c.row_ctx[r]) - 1 < scores.shape[1]
