@@ -623,8 +623,47 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __rest
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (((umine >> j) & 1u) && (all || (fl[j] != 0u && fl[j] >= cu_hi))) fmask |= 1u << j;
-    fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
     cstar = c1;
+    if (upt < 4) {
+      // Common case first: one block scan gives both the number of flagged units and,
+      // were there none, every unit's output offset, so with no flagged unit the
+      // selection is written without a second scan.
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= c1) bits |= 1u << i;
+      const uint32_t umask = m >= 16 ? 0xFFFFu : ((1u << m) - 1u);
+      uint32_t v[4] = {(uint32_t)__popc(fmask), 0u, 0u, 0u}, off[4], tot[4];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < upt) v[1 + j] = (uint32_t)__popc(bits & ((umask << (m * j)) & 0xFFFFu));
+      excl_scan4(v, off, tot, upt + 1, S);
+      nflag = tot[0];
+      fbase = off[0];
+      if (nflag == 0) {
+        uint32_t base = 0, uoff[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          uoff[j] = base + off[1 + j];
+          base += j < upt ? tot[1 + j] : 0u;
+        }
+        const uint32_t total = base;
+        uint32_t* list = S.a.hist;  // free since the search
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int j = i >> lm;
+          const uint32_t oj = j == 0 ? uoff[0] : j == 1 ? uoff[1] : uoff[2];
+          const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
+          if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = 0xFFFFFFFFu - kl[i];
+        }
+        __syncthreads();
+        flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
+        return;
+      }
+      __syncthreads();  // the write path below runs its own scan4
+    } else {
+      fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
+    }
     if (nflag > 0) {
       if (nflag > (uint32_t)FCAP) {
         select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
