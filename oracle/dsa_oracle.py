@@ -380,3 +380,55 @@ def append_tokens(pool: np.ndarray, lay: Layout, layer: int, bt: np.ndarray, row
                 ng = D_IDX // MX_GROUP
                 out[blk, o + bs * half + ng * slot: o + bs * half + ng * (slot + 1)] = e8
     return out.reshape(pool.shape)
+
+
+# ---------------------------------------------------------------------------
+# The exact top-k merge of decode context parallelism, emulated on one set of
+# scores (page 1, DCP section: each of W GPUs holds every W-th token; each sends
+# only its best 1.5 * k / W candidates, each packed with its score into 32 bits
+# from the BF16 score; every GPU radix-selects the same global top-k from the
+# gathered words; a GPU that holds more of the top-k than it sent is detected and
+# resends its full local top-k). Reading: a word is (orderable BF16 key << 16) |
+# slot, slot = the candidate's place in its shard's list; T = the BF16 key of the
+# k-th largest word; a shard whose list was full resends when its weakest sent key
+# reaches T; the answer is the exact fp32 top-k over the sent candidates with key
+# >= T and the resent lists.
+# ---------------------------------------------------------------------------
+
+def bf16_key(x32) -> np.ndarray:
+    """Orderable 16-bit key of fp32 values rounded to BF16 (nearest, ties to even):
+    larger value -> larger key, -0 == +0; 0 only for the all-ones NaN pattern."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16          # round to nearest even on the dropped half
+    b = (r & 0xFFFF).astype(np.uint32)
+    b = np.where(b == 0x8000, 0, b)
+    return np.where(b & 0x8000, (~b) & 0xFFFF, b | 0x8000).astype(np.uint32)
+
+
+def dcp_merge(scores32: np.ndarray, k: int, W: int):
+    """(selected tokens ascending, resend mask over shards, words exchanged)."""
+    s = np.asarray(scores32, dtype=np.float32)
+    n = s.shape[0]
+    M = -(-3 * k // (2 * W))                           # ceil(1.5 k / W)
+    sent, words = [], []
+    for r in range(W):
+        tok = np.arange(r, n, W)
+        loc = select_topk(s[tok], M)
+        g = tok[loc]
+        sent.append((tok, g))
+        keys = bf16_key(s[g]) if g.size else np.zeros(0, np.uint32)
+        words.extend(((keys.astype(np.uint64) << 16) | np.arange(g.size, dtype=np.uint64)).tolist())
+    words = np.array(sorted(words, reverse=True), dtype=np.uint64)
+    T = int(words[k - 1] >> 16) if words.size >= k else 0
+    mask = 0
+    union = []
+    for r, (tok, g) in enumerate(sent):
+        keys = bf16_key(s[g]) if g.size else np.zeros(0, np.uint32)
+        if tok.size > g.size and g.size and int(keys.min()) >= T:
+            mask |= 1 << r
+            union.append(tok[select_topk(s[tok], k)])
+        else:
+            union.append(g[keys >= T])
+    u = np.sort(np.concatenate(union)) if union else np.zeros(0, np.int64)   # token order: ties by token
+    pick = select_topk(s[u], k)
+    return np.sort(u[pick]), mask, int(words.size)

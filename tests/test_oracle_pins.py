@@ -411,3 +411,41 @@ def test_append_tokens_writes_only_the_token_slot():
         l_back = O.read_latents(out, lay, 0, bt[row_seq[r]], [pos[r]])[0]
         assert np.max(np.abs(k_back - key[r])) <= np.abs(key[r]).max() / 448 * 16 + 1e-12
         assert np.max(np.abs(l_back - lat[r])) <= np.abs(lat[r]).max() / 448 * 16 + 1e-12
+
+
+# ----------------------------------------------------------------------------- DCP merge
+def test_bf16_key_orders_like_the_rounded_values():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.normal(0, 1, 4000), [0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38, 1e-40]]).astype(np.float32)
+    import torch
+    b = torch.tensor(x).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)   # torch's own RNE
+    k = O.bf16_key(x).astype(np.int64)
+    i, j = rng.integers(0, x.size, (2, 20000))
+    assert np.array_equal(np.sign(k[i] - k[j]), np.sign(b[i] - b[j]))
+    assert O.bf16_key(np.float32(-0.0)) == O.bf16_key(np.float32(0.0))
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_dcp_merge_equals_the_plain_top_k(W):
+    """Random rows, rows with ties, and rows whose top-k sits in one shard's tokens (which
+    forces that shard to resend): the merged selection is the exact top-k every time."""
+    rng = np.random.default_rng(20 + W)
+    cases = [rng.normal(0, 1, 20000), np.round(rng.normal(0, 1, 20000), 1), rng.normal(0, 1, 300)]
+    hot = rng.normal(0, 1, 20000)
+    hot[3::W] += 5.0                                    # shard 3 % W holds the whole top-k
+    cases.append(hot)
+    for c in cases:
+        s = c.astype(np.float32)
+        got, mask, nw = O.dcp_merge(s, 512, W)
+        assert np.array_equal(got, O.select_topk(s, 512))
+    assert mask & (1 << (3 % W)), "the shard holding the whole top-k must resend"
+    _, mask_rand, nw = O.dcp_merge(cases[0], 512, W)
+    assert nw == W * -(-3 * 512 // (2 * W))              # 32-bit words exchanged: W x ceil(1.5 k / W)
+
+
+def test_dcp_merge_resend_rule_by_hand():
+    """Two shards, k = 4, M = 3: shard 0 holds the four largest scores, so its weakest sent
+    word ties the threshold and it must resend; shard 1 does not."""
+    s = np.array([9, 1, 8, 2, 7, 3, 6, 0.5], dtype=np.float32)   # shard 0: 9 8 7 6, shard 1: 1 2 3 .5
+    got, mask, nw = O.dcp_merge(s, 4, 2)
+    assert np.array_equal(got, [0, 2, 4, 6]) and mask == 1 and nw == 6
