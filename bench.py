@@ -45,6 +45,9 @@ def parse():
                    help="index key format (the headline workload uses fp8)")
     p.add_argument("--block-size", type=int, default=BS)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--dcp", type=int, default=0, metavar="W",
+                   help="instead of the decode step, time the exact top-k merge of decode context parallelism "
+                        "emulated over W token-strided shards, beside the plain top-k, on the indexer's scores")
     p.add_argument("--cpu-layers", type=int, default=4, help="layer-steps the CPU oracle runs for cpu_baseline")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a 1 GiB device copy (for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -142,6 +145,78 @@ def timed_indexer_us(dsa, case, layers, max_ctx, reps):
     return 1000.0 * e0.elapsed_time(e1) / (reps * layers)
 
 
+def bench_dcp(a, dsa, case, dev):
+    """Times dsa_topk_dcp (W emulated shards) and dsa_topk on the same indexer scores,
+    one call per layer from a HIP graph; prints one JSON line."""
+    import torch
+    R, max_ctx, W = case.num_rows, case.max_ctx, a.dcp
+    ld = dsa.dsa_decode_scores_ld(max_ctx)
+    scores = torch.empty((a.layers, R, ld), dtype=torch.float32, device=dev)
+    for l in range(a.layers):
+        dsa.dsa_indexer_score(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l],
+                              case.block_table, case.row_seq, case.row_ctx, max_ctx, scores[l], ld_scores=ld)
+    idx = torch.empty((R, K), dtype=torch.int32, device=dev)
+    mask = torch.empty((R,), dtype=torch.int32, device=dev)
+    wsd = torch.empty(dsa.load_library().dsa_topk_dcp_workspace_bytes(R, max_ctx, K, W), dtype=torch.uint8, device=dev)
+    wst = torch.empty(max(dsa.dsa_workspace_bytes(dsa.DSA_OP_TOPK, R, max_ctx, K), 256), dtype=torch.uint8, device=dev)
+
+    def merge(l):
+        dsa.dsa_topk_dcp(scores[l], case.row_ctx, max_ctx, K, W, idx=idx, resend_mask=mask, workspace=wsd,
+                         ld_scores=ld)
+
+    def plain(l):
+        dsa.dsa_topk(scores[l], case.row_ctx, max_ctx, K, idx=idx, workspace=wst, ld_scores=ld)
+
+    def timed(fn):
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cap):
+            for l in range(a.layers):
+                fn(l)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for l in range(a.layers):
+                fn(l)
+        reps = max(1, a.steps // a.layers)
+        for _ in range(max(1, a.warmup // a.layers)):
+            g.replay()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / (reps * a.layers), reps * a.layers
+
+    us_dcp, n = timed(merge)
+    us_plain, _ = timed(plain)
+    resend = [int(m) & 0xFFFFFFFF for m in mask.tolist()]
+    print(json.dumps({
+        "metric": "exact top-k merge over emulated context-parallel shards",
+        "value": round(1e6 / us_dcp, 1),
+        "unit": "merges/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": a.warmup,
+        "ms_per_step": round(us_dcp / 1000.0, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"top-{K} of batch {R} rows of {a.ctx} indexer scores, {W} token-strided shards "
+                               f"each sending ceil(1.5 k / W) BF16-keyed words, {a.layers} layers rotated",
+                   "batch": R, "ctx": a.ctx, "k": K, "shards": W, "layers_rotated": a.layers,
+                   "launch": "HIP graph replay, one merge per layer"},
+        "plain_topk_us": round(us_plain, 3),
+        "merge_us": round(us_dcp, 3),
+        "resend_mask_last_layer": resend,
+    }), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -170,6 +245,8 @@ def main():
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     R, max_ctx = case.num_rows, case.max_ctx
+    if a.dcp:
+        return bench_dcp(a, dsa, case, dev)
     ws = torch.empty(dsa.dsa_workspace_bytes(dsa.DSA_OP_DECODE_STEP, R, max_ctx, K), dtype=torch.uint8, device=dev)
     idx = torch.empty((R, K), dtype=torch.int32, device=dev)
     out = torch.empty((R, 96, 512), dtype=torch.float32, device=dev)

@@ -230,6 +230,39 @@ dsa_status dsa_cache_append(const dsa_cache_desc* cache, int32_t layer,
                             const float* idx_key, const float* latent,
                             int32_t R, void* stream);
 
+/*
+ * Exact top-k merge of decode context parallelism, emulated on one GPU (page 1,
+ * long-context section on decode context parallelism with the sparse indexer: W
+ * GPUs each hold every W-th token; sub-section on the exact top-k merge with ten
+ * times less traffic: each sends its best ceil(1.5 k / W) candidates as 32-bit
+ * words built from BF16 scores, all radix-select the same global top-k from the
+ * gathered words, and a GPU holding more of the top-k than it sent resends its
+ * full local top-k). Shard s of each row holds tokens t = s (mod W); each shard
+ * ranks its own tokens, and the merge runs as the pages describe:
+ *   word     (key << 16) | j for slot j of the shard's list (its tokens in
+ *            ascending order), key = the score rounded to the nearest BF16 value
+ *            (ties to even) as an order-preserving 16-bit key (b | 0x8000 for a
+ *            non-negative bit pattern b, ~b & 0xFFFF for a negative one; -0 as +0)
+ *   T        key of the k-th largest word (0 if fewer than k words were sent)
+ *   resend   shard s resends iff it holds more tokens than it sent, sent at least
+ *            one, and its smallest sent key is >= T
+ *   result   exact fp32 top-k over the sent candidates with key >= T of the other
+ *            shards and the full local top-k of the resending ones.
+ * The result equals dsa_topk's on the same scores (the merge is exact).
+ *   scores, ld_scores, row_ctx, R, max_ctx, k  as for dsa_topk; R * W <= 65535
+ *   W            shards, 2 .. 32
+ *   idx          int32 [R][k] output, as dsa_topk
+ *   resend_mask  uint32 [R] output (nullable): bit s set when shard s resent
+ *   words        uint32 [R][W * M] output (nullable), M = ceil(1.5 k / W): the word
+ *                shard s sent at slot j at s * M + j, 0xFFFFFFFF where it sent none
+ *   workspace >= dsa_topk_dcp_workspace_bytes(R, max_ctx, k, W), 16-byte aligned
+ */
+size_t dsa_topk_dcp_workspace_bytes(int32_t R, int32_t max_ctx, int32_t k, int32_t W);
+dsa_status dsa_topk_dcp(const float* scores, int64_t ld_scores, const int32_t* row_ctx,
+                        int32_t R, int32_t max_ctx, int32_t k, int32_t W, int32_t* idx,
+                        uint32_t* resend_mask, uint32_t* words,
+                        void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

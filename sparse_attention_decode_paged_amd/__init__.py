@@ -2,12 +2,14 @@
 
 The Python functions are a thin ctypes layer over libdsa.so (include/dsa.h):
 dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step (each decode-step and
-indexer call takes an optional rows_per_seq), and dsa_cache_append.
+indexer call takes an optional rows_per_seq), dsa_cache_append, and dsa_topk_dcp (the
+exact top-k merge of decode context parallelism, emulated over token-strided shards).
 """
 from .binding import (  # noqa: F401
     DSAError, CacheDesc, load_library, make_cache_desc, decode_scores_view, EXPORTED, LIB_PATH,
     dsa_abi_version, dsa_status_string, dsa_workspace_bytes, dsa_decode_scores_ld,
     dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step, dsa_cache_append,
+    dsa_topk_dcp, dcp_send_count,
     DSA_INDEX_FP8, DSA_INDEX_MXFP4, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP,
 )
 from . import accounting  # noqa: F401

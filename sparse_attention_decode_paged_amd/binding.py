@@ -25,7 +25,8 @@ H_IDX, D_IDX, H_Q, D_LAT, D_V = 32, 128, 96, 576, 512
 
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_last_error_detail", "dsa_workspace_bytes",
             "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step",
-            "dsa_indexer_score_multi", "dsa_decode_step_multi", "dsa_cache_append")
+            "dsa_indexer_score_multi", "dsa_decode_step_multi", "dsa_cache_append",
+            "dsa_topk_dcp_workspace_bytes", "dsa_topk_dcp")
 
 
 class DSAError(RuntimeError):
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH):
     L.dsa_decode_step_multi.restype = _i32
     L.dsa_decode_step_multi.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _f32, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.dsa_topk_dcp_workspace_bytes.restype = _sz
+    L.dsa_topk_dcp_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    L.dsa_topk_dcp.restype = _i32
+    L.dsa_topk_dcp.argtypes = [_vp, _i64, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     _lib = L
     return L
 
@@ -189,6 +194,37 @@ def dsa_topk(scores, row_ctx, max_ctx, k, idx=None, workspace=None, ld_scores=No
                     workspace.numel() * workspace.element_size(), _stream(scores.device))
     _check(st, "dsa_topk")
     return idx
+
+
+def dcp_send_count(k, W):
+    """Candidates each shard sends: ceil(1.5 k / W)."""
+    return -(-3 * int(k) // (2 * int(W)))
+
+
+def dsa_topk_dcp(scores, row_ctx, max_ctx, k, W, idx=None, resend_mask=None, words=None, workspace=None,
+                 ld_scores=None, with_words=False):
+    """Exact top-k through the emulated context-parallel merge over W token-strided shards.
+    Returns (idx int32 [R][k], resend_mask int32 [R] (uint32 bits), words int32 [R][W*M] or None)."""
+    L = load_library()
+    R = row_ctx.shape[0]
+    dev = scores.device
+    if ld_scores is None:
+        ld_scores = scores.shape[-1]
+    if idx is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    if resend_mask is None:
+        resend_mask = torch.empty((R,), dtype=torch.int32, device=dev)
+    if words is None and with_words:
+        words = torch.empty((R, W * dcp_send_count(k, W)), dtype=torch.int32, device=dev)
+    need = L.dsa_topk_dcp_workspace_bytes(R, int(max_ctx), int(k), int(W))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = L.dsa_topk_dcp(_dev(scores, "scores", torch.float32), int(ld_scores), _dev(row_ctx, "row_ctx", torch.int32),
+                        R, int(max_ctx), int(k), int(W), _dev(idx, "idx", torch.int32),
+                        _dev(resend_mask, "resend_mask", torch.int32), _dev(words, "words", torch.int32),
+                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "dsa_topk_dcp")
+    return idx, resend_mask, words
 
 
 def dsa_sparse_mla(pool, layout, layer, q_lat, block_table, row_seq, idx, k, sm_scale, out=None, lse=None,

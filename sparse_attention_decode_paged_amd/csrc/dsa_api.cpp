@@ -300,4 +300,28 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const voi
                                max_ctx, k, 1, sm_scale, idx, out, lse, workspace, ws_bytes, stream);
 }
 
+size_t dsa_topk_dcp_workspace_bytes(int32_t R, int32_t max_ctx, int32_t k, int32_t W) {
+  if (R < 0 || max_ctx < 0 || max_ctx > kMaxCtx || k < 1 || k > DSA_MAX_K || W < 2 || W > kDcpShardMax) return 0;
+  return dcp_ws_bytes(R, max_ctx, k, W);
+}
+
+dsa_status dsa_topk_dcp(const float* scores, int64_t ld_scores, const int32_t* row_ctx, int32_t R, int32_t max_ctx,
+                        int32_t k, int32_t W, int32_t* idx, uint32_t* resend_mask, uint32_t* words, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (scores == nullptr || row_ctx == nullptr || idx == nullptr) return fail(DSA_ERR_NULL, "scores / row_ctx / idx is NULL");
+  if (W < 2 || W > kDcpShardMax) return fail(DSA_ERR_ARG, "W %d out of [2, %d]", W, kDcpShardMax);
+  if (R < 0 || (int64_t)R * W > 65535) return fail(DSA_ERR_ARG, "R %d x W %d out of [0, 65535]", R, W);
+  if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
+  if (max_ctx < 0 || max_ctx > kMaxCtx) return fail(DSA_ERR_ARG, "max_ctx %d out of [0, %d]", max_ctx, kMaxCtx);
+  if (ld_scores < max_ctx) return fail(DSA_ERR_ARG, "ld_scores %lld < max_ctx %d", (long long)ld_scores, max_ctx);
+  const size_t need = dcp_ws_bytes(R, max_ctx, k, W);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(workspace)) return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (R == 0) return ok();
+  return hip_status(launch_topk_dcp(scores, ld_scores, row_ctx, R, max_ctx, k, W, idx, resend_mask, words, workspace,
+                                    static_cast<hipStream_t>(stream)),
+                    "topk_dcp");
+}
+
 }  // extern "C"

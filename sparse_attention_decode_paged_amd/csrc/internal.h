@@ -68,6 +68,55 @@ inline size_t mla_ws_bytes(int R, int k) {
   return align_up((size_t)R * s * kHQ * kDV * 4, 256) + align_up((size_t)R * s * kHQ * 2 * 4, 256);
 }
 
+// ---- context-parallel merge emulation workspace -------------------------------------
+constexpr int kDcpShardMax = 32;                       // shards (bits of the resend mask)
+constexpr int kDcpWordCap = 3 * kMaxK / 2 + kDcpShardMax;  // W * ceil(1.5 k / W) < 1.5 k + W
+
+inline int dcp_send_count(int k, int W) { return (3 * k + 2 * W - 1) / (2 * W); }  // ceil(1.5 k / W)
+inline int dcp_shard_len(int max_ctx, int W) { return (max_ctx + W - 1) / W; }
+inline int64_t dcp_shard_ld(int max_ctx, int W) {
+  const int l = dcp_shard_len(max_ctx, W);
+  return (int64_t)align_up((size_t)(l > 0 ? l : 1), 64);
+}
+
+struct DcpWs {
+  float* shard;        // [R W][ls] scores dealt out token-strided
+  int64_t ls;
+  int32_t* shard_ctx;  // [R W]
+  int32_t* idx_m;      // [R W][M] best-M lists (shard-local places)
+  int32_t* idx_k;      // [R W][k] best-k lists
+  uint64_t* ukeys;     // [R][ucap] received candidates (composite keys)
+  int64_t ucap;
+  TopkWs tw;           // two-stage select over the shard rows
+};
+
+inline size_t dcp_ws_bytes(int R, int max_ctx, int k, int W) {
+  const size_t RW = (size_t)R * W, M = (size_t)dcp_send_count(k, W);
+  const size_t ucap = (size_t)W * M + (size_t)W * k;
+  return align_up(RW * dcp_shard_ld(max_ctx, W) * 4, 256) + align_up(RW * 4, 256) + align_up(RW * M * 4, 256) +
+         align_up(RW * k * 4, 256) + align_up((size_t)R * ucap * 8, 256) + topk_ws_bytes((int)RW, dcp_shard_len(max_ctx, W));
+}
+
+inline DcpWs dcp_ws_carve(void* ws, int R, int max_ctx, int k, int W) {
+  DcpWs d;
+  const size_t RW = (size_t)R * W, M = (size_t)dcp_send_count(k, W);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  d.ls = dcp_shard_ld(max_ctx, W);
+  d.ucap = (int64_t)(W * M + (size_t)W * k);
+  d.shard = reinterpret_cast<float*>(p);
+  p += align_up(RW * d.ls * 4, 256);
+  d.shard_ctx = reinterpret_cast<int32_t*>(p);
+  p += align_up(RW * 4, 256);
+  d.idx_m = reinterpret_cast<int32_t*>(p);
+  p += align_up(RW * M * 4, 256);
+  d.idx_k = reinterpret_cast<int32_t*>(p);
+  p += align_up(RW * k * 4, 256);
+  d.ukeys = reinterpret_cast<uint64_t*>(p);
+  p += align_up((size_t)R * d.ucap * 8, 256);
+  d.tw = topk_ws_carve(p, (int)RW, dcp_shard_len(max_ctx, W));
+  return d;
+}
+
 // ---- launches -------------------------------------------------------------------------
 // Indexer; when `ws` is non-null the epilogue also sends each block's top-k candidates.
 hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const float* q_scale,
@@ -106,5 +155,10 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* ro
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
                              const int32_t* phys, const float* pscale, int R, int k, float sm_scale, float* out,
                              float* lse, void* ws, hipStream_t stream);
+
+// Exact top-k merge of decode context parallelism over W token-strided shards, emulated
+// on one GPU (ws: dcp_ws_bytes). resend_mask / words may be null.
+hipError_t launch_topk_dcp(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k, int W,
+                           int32_t* idx, uint32_t* resend_mask, uint32_t* words, void* ws, hipStream_t stream);
 
 }  // namespace dsa

@@ -142,6 +142,26 @@ def test_multi_and_append_reject_bad_arguments(lib):
     assert lib.dsa_cache_append(ctypes.byref(d), 5, FAKE, 128, FAKE, FAKE, FAKE, None, 1, None) != 0   # no layer 5
 
 
+def test_dcp_merge_rejects_bad_arguments(lib):
+    ws = lib.dsa_topk_dcp_workspace_bytes(2, 40000, 2048, 4)
+    assert ws > 0
+    assert lib.dsa_topk_dcp_workspace_bytes(2, 40000, 2048, 1) == 0     # one shard is no split
+    assert lib.dsa_topk_dcp_workspace_bytes(2, 40000, 2048, 33) == 0    # mask holds 32 shards
+    assert lib.dsa_topk_dcp_workspace_bytes(2, 40000, 0, 4) == 0
+    # grows with the shards' candidate lists and with the context
+    assert lib.dsa_topk_dcp_workspace_bytes(2, 80000, 2048, 4) > ws
+    call = lambda R, mc, k, W, w=ws, p=FAKE: lib.dsa_topk_dcp(p, 40000, FAKE, R, mc, k, W, FAKE, None, None, FAKE, w, None)
+    assert call(2, 40000, 2048, 1) == 2
+    assert call(2, 40000, 2048, 33) == 2
+    assert call(20000, 40000, 2048, 4) == 2        # R * W above 65535
+    assert call(2, 40000, 0, 4) == 2
+    assert call(2, 40000, 2049, 4) == 2
+    assert call(2, 50000, 2048, 4) == 2            # ld 40000 < max_ctx
+    assert call(2, 40000, 2048, 4, w=ws - 1) == 4
+    assert call(2, 40000, 2048, 4, p=None) == 1
+    assert call(0, 40000, 2048, 4, w=lib.dsa_topk_dcp_workspace_bytes(0, 40000, 2048, 4)) == 0  # nothing to do
+
+
 def test_binding_refuses_cpu_tensors(lib):
     import torch
     pool = torch.zeros((4, 45568), dtype=torch.uint8)

@@ -414,3 +414,83 @@ def test_append_then_decode(dev):
     scores, idx, out, lse = full_check(c, dev)
     for r in range(2):
         assert int(c.row_ctx[r]) - 1 < scores.shape[1]
+
+
+# ----------------------------------------------------------------------------- context-parallel merge
+
+def _dcp_check(dev, rows, k, W):
+    """rows: list of fp32 score arrays. Bit-exact against the oracle's merge (tokens,
+    resend mask, the words themselves) and against the plain top-k."""
+    R = len(rows)
+    ctx = [len(x) for x in rows]
+    max_ctx = max(ctx)
+    ld = max(max_ctx, 1)
+    S = np.zeros((R, ld), dtype=np.float32)
+    for r, x in enumerate(rows):
+        S[r, :len(x)] = x
+    st = torch.from_numpy(S).to(dev)
+    rc = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    idx, mask, words = dsa.dsa_topk_dcp(st, rc, max_ctx, k, W, with_words=True)
+    plain = dsa.dsa_topk(st, rc, max_ctx, k)
+    torch.cuda.synchronize()
+    idx, plain = idx.cpu().numpy(), plain.cpu().numpy()
+    mask = mask.cpu().numpy().view(np.uint32)
+    words = words.cpu().numpy().view(np.uint32)
+    M = dsa.dcp_send_count(k, W)
+    masks = []
+    for r, x in enumerate(rows):
+        tok, omask, nw = O.dcp_merge(x, k, W)
+        total = min(k, len(x))
+        assert np.array_equal(tok, O.select_topk(x, k)), "oracle merge is not the plain top-k"
+        assert np.array_equal(idx[r, :total], tok) and np.all(idx[r, total:] == -1), f"row {r}: selection"
+        assert np.array_equal(idx[r], plain[r]), f"row {r}: differs from dsa_topk"
+        assert int(mask[r]) == omask, f"row {r}: resend mask {int(mask[r]):#x} vs {omask:#x}"
+        assert int(np.count_nonzero(words[r] != 0xFFFFFFFF)) == nw, f"row {r}: words sent"
+        for s in range(W):
+            sh = np.arange(s, len(x), W)
+            g = sh[O.select_topk(x[sh], M)]
+            want = ((O.bf16_key(x[g]).astype(np.uint64) << 16) | np.arange(g.size, dtype=np.uint64)).astype(np.uint32)
+            got = words[r, s * M:(s + 1) * M]
+            assert np.array_equal(got[:g.size], want) and np.all(got[g.size:] == 0xFFFFFFFF), f"row {r} shard {s}"
+        masks.append(omask)
+    return masks
+
+
+@pytest.mark.parametrize("W", [2, 3, 8])
+def test_dcp_merge_ragged(dev, W):
+    """Ragged rows (shard rows above and below the whole-row select limit), rounded
+    scores with many ties, one shard holding the whole top-k, a short and an empty row."""
+    say(f"case: dcp merge ragged W={W}")
+    rng = np.random.default_rng(300 + W)
+    hot = rng.normal(0, 1, 36000)
+    hot[3 % W::W] += 5.0
+    rows = [rng.normal(0, 1, 40000), np.round(rng.normal(0, 1, 30000), 1), hot, rng.normal(0, 1, 1500),
+            np.zeros(0), rng.normal(0, 1, 5003)]
+    masks = _dcp_check(dev, [x.astype(np.float32) for x in rows], 2048, W)
+    assert masks[2] & (1 << (3 % W)), "the shard holding the whole top-k resends"
+
+
+def test_dcp_merge_constant_scores(dev):
+    """Every score equal: every shard's weakest word ties the threshold, all resend,
+    and the first k tokens win."""
+    say("case: dcp merge constant scores")
+    masks = _dcp_check(dev, [np.zeros(20000, np.float32), np.full(9000, -1.5, np.float32)], 2048, 4)
+    assert masks == [0xF, 0xF]
+
+
+@pytest.mark.parametrize("k", [1, 7, 100])
+def test_dcp_merge_small_k(dev, k):
+    say(f"case: dcp merge k={k}")
+    rng = np.random.default_rng(400 + k)
+    _dcp_check(dev, [rng.normal(0, 1, 9000).astype(np.float32), rng.normal(0, 1, 5).astype(np.float32)], k, 4)
+
+
+@pytest.mark.parametrize("W", [4, 8])
+def test_dcp_merge_indexer_scores_256k(dev, W):
+    """The indexer's own scores at the long-context shape (262,144 tokens, plus a
+    100,000-token row): the merge gives dsa_topk's selection bit for bit."""
+    say(f"case: dcp merge on indexer scores 256k W={W}")
+    c = make_case([262144, 100000], block_size=64, seed=61, device=dev)
+    scores, idx, _, _ = run_step(c, dev)
+    rows = [scores[0, :262144].copy(), scores[1, :100000].copy()]
+    _dcp_check(dev, rows, 2048, W)
