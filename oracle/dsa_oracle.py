@@ -85,13 +85,16 @@ def _f32_from_bytes(b: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 class Layout:
-    """Plain view of the row layout numbers: block_size, index_fmt, row_bytes,
-    lat_off[layer], idx_off[layer]. Accepts any object or dict carrying them."""
+    """Plain view of the row layout numbers: block_size, index_fmt, latent_fmt
+    ("fp8" when absent), row_bytes, lat_off[layer], idx_off[layer]. Accepts any
+    object or dict carrying them."""
 
     def __init__(self, src):
         get = (lambda k: src[k]) if isinstance(src, dict) else (lambda k: getattr(src, k))
+        has = (lambda k: k in src) if isinstance(src, dict) else (lambda k: hasattr(src, k))
         self.block_size = int(get("block_size"))
         self.index_fmt = str(get("index_fmt"))
+        self.latent_fmt = str(get("latent_fmt")) if has("latent_fmt") else "fp8"
         self.row_bytes = int(get("row_bytes"))
         self.lat_off = [int(v) for v in get("lat_off")]
         self.idx_off = [int(v) for v in get("idx_off")]
@@ -135,16 +138,50 @@ def mxfp4_decode(packed: np.ndarray, e8: np.ndarray) -> np.ndarray:
 
 
 def read_latents(pool: np.ndarray, lay: Layout, layer: int, bt_row, tokens) -> np.ndarray:
-    """Dequantised latents c_t [n, 576] (float64): code value times the token's fp32 scale."""
+    """Dequantised latents c_t [n, 576] (float64): the record's values times the
+    token's fp32 scale (FP8: 576 e4m3 codes; NVFP4: see nvfp4_latent_decode)."""
     pool = pool.reshape(-1, lay.row_bytes)
     tokens = np.asarray(tokens, dtype=np.int64)
     if tokens.size == 0:
         return np.zeros((0, D_LAT))
     blk, slot = token_pages(bt_row, tokens, lay.block_size)
     base = lay.lat_off[layer]
-    codes = pool[blk[:, None], base + slot[:, None] * D_LAT + np.arange(D_LAT)]
-    sc = _f32_from_bytes(pool[blk[:, None], base + lay.block_size * D_LAT + slot[:, None] * 4 + np.arange(4)])
-    return E4M3_TABLE[codes] * sc[:, None]
+    w = latent_record_bytes(lay.latent_fmt)
+    rec = pool[blk[:, None], base + slot[:, None] * w + np.arange(w)]
+    sc = _f32_from_bytes(pool[blk[:, None], base + lay.block_size * w + slot[:, None] * 4 + np.arange(4)])
+    vals = E4M3_TABLE[rec] if lay.latent_fmt == "fp8" else nvfp4_latent_decode(rec)
+    return vals * sc[:, None]
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 latent records (page 1, KV-cache section: a token's MLA latent takes 576
+# bytes in FP8 and 352 in NVFP4; FlashInfer's PrimsTS kernel reads NVFP4 latents).
+# The pages give only the width. Reading: the 512 value dims in NVFP4 -- e2m1
+# codes (element 2i in the low nibble of byte i, 256 B) with one e4m3 scale per 16
+# dims (32 B) -- and the last 64 dims as plain e4m3 codes (64 B): 256 + 32 + 64 =
+# 352 B. As for the FP8 latent, each token also has one fp32 scale (the format's
+# second-level scale, taken per token) in the page's scale array:
+#   dim d < 512:   s * E4M3(block_scale[d // 16]) * E2M1(code[d])
+#   dim d >= 512:  s * E4M3(tail[d - 512])
+# ---------------------------------------------------------------------------
+NV_BLOCK = 16
+NV_RECORD = D_V // 2 + D_V // NV_BLOCK + (D_LAT - D_V)   # 352
+
+
+def latent_record_bytes(latent_fmt: str) -> int:
+    """Bytes of one token's latent record before the page's fp32 scale array."""
+    return {"fp8": D_LAT, "nvfp4": NV_RECORD}[latent_fmt]
+
+
+def nvfp4_latent_decode(rec: np.ndarray) -> np.ndarray:
+    """[..., 352] NVFP4 latent records -> float64 [..., 576], before the token scale."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    packed = rec[..., :D_V // 2]
+    bsc = rec[..., D_V // 2:D_V // 2 + D_V // NV_BLOCK]
+    tail = rec[..., D_V // 2 + D_V // NV_BLOCK:]
+    nib = np.stack([packed & 0xF, packed >> 4], axis=-1).reshape(*packed.shape[:-1], D_V)
+    vals = E2M1_TABLE[nib] * np.repeat(E4M3_TABLE[bsc], NV_BLOCK, axis=-1)
+    return np.concatenate([vals, E4M3_TABLE[tail]], axis=-1)
 
 
 def index_query(q_codes: np.ndarray, q_scale: np.ndarray, index_fmt: str) -> np.ndarray:
@@ -343,6 +380,31 @@ def quantize_mxfp4_vector(x) -> tuple:
     return packed, e8
 
 
+def quantize_nvfp4_latent(x) -> tuple:
+    """(record uint8 [352], fp32 token scale) of one 576-dim latent, per the NVFP4
+    record reading above: s = amax / 448 (1 when amax = 0) and y = x / s clamped to
+    +-448, as for FP8; the tail dims are e4m3 codes of y; each 16-dim block of the
+    first 512 gets the e4m3 scale code nearest to max|y_block| / 6 (ties to even)
+    and e2m1 codes of y / that scale's value (all 0 when the value is 0)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0)
+    s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    y = np.clip((x / s).astype(np.float32), np.float32(-448.0), np.float32(448.0))
+    nib = np.zeros(D_V, dtype=np.uint8)
+    bsc = np.zeros(D_V // NV_BLOCK, dtype=np.uint8)
+    for b in range(D_V // NV_BLOCK):
+        blk = y[b * NV_BLOCK:(b + 1) * NV_BLOCK]
+        code = e4m3_encode(np.float32(np.max(np.abs(blk))) / np.float32(6.0))
+        bsc[b] = code
+        sv = np.float32(E4M3_TABLE[code])
+        if sv > 0:
+            for j, v in enumerate(blk):
+                nib[b * NV_BLOCK + j] = e2m1_encode(float(np.float32(v) / sv))
+    packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+    tail = np.array([e4m3_encode(v) for v in y[D_V:]], dtype=np.uint8)
+    return np.concatenate([packed, bsc, tail]), s
+
+
 def append_tokens(pool: np.ndarray, lay: Layout, layer: int, bt: np.ndarray, row_seq, pos,
                   idx_key=None, latent=None) -> np.ndarray:
     """A copy of ``pool`` with row r's quantised index key (fp32 [R][128]) and
@@ -361,10 +423,14 @@ def append_tokens(pool: np.ndarray, lay: Layout, layer: int, bt: np.ndarray, row
         if blk < 0 or blk >= nb:
             continue
         if latent is not None:
-            codes, sc = quantize_fp8_vector(latent[r])
+            if lay.latent_fmt == "fp8":
+                codes, sc = quantize_fp8_vector(latent[r])
+            else:
+                codes, sc = quantize_nvfp4_latent(latent[r])
+            w = codes.size
             o = lay.lat_off[layer]
-            out[blk, o + slot * D_LAT: o + (slot + 1) * D_LAT] = codes
-            out[blk, o + bs * D_LAT + 4 * slot: o + bs * D_LAT + 4 * slot + 4] = np.frombuffer(
+            out[blk, o + slot * w: o + (slot + 1) * w] = codes
+            out[blk, o + bs * w + 4 * slot: o + bs * w + 4 * slot + 4] = np.frombuffer(
                 np.float32(sc).tobytes(), dtype=np.uint8)
         if idx_key is not None:
             o = lay.idx_off[layer]

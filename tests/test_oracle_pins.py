@@ -449,3 +449,69 @@ def test_dcp_merge_resend_rule_by_hand():
     s = np.array([9, 1, 8, 2, 7, 3, 6, 0.5], dtype=np.float32)   # shard 0: 9 8 7 6, shard 1: 1 2 3 .5
     got, mask, nw = O.dcp_merge(s, 4, 2)
     assert np.array_equal(got, [0, 2, 4, 6]) and mask == 1 and nw == 6
+
+
+# ----------------------------------------------------------------------------- NVFP4 latents
+
+def test_nvfp4_latent_record_by_hand():
+    """The NVFP4 latent record (352 B: 256 B of e2m1 pairs, 32 e4m3 block scales, 64 e4m3
+    tail codes) decoded by hand from the format definitions."""
+    rec = np.zeros(352, np.uint8)
+    rec[0] = 0x3 | (0xA << 4)      # dims 0, 1: e2m1 1.5 and -1.0 (0xA: sign | exponent 1)
+    rec[255] = 0x70                # dims 510, 511: e2m1 0 and 6.0
+    rec[256] = 0x40                # block 0 (dims 0..15): e4m3 2.0
+    rec[256 + 31] = 0x30           # block 31 (dims 496..511): e4m3 0.5
+    rec[288] = 0x38                # dim 512: e4m3 1.0
+    rec[351] = 0xFE                # dim 575: e4m3 -448
+    v = O.nvfp4_latent_decode(rec)
+    want = np.zeros(576)
+    want[0], want[1], want[511], want[512], want[575] = 3.0, -2.0, 3.0, 1.0, -448.0
+    assert v.shape == (576,) and np.array_equal(v, want)
+    assert O.latent_record_bytes("nvfp4") == O.latent_bytes("nvfp4") == 352
+
+
+def test_nvfp4_latent_round_trip_of_representable_vectors():
+    """A vector that the format represents exactly (token scale 1: the largest value is a
+    448 tail code; each block's largest magnitude is 6 times its scale) comes back with the
+    same record."""
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        rec = np.zeros(352, np.uint8)
+        nib = rng.integers(0, 16, 512).astype(np.uint8)
+        nib[nib == 0x8] = 0                                  # no negative zero
+        for b in range(32):
+            nib[16 * b + rng.integers(0, 16)] = rng.choice([0x7, 0xF])   # |6| in every block
+        rec[:256] = nib[0::2] | (nib[1::2] << 4)
+        # block scales: positive normal e4m3 values up to 64 (6 * 64 < 448)
+        rec[256:288] = rng.integers(0x08, 0x58, 32)
+        tail = rng.integers(0, 0x7E, 64).astype(np.uint8) | (rng.integers(0, 2, 64).astype(np.uint8) << 7)
+        tail[tail == 0x80] = 0
+        tail[rng.integers(0, 64)] = 0x7E                     # 448: the token's largest value
+        rec[288:] = tail
+        x = O.nvfp4_latent_decode(rec).astype(np.float32)
+        got, s = O.quantize_nvfp4_latent(x)
+        assert s == np.float32(1.0) and np.array_equal(got, rec)
+
+
+def test_nvfp4_latent_quantiser_error_bound_and_scales():
+    """Random latents: every block scale is torch's own e4m3 cast of max|y| / 6, and each
+    dequantised dim lies within one block-scale step (NVFP4 dims) or half an e4m3 step
+    (tail dims) of the input."""
+    import torch
+    rng = np.random.default_rng(6)
+    for t in range(12):
+        x = (rng.normal(0, 1, 576) * (10.0 ** rng.uniform(-3, 3))).astype(np.float32)
+        if t == 0:
+            x[:32] = 0.0                                     # all-zero blocks: scale 0, codes 0
+        rec, s = O.quantize_nvfp4_latent(x)
+        y = np.clip(x / s, -448, 448).astype(np.float32)
+        bam = np.abs(y[:512]).reshape(32, 16).max(axis=1).astype(np.float32) / np.float32(6.0)
+        ref = torch.tensor(bam).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(rec[256:288], ref)
+        xh = O.nvfp4_latent_decode(rec) * float(s)
+        scv = np.repeat(O.E4M3_TABLE[rec[256:288]], 16)
+        err = np.abs(xh - x.astype(np.float64))
+        assert np.all(err[:512] <= float(s) * scv * 1.0 + 1e-30)
+        assert np.all(err[512:] <= float(s) * np.maximum(np.abs(y[512:]) / 16.0, 2.0 ** -10) * 1.0000001)
+        if t == 0:
+            assert np.all(rec[:16] == 0) and np.all(rec[256:258] == 0)
