@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--index-fmt", choices=["fp8", "mxfp4"], default="fp8",
                    help="index key format (the headline workload uses fp8)")
     p.add_argument("--block-size", type=int, default=BS)
+    p.add_argument("--latent-fmt", choices=["fp8", "nvfp4"], default="fp8",
+                   help="latent records: FP8 (576 B + scale) or NVFP4 (352 B + scale)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--dcp", type=int, default=0, metavar="W",
                    help="instead of the decode step, time the exact top-k merge of decode context parallelism "
@@ -95,7 +97,7 @@ def cpu_baseline(case, layers, k):
         lo = lay.lat_off[l]
         hi = lay.idx_off[l] + lay.index_page_bytes
         pool = case.pool[:, lo:hi].cpu().numpy()
-        sub = dict(block_size=lay.block_size, index_fmt=lay.index_fmt, row_bytes=hi - lo,
+        sub = dict(block_size=lay.block_size, index_fmt=lay.index_fmt, latent_fmt=lay.latent_fmt, row_bytes=hi - lo,
                    lat_off=[0], idx_off=[lay.idx_off[l] - lo])
         t0 = time.perf_counter()
         for r in range(R):
@@ -241,7 +243,8 @@ def main():
 
     t0 = time.time()
     case = make_case([a.ctx] * a.batch, block_size=a.block_size, num_layers=a.layers, seed=a.seed, device=dev, k=K,
-                     index_fmt=a.index_fmt, name="decode_b%d_ctx%d_x%dlayers" % (a.batch, a.ctx, a.layers))
+                     index_fmt=a.index_fmt, latent_fmt=a.latent_fmt,
+                     name="decode_b%d_ctx%d_x%dlayers" % (a.batch, a.ctx, a.layers))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     R, max_ctx = case.num_rows, case.max_ctx
@@ -300,12 +303,14 @@ def main():
     ix_us = timed_indexer_us(dsa, case, a.layers, max_ctx, max(2, min(a.steps, 480) // a.layers))
 
     ctxs = [int(c) for c in case.row_ctx.tolist()]
-    step_bytes = A.layer_step_bytes(ctxs, K, a.index_fmt)
+    step_bytes = A.layer_step_bytes(ctxs, K, a.index_fmt, a.latent_fmt)
     ix_bytes = sum(A.indexer_bytes(c, a.index_fmt) for c in ctxs)
     ix_gbps = ix_bytes / (ix_us * 1e-6) / 1e9
     step_gbps = step_bytes / (ms * 1e-3) / 1e9
     traffic = traffic_for(INDEXER_SRC) if a.index_fmt == "fp8" else None
     key_desc = "FP8 index keys (132 B/token)" if a.index_fmt == "fp8" else "MXFP4 index keys (68 B/token)"
+    lat_desc = ("FP8 latents (576 B + fp32 scale)" if a.latent_fmt == "fp8"
+                else "NVFP4 latents (352 B + fp32 scale)")
 
     res = {
         "metric": METRIC,
@@ -322,9 +327,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"DSA decode, batch {R}, context {a.ctx} tokens, top-{K}, block size {a.block_size}, {key_desc} "
-                        f"and FP8 latents (576 B + fp32 scale), {a.layers} independent layers rotated",
+                        f"and {lat_desc}, {a.layers} independent layers rotated",
             "batch": R, "ctx": a.ctx, "k": K, "block_size": a.block_size, "layers_rotated": a.layers,
-            "index_fmt": a.index_fmt,
+            "index_fmt": a.index_fmt, "latent_fmt": a.latent_fmt,
             "launch": "HIP graph replay, one decode step per layer",
         },
         "step_hbm_gbps": round(step_gbps, 1),

@@ -69,10 +69,21 @@ typedef int32_t dsa_status;
 #define DSA_INDEX_FP8 0    /* 128 e4m3 codes + fp32 scale per token */
 #define DSA_INDEX_MXFP4 1  /* 64 B packed e2m1 (element 2i = low nibble) + 4 E8M0 per token */
 
+/* Latent page formats (page 1, KV-cache section: a token's latent takes 576 B in
+ * FP8 and 352 B in NVFP4). Each token record is followed, after the page's
+ * block_size records, by one fp32 scale per token (the value scale s below). */
+#define DSA_LATENT_FP8 0    /* 576 e4m3 codes: c[d] = s * e4m3[d] */
+#define DSA_LATENT_NVFP4 1  /* 352 B: 256 B packed e2m1 for dims 0..511 (element 2i =
+                             * low nibble), 32 e4m3 block scales (one per 16 dims),
+                             * 64 e4m3 codes for dims 512..575:
+                             * c[d] = s * e4m3(bsc[d/16]) * e2m1[d], d < 512;
+                             * c[d] = s * e4m3(tail[d-512]), d >= 512 */
+
 /*
  * Packed cache descriptor (host struct; `pool` is a device pointer).
  * Block row b starts at pool + b * row_bytes. Inside a row, layer l holds
- *   latent page at lat_off[l]: block_size * 576 e4m3 codes (slot s at s*576),
+ *   latent page at lat_off[l]: block_size records of W bytes (slot s at s*W;
+ *                              W = 576 for DSA_LATENT_FP8, 352 for DSA_LATENT_NVFP4),
  *                              then block_size fp32 scales;
  *   index page  at idx_off[l]: FP8   block_size * 128 e4m3 codes, then block_size fp32 scales;
  *                              MXFP4 block_size * 64 packed bytes, then block_size * 4 E8M0.
@@ -87,7 +98,7 @@ typedef struct dsa_cache_desc {
   int32_t block_size;
   int32_t num_layers;
   int32_t index_fmt;
-  int32_t reserved;
+  int32_t latent_fmt;  /* DSA_LATENT_FP8 (0) or DSA_LATENT_NVFP4 (1) */
   int64_t lat_off[DSA_MAX_LAYERS];
   int64_t idx_off[DSA_MAX_LAYERS];
 } dsa_cache_desc;

@@ -10,6 +10,6 @@ from .binding import (  # noqa: F401
     dsa_abi_version, dsa_status_string, dsa_workspace_bytes, dsa_decode_scores_ld,
     dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step, dsa_cache_append,
     dsa_topk_dcp, dcp_send_count,
-    DSA_INDEX_FP8, DSA_INDEX_MXFP4, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP,
+    DSA_INDEX_FP8, DSA_INDEX_MXFP4, DSA_LATENT_FP8, DSA_LATENT_NVFP4, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP,
 )
 from . import accounting  # noqa: F401

@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_INDEX_FP8 = 0
 DSA_INDEX_MXFP4 = 1
+DSA_LATENT_FP8 = 0
+DSA_LATENT_NVFP4 = 1
 DSA_OP_TOPK = 1
 DSA_OP_SPARSE_MLA = 2
 DSA_OP_DECODE_STEP = 3
@@ -43,7 +45,7 @@ class CacheDesc(ctypes.Structure):
         ("block_size", ctypes.c_int32),
         ("num_layers", ctypes.c_int32),
         ("index_fmt", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("latent_fmt", ctypes.c_int32),
         ("lat_off", ctypes.c_int64 * DSA_MAX_LAYERS),
         ("idx_off", ctypes.c_int64 * DSA_MAX_LAYERS),
     ]
@@ -121,8 +123,10 @@ def _stream(device) -> int:
 
 def make_cache_desc(pool: torch.Tensor, layout) -> CacheDesc:
     """Descriptor for a pool tensor uint8 [num_blocks, row_bytes] and a layout object
-    or dict with block_size, num_layers, index_fmt ('fp8'|'mxfp4'), row_bytes, lat_off, idx_off."""
+    or dict with block_size, num_layers, index_fmt ('fp8'|'mxfp4'), latent_fmt
+    ('fp8'|'nvfp4', default 'fp8'), row_bytes, lat_off, idx_off."""
     get = (lambda k: layout[k]) if isinstance(layout, dict) else (lambda k: getattr(layout, k))
+    has = (lambda k: k in layout) if isinstance(layout, dict) else (lambda k: hasattr(layout, k))
     d = CacheDesc()
     d.pool = _dev(pool, "pool", torch.uint8)
     d.row_bytes = int(get("row_bytes"))
@@ -131,6 +135,8 @@ def make_cache_desc(pool: torch.Tensor, layout) -> CacheDesc:
     d.num_layers = int(get("num_layers"))
     fmt = get("index_fmt")
     d.index_fmt = {"fp8": DSA_INDEX_FP8, "mxfp4": DSA_INDEX_MXFP4}.get(fmt, fmt if isinstance(fmt, int) else -1)
+    lf = get("latent_fmt") if has("latent_fmt") else "fp8"
+    d.latent_fmt = {"fp8": DSA_LATENT_FP8, "nvfp4": DSA_LATENT_NVFP4}.get(lf, lf if isinstance(lf, int) else -1)
     for i, v in enumerate(get("lat_off")):
         d.lat_off[i] = int(v)
     for i, v in enumerate(get("idx_off")):

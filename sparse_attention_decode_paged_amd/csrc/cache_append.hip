@@ -12,6 +12,10 @@
 //   MXFP4 per 32 elements E = floor(log2 amax) - 2, clamped to [-127, 127] (0 when
 //         amax = 0), stored as E + 127; y = x * 2^-E rounded to the nearest e2m1
 //         magnitude with ties to the even code, 6 at most; no negative zero.
+//   NVFP4 latent (352 B record: page 1 quotes the width only): s and y as for FP8;
+//         dims 512..575 as e4m3 codes of y; each 16-dim block of the first 512 gets
+//         the e4m3 code nearest to max|y_block| / 6 as its scale, and e2m1 codes of
+//         y / (that scale's value), all 0 when the value is 0.
 // One wave per row: 9 latent and 2 key values per lane, coalesced, byte stores.
 #include "dsa.h"
 #include "common.h"
@@ -78,6 +82,37 @@ __device__ __forceinline__ void put_fp8(uint8_t* codes, uint8_t* scale_at, const
   }
   if (lane == 0) *reinterpret_cast<float*>(scale_at) = scale;
 }
+
+// NVFP4 latent record (element lane + 64 i of the 576-vector on this lane) and its scale.
+__device__ __forceinline__ void put_nvfp4_latent(uint8_t* rec, uint8_t* scale_at, const float* x, int lane) {
+  float v[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) v[i] = x[lane + 64 * i];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max_f(amax);
+  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) v[i] = fminf(fmaxf(__fdiv_rn(v[i], scale), -448.f), 448.f);
+  rec[kDV / 2 + kDV / 16 + lane] = (uint8_t)e4m3_rne(v[8]);  // tail dim 512 + lane
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // block 4 i + lane / 16 = lanes 16 (lane / 16) .. + 15 of element row i
+    float bm = fabsf(v[i]);
+    bm = fmaxf(bm, xshflf<1>(bm));
+    bm = fmaxf(bm, xshflf<2>(bm));
+    bm = fmaxf(bm, xshflf<4>(bm));
+    bm = fmaxf(bm, xshflf<8>(bm));
+    const uint32_t sc = e4m3_rne(__fdiv_rn(bm, 6.f));
+    const float scv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc, 1.0f, false)[0];
+    const uint32_t nib = scv > 0.f ? e2m1_rne(__fdiv_rn(v[i], scv)) : 0u;
+    const uint32_t hi = (uint32_t)__shfl_xor((int)nib, 1, 64);
+    if ((lane & 1) == 0) rec[32 * i + (lane >> 1)] = (uint8_t)(nib | (hi << 4));
+    if ((lane & 15) == 0) rec[kDV / 2 + 4 * i + (lane >> 4)] = (uint8_t)sc;
+  }
+  if (lane == 0) *reinterpret_cast<float*>(scale_at) = scale;
+}
 }  // namespace
 
 __global__ __launch_bounds__(256) void cache_append_kernel(CacheView cv, int32_t index_fmt,
@@ -98,8 +133,12 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheView cv, int32_t
 
   if (latent != nullptr) {
     uint8_t* page = row + cv.lat_off;
-    put_fp8<kDLat>(page + (int64_t)slot * kDLat, page + (int64_t)cv.block_size * kDLat + 4 * slot,
-                   latent + (int64_t)r * kDLat, lane);
+    if (cv.latent_fmt == DSA_LATENT_NVFP4)
+      put_nvfp4_latent(page + (int64_t)slot * kNvRec, page + (int64_t)cv.block_size * kNvRec + 4 * slot,
+                       latent + (int64_t)r * kDLat, lane);
+    else
+      put_fp8<kDLat>(page + (int64_t)slot * kDLat, page + (int64_t)cv.block_size * kDLat + 4 * slot,
+                     latent + (int64_t)r * kDLat, lane);
   }
   if (idx_key == nullptr) return;
   uint8_t* page = row + cv.idx_off;

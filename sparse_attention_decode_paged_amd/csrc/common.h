@@ -12,6 +12,7 @@ constexpr int kHQ = 96;      // latent-query heads
 constexpr int kDLat = 576;   // latent width
 constexpr int kDV = 512;     // value width
 constexpr int kMaxK = 2048;
+constexpr int kNvRec = 352;  // NVFP4 latent record: 256 B e2m1 + 32 e4m3 block scales + 64 e4m3 tail
 constexpr int kWave = 64;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -31,6 +32,7 @@ struct CacheView {
   int64_t idx_off;     // index page offset inside a row
   int32_t block_size;  // power of two
   int32_t log2_bs;
+  int32_t latent_fmt;  // DSA_LATENT_FP8 / DSA_LATENT_NVFP4
 };
 
 // Query-row to cache mapping.

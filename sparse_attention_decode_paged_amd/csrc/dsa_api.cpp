@@ -52,8 +52,10 @@ dsa_status check_cache(const dsa_cache_desc* c, int32_t layer, CacheView* cv) {
   if (!aligned16(c->pool)) return fail(DSA_ERR_ALIGN, "pool is not 16-byte aligned");
   if (c->index_fmt != DSA_INDEX_FP8 && c->index_fmt != DSA_INDEX_MXFP4)
     return fail(DSA_ERR_UNSUPPORTED, "index_fmt %d", c->index_fmt);
+  if (c->latent_fmt != DSA_LATENT_FP8 && c->latent_fmt != DSA_LATENT_NVFP4)
+    return fail(DSA_ERR_UNSUPPORTED, "latent_fmt %d", c->latent_fmt);
   const int64_t bs = c->block_size;
-  const int64_t lat_page = bs * (DSA_D_LAT + 4);
+  const int64_t lat_page = bs * ((c->latent_fmt == DSA_LATENT_FP8 ? DSA_D_LAT : kNvRec) + 4);
   const int64_t idx_page = c->index_fmt == DSA_INDEX_FP8 ? bs * (DSA_D_IDX + 4) : bs * (DSA_D_IDX / 2 + 4);
   for (int l = 0; l < c->num_layers; ++l) {
     if (c->lat_off[l] < 0 || (c->lat_off[l] & 15) || c->lat_off[l] + lat_page > c->row_bytes)
@@ -72,6 +74,7 @@ dsa_status check_cache(const dsa_cache_desc* c, int32_t layer, CacheView* cv) {
   cv->idx_off = c->idx_off[layer];
   cv->block_size = c->block_size;
   cv->log2_bs = ilog2(c->block_size);
+  cv->latent_fmt = c->latent_fmt;
   return DSA_OK;
 }
 

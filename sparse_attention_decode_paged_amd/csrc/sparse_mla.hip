@@ -28,6 +28,23 @@
 // logit and folded into P'. With one split the workgroup writes out / lse; with
 // several it writes unnormalised partials (O, m, l) that the merge kernel
 // combines by log-sum-exp.
+//
+// NVFP4 latents (page 1, KV-cache section: 352 B per token; the record holds the 512
+// value dims as e2m1 codes with one e4m3 scale per 16 dims and the last 64 dims as
+// e4m3 codes). The gather dequantises each record to fp16 on its way to LDS: the
+// e2m1 pair conversion applies the power-of-two part of the block scale, one packed
+// fp16 multiply its 4-bit significand; e2m1 times an e4m3 scale has at most 6
+// significant bits and stays inside fp16's normal range, so the tile is exact. QK
+// then runs on fp16 MFMAs too: each head's query is scaled by a power of two that
+// puts its largest element in [2^14, 2^15) and rounded to fp16, exact for every
+// element within 2^28 of that largest one (8-bit bf16 significands fit fp16's 11);
+// the power of two returns in the logit. (Values below 2^-14 of the head's largest after
+// the scaling would be fp16 subnormals; the pkrtz conversion truncates those, an error
+// under 2^-38 of the largest element.) P . V reads 16-bit columns of the tile with
+// the transposing LDS read (ds_read_b64_tr_b16). The tile's 16-byte chunks are
+// XOR-swizzled within each token row (nv_col) so that the gather's writes do not
+// collide in the LDS banks.
+#include "dsa.h"
 #include "common.h"
 #include "internal.h"
 
@@ -40,19 +57,50 @@ constexpr int NTM = 512;  // attention workgroup: 8 waves, two per SIMD
 constexpr int NWM = NTM / 64;
 constexpr int CH = kMlaChunk;           // 64 tokens per iteration
 constexpr int PIECES = kDLat / 16;      // 36 16-byte pieces per latent
-constexpr int LROW = kDLat + 16;        // LDS row strides padded by 16 bytes so that the
-constexpr int QROW = kDLat + 8;         // 16 rows an MFMA fragment reads fall in distinct banks
-constexpr int LAT_LDS = CH * LROW;      // the latent tile; Q passes through the same bytes first
-static_assert(kMlaGroup * QROW * 2 <= LAT_LDS, "Q staging fits the latent tile");
+constexpr int QROW = kDLat + 8;         // Q staging row (bf16 elements), padded like the tiles
+// LDS row of one token in the latent tile: FP8 codes (576 B) or, for NVFP4 records,
+// dequantised fp16 (1,152 B); both padded by 16 B so that the 16 rows an MFMA fragment
+// reads fall in distinct banks.
+template <bool NV>
+struct Tile {
+  static constexpr int ROW = NV ? 2 * kDLat + 16 : kDLat + 16;
+  static constexpr int BYTES = CH * ROW;  // Q passes through the same bytes first
+  static_assert(kMlaGroup * QROW * 2 <= BYTES, "Q staging fits the latent tile");
+};
 constexpr int XROW = CH + 16;           // logit rows: the four 16-lane groups of a store hit distinct banks
 constexpr float kNegInf = -__builtin_huge_valf();
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-  __bf16 b = (__bf16)f;
-  return __builtin_bit_cast(uint16_t, b);
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Eight e2m1 codes (nibbles of d, element 2i in the low nibble of byte i) times a block
+// scale p * m -> fp16, exact: the conversion applies the power of two p (it uses only
+// the exponent of its scale operand), the packed multiply the significand m (m2 = {m, m};
+// m = 0 for a zero scale).
+__device__ __forceinline__ v8h e2m1x8_scaled_f16(uint32_t d, float p, v2h m2) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p, 0) * m2;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p, 1) * m2;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p, 2) * m2;
+  const v2h e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p, 3) * m2;
+  v8h o;
+  o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+  o[4] = c[0]; o[5] = c[1]; o[6] = e[0]; o[7] = e[1];
+  return o;
 }
+
+// NVFP4 tile: byte offset of fp16 column `col` (a multiple of 4) in a token row. The
+// 16-byte chunk index is XORed with its bits 3..5, so that the eight gather threads of
+// a token, which write chunks 8 q8 + j for the same j, hit eight different bank groups;
+// chunks 64.. (the tail dims) stay in place.
+__device__ __forceinline__ int nv_col(int col) {
+  const int c = col >> 3;
+  return 16 * (c ^ ((c >> 3) & 7)) + 2 * (col & 7);
+}
+
 }  // namespace
 
+template <bool NV>
 __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm, const uint16_t* __restrict__ q_lat,
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ phys, int k, int ts, float c2,
@@ -63,17 +111,22 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 5;  // half of the wave
 
-  __shared__ __attribute__((aligned(16))) uint8_t lat_s[LAT_LDS];
+  constexpr int LROW = Tile<NV>::ROW;
+  __shared__ __attribute__((aligned(16))) uint8_t lat_s[Tile<NV>::BYTES];
   __shared__ __attribute__((aligned(16))) float x_s[kMlaGroup * XROW];  // scaled logits, head-major
   __shared__ __attribute__((aligned(16))) float sc_s[CH];
   __shared__ __attribute__((aligned(16))) float hv_s[NWM][kMlaGroup];  // per-wave exchange of per-head values
+  __shared__ float qe_s[kMlaGroup];  // NVFP4: the power of two each head's fp16 query was scaled down by
 
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
   const int j1 = (j0 + ts < k) ? j0 + ts : k;
   const int seq = rm.row_seq[r];
   const int bs_mask = cv.block_size - 1;
-  const int tt_g = tid >> 3, q8 = tid & 7;  // gather: 8 threads per token, pieces q8 + 8 q (q < 5) of 36
+  // gather: 8 threads per token. FP8: 16-byte pieces q8 + 8 q (q < 5) of 36. NVFP4: code
+  // bytes [32 q8, +32) (dims [64 q8, +64)), their 4 block scales and, for q8 < 4, tail
+  // bytes [16 q8, +16) (dims 512 + 16 q8 ..)
+  const int tt_g = tid >> 3, q8 = tid & 7;
 
   // token id and page slot of this thread's gather token: the head of the load chain,
   // issued before anything else
@@ -104,6 +157,7 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm
       if (tid + NTM * q < QALL) qv[q] = qg[tid + NTM * q];
   }
   v8bf qa[KQ];
+  v8h qh[KQ];  // NVFP4: the same fragments in fp16, scaled by a power of two per head
 
   // running softmax state of head (lane & 31); every wave keeps an identical copy
   float m_run = kNegInf, l_run = 0.f;
@@ -117,6 +171,7 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm
   // while chunk c is computed, and the ids of chunk c + 2 behind them ----
   constexpr int PN = (PIECES + 7) / 8;  // 5 pieces per thread, the last on q8 < 4
   v4i v[PN];
+  uint32_t nbs = 0;  // NVFP4: the four block-scale codes of this thread's dims
   float sv = 0.f;
   bool tv = false;  // the gathered slot holds a token
   auto issue = [&]() {
@@ -134,11 +189,20 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm
       slot = tc & bs_mask;
     }
     const uint8_t* page = cv.pool + blk * cv.row_bytes + cv.lat_off;
-    const uint8_t* lrow = page + (int64_t)slot * kDLat;
-    if (q8 == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
+    if constexpr (NV) {
+      const uint8_t* rec = page + (int64_t)slot * kNvRec;
+      if (q8 == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kNvRec + (int64_t)slot * 4);
+      v[0] = *reinterpret_cast<const v4i*>(rec + 32 * q8);
+      v[1] = *reinterpret_cast<const v4i*>(rec + 32 * q8 + 16);
+      nbs = *reinterpret_cast<const uint32_t*>(rec + kDV / 2 + 4 * q8);
+      if (q8 < 4) v[2] = *reinterpret_cast<const v4i*>(rec + kDV / 2 + kDV / 16 + 16 * q8);
+    } else {
+      const uint8_t* lrow = page + (int64_t)slot * kDLat;
+      if (q8 == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
 #pragma unroll
-    for (int q = 0; q < PN; ++q)
-      if (q8 + 8 * q < PIECES) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (q8 + 8 * q));
+      for (int q = 0; q < PN; ++q)
+        if (q8 + 8 * q < PIECES) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (q8 + 8 * q));
+    }
     tv = t >= 0;
   };
   auto fetch_ids = [&](int c0) {
@@ -159,18 +223,87 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm
       if (i < QALL) *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
     }
     __syncthreads();
-    const uint16_t* qrow = q_s + (16 * hh + hrow) * QROW + kq;
+    if constexpr (NV) {
+      // 16 threads per head (one wave holds 4 heads): each takes 36 consecutive dims of
+      // its head row, the 16 agree on the head's largest magnitude, and each rewrites
+      // its 36 values in place as fp16 scaled by the head's power of two
+      const int h = tid >> 4, part = tid & 15;
+      uint16_t* qp = q_s + h * QROW + 36 * part;
+      uint2 raw[9];
 #pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) qa[kk] = *reinterpret_cast<const v8bf*>(qrow + 32 * kk);
+      for (int i = 0; i < 9; ++i) raw[i] = *reinterpret_cast<const uint2*>(qp + 4 * i);
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        mx = fmaxf(mx, fabsf(__uint_as_float(raw[i].x << 16)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(raw[i].x & 0xFFFF0000u)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(raw[i].y << 16)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(raw[i].y & 0xFFFF0000u)));
+      }
+      mx = fmaxf(mx, xshflf<1>(mx));
+      mx = fmaxf(mx, xshflf<2>(mx));
+      mx = fmaxf(mx, xshflf<4>(mx));
+      mx = fmaxf(mx, xshflf<8>(mx));
+      int ex = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 255u) - 127 - 14 : 0;
+      ex = ex < -100 ? -100 : ex;
+      const float down = __uint_as_float((uint32_t)(127 - ex) << 23);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        const v2h lo = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(raw[i].x << 16) * down,
+                                                                         __uint_as_float(raw[i].x & 0xFFFF0000u) * down));
+        const v2h hi = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(raw[i].y << 16) * down,
+                                                                         __uint_as_float(raw[i].y & 0xFFFF0000u) * down));
+        *reinterpret_cast<uint2*>(qp + 4 * i) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+      if (part == 0) qe_s[h] = __uint_as_float((uint32_t)(127 + ex) << 23);
+      __syncthreads();
+      const uint16_t* qrow = q_s + (16 * hh + hrow) * QROW + kq;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) qh[kk] = *reinterpret_cast<const v8h*>(qrow + 32 * kk);
+    } else {
+      const uint16_t* qrow = q_s + (16 * hh + hrow) * QROW + kq;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) qa[kk] = *reinterpret_cast<const v8bf*>(qrow + 32 * kk);
+    }
     __syncthreads();  // every wave holds its fragments before the latents overwrite them
   }
 
   for (int c0 = j0; c0 < j1; c0 += CH) {
     // LDS is free here: the previous chunk ended with a barrier
+    if constexpr (NV) {
+      uint8_t* trow = lat_s + tt_g * LROW;
+      const v2f s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(nbs, 1.0f, false);
+      const v2f s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(nbs, 1.0f, true);
+      const float bsc[4] = {s01[0], s01[1], s23[0], s23[1]};
 #pragma unroll
-    for (int q = 0; q < PN; ++q)
-      if (q8 + 8 * q < PIECES)
-        *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (q8 + 8 * q)) = tv ? v[q] : v4i{0, 0, 0, 0};
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          // block scale = p * m: p its power of two, m in [1, 2) its significand (0 if zero)
+          const uint32_t sb = __float_as_uint(bsc[2 * i + hb]);
+          const float p = sb ? __uint_as_float(sb & 0x7F800000u) : 1.f;
+          const _Float16 m = sb ? (_Float16)__uint_as_float((sb & 0x007FFFFFu) | 0x3F800000u) : (_Float16)0.f;
+          const v2h m2 = {m, m};
+#pragma unroll
+          for (int w2 = 0; w2 < 2; ++w2) {
+            const int w4 = 2 * hb + w2;
+            const v8h o = tv ? e2m1x8_scaled_f16((uint32_t)v[i][w4], p, m2) : v8h{};
+            *reinterpret_cast<v8h*>(trow + nv_col(64 * q8 + 32 * i + 8 * w4)) = o;
+          }
+        }
+      if (q8 < 4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const v8h o = tv ? e4m3x8_to_f16((uint32_t)v[2][2 * h], (uint32_t)v[2][2 * h + 1]) : v8h{};
+          *reinterpret_cast<v8h*>(trow + nv_col(kDV + 16 * q8 + 8 * h)) = o;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < PN; ++q)
+        if (q8 + 8 * q < PIECES)
+          *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (q8 + 8 * q)) = tv ? v[q] : v4i{0, 0, 0, 0};
+    }
     if (q8 == 0) sc_s[tt_g] = tv ? sv : kNegInf;  // -inf marks an empty slot
     __syncthreads();
     if (c0 + CH < j1) {  // uniform
@@ -194,19 +327,33 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm
     // scaled logits (log2 domain) go to LDS ----
     {
       v4f s0 = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW + kq;
+      if constexpr (NV) {
+        const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW;
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) {
-        uint2 raw = *reinterpret_cast<const uint2*>(lrow + 32 * kk);
-        v8bf b = e4m3x8_to_bf16(raw.x, raw.y);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], b, s0, 0, 0, 0);
+        for (int kk = 0; kk < KQ; ++kk) {
+          const v8h b = *reinterpret_cast<const v8h*>(lrow + nv_col(kq + 32 * kk));
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], b, s0, 0, 0, 0);
+        }
+      } else {
+        const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW + kq;
+#pragma unroll
+        for (int kk = 0; kk < KQ; ++kk) {
+          uint2 raw = *reinterpret_cast<const uint2*>(lrow + 32 * kk);
+          v8bf b = e4m3x8_to_bf16(raw.x, raw.y);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], b, s0, 0, 0, 0);
+        }
       }
       const int tt = 16 * tg + hrow;
       const float sct = sc_s[tt];
       const bool ok = sct != kNegInf;
       const int hb = 16 * hh + 4 * (lane >> 4);
+      if constexpr (NV) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x_s[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
+        for (int i = 0; i < 4; ++i) x_s[(hb + i) * XROW + tt] = ok ? s0[i] * qe_s[hb + i] * (sct * c2) : kNegInf;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x_s[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
+      }
     }
     __syncthreads();
 
@@ -270,15 +417,38 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm
     // by one transposing LDS read: within each 16-lane group, lane 8 a + c' receives byte c'
     // of the 8-byte rows that lanes 2 j + a point at, j = 0..7 (in token order). So lane l
     // points at token row 8 (l >> 5) + ((l & 15) >> 1), columns 16 ((l >> 4) & 1) + 8 (l & 1).
-    const int tr_off = (8 * (lane >> 5) + ((lane & 15) >> 1)) * LROW + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+    // NVFP4 (fp16 tile): the 16-bit transposing read gives 4 values per lane: within each
+    // 16-lane group, lane 4 a + c' receives element c' of the 8-byte rows that lanes
+    // a + 4 j point at, j = 0..3 (in token order). So lane l points at token row
+    // 8 (l >> 5) + ((l & 15) >> 2) (+4 for the second read), columns 16 ((l >> 4) & 1) +
+    // 4 (l & 3).
+    if constexpr (NV) {
+      const int tr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * LROW;
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-    for (int ks = 0; ks < CH / 16; ++ks) {
+      for (int ks = 0; ks < CH / 16; ++ks) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const uint8_t* vp = lat_s + 16 * ks * LROW + 64 * wid + 32 * c + tr_off;
-        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(vp));
-        v8h b = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, acc[c], 0, 0, 0);
+        for (int c = 0; c < 2; ++c) {
+          const uint8_t* vp = lat_s + 16 * ks * LROW + tr_row + nv_col(64 * wid + 32 * c + tr_col);
+          const v4h t0 = __builtin_bit_cast(
+              v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp)));
+          const v4h t1 = __builtin_bit_cast(
+              v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 4 * LROW)));
+          const v8h b = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, acc[c], 0, 0, 0);
+        }
+      }
+    } else {
+      const int tr_off = (8 * (lane >> 5) + ((lane & 15) >> 1)) * LROW + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+#pragma unroll
+      for (int ks = 0; ks < CH / 16; ++ks) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint8_t* vp = lat_s + 16 * ks * LROW + 64 * wid + 32 * c + tr_off;
+          const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(vp));
+          v8h b = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, acc[c], 0, 0, 0);
+        }
       }
     }
     __syncthreads();  // lat_s, x_s, sc_s and hv_s are rewritten by the next chunk
@@ -381,8 +551,12 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     part_o = static_cast<float*>(ws);
     part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 4, 256));
   }
-  hipLaunchKernelGGL(sparse_mla_kernel, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, cv, rm, q_lat, idx, phys,
-                     k, ts, c2, out, lse, part_o, part_ml, nsplit);
+  if (cv.latent_fmt == DSA_LATENT_NVFP4)
+    hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, cv, rm, q_lat,
+                       idx, phys, k, ts, c2, out, lse, part_o, part_ml, nsplit);
+  else
+    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, cv, rm, q_lat,
+                       idx, phys, k, ts, c2, out, lse, part_o, part_ml, nsplit);
   if (nsplit > 1)
     hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
   return hipGetLastError();

@@ -23,8 +23,9 @@ from typing import Optional
 
 import torch
 
-from .layout import (CacheLayout, default_layout, D_IDX, H_IDX, D_LAT, H_Q,
-                     MXFP4_GROUP, INDEX_FP8, INDEX_MXFP4)
+from .layout import (CacheLayout, default_layout, D_IDX, H_IDX, D_LAT, D_V, H_Q,
+                     MXFP4_GROUP, NV_BLOCK, INDEX_FP8, INDEX_MXFP4, LATENT_FP8, LATENT_NVFP4,
+                     latent_record_bytes)
 
 E4M3_MAX = 448.0
 _E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
@@ -50,19 +51,43 @@ def quantize_mxfp4_rows(x: torch.Tensor):
     e = torch.where(amax > 0, torch.floor(torch.log2(torch.clamp(amax, min=1e-30))) - 2,
                     torch.zeros_like(amax)).clamp_(-127, 127)
     y = g / torch.exp2(e).unsqueeze(-1)
+    nib = _e2m1_nibbles(y).reshape(*shp[:-1], shp[-1] // 2, 2)
+    packed = (nib[..., 0] | (nib[..., 1] << 4)).to(torch.uint8)
+    e8 = (e + 127).to(torch.uint8)
+    return packed, e8
+
+
+def _e2m1_nibbles(y: torch.Tensor) -> torch.Tensor:
+    """Nearest e2m1 code of every element (ties to the even code, magnitudes above 6
+    clamp to 6, no negative zero), int64."""
     mag = y.abs()
-    grid = torch.tensor(_E2M1_MAG, dtype=torch.float32, device=x.device)
+    grid = torch.tensor(_E2M1_MAG, dtype=torch.float32, device=y.device)
     mids = (grid[1:] + grid[:-1]) / 2
     i = torch.bucketize(mag.contiguous(), mids)          # mag == mid -> lower index
     on_mid = (i < 7) & (mag == mids[i.clamp(max=6)])
     i = torch.where(on_mid & (i % 2 == 1), i + 1, i)     # ties to the even code
     i = torch.where(mag > 6.0, torch.full_like(i, 7), i)
     sign = ((y < 0) & (i > 0)).to(torch.int64)
-    nib = (sign << 3) | i
-    nib = nib.reshape(*shp[:-1], shp[-1] // 2, 2)
+    return (sign << 3) | i
+
+
+def quantize_nvfp4_latent_rows(x: torch.Tensor):
+    """x float32 [..., 576] -> (records uint8 [..., 352], scale float32 [...]): s = amax / 448
+    (1 when zero), y = x / s clamped to +-448; dims 512.. as e4m3 codes of y; per 16 dims
+    of the first 512 an e4m3 block scale nearest to max|y| / 6 and e2m1 codes of y over
+    that scale's value (0 when it is 0)."""
+    shp = x.shape[:-1]
+    amax = x.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    y = (x / s.unsqueeze(-1)).clamp_(-E4M3_MAX, E4M3_MAX)
+    tail = y[..., D_V:].to(torch.float8_e4m3fn).view(torch.uint8)
+    blk = y[..., :D_V].reshape(*shp, D_V // NV_BLOCK, NV_BLOCK)
+    sc = (blk.abs().amax(dim=-1) / 6.0).to(torch.float8_e4m3fn)
+    scv = sc.to(torch.float32).unsqueeze(-1)
+    q = torch.where(scv > 0, blk / torch.where(scv > 0, scv, torch.ones_like(scv)), torch.zeros_like(blk))
+    nib = _e2m1_nibbles(q).reshape(*shp, D_V // 2, 2)
     packed = (nib[..., 0] | (nib[..., 1] << 4)).to(torch.uint8)
-    e8 = (e + 127).to(torch.uint8)
-    return packed, e8
+    return torch.cat([packed, sc.view(torch.uint8), tail], dim=-1), s.to(torch.float32)
 
 
 # --------------------------------------------------------------------------------------
@@ -147,7 +172,7 @@ def _dequant_query_fp64(codes, scale, index_fmt):
 
 def make_case(ctx_lens, *, row_seq=None, block_size=64, num_layers=1, index_fmt=INDEX_FP8,
               seed=0, device="cpu", k=2048, plant=0, spare_blocks=0, name="case",
-              ctx_lens_are_rows=False) -> DecodeCase:
+              ctx_lens_are_rows=False, latent_fmt=LATENT_FP8) -> DecodeCase:
     """General builder.
 
     ``ctx_lens``: per-sequence cache lengths (tokens held in the cache). By
@@ -158,7 +183,7 @@ def make_case(ctx_lens, *, row_seq=None, block_size=64, num_layers=1, index_fmt=
     """
     device = torch.device(device)
     g = _gen(seed, device)
-    layout = default_layout(block_size, num_layers, index_fmt)
+    layout = default_layout(block_size, num_layers, index_fmt, latent_fmt=latent_fmt)
     if ctx_lens_are_rows:
         assert row_seq is not None
         row_seq_t = torch.as_tensor(row_seq, dtype=torch.int32)
@@ -197,9 +222,13 @@ def make_case(ctx_lens, *, row_seq=None, block_size=64, num_layers=1, index_fmt=
         for b0 in range(0, total, chunk):
             b1 = min(total, b0 + chunk)
             x = _randn(g, (b1 - b0, bs, D_LAT), device)
-            c, s = quantize_e4m3_rows(x)
-            pool[b0:b1, lo:lo + bs * D_LAT] = c.reshape(b1 - b0, bs * D_LAT)
-            pool[b0:b1, lo + bs * D_LAT:lo + bs * (D_LAT + 4)] = s.contiguous().view(torch.uint8).reshape(b1 - b0, bs * 4)
+            rw = latent_record_bytes(latent_fmt)
+            if latent_fmt == LATENT_FP8:
+                c, s = quantize_e4m3_rows(x)
+            else:
+                c, s = quantize_nvfp4_latent_rows(x)
+            pool[b0:b1, lo:lo + bs * rw] = c.reshape(b1 - b0, bs * rw)
+            pool[b0:b1, lo + bs * rw:lo + bs * (rw + 4)] = s.contiguous().view(torch.uint8).reshape(b1 - b0, bs * 4)
         io = layout.idx_off[l]
         kchunk = max(1, (1 << 24) // (bs * D_IDX))
         for b0 in range(0, total, kchunk):

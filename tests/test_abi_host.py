@@ -90,6 +90,9 @@ def _score(lib, d, **kw):
     ({"idx_off": (ctypes.c_int64 * 64)(*([45000] + [0] * 63))}, {}, 3),   # index page past the row end
     ({"pool": 0x10008}, {}, 5),                             # misaligned pool
     ({"index_fmt": 7}, {}, 7),
+    ({"latent_fmt": 2}, {}, 7),                             # unknown latent format
+    ({"latent_fmt": 1, "row_bytes": 22784 + 8448 - 16, "idx_off": (ctypes.c_int64 * 64)(*([22784] + [0] * 63))},
+     {}, 3),                                                # NVFP4 latent page 64 x 356 B, index page one short
     ({}, dict(q=None), 1),
     ({}, dict(max_ctx=128 * 64 + 1), 2),                    # beyond block-table capacity
     ({}, dict(ld=100), 2),

@@ -370,16 +370,25 @@ def _append_inputs(R, seed):
     key[2, :32] = np.array([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 4, dtype=np.float32)  # e2m1 ties, E = 0
     key[2, 32:64] = np.float32(1e-30)                             # tiny group
     key[3] *= -1e5                                                # large values
+    # NVFP4 block-scale decisions (token scale 1: dim 575 holds the amax 448)
+    lat[4, 575] = 448.0
+    lat[4, 0:16] = 0.5
+    lat[4, 0] = 6.375                                             # max/6 = 1.0625: e4m3 tie -> 1.0, then clamp at 6
+    lat[4, 16:32] = np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] * 2, dtype=np.float32)  # e2m1 ties, scale 1
+    lat[4, 32:48] = np.float32(1e-5)                              # block scale rounds to 0: codes 0
+    lat[4, 48:64] = 0.0
+    lat[4, 512:518] = np.array([1.0625, 1.1875, 3.25, -5.5, 0.0068359375, -0.0], dtype=np.float32)
     return key, lat
 
 
-@pytest.mark.parametrize("fmt,bs", [("fp8", 64), ("fp8", 16), ("mxfp4", 128), ("mxfp4", 16)])
-def test_cache_append_bit_exact(dev, fmt, bs):
+@pytest.mark.parametrize("fmt,bs,lat_fmt", [("fp8", 64, "fp8"), ("fp8", 16, "fp8"), ("mxfp4", 128, "fp8"),
+                                            ("mxfp4", 16, "fp8"), ("fp8", 64, "nvfp4"), ("mxfp4", 16, "nvfp4")])
+def test_cache_append_bit_exact(dev, fmt, bs, lat_fmt):
     """New-token append: the whole pool after the GPU append equals the oracle's append of
     the same inputs byte for byte; rows outside their table or on an unmapped block write nothing."""
-    say(f"case: cache append {fmt} bs {bs}")
+    say(f"case: cache append {fmt} bs {bs} latents {lat_fmt}")
     c = make_case([300, 1000, 64, 2000, 5], block_size=bs, seed=95, k=64, index_fmt=fmt, num_layers=2,
-                  spare_blocks=2).to(dev)
+                  spare_blocks=2, latent_fmt=lat_fmt).to(dev)
     R = 9
     key, lat = _append_inputs(R, 96)
     # rows 5, 6, 8 write nothing: a negative position, one past the table, one on an unmapped (-1) block
@@ -414,6 +423,46 @@ def test_append_then_decode(dev):
     scores, idx, out, lse = full_check(c, dev)
     for r in range(2):
         assert int(c.row_ctx[r]) - 1 < scores.shape[1]
+
+
+# ----------------------------------------------------------------------------- NVFP4 latents
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_nvfp4_latents_ragged(dev, bs):
+    """NVFP4 latent records (352 B) through the whole step: ragged rows, one shorter than k."""
+    say(f"case: nvfp4 latents bs {bs}")
+    c = make_case([300, 5000, 9001, 40000], block_size=bs, seed=120 + bs, k=2048, latent_fmt="nvfp4")
+    full_check(c, dev)
+
+
+def test_nvfp4_latents_with_mxfp4_keys_and_empty_rows(dev):
+    """The pages' smallest cache: NVFP4 latents with MXFP4 index keys, block size 128, two
+    layers; an empty row gives zeros and -inf."""
+    say("case: nvfp4 latents + mxfp4 keys")
+    c = make_case([20000, 0, 70000, 700], block_size=128, seed=131, k=2048, index_fmt="mxfp4",
+                  latent_fmt="nvfp4", num_layers=2)
+    _, idx, out, lse = full_check(c, dev, layer=1)
+    assert np.all(idx[1] == -1) and np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+@pytest.mark.parametrize("k", [7, 100])
+def test_nvfp4_latents_small_k(dev, k):
+    say(f"case: nvfp4 latents k {k}")
+    c = make_case([5000, 64, 3], block_size=64, seed=140 + k, k=k, latent_fmt="nvfp4")
+    full_check(c, dev)
+
+
+def test_nvfp4_append_then_decode(dev):
+    """Append into an NVFP4 latent page, then decode over the new token."""
+    say("case: nvfp4 append then decode")
+    c = make_case([5000, 30000], block_size=64, seed=151, k=2048, spare_blocks=2, latent_fmt="nvfp4").to(dev)
+    rng = np.random.default_rng(152)
+    key = (rng.normal(0, 1, (2, 128)) * 4).astype(np.float32)
+    lat = rng.normal(0, 1, (2, 576)).astype(np.float32)
+    dsa.dsa_cache_append(c.pool, c.layout, 0, c.block_table, c.row_seq, c.row_ctx.clone(),
+                         idx_key=torch.tensor(key, device=dev), latent=torch.tensor(lat, device=dev))
+    c.row_ctx += 1
+    full_check(c, dev)
 
 
 # ----------------------------------------------------------------------------- context-parallel merge

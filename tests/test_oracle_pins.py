@@ -515,3 +515,17 @@ def test_nvfp4_latent_quantiser_error_bound_and_scales():
         assert np.all(err[512:] <= float(s) * np.maximum(np.abs(y[512:]) / 16.0, 2.0 ** -10) * 1.0000001)
         if t == 0:
             assert np.all(rec[:16] == 0) and np.all(rec[256:258] == 0)
+
+
+def test_generator_writes_nvfp4_records_as_the_oracle_reads_them():
+    """The synthetic cache's NVFP4 quantiser (torch, generator side) and the oracle's
+    reading of it give the same bytes on CPU."""
+    import torch
+    from synth.cases import quantize_nvfp4_latent_rows
+    rng = np.random.default_rng(8)
+    x = (rng.normal(0, 1, (16, 576)) * (10.0 ** rng.uniform(-2, 2, (16, 1)))).astype(np.float32)
+    x[3, :40] = 0.0
+    rec, s = quantize_nvfp4_latent_rows(torch.from_numpy(x))
+    for i in range(16):
+        want, ws = O.quantize_nvfp4_latent(x[i])
+        assert np.array_equal(rec[i].numpy(), want) and np.float32(s[i].item()) == ws
