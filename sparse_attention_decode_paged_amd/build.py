@@ -15,6 +15,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar / pointer kernel arguments arrive preloaded in SGPRs (gfx950)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"),
 ]

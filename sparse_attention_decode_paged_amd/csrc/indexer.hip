@@ -46,8 +46,15 @@ __device__ __forceinline__ int swz(int tn, int c) { return tn * kDIdx + 16 * (c 
 // [64w, 64w + 64) of it. PAGED32: block size >= 32, so a tile lies inside one page.
 // Waves past the row's end stay to the epilogue, whose 256-token units take a
 // workgroup barrier. SEND: also run stage 1 of the top-k on the fresh scores.
+// The three row-map pointers lead the argument list so that they arrive preloaded in
+// scalar registers (kernel-argument preloading covers leading scalar and pointer
+// arguments, not structures): the first loads of the dependent chain row -> block
+// table -> keys need no kernel-argument fetch before them.
 template <bool PAGED32, bool SEND>
-__global__ __launch_bounds__(256) void indexer_fp8_kernel(CacheView cv, RowMap rm, const uint8_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restrict__ row_seq,
+                                                          const int32_t* __restrict__ row_ctx,
+                                                          const int32_t* __restrict__ block_table, CacheView cv,
+                                                          RowMap rm, const uint8_t* __restrict__ q_idx,
                                                           const float* __restrict__ q_scale,
                                                           const float* __restrict__ w, float* __restrict__ scores,
                                                           int64_t ld, TopkWs tw) {
@@ -58,8 +65,9 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(CacheView cv, RowMap r
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // the row's length and block-table row are read together; a workgroup past the
   // row's end still issues its (clamped, valid) loads and leaves after them
-  const int seq = rm.row_seq[r];
-  int ctx = row_len(rm, r);
+  const int seq = row_seq[r];
+  int ctx = row_ctx[r];
+  ctx = ctx < 0 ? 0 : (ctx > rm.max_ctx ? rm.max_ctx : ctx);
   const bool past = blockIdx.x * 256 >= ctx;  // whole workgroup
   ctx = ctx > 0 ? ctx : 1;
   const int tok0 = blockIdx.x * 256 + wid * 64;
@@ -74,7 +82,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(CacheView cv, RowMap r
   const int tb1 = tok0 + kTileTok < last_tile ? tok0 + kTileTok : last_tile;
   const int tb0 = tok0 < last_tile ? tok0 : last_tile;
   if (PAGED32) {  // both block-table entries are loaded before either is used
-    const int32_t* btrow = rm.block_table + (int64_t)seq * rm.bt_stride;
+    const int32_t* btrow = block_table + (int64_t)seq * rm.bt_stride;
     // read as unsigned (no sign extension between the two loads), so both are in
     // flight together; ids outside [0, num_blocks) are clamped like token_block does
     const uint32_t e0 = (uint32_t)btrow[tb0 >> cv.log2_bs], e1 = (uint32_t)btrow[tb1 >> cv.log2_bs];
@@ -182,13 +190,17 @@ hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8
   dim3 grid(nx, R);
   const bool p32 = cv.block_size >= kTileTok;
   if (send && p32)
-    hipLaunchKernelGGL((indexer_fp8_kernel<true, true>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
+    hipLaunchKernelGGL((indexer_fp8_kernel<true, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                       rm, q_idx, q_scale, w, scores, ld, tw);
   else if (send)
-    hipLaunchKernelGGL((indexer_fp8_kernel<false, true>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
+    hipLaunchKernelGGL((indexer_fp8_kernel<false, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                       rm, q_idx, q_scale, w, scores, ld, tw);
   else if (p32)
-    hipLaunchKernelGGL((indexer_fp8_kernel<true, false>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
+    hipLaunchKernelGGL((indexer_fp8_kernel<true, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                       rm, q_idx, q_scale, w, scores, ld, tw);
   else
-    hipLaunchKernelGGL((indexer_fp8_kernel<false, false>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_scale, w, scores, ld, tw);
+    hipLaunchKernelGGL((indexer_fp8_kernel<false, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                       rm, q_idx, q_scale, w, scores, ld, tw);
   return hipGetLastError();
 }
 

@@ -56,8 +56,12 @@ __device__ __forceinline__ v8bf e2m1x8_to_bf16(uint32_t v, float scale) {
 // [64w, 64w + 64). PAGED32: block size >= 32, so a tile lies inside one page.
 // SEND: also run stage 1 of the top-k on the fresh scores.
 template <bool PAGED32, bool SEND>
-__global__ __launch_bounds__(256) void indexer_mxfp4_kernel(CacheView cv, RowMap rm,
-                                                            const uint8_t* __restrict__ q_idx,
+// Row-map pointers lead the argument list (preloaded in scalar registers), as for the
+// FP8 kernel.
+__global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __restrict__ row_seq,
+                                                            const int32_t* __restrict__ row_ctx,
+                                                            const int32_t* __restrict__ block_table, CacheView cv,
+                                                            RowMap rm, const uint8_t* __restrict__ q_idx,
                                                             const uint8_t* __restrict__ q_e8,
                                                             const float* __restrict__ w, float* __restrict__ scores,
                                                             int64_t ld, TopkWs tw) {
@@ -68,8 +72,9 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(CacheView cv, RowMap
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // the row's length and block-table row are read together; a workgroup past the
   // row's end still issues its (clamped, valid) loads and leaves after them
-  const int seq = rm.row_seq[r];
-  int ctx = row_len(rm, r);
+  const int seq = row_seq[r];
+  int ctx = row_ctx[r];
+  ctx = ctx < 0 ? 0 : (ctx > rm.max_ctx ? rm.max_ctx : ctx);
   const bool past = blockIdx.x * 256 >= ctx;  // whole workgroup
   ctx = ctx > 0 ? ctx : 1;
   const int tok0 = blockIdx.x * 256 + wid * 64;
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(CacheView cv, RowMap
   if (PAGED32) {
     // read as unsigned (no sign extension between the two loads), so both are in
     // flight together; ids outside [0, num_blocks) are clamped like token_block does
-    const int32_t* btrow = rm.block_table + (int64_t)seq * rm.bt_stride;
+    const int32_t* btrow = block_table + (int64_t)seq * rm.bt_stride;
     const uint32_t e0 = (uint32_t)btrow[tb0 >> cv.log2_bs], e1 = (uint32_t)btrow[tb1 >> cv.log2_bs];
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t nb = (uint32_t)cv.num_blocks;
@@ -190,16 +195,20 @@ hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uin
   dim3 grid(nx, R);
   const bool p32 = cv.block_size >= kTileTok;
   if (send && p32)
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<true, true>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_e8, w, scores,
+    hipLaunchKernelGGL((indexer_mxfp4_kernel<true, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
                        ld, tw);
   else if (send)
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<false, true>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_e8, w, scores,
+    hipLaunchKernelGGL((indexer_mxfp4_kernel<false, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
                        ld, tw);
   else if (p32)
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<true, false>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_e8, w, scores,
+    hipLaunchKernelGGL((indexer_mxfp4_kernel<true, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
                        ld, tw);
   else
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<false, false>), grid, dim3(256), 0, stream, cv, rm, q_idx, q_e8, w, scores,
+    hipLaunchKernelGGL((indexer_mxfp4_kernel<false, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
                        ld, tw);
   return hipGetLastError();
 }

@@ -100,10 +100,15 @@ __device__ __forceinline__ int nv_col(int col) {
 
 }  // namespace
 
+// The index list, page slots and queries lead the argument list so that their
+// addresses arrive preloaded in scalar registers (kernel-argument preloading covers
+// leading scalar and pointer arguments, not structures): the head of the load chain
+// needs no kernel-argument fetch before it.
 template <bool NV>
-__global__ __launch_bounds__(NTM) void sparse_mla_kernel(CacheView cv, RowMap rm, const uint16_t* __restrict__ q_lat,
-                                                        const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ phys, int k, int ts, float c2,
+__global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ phys,
+                                                        const uint16_t* __restrict__ q_lat, int k, int ts, float c2,
+                                                        CacheView cv, RowMap rm,
                                                         float* __restrict__ out, float* __restrict__ lse,
                                                         float* __restrict__ part_o, float* __restrict__ part_ml,
                                                         int nsplit) {
@@ -552,11 +557,11 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 4, 256));
   }
   if (cv.latent_fmt == DSA_LATENT_NVFP4)
-    hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, cv, rm, q_lat,
-                       idx, phys, k, ts, c2, out, lse, part_o, part_ml, nsplit);
+    hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, idx, phys,
+                       q_lat, k, ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
   else
-    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, cv, rm, q_lat,
-                       idx, phys, k, ts, c2, out, lse, part_o, part_ml, nsplit);
+    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, idx, phys,
+                       q_lat, k, ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
   if (nsplit > 1)
     hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
   return hipGetLastError();

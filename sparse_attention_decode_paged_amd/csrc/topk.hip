@@ -488,10 +488,17 @@ __global__ __launch_bounds__(256) void topk_send_kernel(const float* __restrict_
 
 // CAND: rows may be longer than kTopkFullRow, so candidates were sent.
 template <bool CAND>
-__global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
+// The candidate arrays lead the argument list so that their addresses arrive preloaded in
+// scalar registers (kernel-argument preloading covers leading scalar and pointer
+// arguments, not structures) and the candidate loads start with the kernel.
+__global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __restrict__ cand_hi,
+                                                             const uint32_t* __restrict__ cand_lo,
+                                                             const uint32_t* __restrict__ floors,
+                                                             const float* __restrict__ scores, int64_t ld,
                                                              const int32_t* __restrict__ row_ctx, int max_ctx, int k,
-                                                             TopkWs ws, int32_t* __restrict__ idx,
-                                                             int32_t* __restrict__ phys, CacheView cv, RowMap rm) {
+                                                             int32_t* __restrict__ idx, int32_t* __restrict__ phys,
+                                                             CacheView cv, RowMap rm) {
+  const TopkWs ws{const_cast<uint32_t*>(cand_hi), const_cast<uint32_t*>(cand_lo), const_cast<uint32_t*>(floors)};
   __shared__ SelShared S;
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   // candidate slots and unit floors first: their addresses need only the kernel
@@ -816,11 +823,11 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* ro
   }
   if (!phys) m.row_seq = row_ctx;  // read, never used
   if (max_ctx > kTopkFullRow)
-    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(R), dim3(SEL_NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws,
-                       idx, phys, c, m);
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(R), dim3(SEL_NT), 0, stream, ws.cand_hi, ws.cand_lo, ws.floors,
+                       scores, ld, row_ctx, max_ctx, k, idx, phys, c, m);
   else
-    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(R), dim3(SEL_NT), 0, stream, scores, ld, row_ctx, max_ctx, k, ws,
-                       idx, phys, c, m);
+    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(R), dim3(SEL_NT), 0, stream, ws.cand_hi, ws.cand_lo, ws.floors,
+                       scores, ld, row_ctx, max_ctx, k, idx, phys, c, m);
   return hipGetLastError();
 }
 
