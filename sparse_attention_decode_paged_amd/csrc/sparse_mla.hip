@@ -15,9 +15,9 @@
 //   behind them) and go to LDS once chunk c is done with it;
 //   S = Q . C^T on 16x16x32 bf16 MFMAs (8 waves, each 16 tokens x 16 heads), scaled
 //   logits (log2 domain) to LDS;
-//   every wave then runs the online softmax of the whole chunk for the 32 heads
-//   itself (running max / sum per head, identical in every wave), so one barrier
-//   separates S from P . V;
+//   the online softmax of the chunk is split across the waves (each owns 4 heads and
+//   keeps their running max / sum), and P'' and the heads' rescale factors pass through
+//   LDS to every wave;
 //   P'' = p * scale_t / (largest scale in the chunk), in [0, 1], as fp16 straight
 //   into the MFMA operand registers;
 //   O += P'' . codes on 32x32x16 fp16 MFMAs (each wave: 64 of the 512 value
@@ -68,6 +68,7 @@ struct Tile {
   static_assert(kMlaGroup * QROW * 2 <= BYTES, "Q staging fits the latent tile");
 };
 constexpr int XROW = CH + 16;           // logit rows: the four 16-lane groups of a store hit distinct banks
+constexpr int PROW = CH + 8;            // P'' rows (fp16), padded so the fragment reads spread over the banks
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -120,8 +121,10 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   __shared__ __attribute__((aligned(16))) uint8_t lat_s[Tile<NV>::BYTES];
   __shared__ __attribute__((aligned(16))) float x_s[kMlaGroup * XROW];  // scaled logits, head-major
   __shared__ __attribute__((aligned(16))) float sc_s[CH];
-  __shared__ __attribute__((aligned(16))) float hv_s[NWM][kMlaGroup];  // per-wave exchange of per-head values
   __shared__ float qe_s[kMlaGroup];  // NVFP4: the power of two each head's fp16 query was scaled down by
+  __shared__ __attribute__((aligned(16))) _Float16 p_s[kMlaGroup * PROW];  // the chunk's P'', head-major
+  __shared__ float al_s[kMlaGroup];   // each head's rescale factor for the chunk
+  __shared__ float2 ml_s[kMlaGroup];  // each head's running (max, sum), kept by its owning wave
 
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
@@ -164,8 +167,9 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   v8bf qa[KQ];
   v8h qh[KQ];  // NVFP4: the same fragments in fp16, scaled by a power of two per head
 
-  // running softmax state of head (lane & 31); every wave keeps an identical copy
+  // running softmax state of head 4 wid + (lane >> 4), the head this lane's wave owns
   float m_run = kNegInf, l_run = 0.f;
+  if (tid < kMlaGroup) ml_s[tid] = float2{kNegInf, 0.f};  // ordered by the staging barriers below
   v16f acc[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) acc[c] = v16f{};
@@ -362,56 +366,57 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
     }
     __syncthreads();
 
-    // ---- softmax of head h = lane & 31 over the chunk, by every wave: this lane's
-    // 32 tokens are the ones its P fragments cover (16 ks + 8 g + e) ----
-    v8h pa[4];
-    float alpha;
+    // ---- softmax over the chunk, split across the waves: wave w owns heads 4w .. 4w+3,
+    // lane l head 4w + (l >> 4) and tokens 4 (l & 15) .. +4. P'' = p * scale_t / smax
+    // (fp16, in [0, 1]) and each head's rescale factor go to LDS for every wave ----
     {
-      const int h = lane & 31;
-      float xv[4][8], sv[4][8];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const float4* xp = reinterpret_cast<const float4*>(x_s + h * XROW + 16 * ks + 8 * g);
-        const float4* sp = reinterpret_cast<const float4*>(sc_s + 16 * ks + 8 * g);
-        const float4 x0 = xp[0], x1 = xp[1], q0 = sp[0], q1 = sp[1];
-        xv[ks][0] = x0.x; xv[ks][1] = x0.y; xv[ks][2] = x0.z; xv[ks][3] = x0.w;
-        xv[ks][4] = x1.x; xv[ks][5] = x1.y; xv[ks][6] = x1.z; xv[ks][7] = x1.w;
-        sv[ks][0] = q0.x; sv[ks][1] = q0.y; sv[ks][2] = q0.z; sv[ks][3] = q0.w;
-        sv[ks][4] = q1.x; sv[ks][5] = q1.y; sv[ks][6] = q1.z; sv[ks][7] = q1.w;
-      }
-      float cm = kNegInf;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cm = fmaxf(cm, xv[ks][e]);
-      cm = fmaxf(cm, xshflf<32>(cm));
+      const int h = 4 * wid + (lane >> 4), t4 = 4 * (lane & 15);
+      const float4 x4 = *reinterpret_cast<const float4*>(x_s + h * XROW + t4);
+      const float4 s4 = *reinterpret_cast<const float4*>(sc_s + t4);
+      const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      float cm = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
+      cm = fmaxf(cm, xshflf<1>(cm));
+      cm = fmaxf(cm, xshflf<2>(cm));
+      cm = fmaxf(cm, xshflf<4>(cm));
+      cm = fmaxf(cm, xshflf<8>(cm));
       const float mn = fmaxf(m_run, cm);
-      alpha = (mn == kNegInf) ? 1.f : exp2f(m_run - mn);
+      const float alpha = (mn == kNegInf) ? 1.f : exp2f(m_run - mn);
       const float inv_smax = 1.f / smax;
       float psum = 0.f;
+      v4h ph;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = (xv[ks][e] == kNegInf) ? 0.f : exp2f(xv[ks][e] - mn);
-          psum += p;
-          const float sfac = sv[ks][e] != kNegInf ? sv[ks][e] * inv_smax : 0.f;
-          pa[ks][e] = (_Float16)(p * sfac);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float p = (xv[e] == kNegInf) ? 0.f : exp2f(xv[e] - mn);
+        psum += p;
+        const float sfac = sv[e] != kNegInf ? sv[e] * inv_smax : 0.f;
+        ph[e] = (_Float16)(p * sfac);
       }
-      psum += xshflf<32>(psum);
+      psum += xshflf<1>(psum);
+      psum += xshflf<2>(psum);
+      psum += xshflf<4>(psum);
+      psum += xshflf<8>(psum);
       l_run = l_run * alpha + psum;
       m_run = mn;
+      *reinterpret_cast<v4h*>(p_s + h * PROW + t4) = ph;
+      if ((lane & 15) == 0) {
+        al_s[h] = alpha;
+        ml_s[h] = float2{m_run, l_run};
+      }
     }
+    __syncthreads();
+    // P'' fragments: row = head lane & 31, k = tokens 16 ks + 8 g .. +8
+    v8h pa[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pa[ks] = *reinterpret_cast<const v8h*>(p_s + (lane & 31) * PROW + 16 * ks + 8 * g);
 
     // ---- acc = acc * alpha * (s_run / smax) + P'' . codes : wave w -> columns [64w, 64w+64) ----
     // accumulator row rr of this lane is head 8 (rr >> 2) + 4 g + (rr & 3)
-    if (lane < kMlaGroup) hv_s[wid][lane] = alpha;  // read back by this wave only
     const float rescale = s_run / smax;
     s_run = smax;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&hv_s[wid][8 * jj + 4 * g]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&al_s[8 * jj + 4 * g]);
       const float a[4] = {a4.x * rescale, a4.y * rescale, a4.z * rescale, a4.w * rescale};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -456,16 +461,17 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
         }
       }
     }
-    __syncthreads();  // lat_s, x_s, sc_s and hv_s are rewritten by the next chunk
+    __syncthreads();  // lat_s, x_s, sc_s, p_s and al_s are rewritten by the next chunk
   }
 
   // ---- epilogue ----
+  // (the loop's last barrier, or the staging barriers for a split with no tokens, has
+  // ordered every head's final (max, sum) in ml_s)
   if (nsplit == 1) {
-    if (lane < kMlaGroup) hv_s[wid][lane] = l_run;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&hv_s[wid][8 * jj + 4 * g]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float lv[4] = {ml_s[8 * jj + 4 * g].y, ml_s[8 * jj + 4 * g + 1].y, ml_s[8 * jj + 4 * g + 2].y,
+                           ml_s[8 * jj + 4 * g + 3].y};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 8 * jj + 4 * g + i;
@@ -475,8 +481,10 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
         for (int c = 0; c < 2; ++c) orow[32 * c] = acc[c][4 * jj + i] * f;
       }
     }
-    if (lse != nullptr && tid < kMlaGroup)
-      lse[(int64_t)r * kHQ + hg * kMlaGroup + tid] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : kNegInf;
+    if (lse != nullptr && tid < kMlaGroup) {
+      const float2 ml = ml_s[tid];
+      lse[(int64_t)r * kHQ + hg * kMlaGroup + tid] = ml.y > 0.f ? (ml.x + log2f(ml.y)) * 0.69314718055994531f : kNegInf;
+    }
   } else {
     const int64_t pbase = ((int64_t)r * nsplit + split) * kHQ + hg * kMlaGroup;
 #pragma unroll
@@ -487,8 +495,9 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
       for (int c = 0; c < 2; ++c) __builtin_nontemporal_store(acc[c][rr] * s_run, orow + 32 * c);
     }
     if (tid < kMlaGroup) {
-      part_ml[(pbase + tid) * 2 + 0] = m_run;
-      part_ml[(pbase + tid) * 2 + 1] = l_run;
+      const float2 ml = ml_s[tid];
+      part_ml[(pbase + tid) * 2 + 0] = ml.x;
+      part_ml[(pbase + tid) * 2 + 1] = ml.y;
     }
   }
 }
