@@ -129,8 +129,6 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
   const int j1 = (j0 + ts < k) ? j0 + ts : k;
-  const int seq = rm.row_seq[r];
-  const int bs_mask = cv.block_size - 1;
   // gather: 8 threads per token. FP8: 16-byte pieces q8 + 8 q (q < 5) of 36. NVFP4: code
   // bytes [32 q8, +32) (dims [64 q8, +64)), their 4 block scales and, for q8 < 4, tail
   // bytes [16 q8, +16) (dims 512 + 16 q8 ..)
@@ -164,6 +162,12 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
     for (int q = 0; q < QN; ++q)
       if (tid + NTM * q < QALL) qv[q] = qg[tid + NTM * q];
   }
+  // Only now the loads that need the structure arguments (fetched from memory, unlike the
+  // leading pointers): the id and query loads above go out without waiting for them.
+  // The row's block-table row is needed only without page slots.
+  __builtin_amdgcn_sched_barrier(0);
+  const int seq = phys == nullptr ? rm.row_seq[r] : 0;
+  const int bs_mask = cv.block_size - 1;
   v8bf qa[KQ];
   v8h qh[KQ];  // NVFP4: the same fragments in fp16, scaled by a power of two per head
 
