@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
                                                                int64_t ld, TopkWs tw, int R, int G) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kTileBytes];
   __shared__ uint32_t send_lds[2][68];  // double-buffered by row: a wave runs at most one row ahead
+  __shared__ float wf_s[kRowsPerGroupMax * kHIdx];  // folded head weights w * q_scale of the group's rows
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = blockIdx.y * G;
@@ -106,25 +107,34 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     }
   };
 
+  // The group's folded head weights go to LDS once, and (without the send epilogue, whose
+  // registers would cost a wave per SIMD) each row's query fragment is fetched one row
+  // ahead, so no row waits on a global load of its own.
+  for (int i = threadIdx.x; i < (r1 - r0) * kHIdx; i += 256)
+    wf_s[i] = w[(int64_t)r0 * kHIdx + i] * q_scale[(int64_t)r0 * kHIdx + i];
+  __syncthreads();
+  // query fragment of a row: head n, bytes [64g, 64g + 64)
+  auto q_frag = [&](int rr, v4i (&qf)[4]) {
+    const v4i* qp = reinterpret_cast<const v4i*>(q_idx + ((int64_t)rr * kHIdx + n) * kDIdx + 64 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf[i] = qp[i];
+  };
+  v4i qr[4];
+  if (!SEND) q_frag(r0, qr);
+
   int seq_cur = -1;
   for (int r = r0; r < r1; ++r) {
+    v4i qn[4] = {};
+    if (SEND)
+      q_frag(r, qr);
+    else if (r + 1 < r1)  // uniform
+      q_frag(r + 1, qn);
     const int seq = rm.row_seq[r];
     const int ctx = row_len(rm, r);
     if (seq != seq_cur) {  // uniform
       load_keys(seq);
       seq_cur = seq;
     }
-    // query fragment of row r (head n, bytes [64g, 64g + 64)) and its folded head weights
-    v4i qr[4];
-    {
-      const v4i* qp = reinterpret_cast<const v4i*>(q_idx + ((int64_t)r * kHIdx + n) * kDIdx + 64 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qr[i] = qp[i];
-    }
-    float W[kHIdx];
-#pragma unroll
-    for (int h = 0; h < kHIdx; ++h)
-      W[h] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w[r * kHIdx + h] * q_scale[r * kHIdx + h])));
     v8bf qa[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -134,7 +144,13 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     // accumulator element rr of lane (n, g) is head 8 (rr >> 2) + 4 g + (rr & 3)
     float wq[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) wq[rr] = g ? W[8 * (rr >> 2) + 4 + (rr & 3)] : W[8 * (rr >> 2) + (rr & 3)];
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(&wf_s[(r - r0) * kHIdx + 8 * j + 4 * g]);
+      wq[4 * j] = v.x;
+      wq[4 * j + 1] = v.y;
+      wq[4 * j + 2] = v.z;
+      wq[4 * j + 3] = v.w;
+    }
     float res[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -153,6 +169,10 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     if (t < ctx) scores[(int64_t)r * ld + t] = sc;
     // the workgroup's span must reach into the row, or its unit would lie past the row
     if (SEND && blockIdx.x * 256 < ctx) send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds[r & 1]);
+    if (!SEND) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qr[i] = qn[i];
+    }
   }
 }
 
