@@ -63,6 +63,11 @@ __device__ __forceinline__ const uint8_t* row_base(const CacheView& cv, int64_t 
   return cv.pool + blk * cv.row_bytes;
 }
 
+// max(x, 0) as one integer max on the bit pattern: a float with the sign bit set is a
+// negative int32 (-0 and negative values give +0), a positive float keeps its bits.
+// (fmaxf would first canonicalise an MFMA result, a second instruction per value.)
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // fp32 -> order-preserving unsigned key (larger float -> larger key), -0.0 == +0.0.
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restr
     }
     float s = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) s = fmaf(wq[rr], fmaxf(acc[rr], 0.f), s);
+    for (int rr = 0; rr < 16; ++rr) s = fmaf(wq[rr], relu_bits(acc[rr]), s);
     s += xshflf<32>(s);
     res[j] = s;
   }

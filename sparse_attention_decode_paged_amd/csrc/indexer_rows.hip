@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
       for (int kk = 0; kk < 8; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kb[j][kk], acc, 0, 0, 0);
       float s = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) s = fmaf(wq[rr], fmaxf(acc[rr], 0.f), s);
+      for (int rr = 0; rr < 16; ++rr) s = fmaf(wq[rr], relu_bits(acc[rr]), s);
       s += xshflf<32>(s);
       res[j] = s;
     }
