@@ -147,6 +147,35 @@ def timed_indexer_us(dsa, case, layers, max_ctx, reps):
     return 1000.0 * e0.elapsed_time(e1) / (reps * layers)
 
 
+def hbm_read_ceiling(dsa, buf, reps=3, grids=(512, 1024, 2048, 4096)):
+    """Streaming-read rate (GB/s) of dsa_hbm_read_probe over the whole tensor `buf`, at a
+    few grid sizes: per grid the median of `reps` launches, each timed alone with
+    events; the best grid's median is the ceiling."""
+    import torch
+    dev = buf.device
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    nbytes = buf.numel() * buf.element_size()
+    per_grid = {}
+    for grid in grids:
+        for _ in range(2):
+            dsa.dsa_hbm_read_probe(buf, sink, grid)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            dsa.dsa_hbm_read_probe(buf, sink, grid)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        rates = sorted(nbytes / (ev[i].elapsed_time(ev[i + 1]) * 1e-3) / 1e9 for i in range(reps))
+        per_grid[grid] = round(rates[len(rates) // 2], 1)
+    best = max(per_grid, key=per_grid.get)
+    return {"gbps": per_grid[best], "grid": best, "median_by_grid": {str(g): v for g, v in per_grid.items()},
+            "bytes": nbytes, "unit": "GB/s",
+            "kernel": "hbm_read_kernel (dsa_hbm_read_probe: 16-byte nontemporal loads in 16-KB chunks per "
+                      "256-thread workgroup, over the whole layer-rotated cache pool)"}
+
+
 def bench_dcp(a, dsa, case, dev):
     """Times dsa_topk_dcp (W emulated shards) and dsa_topk on the same indexer scores,
     one call per layer from a HIP graph; prints one JSON line."""
@@ -300,6 +329,19 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
 
+    # spread: each replay of the layer-rotation graph timed alone
+    nrep = max(5, min(100, a.steps // a.layers))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
+    ev[0].record(stream)
+    for i in range(nrep):
+        g_all.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(1000.0 * ev[i].elapsed_time(ev[i + 1]) / a.layers for i in range(nrep))
+    spread = {"p10": round(per[int(0.1 * (nrep - 1))], 3), "p50": round(per[(nrep - 1) // 2], 3),
+              "p90": round(per[int(0.9 * (nrep - 1))], 3), "replays": nrep, "steps_per_replay": a.layers}
+    ceiling = hbm_read_ceiling(dsa, case.pool)
+
     ix_us = timed_indexer_us(dsa, case, a.layers, max_ctx, max(2, min(a.steps, 480) // a.layers))
 
     ctxs = [int(c) for c in case.row_ctx.tolist()]
@@ -332,6 +374,7 @@ def main():
             "index_fmt": a.index_fmt, "latent_fmt": a.latent_fmt,
             "launch": "HIP graph replay, one decode step per layer",
         },
+        "step_us": spread,
         "step_hbm_gbps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
@@ -345,7 +388,9 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": ix_bytes,
             "avg_launch_us": round(ix_us, 3),
+            "frac_of_measured_read_ceiling": round(ix_gbps / ceiling["gbps"], 4),
         },
+        "hbm_read_ceiling": ceiling,
         "gen_seconds": round(gen_s, 1),
     }
     if not a.no_cpu_baseline:

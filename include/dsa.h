@@ -22,9 +22,10 @@
  *
  * Memory: every pointer argument except `cache` itself is a DEVICE pointer,
  * except where marked (host). The caller owns every buffer. The library never
- * allocates, frees or synchronises; all work is enqueued on `stream` (a
- * hipStream_t; NULL = the default stream). Calls are stateless and may be made
- * from several host threads on different streams with different workspaces.
+ * allocates or frees, and only dsa_device_status synchronises; all work is enqueued
+ * on `stream` (a hipStream_t; NULL = the default stream). Calls are stateless (apart
+ * from the device status word at the end of this header) and may be made from
+ * several host threads on different streams with different workspaces.
  *
  * Errors: a non-zero dsa_status is returned before anything is enqueued when an
  * argument is invalid; dsa_last_error_detail() then holds a message for the
@@ -32,7 +33,8 @@
  * problems found on the device never fault: a row's ctx above the block-table
  * capacity or max_ctx is clamped, ctx <= 0 gives an empty row (idx all -1, out 0,
  * lse -inf), and a block id outside [0, num_blocks) is clamped into the pool
- * (that token's values are then unspecified).
+ * (that token's values are then unspecified). The kernels record each such repair
+ * in a per-device status word (dsa_device_status, at the end of this header).
  */
 #ifndef DSA_H
 #define DSA_H
@@ -273,6 +275,40 @@ dsa_status dsa_topk_dcp(const float* scores, int64_t ld_scores, const int32_t* r
                         int32_t R, int32_t max_ctx, int32_t k, int32_t W, int32_t* idx,
                         uint32_t* resend_mask, uint32_t* words,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Device status word. Data problems that the kernels repair instead of faulting
+ * (see the top of this header) are also reported: each GPU holds one 32-bit word,
+ * shared by every call on it, into which kernels OR
+ *   DSA_DEV_CTX_CLAMPED    a row_ctx above max_ctx was used as max_ctx
+ *                          (indexer, top-k, decode step);
+ *   DSA_DEV_BLOCK_CLAMPED  a block-table entry outside [0, num_blocks) was met: reads
+ *                          clamp it into the pool, cache appends skip the row;
+ *   DSA_DEV_INDEX_RANGE    sparse MLA skipped an idx entry at or past the block-table
+ *                          row's capacity.
+ * The word keeps its bits until cleared. dsa_device_status waits for the work queued on
+ * `stream` (it synchronises that stream, unlike every other call here), stores the word
+ * of the current device in *status, and then clears it when `clear` is nonzero. Calls
+ * that run concurrently on one device report into the same word. The word's device
+ * address is looked up (hipGetSymbolAddress) on the library's first call on each
+ * device; calls made while that lookup fails report nothing. dsa_topk_dcp does not
+ * report. DSA_ERR_NULL for a NULL status, DSA_ERR_HIP if the word cannot be read.
+ */
+#define DSA_DEV_CTX_CLAMPED 1u
+#define DSA_DEV_BLOCK_CLAMPED 2u
+#define DSA_DEV_INDEX_RANGE 4u
+dsa_status dsa_device_status(void* stream, int32_t clear, uint32_t* status);
+
+/*
+ * Measurement reference, not a step of the method: reads every byte of
+ * [p, p + bytes) once (16-byte nontemporal loads; `grid` workgroups of 256 threads
+ * take 16-KB chunks in turn) and writes nothing, except *sink in the practically
+ * impossible case that the XOR of all words read equals 0x9E3779B9. Timed over a
+ * buffer much larger than the last-level cache it gives the streaming-read rate the
+ * indexer's HBM roofline can be compared with. p 16-byte aligned, bytes a multiple of
+ * 16 (DSA_ERR_ALIGN), grid in [1, 65535] (DSA_ERR_ARG), sink a device uint32.
+ */
+dsa_status dsa_hbm_read_probe(const void* p, size_t bytes, uint32_t* sink, int32_t grid, void* stream);
 
 #ifdef __cplusplus
 }

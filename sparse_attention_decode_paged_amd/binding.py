@@ -28,7 +28,8 @@ H_IDX, D_IDX, H_Q, D_LAT, D_V = 32, 128, 96, 576, 512
 EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_last_error_detail", "dsa_workspace_bytes",
             "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step",
             "dsa_indexer_score_multi", "dsa_decode_step_multi", "dsa_cache_append",
-            "dsa_topk_dcp_workspace_bytes", "dsa_topk_dcp")
+            "dsa_topk_dcp_workspace_bytes", "dsa_topk_dcp", "dsa_device_status",
+            "dsa_hbm_read_probe")
 
 
 class DSAError(RuntimeError):
@@ -95,6 +96,10 @@ def load_library(path: str = LIB_PATH):
     L.dsa_topk_dcp_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
     L.dsa_topk_dcp.restype = _i32
     L.dsa_topk_dcp.argtypes = [_vp, _i64, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.dsa_device_status.restype = _i32
+    L.dsa_device_status.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_uint32)]
+    L.dsa_hbm_read_probe.restype = _i32
+    L.dsa_hbm_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
     _lib = L
     return L
 
@@ -200,6 +205,30 @@ def dsa_topk(scores, row_ctx, max_ctx, k, idx=None, workspace=None, ld_scores=No
                     workspace.numel() * workspace.element_size(), _stream(scores.device))
     _check(st, "dsa_topk")
     return idx
+
+
+DSA_DEV_CTX_CLAMPED = 1
+DSA_DEV_BLOCK_CLAMPED = 2
+DSA_DEV_INDEX_RANGE = 4
+
+
+def dsa_device_status(device=None, clear=True):
+    """The current device's status word (DSA_DEV_* bits) once the current stream's work
+    has finished; cleared afterwards when `clear`. Synchronises the stream."""
+    L = load_library()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    v = ctypes.c_uint32(0)
+    with torch.cuda.device(dev):
+        _check(L.dsa_device_status(_stream(dev), 1 if clear else 0, ctypes.byref(v)), "dsa_device_status")
+    return int(v.value)
+
+
+def dsa_hbm_read_probe(buf, sink, grid=2048):
+    """Enqueue one streaming read of the whole tensor `buf` (measurement reference)."""
+    L = load_library()
+    nbytes = buf.numel() * buf.element_size()
+    _check(L.dsa_hbm_read_probe(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), int(grid), _stream(buf.device)),
+           "dsa_hbm_read_probe")
 
 
 def dcp_send_count(k, W):

@@ -8,7 +8,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
 SOURCES = ["dsa_api.cpp", "indexer.hip", "indexer_rows.hip", "indexer_mxfp4.hip", "topk.hip", "sparse_mla.hip",
-           "cache_append.hip", "dcp_merge.hip"]
+           "cache_append.hip", "dcp_merge.hip", "hbm_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -127,7 +127,10 @@ __global__ __launch_bounds__(256) void cache_append_kernel(CacheView cv, int32_t
   const int p = pos[r];
   if (p < 0 || (int64_t)(p >> cv.log2_bs) >= (int64_t)bt_stride) return;
   const int64_t blk = block_table[(int64_t)row_seq[r] * bt_stride + (p >> cv.log2_bs)];
-  if (blk < 0 || blk >= cv.num_blocks) return;  // never write outside the pool
+  if (blk < 0 || blk >= cv.num_blocks) {  // never write outside the pool
+    if (lane == 0) raise_status(cv.status, kStBlockClamped);
+    return;
+  }
   const int slot = p & (cv.block_size - 1);
   uint8_t* row = const_cast<uint8_t*>(cv.pool) + blk * cv.row_bytes;
 

@@ -33,6 +33,7 @@ struct CacheView {
   int32_t block_size;  // power of two
   int32_t log2_bs;
   int32_t latent_fmt;  // DSA_LATENT_FP8 / DSA_LATENT_NVFP4
+  uint32_t* status;    // this device's status word (nullable)
 };
 
 // Query-row to cache mapping.
@@ -44,17 +45,35 @@ struct RowMap {
   int32_t max_ctx;  // host bound, also <= bt_stride * block_size
 };
 
+// Bits of the device status word (the DSA_DEV_* values of the C header).
+constexpr uint32_t kStCtxClamped = 1u;    // a row length above max_ctx was clamped
+constexpr uint32_t kStBlockClamped = 2u;  // a block-table entry outside the pool was met
+constexpr uint32_t kStIndexRange = 4u;    // sparse MLA skipped an index past the block table
+
+// Sets `bit` in the status word (no-op without one). Called only on the branches that
+// repair bad data, so good data never reaches the atomic.
+__device__ __forceinline__ void raise_status(uint32_t* st, uint32_t bit) {
+  if (st != nullptr) atomicOr(st, bit);
+}
+
 // Eligible length of row r, clamped to [0, max_ctx].
-__device__ __forceinline__ int row_len(const RowMap& m, int r) {
+__device__ __forceinline__ int row_len(const RowMap& m, int r, uint32_t* st) {
   int c = m.row_ctx[r];
   c = c < 0 ? 0 : c;
-  return c > m.max_ctx ? m.max_ctx : c;
+  if (c > m.max_ctx) {
+    raise_status(st, kStCtxClamped);
+    c = m.max_ctx;
+  }
+  return c;
 }
 
 // Physical block of token t of the block-table row `seq`, clamped into the pool.
 __device__ __forceinline__ int64_t token_block(const CacheView& cv, const RowMap& m, int seq, int t) {
   int64_t b = m.block_table[(int64_t)seq * m.bt_stride + (t >> cv.log2_bs)];
-  if ((uint64_t)b >= (uint64_t)cv.num_blocks) b = b < 0 ? 0 : cv.num_blocks - 1;
+  if ((uint64_t)b >= (uint64_t)cv.num_blocks) {
+    raise_status(cv.status, kStBlockClamped);
+    b = b < 0 ? 0 : cv.num_blocks - 1;
+  }
   return b;
 }
 

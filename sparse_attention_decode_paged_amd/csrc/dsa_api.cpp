@@ -1,6 +1,7 @@
 // C ABI entry points: argument checks, workspace carving, kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -11,7 +12,34 @@
 
 using namespace dsa;
 
+// The device status word: every GPU that runs this library holds its own copy. In host
+// code the symbol's name is not a device address; status_word() looks the address up
+// per device (hipGetSymbolAddress) and kernels receive that address.
+__device__ uint32_t g_device_status;
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t*> g_status_addr[kMaxDevices];
+
+// This device's status word, looked up on the first call on the device; NULL when the
+// lookup fails (the kernels then report nothing).
+uint32_t* status_word() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  uint32_t* p = g_status_addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  void* a = nullptr;
+  if (hipGetSymbolAddress(&a, HIP_SYMBOL(g_device_status)) != hipSuccess || a == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_status_addr[dev].store(static_cast<uint32_t*>(a), std::memory_order_release);
+  return static_cast<uint32_t*>(a);
+}
 
 thread_local std::string g_detail;
 
@@ -75,6 +103,7 @@ dsa_status check_cache(const dsa_cache_desc* c, int32_t layer, CacheView* cv) {
   cv->block_size = c->block_size;
   cv->log2_bs = ilog2(c->block_size);
   cv->latent_fmt = c->latent_fmt;
+  cv->status = status_word();
   return DSA_OK;
 }
 
@@ -152,6 +181,24 @@ const char* dsa_status_string(dsa_status s) {
 
 const char* dsa_last_error_detail(void) { return g_detail.c_str(); }
 
+dsa_status dsa_device_status(void* stream, int32_t clear, uint32_t* status) {
+  if (status == nullptr) return fail(DSA_ERR_NULL, "status is NULL");
+  uint32_t* p = status_word();
+  if (p == nullptr) return fail(DSA_ERR_HIP, "the device status word has no address on this device");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, p, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && clear) {
+    static const uint32_t zero = 0u;
+    e = hipMemcpyAsync(p, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+  }
+  if (e != hipSuccess) return hip_status(e, "device_status");
+  *status = v;
+  return ok();
+}
+
 int64_t dsa_decode_scores_ld(int32_t max_ctx) { return scores_ld(max_ctx); }
 
 size_t dsa_workspace_bytes(int32_t op, int32_t R, int32_t max_ctx, int32_t k) {
@@ -208,8 +255,10 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_c
   if (R == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   TopkWs tw = topk_ws_carve(workspace, R, max_ctx);
+  CacheView st{};  // no cache: carries only the status word
+  st.status = status_word();
   hipError_t e = launch_topk_send(scores, ld_scores, row_ctx, R, max_ctx, tw, s);
-  if (e == hipSuccess) e = launch_topk_select(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, nullptr, nullptr, nullptr, nullptr, s);
+  if (e == hipSuccess) e = launch_topk_select(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, nullptr, nullptr, &st, nullptr, s);
   return hip_status(e, "topk");
 }
 
@@ -325,6 +374,14 @@ dsa_status dsa_topk_dcp(const float* scores, int64_t ld_scores, const int32_t* r
   return hip_status(launch_topk_dcp(scores, ld_scores, row_ctx, R, max_ctx, k, W, idx, resend_mask, words, workspace,
                                     static_cast<hipStream_t>(stream)),
                     "topk_dcp");
+}
+
+dsa_status dsa_hbm_read_probe(const void* p, size_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+  if (p == nullptr || sink == nullptr) return fail(DSA_ERR_NULL, "buffer / sink is NULL");
+  if (!aligned16(p) || (bytes & 15u)) return fail(DSA_ERR_ALIGN, "buffer is not 16-byte aligned or bytes %% 16 != 0");
+  if (grid < 1 || grid > 65535) return fail(DSA_ERR_ARG, "grid %d out of [1, 65535]", grid);
+  if (bytes == 0) return ok();
+  return hip_status(launch_hbm_read(p, bytes, sink, grid, static_cast<hipStream_t>(stream)), "hbm_read_probe");
 }
 
 }  // extern "C"

@@ -74,7 +74,11 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __res
   // row's end still issues its (clamped, valid) loads and leaves after them
   const int seq = row_seq[r];
   int ctx = row_ctx[r];
-  ctx = ctx < 0 ? 0 : (ctx > rm.max_ctx ? rm.max_ctx : ctx);
+  if (ctx > rm.max_ctx) {
+    raise_status(cv.status, kStCtxClamped);
+    ctx = rm.max_ctx;
+  }
+  ctx = ctx < 0 ? 0 : ctx;
   const bool past = blockIdx.x * 256 >= ctx;  // whole workgroup
   ctx = ctx > 0 ? ctx : 1;
   const int tok0 = blockIdx.x * 256 + wid * 64;
@@ -98,6 +102,7 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __res
     const uint32_t nb = (uint32_t)cv.num_blocks;
     const uint32_t b0 = e0 < nb ? e0 : ((int32_t)e0 < 0 ? 0u : nb - 1u);
     const uint32_t b1 = e1 < nb ? e1 : ((int32_t)e1 < 0 ? 0u : nb - 1u);
+    if (e0 >= nb || e1 >= nb) raise_status(cv.status, kStBlockClamped);
     toff[0] = (int64_t)b0 * cv.row_bytes + cv.idx_off;
     toff[1] = (int64_t)b1 * cv.row_bytes + cv.idx_off;
   }

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
   // the group's longest row decides which tiles exist
   int gmax = 0;
   for (int r = r0; r < r1; ++r) {
-    const int c = row_len(rm, r);
+    const int c = row_len(rm, r, cv.status);
     gmax = c > gmax ? c : gmax;
   }
   if (blockIdx.x * 256 >= gmax) return;  // whole workgroup
@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
       const uint32_t nb = (uint32_t)cv.num_blocks;
       const uint32_t b0 = e0 < nb ? e0 : ((int32_t)e0 < 0 ? 0u : nb - 1u);
       const uint32_t b1 = e1 < nb ? e1 : ((int32_t)e1 < 0 ? 0u : nb - 1u);
+      if (e0 >= nb || e1 >= nb) raise_status(cv.status, kStBlockClamped);
       toff[0] = (int64_t)b0 * cv.row_bytes + cv.idx_off;
       toff[1] = (int64_t)b1 * cv.row_bytes + cv.idx_off;
     }
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     else if (r + 1 < r1)  // uniform
       q_frag(r + 1, qn);
     const int seq = rm.row_seq[r];
-    const int ctx = row_len(rm, r);
+    const int ctx = row_len(rm, r, cv.status);
     if (seq != seq_cur) {  // uniform
       load_keys(seq);
       seq_cur = seq;

@@ -161,4 +161,7 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
 hipError_t launch_topk_dcp(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k, int W,
                            int32_t* idx, uint32_t* resend_mask, uint32_t* words, void* ws, hipStream_t stream);
 
+// One streaming read of [p, p + bytes) (bytes a multiple of 16) by `grid` workgroups.
+hipError_t launch_hbm_read(const void* p, size_t bytes, uint32_t* sink, int grid, hipStream_t stream);
+
 }  // namespace dsa

@@ -188,6 +188,7 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   float sv = 0.f;
   bool tv = false;  // the gathered slot holds a token
   auto issue = [&]() {
+    if (t_n >= rm.max_ctx) raise_status(cv.status, kStIndexRange);
     const int t = t_n < rm.max_ctx ? t_n : -1;
     const int tc = t >= 0 ? t : 0;  // every load below stays in the pool; empty slots are masked
     int64_t blk;

@@ -59,10 +59,15 @@ constexpr int BTCAP = 4096;          // block-table entries of a row staged in L
 static_assert(PER * SEL_NT == kCandRowCap && PER * SEL_NT == kTopkFullRow, "register tiling");
 static_assert(NBIN == 2 * SEL_NT, "two histogram bins per thread");
 
-__device__ __forceinline__ int clamp_ctx(const int32_t* row_ctx, int r, int max_ctx) {
+// Row length clamped to [0, max_ctx]; a clamp from above is reported in `st`.
+__device__ __forceinline__ int clamp_ctx(const int32_t* row_ctx, int r, int max_ctx, uint32_t* st) {
   int c = row_ctx[r];
   c = c < 0 ? 0 : c;
-  return c > max_ctx ? max_ctx : c;
+  if (c > max_ctx) {
+    raise_status(st, kStCtxClamped);
+    c = max_ctx;
+  }
+  return c;
 }
 
 struct SelShared {
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(256) void topk_send_kernel(const float* __restrict_
                                                         TopkWs ws) {
   __shared__ uint32_t send_lds[68];
   const int r = blockIdx.y;
-  const int ctx = clamp_ctx(row_ctx, r, max_ctx);
+  const int ctx = clamp_ctx(row_ctx, r, max_ctx, nullptr);  // the select reports it
   const int base = blockIdx.x * 256;
   if (base >= ctx) return;  // whole workgroup
   const int t = base + threadIdx.x;
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
 #pragma unroll
     for (int j = 0; j < 4; ++j) fl[j] = rf[tid + SEL_NT * j];
   }
-  const int ctx = clamp_ctx(row_ctx, r, max_ctx);
+  const int ctx = clamp_ctx(row_ctx, r, max_ctx, cv.status);
   const int seq = rm.row_seq[r];  // the launch points row_seq at row_ctx when there are no page slots
   int32_t* orow = idx + (int64_t)r * k;
   int32_t* prow = phys ? phys + (int64_t)r * k : nullptr;
@@ -558,7 +563,10 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
       const int i = tid + SEL_NT * q;
       int64_t b = bv[q];
-      if ((uint64_t)b >= (uint64_t)nb) b = b < 0 ? 0 : nb - 1;
+      if (i < nblk && (uint64_t)b >= (uint64_t)nb) {
+        raise_status(cv.status, kStBlockClamped);
+        b = b < 0 ? 0 : nb - 1;
+      }
       if (i < nblk) S.bt[i] = (int32_t)b;
     }
   };
@@ -817,10 +825,8 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* ro
   if (R <= 0) return hipSuccess;
   CacheView c{};
   RowMap m{};
-  if (phys) {
-    c = *cv;
-    m = *rm;
-  }
+  if (cv) c = *cv;  // without page slots only its status word is used
+  if (phys) m = *rm;
   if (!phys) m.row_seq = row_ctx;  // read, never used
   if (max_ctx > kTopkFullRow)
     hipLaunchKernelGGL(topk_select_kernel<true>, dim3(R), dim3(SEL_NT), 0, stream, ws.cand_hi, ws.cand_lo, ws.floors,

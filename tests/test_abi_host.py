@@ -109,6 +109,18 @@ def test_null_descriptor(lib):
     assert _score(lib, None) == 1
 
 
+def test_device_status_rejects_null(lib):
+    assert lib.dsa_device_status(None, 1, None) == 1
+    assert "status" in lib.dsa_last_error_detail().decode()
+
+
+def test_hbm_read_probe_rejects_bad_arguments(lib):
+    assert lib.dsa_hbm_read_probe(None, 1024, FAKE, 64, None) == 1      # NULL buffer
+    assert lib.dsa_hbm_read_probe(FAKE, 1000, FAKE, 64, None) == 5      # bytes % 16
+    assert lib.dsa_hbm_read_probe(FAKE, 1024, FAKE, 0, None) == 2       # grid < 1
+    assert lib.dsa_hbm_read_probe(FAKE, 0, FAKE, 64, None) == 0         # nothing to read, no launch
+
+
 def test_topk_and_mla_reject_bad_arguments(lib):
     ws = dsa.dsa_workspace_bytes(dsa.DSA_OP_TOPK, 1, 8192, 2048)
     assert lib.dsa_topk(FAKE, 8192, FAKE, 1, 8192, 0, FAKE, FAKE, ws, None) == 2          # k = 0

@@ -324,6 +324,68 @@ def test_out_of_range_block_ids_do_not_fault(dev):
     assert np.all(np.isfinite(scores[0, :3000])) and np.all(np.isfinite(out))
 
 
+def test_device_status_word(dev):
+    """Repairs of bad data are reported in the device status word, and only then: a
+    clean step leaves it at 0; a corrupt block table, a row_ctx above max_ctx (which
+    then behaves as a row of max_ctx tokens), an MLA index past the block table
+    (skipped like -1) and an append into a block outside the pool each set their bit."""
+    say("case: device status word")
+    dsa.dsa_device_status(clear=True)
+    c = make_case([3000, 5000], block_size=64, seed=6, k=256, spare_blocks=1).to(dev)
+    ref = run_step(c, dev)
+    assert dsa.dsa_device_status(clear=True) == 0
+
+    bt = c.block_table.clone()
+    bt[0, 3] = 10 ** 6
+    c_bad = type(c)(c.name, c.layout, c.pool, bt, c.row_seq, c.row_ctx, c.q_idx, c.q_idx_scale, c.w, c.q_lat, c.k,
+                    c.sm_scale)
+    run_step(c_bad, dev)
+    assert dsa.dsa_device_status(clear=True) == dsa.DSA_DEV_BLOCK_CLAMPED
+    assert dsa.dsa_device_status(clear=False) == 0
+
+    # row 1 claims 5000 tokens but the call's bound is 4000: it is scored as 4000 tokens
+    say("  row_ctx above max_ctx")
+    lim = 4000
+    idx, out, lse, _ = dsa.dsa_decode_step(c.pool, c.layout, 0, c.q_idx[0], c.q_idx_scale[0], c.w[0], c.q_lat[0],
+                                           c.block_table, c.row_seq, c.row_ctx, lim, c.k, c.sm_scale)
+    assert dsa.dsa_device_status(clear=True) == dsa.DSA_DEV_CTX_CLAMPED
+    short = c.row_ctx.clone()
+    short[1] = lim
+    idx2, out2, lse2, _ = dsa.dsa_decode_step(c.pool, c.layout, 0, c.q_idx[0], c.q_idx_scale[0], c.w[0], c.q_lat[0],
+                                              c.block_table, c.row_seq, short, lim, c.k, c.sm_scale)
+    assert dsa.dsa_device_status(clear=True) == 0
+    assert torch.equal(idx, idx2) and torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert np.array_equal(idx.cpu().numpy()[0], ref[1][0])
+
+    say("  standalone top-k, row_ctx above max_ctx")
+    sc = torch.tensor(ref[0], device=dev)
+    dsa.dsa_topk(sc, c.row_ctx, lim, c.k)
+    assert dsa.dsa_device_status(clear=True) == dsa.DSA_DEV_CTX_CLAMPED
+
+    say("  sparse MLA index past the block table")
+    cap = c.block_table.shape[1] * c.layout.block_size
+    sel = torch.tensor(ref[1], device=dev)
+    bad = sel.clone()
+    bad[0, 5] = cap + 3
+    skip = sel.clone()
+    skip[0, 5] = -1
+    o1, l1 = dsa.dsa_sparse_mla(c.pool, c.layout, 0, c.q_lat[0], c.block_table, c.row_seq, bad, c.k, c.sm_scale)
+    assert dsa.dsa_device_status(clear=True) == dsa.DSA_DEV_INDEX_RANGE
+    o2, l2 = dsa.dsa_sparse_mla(c.pool, c.layout, 0, c.q_lat[0], c.block_table, c.row_seq, skip, c.k, c.sm_scale)
+    assert dsa.dsa_device_status(clear=True) == 0
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+    say("  cache append into a block outside the pool")
+    before = c.pool.clone()
+    pos = c.row_ctx.clone()
+    bt2 = c.block_table.clone()
+    bt2[:, pos[0].item() // c.layout.block_size] = -5
+    bt2[1, pos[1].item() // c.layout.block_size] = 10 ** 6
+    dsa.dsa_cache_append(c.pool, c.layout, 0, bt2, c.row_seq, pos, latent=torch.ones((2, 576), device=dev))
+    assert dsa.dsa_device_status(clear=True) == dsa.DSA_DEV_BLOCK_CLAMPED
+    assert torch.equal(before, c.pool)
+
+
 def test_select_paths_mixed_batch(dev):
     """One batch whose rows take every selection path: ctx <= k, whole row in LDS
     (<= 16384), and block candidates with rescans (> 16384)."""
