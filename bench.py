@@ -51,6 +51,9 @@ def parse():
                    help="instead of the decode step, time the exact top-k merge of decode context parallelism "
                         "emulated over W token-strided shards, beside the plain top-k, on the indexer's scores")
     p.add_argument("--cpu-layers", type=int, default=4, help="layer-steps the CPU oracle runs for cpu_baseline")
+    p.add_argument("--cpu-configs", action="store_true",
+                   help="only time the CPU oracle on bounded samples of the other workloads (8K, batch 16, 1M, "
+                        "prefill-append, batch-64 MXFP4) and print one JSON line")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a 1 GiB device copy (for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
@@ -110,6 +113,92 @@ def cpu_baseline(case, layers, k):
                        f"full indexer + top-{k} + sparse MLA per layer (float64 numpy, BLAS threads={threads})")
 
 
+def host_info():
+    """CPU model, usable cores and the BLAS numpy calls (threadpoolctl)."""
+    import os
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{k: i.get(k) for k in ("internal_api", "num_threads", "version")} for i in threadpool_info()]
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "cores_usable": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+def oracle_rows_seconds(case, layer, rows, k):
+    """Wall seconds of the CPU oracle (full indexer + top-k + sparse MLA) on each row of
+    `rows` of one layer; only that layer's pages are copied to the host."""
+    import numpy as np
+    import torch
+    from oracle import dsa_oracle as O
+    lay = case.layout
+    lo = lay.lat_off[layer]
+    hi = lay.idx_off[layer] + lay.index_page_bytes
+    pool = case.pool[:, lo:hi].cpu().numpy()
+    sub = dict(block_size=lay.block_size, index_fmt=lay.index_fmt, latent_fmt=lay.latent_fmt, row_bytes=hi - lo,
+               lat_off=[0], idx_off=[lay.idx_off[layer] - lo])
+    bt = case.block_table.cpu().numpy()
+    seq = case.row_seq.cpu().numpy()
+    ctxs = case.row_ctx.cpu().numpy()
+    q_lat = case.q_lat[layer].cpu().view(torch.int16).numpy().view(np.uint16)
+    q_idx = case.q_idx[layer].cpu().numpy()
+    q_sc = case.q_idx_scale[layer].cpu().numpy()
+    w = case.w[layer].cpu().numpy()
+    secs = []
+    for r in rows:
+        t0 = time.perf_counter()
+        O.decode_row(pool, sub, 0, bt[seq[r]], int(ctxs[r]), q_idx[r], q_sc[r], w[r], q_lat[r], k, case.sm_scale)
+        secs.append(time.perf_counter() - t0)
+    return secs
+
+
+def cpu_configs(dev):
+    """The oracle timed on bounded samples of the other workloads. Rows not timed are
+    extrapolated in proportion to their context length (the oracle's work is the
+    indexer over ctx tokens plus a top-k and attention that vary little)."""
+    import torch
+    from synth import config_small, config_batch16, config_long_1m, config_prefill_append, config_mixed_mxfp4
+    res = {"host": host_info(), "configs": []}
+    plans = [
+        ("decode, batch 1, 8,192 tokens, bs 64, FP8 keys", lambda: config_small(device=dev), None),
+        ("decode, batch 16, U[16384, 65536] tokens, bs 64, FP8 keys", lambda: config_batch16(device=dev), 4),
+        ("decode, batch 1, 1,048,576 tokens (2,048 planted), bs 64, FP8 keys", lambda: config_long_1m(device=dev),
+         None),
+        ("prefill-append, 2,048 rows on a 150,000-token prefix, bs 64, FP8 keys",
+         lambda: config_prefill_append(device=dev), 4),
+        ("decode, batch 64, log-uniform [4096, 262144] tokens, bs 128, MXFP4 keys (one of 24 layers)",
+         lambda: config_mixed_mxfp4(device=dev, num_layers=1), 4),
+    ]
+    for name, build, nsample in plans:
+        case = build()
+        if case.pool.is_cuda:
+            torch.cuda.synchronize()
+        R = case.num_rows
+        ctxs = [int(c) for c in case.row_ctx.tolist()]
+        rows = list(range(R)) if nsample is None or nsample >= R else \
+            sorted(set(int(round(i * (R - 1) / (nsample - 1))) for i in range(nsample)))
+        secs = oracle_rows_seconds(case, 0, rows, K)
+        t_sample = sum(secs)
+        t_all = t_sample * sum(ctxs) / max(1, sum(ctxs[r] for r in rows))
+        res["configs"].append({
+            "workload": name, "rows": R, "rows_timed": rows, "seconds_timed": round(t_sample, 3),
+            "seconds_per_layer_step": round(t_all, 3), "layer_steps_per_s": round(1.0 / t_all, 4),
+            "extrapolated": len(rows) < R})
+        print(f"cpu oracle: {name}: {t_all:.3f} s per layer-step", file=sys.stderr, flush=True)
+        del case
+        if torch.cuda.is_available():
+            torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
 def timed_indexer_us(dsa, case, layers, max_ctx, reps):
     """Average duration of the scoring kernel alone (dsa_indexer_score): a HIP graph
     holds one launch per layer back to back, and the graph is replayed `reps` times
@@ -147,7 +236,7 @@ def timed_indexer_us(dsa, case, layers, max_ctx, reps):
     return 1000.0 * e0.elapsed_time(e1) / (reps * layers)
 
 
-def hbm_read_ceiling(dsa, buf, reps=3, grids=(512, 1024, 2048, 4096)):
+def hbm_read_ceiling(dsa, buf, reps=3, grids=(256, 512, 1024, 2048, 4096)):
     """Streaming-read rate (GB/s) of dsa_hbm_read_probe over the whole tensor `buf`, at a
     few grid sizes: per grid the median of `reps` launches, each timed alone with
     events; the best grid's median is the ceiling."""
@@ -261,6 +350,8 @@ def main():
 
     dev = torch.device("cuda:0")
     dsa.load_library()
+    if a.cpu_configs:
+        return cpu_configs(dev)
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
