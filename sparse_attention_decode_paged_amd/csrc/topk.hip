@@ -183,27 +183,6 @@ __device__ __forceinline__ void block_minmax32(uint32_t& lo, uint32_t& hi, SelSh
   par ^= 1;
 }
 
-// Sorts up to 64 keys (one per lane, 0 = empty) in descending order across the wave.
-__device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int kk = 2; kk <= 64; kk <<= 1) {
-#pragma unroll
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      uint64_t o;
-      if (j == 32) o = xshfl64<32>(v);
-      else if (j == 16) o = xshfl64<16>(v);
-      else if (j == 8) o = xshfl64<8>(v);
-      else if (j == 4) o = xshfl64<4>(v);
-      else if (j == 2) o = xshfl64<2>(v);
-      else o = xshfl64<1>(v);
-      const bool take_max = ((lane & kk) == 0) == ((lane & j) == 0);
-      v = take_max ? (v > o ? v : o) : (v < o ? v : o);
-    }
-  }
-  return v;
-}
-
 // The need-th largest (1 <= need <= number of live keys) of the nonzero keys in
 // kh[]/kl[] and, with EXTRA, in xs[0, nx) (LDS, thread t reading xs[t + SEL_NT j]), held
 // across the workgroup. Keys are distinct.
@@ -215,10 +194,16 @@ __device__ __forceinline__ void clear_hist(SelShared& S) {
 
 // Register keys come as score words kh[] and token words kl[] (key = kh << 32 | kl;
 // kh == 0 marks an empty slot: no finite score maps to 0). The passes read only the
-// score words, so the token words may still be in flight until the bucket stage.
-template <int N, bool EXTRA>
+// score words, so the token words may still be in flight until the bucket stage:
+// `late()` runs once, after the first histogram pass (or before the bucket stage when
+// no pass runs), where the caller issues the loads that only later stages need (the
+// token words among them): they then neither compete with the score words for the
+// workgroup's load bandwidth nor stall the min / max and histogram phases, and arrive
+// while the digit scan runs. PRECLEARED: the caller has already zeroed the histogram
+// and the bucket count (before its first barrier).
+template <int N, bool EXTRA, bool PRECLEARED = false, typename Late>
 __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const uint32_t (&kl)[N], const uint64_t* xs,
-                                                uint32_t nx, uint32_t need, SelShared& S, int& par) {
+                                                uint32_t nx, uint32_t need, SelShared& S, int& par, Late&& late) {
   const int tid = threadIdx.x, lane = tid & 63;
   // fn(score word, token word) over the register keys, then (only when the LDS list
   // is not empty, a uniform branch) over xs[tid + SEL_NT x], x < XPER
@@ -234,8 +219,10 @@ __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const u
       }
     }
   };
-  if (tid == 0) S.bcount = 0u;  // the bucket gather is ordered after this by the barriers below
-  clear_hist(S);                // ordered before the first pass by the min / max barrier
+  if (!PRECLEARED) {
+    if (tid == 0) S.bcount = 0u;  // the bucket gather is ordered after this by the barriers below
+    clear_hist(S);                // ordered before the first pass by the min / max barrier
+  }
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   for_keys([&](uint32_t w, uint32_t) {
     if (w != 0u) {
@@ -257,6 +244,7 @@ __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const u
     const int width = top + 1 < HBITS ? top + 1 : HBITS;
     const int sh = top + 1 - width;
     const uint32_t dm = (1u << width) - 1u;
+    const bool pass0 = first;
     if (!first) {
       clear_hist(S);
       __syncthreads();
@@ -267,6 +255,7 @@ __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const u
       if (w != 0u && (w & mask) == prefix) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
     });
     __syncthreads();
+    if (pass0) late();
     // thread t holds bins NBIN-1-2t (upper) and NBIN-2-2t: thread order = descending digits
     uint32_t h0, h1;
     {
@@ -297,6 +286,7 @@ __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const u
     top = sh - 1;
     if (cnt <= 64u) break;
   }
+  if (first) late();  // no histogram pass ran
   // the bucket: live keys whose score word matches; need-th largest among them
   if (top < 0 && cnt == 0u) {
     // no pass ran (one score word): count the bucket
@@ -311,14 +301,20 @@ __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const u
       if (w != 0u && (w & mask) == prefix) S.bucket[atomicAdd(&S.bcount, 1u) & 63u] = ((uint64_t)w << 32) | l;
     });
     __syncthreads();
-    if (tid < 64) {  // one wave resolves the bucket
+    // The bucket's keys are distinct, so the need-th largest is the one with exactly
+    // need - 1 larger keys. Wave w ranks bucket keys 4 w .. 4 w + 3 (one compare per
+    // lane against every bucket key and a ballot each), all waves at once.
+    {
+      const int wid = tid >> 6;
       const uint64_t v = (uint32_t)lane < cnt ? S.bucket[lane] : 0ull;
-      if (need == cnt) {  // every bucket key is selected: the threshold is the smallest
-        const uint64_t mn = wave_min_u64((uint32_t)lane < cnt ? v : ~0ull);
-        if (lane == 0) S.res64 = mn;
-      } else {
-        const uint64_t sorted = wave_sort_desc_u64(v);
-        if (lane == (int)need - 1) S.res64 = sorted;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t j = 4u * (uint32_t)wid + (uint32_t)q;
+        if (j < cnt) {  // uniform
+          const uint64_t pj = S.bucket[j];
+          const uint32_t rank = (uint32_t)__popcll(__ballot(v > pj));
+          if (rank == need - 1u && lane == 0) S.res64 = pj;
+        }
       }
     }
     __syncthreads();
@@ -506,22 +502,17 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
   const TopkWs ws{const_cast<uint32_t*>(cand_hi), const_cast<uint32_t*>(cand_lo), const_cast<uint32_t*>(floors)};
   __shared__ SelShared S;
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  // candidate slots and unit floors first: their addresses need only the kernel
-  // arguments, so they load alongside the row's length (slots the row's plan does not
-  // use are cleared once the length is known)
-  // score words first (the passes need only them), then token words and floors
+  // The candidates' score words load first, alone: their addresses need only the kernel
+  // arguments, so they go out with the row's length (slots the row's plan does not use
+  // are cleared once the length is known), and the first search needs nothing else. The
+  // token words, unit floors and block-table entries are issued after the search's first
+  // histogram pass, so that one workgroup's load bandwidth goes to the score words first.
   uint32_t kh[PER], kl[PER];
   uint32_t fl[4] = {0u, 0u, 0u, 0u};
   if (CAND) {
     const uint32_t* ch = ws.cand_hi + (int64_t)r * kCandRowCap;
 #pragma unroll
     for (int i = 0; i < PER; ++i) kh[i] = ch[i * SEL_NT + tid];
-    const uint32_t* cl = ws.cand_lo + (int64_t)r * kCandRowCap;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) kl[i] = cl[i * SEL_NT + tid];
-    const uint32_t* rf = ws.floors + (int64_t)r * kFloorRowCap;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fl[j] = rf[tid + SEL_NT * j];
   }
   const int ctx = clamp_ctx(row_ctx, r, max_ctx, cv.status);
   const int seq = rm.row_seq[r];  // the launch points row_seq at row_ctx when there are no page slots
@@ -545,14 +536,16 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
   const int nblk = (ctx + cv.block_size - 1) >> cv.log2_bs;
   const bool btl = prow != nullptr && nblk <= BTCAP;
   int32_t bv[BTCAP / SEL_NT];
-  if (btl) {
+  auto load_bt = [&]() {
+    if (!btl) return;
     const int32_t* btr = rm.block_table + (int64_t)seq * rm.bt_stride;
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
       const int i = tid + SEL_NT * q;
       bv[q] = i < nblk ? btr[i] : 0;
     }
-  }
+  };
+  if (!CAND) load_bt();
   // The entries reach LDS after the first search: they sit one scalar round trip
   // further down the load chain than the candidates, and a store waiting for them
   // ahead of the search's first barrier would hold every wave.
@@ -607,7 +600,7 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
   uint64_t cstar;
   if (!CAND) {
     load_own();
-    cstar = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par);
+    cstar = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par, [] {});
     stage_bt();
   } else {
     const CandPlan p = cand_plan(ctx);
@@ -618,13 +611,28 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (j < upt && tid + SEL_NT * j < p.nu) umine |= 1u << j;
+    // the search's histogram and bucket count are cleared while the score words are in
+    // flight (ordered before the first pass by the search's first barrier)
+    if (tid == 0) S.bcount = 0u;
+    clear_hist(S);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if (!((umine >> (i >> lm)) & 1u)) kh[i] = 0u;
+    auto late = [&]() {
+      const uint32_t* cl = ws.cand_lo + (int64_t)r * kCandRowCap;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) kl[i] = cl[i * SEL_NT + tid];
+      const uint32_t* rf = ws.floors + (int64_t)r * kFloorRowCap;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < upt) fl[j] = rf[tid + SEL_NT * j];
+      load_bt();
+    };
     // The first search comes before the short-row exits so that nothing between the
     // kernel's start and the first use of the candidates is a branch (a branch lets
     // the compiler sink the loads behind the row-length round trip).
-    const uint64_t c1 = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par);
+    const uint64_t c1 = kth_largest<PER, false, true>(kh, kl, nullptr, 0u, (uint32_t)k, S, par, late);
     if (ctx <= k) {
       write_all();
       return;
@@ -741,7 +749,7 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
         const bool flagged = (fmask >> (i >> lm)) & 1u;
         if (flagged || (((uint64_t)kh[i] << 32) | kl[i]) < cu) kh[i] = 0u;
       }
-      cstar = kth_largest<PER, true>(kh, kl, S.a.ext, ne, (uint32_t)k, S, par);
+      cstar = kth_largest<PER, true>(kh, kl, S.a.ext, ne, (uint32_t)k, S, par, [] {});
       // selected keys of each rescanned unit
       for (uint32_t sl = wid; sl < nflag; sl += NW) {
         const uint32_t st = S.fstart[sl], len = S.flen[sl];
