@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode layer-steps/sec + achieved HBM GB/s (% of peak) at 256K ctx"
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix peak (the indexer's contraction runs in bf16)
 CTX = 262144
 LAYERS = 24
 K = 2048
@@ -51,6 +52,12 @@ def parse():
                    help="instead of the decode step, time the exact top-k merge of decode context parallelism "
                         "emulated over W token-strided shards, beside the plain top-k, on the indexer's scores")
     p.add_argument("--cpu-layers", type=int, default=4, help="layer-steps the CPU oracle runs for cpu_baseline")
+    p.add_argument("--config", choices=["headline", "small", "batch16", "long1m", "prefill", "mixed_mxfp4"],
+                   default="headline",
+                   help="workload: headline (batch x ctx from --batch/--ctx/--layers, the default), or one of the "
+                        "other measured workloads: small (1 x 8,192), batch16 (16 rows, 16K-64K), long1m (1 x 1M, "
+                        "2,048 planted keys, 2 layers), prefill (2,048 rows on a 150,000-token prefix), mixed_mxfp4 "
+                        "(64 rows, 4K-256K log-uniform, bs 128, MXFP4 keys, 24 layers)")
     p.add_argument("--cpu-configs", action="store_true",
                    help="only time the CPU oracle on bounded samples of the other workloads (8K, batch 16, 1M, "
                         "prefill-append, batch-64 MXFP4) and print one JSON line")
@@ -199,10 +206,12 @@ def cpu_configs(dev):
     print(json.dumps(res), flush=True)
 
 
-def timed_indexer_us(dsa, case, layers, max_ctx, reps):
+def timed_indexer_us(dsa, case, layers, max_ctx, reps, rows_per_seq=1, per_graph=None):
     """Average duration of the scoring kernel alone (dsa_indexer_score): a HIP graph
-    holds one launch per layer back to back, and the graph is replayed `reps` times
-    between one pair of events, so no host launch cost falls inside the timing."""
+    holds `per_graph` launches back to back (rotating over the layers), and the graph
+    is replayed `reps` times between one pair of events, so no host launch cost falls
+    inside the timing."""
+    per_graph = per_graph or layers
     import torch
     R = case.num_rows
     dev = case.pool.device
@@ -210,7 +219,8 @@ def timed_indexer_us(dsa, case, layers, max_ctx, reps):
 
     def launch(l):
         dsa.dsa_indexer_score(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l],
-                              case.block_table, case.row_seq, case.row_ctx, max_ctx, scores=scores)
+                              case.block_table, case.row_seq, case.row_ctx, max_ctx, scores=scores,
+                              rows_per_seq=rows_per_seq)
 
     cap = torch.cuda.Stream(dev)
     cap.wait_stream(torch.cuda.current_stream(dev))
@@ -220,8 +230,8 @@ def timed_indexer_us(dsa, case, layers, max_ctx, reps):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):
-        for l in range(layers):
-            launch(l)
+        for l in range(per_graph):
+            launch(l % layers)
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
@@ -233,7 +243,7 @@ def timed_indexer_us(dsa, case, layers, max_ctx, reps):
         g.replay()
     e1.record(stream)
     torch.cuda.synchronize()
-    return 1000.0 * e0.elapsed_time(e1) / (reps * layers)
+    return 1000.0 * e0.elapsed_time(e1) / (reps * per_graph)
 
 
 def hbm_read_ceiling(dsa, buf, reps=3, grids=(256, 512, 1024, 2048, 4096)):
@@ -337,6 +347,39 @@ def bench_dcp(a, dsa, case, dev):
     }), flush=True)
 
 
+def build_workload(a, dev):
+    """The synthetic case of the chosen workload, its rows_per_seq hint and its name."""
+    from synth import (make_case, config_small, config_batch16, config_prefill_append, config_mixed_mxfp4)
+    if a.config == "headline":
+        key_desc = "FP8 index keys (132 B/token)" if a.index_fmt == "fp8" else "MXFP4 index keys (68 B/token)"
+        lat_desc = ("FP8 latents (576 B + fp32 scale)" if a.latent_fmt == "fp8"
+                    else "NVFP4 latents (352 B + fp32 scale)")
+        case = make_case([a.ctx] * a.batch, block_size=a.block_size, num_layers=a.layers, seed=a.seed, device=dev,
+                         k=K, index_fmt=a.index_fmt, latent_fmt=a.latent_fmt,
+                         name="decode_b%d_ctx%d_x%dlayers" % (a.batch, a.ctx, a.layers))
+        return case, 1, (f"DSA decode, batch {a.batch}, context {a.ctx} tokens, top-{K}, block size {a.block_size}, "
+                         f"{key_desc} and {lat_desc}, {a.layers} independent layers rotated")
+    if a.config == "small":
+        return (config_small(seed=a.seed, device=dev), 1,
+                "DSA decode, batch 1, context 8,192 tokens, top-2048, block size 64, FP8 keys and latents, one layer")
+    if a.config == "batch16":
+        return (config_batch16(seed=a.seed, device=dev), 1,
+                "DSA decode, batch 16, contexts uniform on [16,384, 65,536], pages shuffled in one pool, top-2048, "
+                "block size 64, FP8 keys and latents, one layer")
+    if a.config == "long1m":
+        case = make_case([1 << 20], block_size=64, num_layers=2, seed=a.seed, device=dev, plant=2048,
+                         name="decode_b1_ctx1m_planted_x2layers")
+        return (case, 1, "DSA decode, batch 1, context 1,048,576 tokens with 2,048 planted keys, top-2048, block "
+                         "size 64, FP8 keys and latents, 2 independent layers rotated")
+    if a.config == "prefill":
+        return (config_prefill_append(seed=a.seed, device=dev), 2048,
+                "DSA prefill-append, 2,048 query rows on a 150,000-token prefix (row r sees tokens <= 150,000 + r), "
+                "top-2048 per row, block size 64, FP8 keys and latents, one layer")
+    return (config_mixed_mxfp4(seed=a.seed, device=dev), 1,
+            "DSA decode, batch 64, contexts log-uniform on [4,096, 262,144], top-2048, block size 128, MXFP4 index "
+            "keys and FP8 latents, 24 layers in one packed row, rotated")
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -362,11 +405,11 @@ def main():
         return
 
     t0 = time.time()
-    case = make_case([a.ctx] * a.batch, block_size=a.block_size, num_layers=a.layers, seed=a.seed, device=dev, k=K,
-                     index_fmt=a.index_fmt, latent_fmt=a.latent_fmt,
-                     name="decode_b%d_ctx%d_x%dlayers" % (a.batch, a.ctx, a.layers))
+    case, rows_per_seq, workload = build_workload(a, dev)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
+    a.layers = case.layout.num_layers
+    a.index_fmt, a.latent_fmt, a.block_size = case.layout.index_fmt, case.layout.latent_fmt, case.layout.block_size
     R, max_ctx = case.num_rows, case.max_ctx
     if a.dcp:
         return bench_dcp(a, dsa, case, dev)
@@ -379,11 +422,13 @@ def main():
         l = i % a.layers
         dsa.dsa_decode_step(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l], case.q_lat[l],
                             case.block_table, case.row_seq, case.row_ctx, max_ctx, K, case.sm_scale,
-                            idx=idx, out=out, lse=lse, workspace=ws)
+                            idx=idx, out=out, lse=lse, workspace=ws, rows_per_seq=rows_per_seq)
 
-    # Steps run from HIP graphs: one graph holds one step per layer (the rotation), and
+    # Steps run from HIP graphs: one graph holds G steps (the layer rotation, repeated up
+    # to at least 24 steps so that one replay's launch cost is spread thin), and
     # single-step graphs cover a remainder, so exactly `steps` layer-steps are timed
     # with no host launch cost inside the timed region.
+    G = a.layers * -(-24 // a.layers)
     cap = torch.cuda.Stream(dev)
     cap.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(cap):
@@ -392,9 +437,9 @@ def main():
     torch.cuda.synchronize()
     g_all = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_all, stream=cap):
-        for i in range(a.layers):
+        for i in range(G):
             step(i)
-    rem = a.steps % a.layers
+    rem = a.steps % G
     g_rem = []
     for i in range(rem):
         g = torch.cuda.CUDAGraph()
@@ -404,12 +449,12 @@ def main():
     torch.cuda.synchronize()
 
     def run(nsteps):
-        for _ in range(nsteps // a.layers):
+        for _ in range(nsteps // G):
             g_all.replay()
-        for g in g_rem[: nsteps % a.layers]:
+        for g in g_rem[: nsteps % G]:
             g.replay()
 
-    run(max(a.warmup, a.layers))
+    run(max(a.warmup, G))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -421,29 +466,40 @@ def main():
     ms = e0.elapsed_time(e1) / a.steps
 
     # spread: each replay of the layer-rotation graph timed alone
-    nrep = max(5, min(100, a.steps // a.layers))
+    nrep = max(5, min(100, a.steps // G))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
     ev[0].record(stream)
     for i in range(nrep):
         g_all.replay()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    per = sorted(1000.0 * ev[i].elapsed_time(ev[i + 1]) / a.layers for i in range(nrep))
+    per = sorted(1000.0 * ev[i].elapsed_time(ev[i + 1]) / G for i in range(nrep))
     spread = {"p10": round(per[int(0.1 * (nrep - 1))], 3), "p50": round(per[(nrep - 1) // 2], 3),
-              "p90": round(per[int(0.9 * (nrep - 1))], 3), "replays": nrep, "steps_per_replay": a.layers}
-    ceiling = hbm_read_ceiling(dsa, case.pool)
+              "p90": round(per[int(0.9 * (nrep - 1))], 3), "replays": nrep, "steps_per_replay": G}
+    # the read ceiling needs a buffer far beyond the 256 MB last-level cache
+    pool_bytes = case.pool.numel() * case.pool.element_size()
+    ceiling = hbm_read_ceiling(dsa, case.pool) if pool_bytes >= (1 << 30) else None
 
-    ix_us = timed_indexer_us(dsa, case, a.layers, max_ctx, max(2, min(a.steps, 480) // a.layers))
+    ix_us = timed_indexer_us(dsa, case, a.layers, max_ctx, max(2, min(a.steps, 480) // G), rows_per_seq, G)
 
     ctxs = [int(c) for c in case.row_ctx.tolist()]
-    step_bytes = A.layer_step_bytes(ctxs, K, a.index_fmt, a.latent_fmt)
-    ix_bytes = sum(A.indexer_bytes(c, a.index_fmt) for c in ctxs)
-    ix_gbps = ix_bytes / (ix_us * 1e-6) / 1e9
-    step_gbps = step_bytes / (ms * 1e-3) / 1e9
-    traffic = traffic_for(INDEXER_SRC) if a.index_fmt == "fp8" else None
-    key_desc = "FP8 index keys (132 B/token)" if a.index_fmt == "fp8" else "MXFP4 index keys (68 B/token)"
-    lat_desc = ("FP8 latents (576 B + fp32 scale)" if a.latent_fmt == "fp8"
-                else "NVFP4 latents (352 B + fp32 scale)")
+    if rows_per_seq > 1:
+        # rows share one sequence's keys: bytes are not the bound, the contraction is
+        step_bytes = None
+        ix_flops = A.indexer_flops(ctxs)
+        roof = {"bound": "mfma", "achieved": round(ix_flops / (ix_us * 1e-6) / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ix_flops / (ix_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "algorithmic_flops_per_launch": ix_flops}
+    else:
+        step_bytes = A.layer_step_bytes(ctxs, K, a.index_fmt, a.latent_fmt)
+        ix_bytes = sum(A.indexer_bytes(c, a.index_fmt) for c in ctxs)
+        ix_gbps = ix_bytes / (ix_us * 1e-6) / 1e9
+        traffic = (traffic_for(INDEXER_SRC) if a.index_fmt == "fp8" and a.config == "headline" and a.batch == 1
+                   and a.ctx == CTX and a.block_size == BS else None)
+        roof = {"bound": "hbm", "achieved": round(ix_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ix_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic, "algorithmic_bytes_per_launch": ix_bytes,
+                "frac_of_measured_read_ceiling": round(ix_gbps / ceiling["gbps"], 4) if ceiling else None}
+    step_gbps = step_bytes / (ms * 1e-3) / 1e9 if step_bytes else None
 
     res = {
         "metric": METRIC,
@@ -459,32 +515,23 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"DSA decode, batch {R}, context {a.ctx} tokens, top-{K}, block size {a.block_size}, {key_desc} "
-                        f"and {lat_desc}, {a.layers} independent layers rotated",
-            "batch": R, "ctx": a.ctx, "k": K, "block_size": a.block_size, "layers_rotated": a.layers,
-            "index_fmt": a.index_fmt, "latent_fmt": a.latent_fmt,
+            "workload": workload,
+            "name": a.config,
+            "batch": R, "ctx": max_ctx, "k": K, "block_size": a.block_size, "layers_rotated": a.layers,
+            "index_fmt": a.index_fmt, "latent_fmt": a.latent_fmt, "rows_per_seq": rows_per_seq,
             "launch": "HIP graph replay, one decode step per layer",
         },
         "step_us": spread,
-        "step_hbm_gbps": round(step_gbps, 1),
-        "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "step_hbm_gbps": round(step_gbps, 1) if step_gbps else None,
+        "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4) if step_gbps else None,
         "step_algorithmic_bytes": step_bytes,
-        "roofline": {
-            "kernel": f"indexer_{a.index_fmt}_kernel (scoring only, as dsa_indexer_score launches it)",
-            "bound": "hbm",
-            "achieved": round(ix_gbps, 1),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(ix_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": ix_bytes,
-            "avg_launch_us": round(ix_us, 3),
-            "frac_of_measured_read_ceiling": round(ix_gbps / ceiling["gbps"], 4),
-        },
+        "roofline": dict({"kernel": (f"indexer_{a.index_fmt}" + ("_rows" if rows_per_seq > 1 else "") +
+                                     "_kernel (scoring only, as dsa_indexer_score launches it)")},
+                         **roof, avg_launch_us=round(ix_us, 3)),
         "hbm_read_ceiling": ceiling,
         "gen_seconds": round(gen_s, 1),
     }
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and a.config == "headline":
         res["cpu_baseline"] = cpu_baseline(case, min(a.cpu_layers, a.layers), K)
     print(json.dumps(res), flush=True)
 

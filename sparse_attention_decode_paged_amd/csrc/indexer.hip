@@ -28,6 +28,8 @@
 //
 // Epilogue for the exact top-k: each unit of 64 or 256 tokens sends its best m keys
 // (in token order) plus a floor (topk_send.h).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "topk_send.h"
@@ -46,11 +48,13 @@ __device__ __forceinline__ int swz(int tn, int c) { return tn * kDIdx + 16 * (c 
 // [64w, 64w + 64) of it. PAGED32: block size >= 32, so a tile lies inside one page.
 // Waves past the row's end stay to the epilogue, whose 256-token units take a
 // workgroup barrier. SEND: also run stage 1 of the top-k on the fresh scores.
+// EARLY (launches of several rows): workgroups past their row's end leave before
+// loading keys.
 // The three row-map pointers lead the argument list so that they arrive preloaded in
 // scalar registers (kernel-argument preloading covers leading scalar and pointer
 // arguments, not structures): the first loads of the dependent chain row -> block
 // table -> keys need no kernel-argument fetch before them.
-template <bool PAGED32, bool SEND>
+template <bool PAGED32, bool SEND, bool EARLY>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restrict__ row_seq,
                                                           const int32_t* __restrict__ row_ctx,
                                                           const int32_t* __restrict__ block_table, CacheView cv,
@@ -63,8 +67,11 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restr
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // the row's length and block-table row are read together; a workgroup past the
-  // row's end still issues its (clamped, valid) loads and leaves after them
+  // the row's length and block-table row are read together. A workgroup past the
+  // row's end leaves as soon as the length is in when the launch has several rows
+  // (EARLY: rows of mixed lengths leave many such workgroups); with one row it still
+  // issues its clamped, valid loads and leaves after them, which keeps a branch out of
+  // the key stream's issue.
   const int seq = row_seq[r];
   int ctx = row_ctx[r];
   if (ctx > rm.max_ctx) {
@@ -73,6 +80,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restr
   }
   ctx = ctx < 0 ? 0 : ctx;
   const bool past = blockIdx.x * 256 >= ctx;  // whole workgroup
+  if (EARLY && past) return;                  // no barrier reached
   ctx = ctx > 0 ? ctx : 1;
   const int tok0 = blockIdx.x * 256 + wid * 64;
   const int bs_mask = cv.block_size - 1;
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restr
 
   // every load of the wave is in flight before anything waits on one
   __builtin_amdgcn_sched_barrier(0);
-  if (past) return;  // whole workgroup, no barrier reached
+  if (!EARLY && past) return;  // whole workgroup, no barrier reached
 
   v8bf qa[8];
 #pragma unroll
@@ -194,18 +202,25 @@ hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8
   const int send = (ws != nullptr && rm.max_ctx > kTopkFullRow) ? 1 : 0;
   dim3 grid(nx, R);
   const bool p32 = cv.block_size >= kTileTok;
-  if (send && p32)
-    hipLaunchKernelGGL((indexer_fp8_kernel<true, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
-                       rm, q_idx, q_scale, w, scores, ld, tw);
-  else if (send)
-    hipLaunchKernelGGL((indexer_fp8_kernel<false, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
-                       rm, q_idx, q_scale, w, scores, ld, tw);
-  else if (p32)
-    hipLaunchKernelGGL((indexer_fp8_kernel<true, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
-                       rm, q_idx, q_scale, w, scores, ld, tw);
+  auto go = [&](auto early) {
+    constexpr bool E = decltype(early)::value;
+    if (send && p32)
+      hipLaunchKernelGGL((indexer_fp8_kernel<true, true, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                         rm, q_idx, q_scale, w, scores, ld, tw);
+    else if (send)
+      hipLaunchKernelGGL((indexer_fp8_kernel<false, true, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                         rm, q_idx, q_scale, w, scores, ld, tw);
+    else if (p32)
+      hipLaunchKernelGGL((indexer_fp8_kernel<true, false, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                         rm, q_idx, q_scale, w, scores, ld, tw);
+    else
+      hipLaunchKernelGGL((indexer_fp8_kernel<false, false, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+                         rm, q_idx, q_scale, w, scores, ld, tw);
+  };
+  if (R > 1)
+    go(std::true_type{});
   else
-    hipLaunchKernelGGL((indexer_fp8_kernel<false, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
-                       rm, q_idx, q_scale, w, scores, ld, tw);
+    go(std::false_type{});
   return hipGetLastError();
 }
 

@@ -22,6 +22,8 @@
 // lines (lane l takes byte 16 l), nontemporal, and goes through a wave-private LDS
 // buffer with the 16-byte chunks XOR-swizzled by token. E8M0 exponents come with one
 // dword load per lane (its token's four).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "topk_send.h"
@@ -54,8 +56,8 @@ __device__ __forceinline__ v8bf e2m1x8_to_bf16(uint32_t v, float scale) {
 
 // One workgroup = 4 waves = 256 consecutive tokens of one row; wave w owns tokens
 // [64w, 64w + 64). PAGED32: block size >= 32, so a tile lies inside one page.
-// SEND: also run stage 1 of the top-k on the fresh scores.
-template <bool PAGED32, bool SEND>
+// SEND: also run stage 1 of the top-k on the fresh scores. EARLY: as for the FP8 kernel.
+template <bool PAGED32, bool SEND, bool EARLY>
 // Row-map pointers lead the argument list (preloaded in scalar registers), as for the
 // FP8 kernel.
 __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __restrict__ row_seq,
@@ -70,8 +72,11 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __res
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // the row's length and block-table row are read together; a workgroup past the
-  // row's end still issues its (clamped, valid) loads and leaves after them
+  // the row's length and block-table row are read together. A workgroup past the
+  // row's end leaves as soon as the length is in when the launch has several rows
+  // (EARLY: rows of mixed lengths leave many such workgroups); with one row it still
+  // issues its clamped, valid loads and leaves after them, which keeps a branch out of
+  // the key stream's issue.
   const int seq = row_seq[r];
   int ctx = row_ctx[r];
   if (ctx > rm.max_ctx) {
@@ -80,6 +85,7 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __res
   }
   ctx = ctx < 0 ? 0 : ctx;
   const bool past = blockIdx.x * 256 >= ctx;  // whole workgroup
+  if (EARLY && past) return;                  // no barrier reached
   ctx = ctx > 0 ? ctx : 1;
   const int tok0 = blockIdx.x * 256 + wid * 64;
   const int bs_mask = cv.block_size - 1;
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __res
 
   // every load of the wave is in flight before anything waits on one
   __builtin_amdgcn_sched_barrier(0);
-  if (past) return;  // whole workgroup, no barrier reached
+  if (!EARLY && past) return;  // whole workgroup, no barrier reached
 
   // step kk covers dims 64 g + 8 kk ..: dword kk of the lane's half, block 2 g + kk / 4
   v8bf qa[8];
@@ -199,22 +205,29 @@ hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uin
   const int send = (ws != nullptr && rm.max_ctx > kTopkFullRow) ? 1 : 0;
   dim3 grid(nx, R);
   const bool p32 = cv.block_size >= kTileTok;
-  if (send && p32)
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<true, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
-                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
-                       ld, tw);
-  else if (send)
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<false, true>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
-                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
-                       ld, tw);
-  else if (p32)
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<true, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
-                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
-                       ld, tw);
+  auto go = [&](auto early) {
+    constexpr bool E = decltype(early)::value;
+    if (send && p32)
+      hipLaunchKernelGGL((indexer_mxfp4_kernel<true, true, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                         rm.block_table, cv, rm, q_idx, q_e8, w, scores,
+                         ld, tw);
+    else if (send)
+      hipLaunchKernelGGL((indexer_mxfp4_kernel<false, true, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                         rm.block_table, cv, rm, q_idx, q_e8, w, scores,
+                         ld, tw);
+    else if (p32)
+      hipLaunchKernelGGL((indexer_mxfp4_kernel<true, false, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                         rm.block_table, cv, rm, q_idx, q_e8, w, scores,
+                         ld, tw);
+    else
+      hipLaunchKernelGGL((indexer_mxfp4_kernel<false, false, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
+                         rm.block_table, cv, rm, q_idx, q_e8, w, scores,
+                         ld, tw);
+  };
+  if (R > 1)
+    go(std::true_type{});
   else
-    hipLaunchKernelGGL((indexer_mxfp4_kernel<false, false>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx,
-                       rm.block_table, cv, rm, q_idx, q_e8, w, scores,
-                       ld, tw);
+    go(std::false_type{});
   return hipGetLastError();
 }
 
