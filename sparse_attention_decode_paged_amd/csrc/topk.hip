@@ -19,9 +19,11 @@
 // Stage 2 (topk_select_kernel, one 1024-thread workgroup per row). Every thread
 // holds up to 16 keys in registers:
 //   ctx <= k      every token;
-//   launches whose row-length bound is at most 16384: the row's own keys, tokens
-//                 [16 t, 16 t + 16) on thread t;
-//   otherwise     the candidates of units t + 1024 j (j < units per thread), read
+//   rows of at most 16384 tokens: the row's own keys, tokens [16 t, 16 t + 16) on
+//                 thread t (in a launch with longer rows, after a first search over
+//                 the candidates, which the kernel starts on before it knows the
+//                 row's length);
+//   longer rows   the candidates of units t + 1024 j (j < units per thread), read
 //                 slot-major so that each load instruction covers 64 consecutive
 //                 units and no address depends on the row length (the loads start
 //                 with the kernel). c_u = their k-th largest key. A unit whose floor
@@ -33,8 +35,9 @@
 // the highest bit in which they differ; an 11-bit digit histogram over the next
 // bits (8 copies, lane l adding into copy l % 8, so at most 8 lanes of one
 // instruction hit one LDS word) fixes the bucket of the k-th key. A bucket of at
-// most 64 keys is gathered into LDS and one wave sorts it (64-bit keys, so equal
-// scores order by token); a larger one takes another pass over lower bits. The
+// most 64 keys is gathered into LDS and ranked (64-bit keys, so equal scores order by
+// token; every wave ranks four of them with ballots); a larger one takes another pass
+// over lower bits. The
 // selection is written in token order: per-unit counts and one block prefix sum over
 // units place every selected token in an LDS list, which one coalesced pass then
 // writes out with the tokens' page slots (block-table row staged in LDS).
@@ -637,131 +640,142 @@ __global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __r
       write_all();
       return;
     }
-    stage_bt();
-    // A row of at most 4k tokens may have sent fewer than k candidates (a 64-token unit
-    // sends at least a quarter of its tokens): every unit is rescanned whole.
-    const bool all = ctx <= 4 * k;
-    const uint64_t cu = all ? 1ull : c1;  // every real key is >= 1
-    const uint32_t cu_hi = (uint32_t)(cu >> 32);
+    if (ctx <= kTopkFullRow) {
+      // A short row in a launch with longer rows: its own scores, read whole, take one
+      // search. (Its 64-token units sent a quarter of their tokens, which can be fewer
+      // than k, and every unit would need a rescan.)
+      load_own();
+      cstar = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par, [] {});
+      stage_bt();
+      m = PER;
+      lm = 4;
+      upt = 1;
+    } else {
+      stage_bt();
+      // Rows longer than kTopkFullRow sent at least 4096 >= k candidates (a 64-token unit
+      // sends a quarter of its tokens, a 256-token unit m with nu * m >= 4096).
+      const uint64_t cu = c1;
+      const uint32_t cu_hi = (uint32_t)(cu >> 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (((umine >> j) & 1u) && (all || (fl[j] != 0u && fl[j] >= cu_hi))) fmask |= 1u << j;
-    cstar = c1;
-    if (upt < 4) {
-      // Common case first: one block scan gives both the number of flagged units and,
-      // were there none, every unit's output offset, so with no flagged unit the
-      // selection is written without a second scan.
-      uint32_t bits = 0;
+      for (int j = 0; j < 4; ++j)
+        if (((umine >> j) & 1u) && fl[j] != 0u && fl[j] >= cu_hi) fmask |= 1u << j;
+      cstar = c1;
+      if (upt < 4) {
+        // Common case first: one block scan gives both the number of flagged units and,
+        // were there none, every unit's output offset, so with no flagged unit the
+        // selection is written without a second scan.
+        uint32_t bits = 0;
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= c1) bits |= 1u << i;
-      const uint32_t umask = m >= 16 ? 0xFFFFu : ((1u << m) - 1u);
-      uint32_t v[4] = {(uint32_t)__popc(fmask), 0u, 0u, 0u}, off[4], tot[4];
+        for (int i = 0; i < PER; ++i)
+          if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= c1) bits |= 1u << i;
+        const uint32_t umask = m >= 16 ? 0xFFFFu : ((1u << m) - 1u);
+        uint32_t v[4] = {(uint32_t)__popc(fmask), 0u, 0u, 0u}, off[4], tot[4];
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < upt) v[1 + j] = (uint32_t)__popc(bits & ((umask << (m * j)) & 0xFFFFu));
-      excl_scan4(v, off, tot, upt + 1, S);
-      nflag = tot[0];
-      fbase = off[0];
-      if (nflag == 0) {
-        uint32_t base = 0, uoff[3];
+        for (int j = 0; j < 3; ++j)
+          if (j < upt) v[1 + j] = (uint32_t)__popc(bits & ((umask << (m * j)) & 0xFFFFu));
+        excl_scan4(v, off, tot, upt + 1, S);
+        nflag = tot[0];
+        fbase = off[0];
+        if (nflag == 0) {
+          uint32_t base = 0, uoff[3];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
-          uoff[j] = base + off[1 + j];
-          base += j < upt ? tot[1 + j] : 0u;
+          for (int j = 0; j < 3; ++j) {
+            uoff[j] = base + off[1 + j];
+            base += j < upt ? tot[1 + j] : 0u;
+          }
+          const uint32_t total = base;
+          uint32_t* list = S.a.hist;  // free since the search
+#pragma unroll
+          for (int i = 0; i < PER; ++i) {
+            const int j = i >> lm;
+            const uint32_t oj = j == 0 ? uoff[0] : j == 1 ? uoff[1] : uoff[2];
+            const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
+            if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = 0xFFFFFFFFu - kl[i];
+          }
+          __syncthreads();
+          flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
+          return;
         }
-        const uint32_t total = base;
-        uint32_t* list = S.a.hist;  // free since the search
+        __syncthreads();  // the write path below runs its own scan4
+      } else {
+        fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
+      }
+      if (nflag > 0) {
+        if (nflag > (uint32_t)FCAP) {
+          select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+          return;
+        }
+        // ---- resend: each flagged unit's keys >= c_u, rescanned by one wave per unit ----
+        {
+          uint32_t fm = fmask, sl = fbase;
+          while (fm) {
+            const int j = __ffs(fm) - 1;
+            fm &= fm - 1u;
+            S.funit[sl++] = (uint32_t)(tid + SEL_NT * j);
+          }
+        }
+        if (tid == 0) S.ecount = 0u;
+        __syncthreads();
+        const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1 or 4
+        for (uint32_t sl = wid; sl < nflag; sl += NW) {
+          const int t0 = (int)S.funit[sl] * p.unit;
+          float f[4];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int j = i >> lm;
-          const uint32_t oj = j == 0 ? uoff[0] : j == 1 ? uoff[1] : uoff[2];
-          const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
-          if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = 0xFFFFFFFFu - kl[i];
+          for (int c = 0; c < 4; ++c) {
+            const int t = t0 + 64 * c + lane;
+            f[c] = (c < chunks && t < ctx) ? srow[t] : 0.f;
+          }
+          uint64_t bal[4];
+          uint32_t tot = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int t = t0 + 64 * c + lane;
+            const bool keep = c < chunks && t < ctx && composite_key(f[c], t) >= cu;
+            bal[c] = __ballot(keep);
+            tot += (uint32_t)__popcll(bal[c]);
+          }
+          uint32_t st = 0;
+          if (lane == 0) st = atomicAdd(&S.ecount, tot);
+          st = (uint32_t)__shfl((int)st, 0, 64);
+          uint32_t run = st;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int t = t0 + 64 * c + lane;
+            const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
+            if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
+            run += (uint32_t)__popcll(bal[c]);
+          }
+          if (lane == 0) {
+            S.fstart[sl] = st;
+            S.flen[sl] = tot;
+          }
         }
         __syncthreads();
-        flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
-        return;
-      }
-      __syncthreads();  // the write path below runs its own scan4
-    } else {
-      fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
-    }
-    if (nflag > 0) {
-      if (nflag > (uint32_t)FCAP) {
-        select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
-        return;
-      }
-      // ---- resend: each flagged unit's keys >= c_u, rescanned by one wave per unit ----
-      {
-        uint32_t fm = fmask, sl = fbase;
-        while (fm) {
-          const int j = __ffs(fm) - 1;
-          fm &= fm - 1u;
-          S.funit[sl++] = (uint32_t)(tid + SEL_NT * j);
+        const uint32_t ne = S.ecount;
+        if (ne > (uint32_t)ECAP) {
+          select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
+          return;
         }
-      }
-      if (tid == 0) S.ecount = 0u;
-      __syncthreads();
-      const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1 or 4
-      for (uint32_t sl = wid; sl < nflag; sl += NW) {
-        const int t0 = (int)S.funit[sl] * p.unit;
-        float f[4];
+        // union: unflagged candidates >= c_u in registers, rescanned keys from LDS
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int t = t0 + 64 * c + lane;
-          f[c] = (c < chunks && t < ctx) ? srow[t] : 0.f;
+        for (int i = 0; i < PER; ++i) {
+          const bool flagged = (fmask >> (i >> lm)) & 1u;
+          if (flagged || (((uint64_t)kh[i] << 32) | kl[i]) < cu) kh[i] = 0u;
         }
-        uint64_t bal[4];
-        uint32_t tot = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int t = t0 + 64 * c + lane;
-          const bool keep = c < chunks && t < ctx && composite_key(f[c], t) >= cu;
-          bal[c] = __ballot(keep);
-          tot += (uint32_t)__popcll(bal[c]);
+        cstar = kth_largest<PER, true>(kh, kl, S.a.ext, ne, (uint32_t)k, S, par, [] {});
+        // selected keys of each rescanned unit
+        for (uint32_t sl = wid; sl < nflag; sl += NW) {
+          const uint32_t st = S.fstart[sl], len = S.flen[sl];
+          uint32_t c = 0;
+          for (uint32_t q0 = 0; q0 < len; q0 += 64) {
+            const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
+            c += (uint32_t)__popcll(__ballot(sel));
+          }
+          if (lane == 0) S.fcnt[sl] = c;
         }
-        uint32_t st = 0;
-        if (lane == 0) st = atomicAdd(&S.ecount, tot);
-        st = (uint32_t)__shfl((int)st, 0, 64);
-        uint32_t run = st;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int t = t0 + 64 * c + lane;
-          const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
-          if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
-          run += (uint32_t)__popcll(bal[c]);
-        }
-        if (lane == 0) {
-          S.fstart[sl] = st;
-          S.flen[sl] = tot;
-        }
+        __syncthreads();
       }
-      __syncthreads();
-      const uint32_t ne = S.ecount;
-      if (ne > (uint32_t)ECAP) {
-        select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
-        return;
-      }
-      // union: unflagged candidates >= c_u in registers, rescanned keys from LDS
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const bool flagged = (fmask >> (i >> lm)) & 1u;
-        if (flagged || (((uint64_t)kh[i] << 32) | kl[i]) < cu) kh[i] = 0u;
-      }
-      cstar = kth_largest<PER, true>(kh, kl, S.a.ext, ne, (uint32_t)k, S, par, [] {});
-      // selected keys of each rescanned unit
-      for (uint32_t sl = wid; sl < nflag; sl += NW) {
-        const uint32_t st = S.fstart[sl], len = S.flen[sl];
-        uint32_t c = 0;
-        for (uint32_t q0 = 0; q0 < len; q0 += 64) {
-          const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
-          c += (uint32_t)__popcll(__ballot(sel));
-        }
-        if (lane == 0) S.fcnt[sl] = c;
-      }
-      __syncthreads();
-    }
+    }  // rows longer than kTopkFullRow
   }
 
   // ---- ordered write: unit counts, prefix sums over units (unit u = tid + 1024 j) ----
