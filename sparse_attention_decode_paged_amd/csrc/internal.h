@@ -48,15 +48,29 @@ inline TopkWs topk_ws_carve(void* ws, int R, int max_ctx) {
 constexpr int kMlaChunk = 64;   // tokens per inner iteration
 constexpr int kMlaGroup = 32;   // latent-query heads per workgroup
 
+// Splits of a row's k tokens for sparse MLA. A workgroup (one per CU: its registers
+// allow no second) takes whole 64-token chunks; R rows x 3 head groups x s splits
+// run in rounds of kMlaSlots workgroups. The choice minimises the estimated time
+// rounds x (chunks per split + a prologue worth 1.5 chunks), plus one chunk's worth
+// for the merge kernel when s > 1; ties go to fewer splits.
+constexpr int kMlaSlots = 256;  // CUs of the device
 inline int mla_splits(int R, int k) {
   if (R <= 0) return 1;
-  int maxs = (k + kMlaChunk - 1) / kMlaChunk;
-  int want = (512 + 3 * R - 1) / (3 * R);
-  int s = want < 1 ? 1 : (want > maxs ? maxs : want);
-  int ts = (k + s - 1) / s;
-  ts = (ts + kMlaChunk - 1) / kMlaChunk * kMlaChunk;
-  s = (k + ts - 1) / ts;
-  return s < 1 ? 1 : s;
+  const int nch = (k + kMlaChunk - 1) / kMlaChunk;
+  int best = 1;
+  double best_cost = 0.0;
+  for (int s = 1; s <= nch; ++s) {
+    const int cps = (nch + s - 1) / s;  // chunks per split
+    if ((nch + cps - 1) / cps != s) continue;  // s is not reached by whole chunks
+    const int64_t wgs = (int64_t)R * (kHQ / kMlaGroup) * s;
+    const double rounds = (double)((wgs + kMlaSlots - 1) / kMlaSlots);
+    const double cost = rounds * (cps + 1.5) + (s > 1 ? 1.0 : 0.0);
+    if (s == 1 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 inline int mla_split_tokens(int k, int nsplit) {
   int ts = (k + nsplit - 1) / nsplit;

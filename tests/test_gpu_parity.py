@@ -185,7 +185,11 @@ def test_determinism_and_staged_calls(dev):
 
 
 def test_batch_invariance(dev):
-    """A row's scores and selection do not depend on the batch it runs in."""
+    """A row's scores and selection do not depend on the batch it runs in (bit for bit).
+    Its attention output may: sparse MLA splits a row's tokens into a number of splits
+    chosen from the batch size, and each split rounds its probabilities to fp16 against
+    its own running maximum, so outputs agree to that rounding (2^-11 relative per
+    probability), well inside the parity bar."""
     say("case: batch invariance")
     c = make_case([30000, 17000, 50000, 2500], block_size=64, seed=31, k=2048).to(dev)
     s_all, i_all, o_all, l_all = run_step(c, dev)
@@ -198,7 +202,9 @@ def test_batch_invariance(dev):
         ctx = int(c.row_ctx[r])
         assert np.array_equal(s1[0, :ctx], s_all[r, :ctx])
         assert np.array_equal(i1[0], i_all[r])
-        assert np.allclose(o1[0], o_all[r], rtol=1e-4, atol=1e-5)
+        err = np.abs(o1[0] - o_all[r])
+        say(f"  row {r}: attention max abs diff across batch sizes {err.max():.3g}")
+        assert np.all(err <= 1e-4 + 1e-3 * np.abs(o_all[r]))
 
 
 def test_batch16_mixed_lengths(dev):
