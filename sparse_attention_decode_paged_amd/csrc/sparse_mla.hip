@@ -52,7 +52,8 @@ namespace dsa {
 
 namespace {
 using v8h = v8hf;
-constexpr int NT = 256;   // merge workgroup
+constexpr int NT = 64;    // merge workgroup: one wave
+constexpr int kMergeParts = kDV / (2 * NT);  // merge workgroups per head (128 value columns each)
 constexpr int NTM = 512;  // attention workgroup: 8 waves, two per SIMD
 constexpr int NWM = NTM / 64;
 constexpr int CH = kMlaChunk;           // 64 tokens per iteration
@@ -508,18 +509,20 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
 }
 
 // out[r][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s ; empty splits (m = -inf)
-// weigh 0. Lane s of every wave reads split s's (m, l); each thread then loads its two
-// value columns of every split at once (splits past nsplit repeat the last one with
-// weight 0), so the whole merge is one round of loads.
+// weigh 0. One wave per (row, head, 128 value columns), so that the partials spread
+// over four times as many CUs as heads: lane s reads split s's (m, l); each lane then
+// loads its two value columns of every split at once (splits past nsplit repeat the
+// last one with weight 0), so the whole merge is one round of loads.
 __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml, int nsplit,
                                                        float* __restrict__ out, float* __restrict__ lse) {
   constexpr int MS = kMaxK / kMlaChunk;  // most splits a row can have
   static_assert(MS <= 64, "one split per lane");
-  const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int h = blockIdx.x / kMergeParts, q = blockIdx.x % kMergeParts, r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (int64_t)r * nsplit * kHQ + h;
   const float2 e = lane < nsplit ? ml[(int64_t)lane * kHQ] : float2{kNegInf, 0.f};
-  const float* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + tid;
+  const float* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + 2 * NT * q + tid;
   float x0[MS], x1[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
@@ -550,10 +553,11 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
     o1 = fmaf(ws, x1[s], o1);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* orow = out + ((int64_t)r * kHQ + h) * kDV;
+  float* orow = out + ((int64_t)r * kHQ + h) * kDV + 2 * NT * q;
   orow[tid] = o0 * inv;
   orow[tid + NT] = o1 * inv;
-  if (lse != nullptr && tid == 0) lse[(int64_t)r * kHQ + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+  if (lse != nullptr && q == 0 && tid == 0)
+    lse[(int64_t)r * kHQ + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
 
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
@@ -577,7 +581,8 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, idx, phys,
                        q_lat, k, ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
   if (nsplit > 1)
-    hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
+    hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ * kMergeParts, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out,
+                       lse);
   return hipGetLastError();
 }
 
