@@ -53,7 +53,8 @@ namespace dsa {
 namespace {
 using v8h = v8hf;
 constexpr int NT = 64;    // merge workgroup: one wave
-constexpr int kMergeParts = kDV / (2 * NT);  // merge workgroups per head (128 value columns each)
+constexpr int kMergeCols = 2;                         // value columns per merge lane
+constexpr int kMergeParts = kDV / (kMergeCols * NT);  // merge workgroups per head
 constexpr int NTM = 512;  // attention workgroup: 8 waves, two per SIMD
 constexpr int NWM = NTM / 64;
 constexpr int CH = kMlaChunk;           // 64 tokens per iteration
@@ -509,10 +510,10 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
 }
 
 // out[r][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s ; empty splits (m = -inf)
-// weigh 0. One wave per (row, head, 128 value columns), so that the partials spread
-// over four times as many CUs as heads: lane s reads split s's (m, l); each lane then
-// loads its two value columns of every split at once (splits past nsplit repeat the
-// last one with weight 0), so the whole merge is one round of loads.
+// weigh 0. One wave per (row, head, 64 kMergeCols value columns), so that the partials
+// spread over several times as many CUs as heads: lane s reads split s's (m, l); each
+// lane then loads its value columns of every split at once (splits past nsplit repeat
+// the last one with weight 0), so the whole merge is one round of loads.
 __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml, int nsplit,
                                                        float* __restrict__ out, float* __restrict__ lse) {
@@ -522,13 +523,13 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
   const int tid = threadIdx.x, lane = tid & 63;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (int64_t)r * nsplit * kHQ + h;
   const float2 e = lane < nsplit ? ml[(int64_t)lane * kHQ] : float2{kNegInf, 0.f};
-  const float* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + 2 * NT * q + tid;
-  float x0[MS], x1[MS];
+  const float* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + kMergeCols * NT * q + tid;
+  float x[kMergeCols][MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
     const int sc = s < nsplit ? s : nsplit - 1;
-    x0[s] = po[(int64_t)sc * kHQ * kDV];
-    x1[s] = po[(int64_t)sc * kHQ * kDV + NT];
+#pragma unroll
+    for (int c = 0; c < kMergeCols; ++c) x[c][s] = po[(int64_t)sc * kHQ * kDV + NT * c];
   }
   float M = e.x;
   M = fmaxf(M, xshflf<1>(M));
@@ -545,17 +546,17 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
   L += xshflf<8>(L);
   L += xshflf<16>(L);
   L += xshflf<32>(L);
-  float o0 = 0.f, o1 = 0.f;
+  float o[kMergeCols] = {};
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
     const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s));
-    o0 = fmaf(ws, x0[s], o0);
-    o1 = fmaf(ws, x1[s], o1);
+#pragma unroll
+    for (int c = 0; c < kMergeCols; ++c) o[c] = fmaf(ws, x[c][s], o[c]);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* orow = out + ((int64_t)r * kHQ + h) * kDV + 2 * NT * q;
-  orow[tid] = o0 * inv;
-  orow[tid + NT] = o1 * inv;
+  float* orow = out + ((int64_t)r * kHQ + h) * kDV + kMergeCols * NT * q;
+#pragma unroll
+  for (int c = 0; c < kMergeCols; ++c) orow[tid + NT * c] = o[c] * inv;
   if (lse != nullptr && q == 0 && tid == 0)
     lse[(int64_t)r * kHQ + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
