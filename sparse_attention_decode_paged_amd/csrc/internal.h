@@ -46,7 +46,10 @@ inline TopkWs topk_ws_carve(void* ws, int R, int max_ctx) {
 
 // ---- sparse MLA workspace -------------------------------------------------------------
 constexpr int kMlaChunk = 64;   // tokens per inner iteration
-constexpr int kMlaGroup = 32;   // latent-query heads per workgroup
+// Latent-query heads per sparse-MLA workgroup: 16 for batches of up to 4 rows (a row's
+// work spreads over twice as many CUs), 32 above (each gathered latent serves twice as
+// many heads).
+inline int mla_group(int R) { return R <= 4 ? 16 : 32; }
 
 // Splits of a row's k tokens for sparse MLA. A workgroup (one per CU: its registers
 // allow no second) takes whole 64-token chunks; R rows x 3 head groups x s splits
@@ -62,7 +65,7 @@ inline int mla_splits(int R, int k) {
   for (int s = 1; s <= nch; ++s) {
     const int cps = (nch + s - 1) / s;  // chunks per split
     if ((nch + cps - 1) / cps != s) continue;  // s is not reached by whole chunks
-    const int64_t wgs = (int64_t)R * (kHQ / kMlaGroup) * s;
+    const int64_t wgs = (int64_t)R * (kHQ / mla_group(R)) * s;
     const double rounds = (double)((wgs + kMlaSlots - 1) / kMlaSlots);
     const double cost = rounds * (cps + 1.5) + (s > 1 ? 1.0 : 0.0);
     if (s == 1 || cost < best_cost) {

@@ -7,22 +7,29 @@
 // adds parallelism inside a query row. Absorbed queries live in the 576-wide
 // latent space (keys = all 576 dims, values = first 512; page 3 model table: NoPE).
 //
-// Grid (split, row, head group of 32). A workgroup walks its split's slice of the
-// row's index list 64 tokens at a time:
+// Grid (split, row, head group of G = 16 or 32 heads). A workgroup walks its split's
+// slice of the row's index list 64 tokens at a time (the steps below are for G = 16;
+// G = 32 keeps all 576 dims per wave and splits the heads, 4 heads per wave in the
+// softmax and 32x32x16 MFMAs for O):
 //   the chunk's token ids / page slots are the head of a load chain (ids -> latent
 //   rows), so they are fetched first; the 64 latents (576 e4m3 bytes each) of chunk
 //   c + 1 are loaded into registers while chunk c is computed (the ids of c + 2
 //   behind them) and go to LDS once chunk c is done with it;
-//   S = Q . C^T on 16x16x32 bf16 MFMAs (8 waves, each 16 tokens x 16 heads), scaled
+//   S = Q . C^T on 16x16x32 bf16 MFMAs (8 waves, each 16 tokens x 16 heads over one
+//   half of the 576 dims, so a wave holds 9 query fragments), the two halves' scaled
 //   logits (log2 domain) to LDS;
-//   the online softmax of the chunk is split across the waves (each owns 4 heads and
-//   keeps their running max / sum), and P'' and the heads' rescale factors pass through
-//   LDS to every wave;
+//   the online softmax of the chunk adds the halves and is split across the waves
+//   (each owns 2 heads and keeps their running max / sum), and P'' and the heads'
+//   rescale factors pass through LDS to every wave;
 //   P'' = p * scale_t / (largest scale in the chunk), in [0, 1], as fp16 straight
 //   into the MFMA operand registers;
-//   O += P'' . codes on 32x32x16 fp16 MFMAs (each wave: 64 of the 512 value
+//   O += P'' . codes on 16x16x32 fp16 MFMAs (each wave: 64 of the 512 value
 //   columns); e4m3 codes are exact in fp16, and fp16 P keeps 11 significant bits
 //   (bf16's 8 were visibly too few on rows dominated by a handful of tokens).
+// Sixteen heads per workgroup spread a row over twice as many CUs and keep the FP8
+// kernel at 128 registers (two workgroups per CU): the choice for batches of up to 4
+// rows. Larger batches fill the GPU anyway and take 32, which gathers each latent once
+// per 32 heads instead of once per 16.
 //   The chunk's scale factor joins the per-head softmax rescale.
 // e4m3 codes convert to bf16 exactly; the per-token scale is applied to the
 // logit and folded into P'. With one split the workgroup writes out / lse; with
@@ -44,6 +51,8 @@
 // the transposing LDS read (ds_read_b64_tr_b16). The tile's 16-byte chunks are
 // XOR-swizzled within each token row (nv_col) so that the gather's writes do not
 // collide in the LDS banks.
+#include <type_traits>
+
 #include "dsa.h"
 #include "common.h"
 #include "internal.h"
@@ -67,7 +76,7 @@ template <bool NV>
 struct Tile {
   static constexpr int ROW = NV ? 2 * kDLat + 16 : kDLat + 16;
   static constexpr int BYTES = CH * ROW;  // Q passes through the same bytes first
-  static_assert(kMlaGroup * QROW * 2 <= BYTES, "Q staging fits the latent tile");
+  static_assert(32 * QROW * 2 <= BYTES, "Q staging (up to 32 heads) fits the latent tile");
 };
 constexpr int XROW = CH + 16;           // logit rows: the four 16-lane groups of a store hit distinct banks
 constexpr int PROW = CH + 8;            // P'' rows (fp16), padded so the fragment reads spread over the banks
@@ -107,7 +116,7 @@ __device__ __forceinline__ int nv_col(int col) {
 // addresses arrive preloaded in scalar registers (kernel-argument preloading covers
 // leading scalar and pointer arguments, not structures): the head of the load chain
 // needs no kernel-argument fetch before it.
-template <bool NV>
+template <bool NV, int G>
 __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ phys,
                                                         const uint16_t* __restrict__ q_lat, int k, int ts, float c2,
@@ -117,16 +126,16 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
                                                         int nsplit) {
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int g = lane >> 5;  // half of the wave
 
   constexpr int LROW = Tile<NV>::ROW;
   __shared__ __attribute__((aligned(16))) uint8_t lat_s[Tile<NV>::BYTES];
-  __shared__ __attribute__((aligned(16))) float x_s[kMlaGroup * XROW];  // scaled logits, head-major
+  // scaled logits, head-major (G = 16: one array per half of the dims)
+  __shared__ __attribute__((aligned(16))) float x_s[(G == 16 ? 2 : 1) * G * XROW];
   __shared__ __attribute__((aligned(16))) float sc_s[CH];
-  __shared__ float qe_s[kMlaGroup];  // NVFP4: the power of two each head's fp16 query was scaled down by
-  __shared__ __attribute__((aligned(16))) _Float16 p_s[kMlaGroup * PROW];  // the chunk's P'', head-major
-  __shared__ float al_s[kMlaGroup];   // each head's rescale factor for the chunk
-  __shared__ float2 ml_s[kMlaGroup];  // each head's running (max, sum), kept by its owning wave
+  __shared__ float qe_s[G];  // NVFP4: the power of two each head's fp16 query was scaled down by
+  __shared__ __attribute__((aligned(16))) _Float16 p_s[G * PROW];  // the chunk's P'', head-major
+  __shared__ float al_s[G];   // each head's rescale factor for the chunk
+  __shared__ float2 ml_s[G];  // each head's running (max, sum), kept by its owning wave
 
   const int32_t* irow = idx + (int64_t)r * k;
   const int j0 = split * ts;
@@ -152,14 +161,16 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   // contiguous) and passes through the latent tile's LDS bytes, which the first chunk's
   // latents overwrite after a barrier.
   const int hrow = lane & 15, kq = 8 * (lane >> 4);
-  const int tg = wid & 3, hh = wid >> 2;  // QK tile of this wave: tokens 16 tg.., heads 16 hh..
-  constexpr int KQ = kDLat / 32;          // 18 steps of 32 dims
+  // QK tile of this wave: tokens 16 tg..; G = 16: all heads, dims 288 wq..;
+  // G = 32: heads 16 wq.., all dims
+  const int tg = wid & 3, wq = wid >> 2;
+  constexpr int KQ = G == 16 ? kDLat / 64 : kDLat / 32;  // steps of 32 dims
   constexpr int QP = kDLat / 8;           // 72 16-byte pieces per head row
-  constexpr int QALL = kMlaGroup * QP;
+  constexpr int QALL = G * QP;
   constexpr int QN = (QALL + NTM - 1) / NTM;
   v4i qv[QN];
   {
-    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * kMlaGroup) * kDLat);
+    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * G) * kDLat);
 #pragma unroll
     for (int q = 0; q < QN; ++q)
       if (tid + NTM * q < QALL) qv[q] = qg[tid + NTM * q];
@@ -173,12 +184,19 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   v8bf qa[KQ];
   v8h qh[KQ];  // NVFP4: the same fragments in fp16, scaled by a power of two per head
 
-  // running softmax state of head 4 wid + (lane >> 4), the head this lane's wave owns
+  // running softmax state of the head this lane's wave owns (G = 16: head
+  // 2 wid + (lane >> 5); G = 32: head 4 wid + (lane >> 4))
   float m_run = kNegInf, l_run = 0.f;
-  if (tid < kMlaGroup) ml_s[tid] = float2{kNegInf, 0.f};  // ordered by the staging barriers below
-  v16f acc[2];
+  if (tid < G) ml_s[tid] = float2{kNegInf, 0.f};  // ordered by the staging barriers below
+  // O accumulators. G = 16: value columns 64 wid + 16 cb + (lane & 15), heads
+  // 4 (lane >> 4) + i. G = 32: columns 64 wid + 32 c + (lane & 31), row rr = head
+  // 8 (rr >> 2) + 4 (lane >> 5) + (rr & 3).
+  v4f acc[4];
+  v16f accw[2];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) acc[c] = v16f{};
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) accw[c] = v16f{};
   float s_run = 1.f;  // acc holds O / s_run (token scales folded into P per chunk)
 
   // ---- gather, software-pipelined: the latents of chunk c + 1 are loaded into
@@ -240,10 +258,12 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
     }
     __syncthreads();
     if constexpr (NV) {
-      // 16 threads per head (one wave holds 4 heads): each takes 36 consecutive dims of
-      // its head row, the 16 agree on the head's largest magnitude, and each rewrites
-      // its 36 values in place as fp16 scaled by the head's power of two
+      // 16 threads per head (one wave holds 4 heads; the first 16 G threads):
+      // each takes 36 consecutive dims of its head row, the 16 agree on the head's
+      // largest magnitude, and each rewrites its 36 values in place as fp16 scaled by
+      // the head's power of two
       const int h = tid >> 4, part = tid & 15;
+      if (tid < 16 * G) {  // whole waves
       uint16_t* qp = q_s + h * QROW + 36 * part;
       uint2 raw[9];
 #pragma unroll
@@ -272,12 +292,13 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
         *reinterpret_cast<uint2*>(qp + 4 * i) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       }
       if (part == 0) qe_s[h] = __uint_as_float((uint32_t)(127 + ex) << 23);
+      }
       __syncthreads();
-      const uint16_t* qrow = q_s + (16 * hh + hrow) * QROW + kq;
+      const uint16_t* qrow = q_s + (G == 16 ? hrow : 16 * wq + hrow) * QROW + kq + (G == 16 ? (kDLat / 2) * wq : 0);
 #pragma unroll
       for (int kk = 0; kk < KQ; ++kk) qh[kk] = *reinterpret_cast<const v8h*>(qrow + 32 * kk);
     } else {
-      const uint16_t* qrow = q_s + (16 * hh + hrow) * QROW + kq;
+      const uint16_t* qrow = q_s + (G == 16 ? hrow : 16 * wq + hrow) * QROW + kq + (G == 16 ? (kDLat / 2) * wq : 0);
 #pragma unroll
       for (int kk = 0; kk < KQ; ++kk) qa[kk] = *reinterpret_cast<const v8bf*>(qrow + 32 * kk);
     }
@@ -339,19 +360,20 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
       smax = v > 0.f ? v : 1.f;
     }
 
-    // ---- S = Q . C^T : wave w -> tokens [16 (w & 3), +16), heads [16 (w >> 2), +16);
-    // scaled logits (log2 domain) go to LDS ----
+    // ---- S = Q . C^T : wave w -> tokens [16 (w & 3), +16), all 16 heads, dims
+    // [288 (w >> 2), +288); each half's scaled logits (log2 domain) go to LDS and the
+    // softmax adds the two ----
     {
       v4f s0 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (NV) {
         const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW;
 #pragma unroll
         for (int kk = 0; kk < KQ; ++kk) {
-          const v8h b = *reinterpret_cast<const v8h*>(lrow + nv_col(kq + 32 * kk));
+          const v8h b = *reinterpret_cast<const v8h*>(lrow + nv_col(kq + (G == 16 ? (kDLat / 2) * wq : 0) + 32 * kk));
           s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], b, s0, 0, 0, 0);
         }
       } else {
-        const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW + kq;
+        const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW + kq + (G == 16 ? (kDLat / 2) * wq : 0);
 #pragma unroll
         for (int kk = 0; kk < KQ; ++kk) {
           uint2 raw = *reinterpret_cast<const uint2*>(lrow + 32 * kk);
@@ -362,20 +384,63 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
       const int tt = 16 * tg + hrow;
       const float sct = sc_s[tt];
       const bool ok = sct != kNegInf;
-      const int hb = 16 * hh + 4 * (lane >> 4);
+      const int hb = (G == 16 ? 0 : 16 * wq) + 4 * (lane >> 4);
+      float* xh = x_s + (G == 16 ? wq * G * XROW : 0);
       if constexpr (NV) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x_s[(hb + i) * XROW + tt] = ok ? s0[i] * qe_s[hb + i] * (sct * c2) : kNegInf;
+        for (int i = 0; i < 4; ++i) xh[(hb + i) * XROW + tt] = ok ? s0[i] * qe_s[hb + i] * (sct * c2) : kNegInf;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x_s[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
+        for (int i = 0; i < 4; ++i) xh[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
       }
     }
     __syncthreads();
 
-    // ---- softmax over the chunk, split across the waves: wave w owns heads 4w .. 4w+3,
-    // lane l head 4w + (l >> 4) and tokens 4 (l & 15) .. +4. P'' = p * scale_t / smax
+    if constexpr (G == 16) {
+    // ---- softmax over the chunk, split across the waves: wave w owns heads 2w, 2w+1,
+    // lane l head 2w + (l >> 5) and tokens 2 (l & 31) .. +2. P'' = p * scale_t / smax
     // (fp16, in [0, 1]) and each head's rescale factor go to LDS for every wave ----
+    {
+      const int h = 2 * wid + (lane >> 5), t2 = 2 * (lane & 31);
+      const float2 xa = *reinterpret_cast<const float2*>(x_s + h * XROW + t2);
+      const float2 xb = *reinterpret_cast<const float2*>(x_s + (G + h) * XROW + t2);
+      const float2 s2 = *reinterpret_cast<const float2*>(sc_s + t2);
+      const float xv[2] = {xa.x + xb.x, xa.y + xb.y};  // -inf for an empty slot in both halves
+      const float sv[2] = {s2.x, s2.y};
+      float cm = fmaxf(xv[0], xv[1]);
+      cm = fmaxf(cm, xshflf<1>(cm));
+      cm = fmaxf(cm, xshflf<2>(cm));
+      cm = fmaxf(cm, xshflf<4>(cm));
+      cm = fmaxf(cm, xshflf<8>(cm));
+      cm = fmaxf(cm, xshflf<16>(cm));
+      const float mn = fmaxf(m_run, cm);
+      const float alpha = (mn == kNegInf) ? 1.f : exp2f(m_run - mn);
+      const float inv_smax = 1.f / smax;
+      float psum = 0.f;
+      v2h ph;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float p = (xv[e] == kNegInf) ? 0.f : exp2f(xv[e] - mn);
+        psum += p;
+        const float sfac = sv[e] != kNegInf ? sv[e] * inv_smax : 0.f;
+        ph[e] = (_Float16)(p * sfac);
+      }
+      psum += xshflf<1>(psum);
+      psum += xshflf<2>(psum);
+      psum += xshflf<4>(psum);
+      psum += xshflf<8>(psum);
+      psum += xshflf<16>(psum);
+      l_run = l_run * alpha + psum;
+      m_run = mn;
+      *reinterpret_cast<v2h*>(p_s + h * PROW + t2) = ph;
+      if ((lane & 31) == 0) {
+        al_s[h] = alpha;
+        ml_s[h] = float2{m_run, l_run};
+      }
+    }
+    } else {
+    // ---- softmax over the chunk, split across the waves: wave w owns heads 4w .. 4w+3,
+    // lane l head 4w + (l >> 4) and tokens 4 (l & 15) .. +4 ----
     {
       const int h = 4 * wid + (lane >> 4), t4 = 4 * (lane & 15);
       const float4 x4 = *reinterpret_cast<const float4*>(x_s + h * XROW + t4);
@@ -411,60 +476,105 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
         ml_s[h] = float2{m_run, l_run};
       }
     }
+    }
     __syncthreads();
-    // P'' fragments: row = head lane & 31, k = tokens 16 ks + 8 g .. +8
-    v8h pa[4];
+    // P'' fragments. G = 16 (16x16x32 A operand): row = head lane & 15, k = tokens
+    // 32 ks + 8 (lane >> 4) .. +8. G = 32 (32x32x16): row = head lane & 31, k = tokens
+    // 16 ks + 8 (lane >> 5) .. +8.
+    v8h pa[G == 16 ? 2 : 4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pa[ks] = *reinterpret_cast<const v8h*>(p_s + (lane & 31) * PROW + 16 * ks + 8 * g);
+    for (int ks = 0; ks < (G == 16 ? 2 : 4); ++ks)
+      pa[ks] = G == 16 ? *reinterpret_cast<const v8h*>(p_s + (lane & 15) * PROW + 32 * ks + 8 * (lane >> 4))
+                       : *reinterpret_cast<const v8h*>(p_s + (lane & 31) * PROW + 16 * ks + 8 * (lane >> 5));
 
     // ---- acc = acc * alpha * (s_run / smax) + P'' . codes : wave w -> columns [64w, 64w+64) ----
-    // accumulator row rr of this lane is head 8 (rr >> 2) + 4 g + (rr & 3)
     const float rescale = s_run / smax;
     s_run = smax;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&al_s[8 * jj + 4 * g]);
+    if constexpr (G == 16) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&al_s[4 * (lane >> 4)]);
       const float a[4] = {a4.x * rescale, a4.y * rescale, a4.z * rescale, a4.w * rescale};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[c][4 * jj + i] *= a[i];
+        for (int i = 0; i < 4; ++i) acc[cb][i] *= a[i];
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&al_s[8 * jj + 4 * (lane >> 5)]);
+        const float a[4] = {a4.x * rescale, a4.y * rescale, a4.z * rescale, a4.w * rescale};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) accw[c][4 * jj + i] *= a[i];
+      }
     }
-    // B operand (codes of tokens 16 ks + 8 g .. +8 at value column 64 w + 32 c + (lane & 31))
-    // by one transposing LDS read: within each 16-lane group, lane 8 a + c' receives byte c'
-    // of the 8-byte rows that lanes 2 j + a point at, j = 0..7 (in token order). So lane l
-    // points at token row 8 (l >> 5) + ((l & 15) >> 1), columns 16 ((l >> 4) & 1) + 8 (l & 1).
+    // B operand (16x16x32: codes of tokens 32 ks + 8 (lane >> 4) .. +8 at value column
+    // 64 w + 16 cb + (lane & 15)) by one transposing LDS read: within each 16-lane group,
+    // lane 8 a + c' receives byte c' of the 8-byte rows that lanes 2 j + a point at,
+    // j = 0..7 (in token order). So lane l points at token row 8 (l >> 4) + ((l & 15) >> 1),
+    // columns 8 (l & 1).
     // NVFP4 (fp16 tile): the 16-bit transposing read gives 4 values per lane: within each
     // 16-lane group, lane 4 a + c' receives element c' of the 8-byte rows that lanes
     // a + 4 j point at, j = 0..3 (in token order). So lane l points at token row
-    // 8 (l >> 5) + ((l & 15) >> 2) (+4 for the second read), columns 16 ((l >> 4) & 1) +
-    // 4 (l & 3).
-    if constexpr (NV) {
-      const int tr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * LROW;
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-      for (int ks = 0; ks < CH / 16; ++ks) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint8_t* vp = lat_s + 16 * ks * LROW + tr_row + nv_col(64 * wid + 32 * c + tr_col);
-          const v4h t0 = __builtin_bit_cast(
-              v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp)));
-          const v4h t1 = __builtin_bit_cast(
-              v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 4 * LROW)));
-          const v8h b = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, acc[c], 0, 0, 0);
+    // 8 (l >> 4) + ((l & 15) >> 2) (+4 for the second read), columns 4 (l & 3).
+    if constexpr (G == 16) {
+      if constexpr (NV) {
+        const int tr_row = (8 * (lane >> 4) + ((lane & 15) >> 2)) * LROW;
+        const int tr_col = 4 * (lane & 3);
+  #pragma unroll
+        for (int ks = 0; ks < CH / 32; ++ks) {
+  #pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const uint8_t* vp = lat_s + 32 * ks * LROW + tr_row + nv_col(64 * wid + 16 * cb + tr_col);
+            const v4h t0 = __builtin_bit_cast(
+                v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp)));
+            const v4h t1 = __builtin_bit_cast(
+                v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 4 * LROW)));
+            const v8h b = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[ks], b, acc[cb], 0, 0, 0);
+          }
+        }
+      } else {
+        const int tr_off = (8 * (lane >> 4) + ((lane & 15) >> 1)) * LROW + 8 * (lane & 1);
+  #pragma unroll
+        for (int ks = 0; ks < CH / 32; ++ks) {
+  #pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const uint8_t* vp = lat_s + 32 * ks * LROW + 64 * wid + 16 * cb + tr_off;
+            const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(vp));
+            const v8h b = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[ks], b, acc[cb], 0, 0, 0);
+          }
         }
       }
     } else {
-      const int tr_off = (8 * (lane >> 5) + ((lane & 15) >> 1)) * LROW + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
-#pragma unroll
-      for (int ks = 0; ks < CH / 16; ++ks) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint8_t* vp = lat_s + 16 * ks * LROW + 64 * wid + 32 * c + tr_off;
-          const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(vp));
-          v8h b = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, acc[c], 0, 0, 0);
+      if constexpr (NV) {
+        const int tr_row = (8 * (lane >> 5) + ((lane & 15) >> 2)) * LROW;
+        const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  #pragma unroll
+        for (int ks = 0; ks < CH / 16; ++ks) {
+  #pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint8_t* vp = lat_s + 16 * ks * LROW + tr_row + nv_col(64 * wid + 32 * c + tr_col);
+            const v4h t0 = __builtin_bit_cast(
+                v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp)));
+            const v4h t1 = __builtin_bit_cast(
+                v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vp + 4 * LROW)));
+            const v8h b = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+            accw[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, accw[c], 0, 0, 0);
+          }
+        }
+      } else {
+        const int tr_off = (8 * (lane >> 5) + ((lane & 15) >> 1)) * LROW + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+  #pragma unroll
+        for (int ks = 0; ks < CH / 16; ++ks) {
+  #pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const uint8_t* vp = lat_s + 16 * ks * LROW + 64 * wid + 32 * c + tr_off;
+            const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(vp));
+            v8h b = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
+            accw[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, accw[c], 0, 0, 0);
+          }
         }
       }
     }
@@ -475,33 +585,51 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   // (the loop's last barrier, or the staging barriers for a split with no tokens, has
   // ordered every head's final (max, sum) in ml_s)
   if (nsplit == 1) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float lv[4] = {ml_s[8 * jj + 4 * g].y, ml_s[8 * jj + 4 * g + 1].y, ml_s[8 * jj + 4 * g + 2].y,
-                           ml_s[8 * jj + 4 * g + 3].y};
+    if constexpr (G == 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int h = 8 * jj + 4 * g + i;
-        const float f = lv[i] > 0.f ? s_run / lv[i] : 0.f;
-        float* orow = out + ((int64_t)r * kHQ + hg * kMlaGroup + h) * kDV + 64 * wid + (lane & 31);
+        const int h = 4 * (lane >> 4) + i;
+        const float lv = ml_s[h].y;
+        const float f = lv > 0.f ? s_run / lv : 0.f;
+        float* orow = out + ((int64_t)r * kHQ + hg * G + h) * kDV + 64 * wid + (lane & 15);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) orow[32 * c] = acc[c][4 * jj + i] * f;
+        for (int cb = 0; cb < 4; ++cb) orow[16 * cb] = acc[cb][i] * f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const float lv = ml_s[h].y;
+        const float f = lv > 0.f ? s_run / lv : 0.f;
+        float* orow = out + ((int64_t)r * kHQ + hg * G + h) * kDV + 64 * wid + (lane & 31);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) orow[32 * c] = accw[c][i] * f;
       }
     }
-    if (lse != nullptr && tid < kMlaGroup) {
+    if (lse != nullptr && tid < G) {
       const float2 ml = ml_s[tid];
-      lse[(int64_t)r * kHQ + hg * kMlaGroup + tid] = ml.y > 0.f ? (ml.x + log2f(ml.y)) * 0.69314718055994531f : kNegInf;
+      lse[(int64_t)r * kHQ + hg * G + tid] = ml.y > 0.f ? (ml.x + log2f(ml.y)) * 0.69314718055994531f : kNegInf;
     }
   } else {
-    const int64_t pbase = ((int64_t)r * nsplit + split) * kHQ + hg * kMlaGroup;
+    const int64_t pbase = ((int64_t)r * nsplit + split) * kHQ + hg * G;
+    if constexpr (G == 16) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int h = 8 * (rr >> 2) + 4 * g + (rr & 3);
-      float* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 31);
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * (lane >> 4) + i;
+        float* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 15);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) __builtin_nontemporal_store(acc[c][rr] * s_run, orow + 32 * c);
+        for (int cb = 0; cb < 4; ++cb) __builtin_nontemporal_store(acc[cb][i] * s_run, orow + 16 * cb);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        float* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 31);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) __builtin_nontemporal_store(accw[c][i] * s_run, orow + 32 * c);
+      }
     }
-    if (tid < kMlaGroup) {
+    if (tid < G) {
       const float2 ml = ml_s[tid];
       part_ml[(pbase + tid) * 2 + 0] = ml.x;
       part_ml[(pbase + tid) * 2 + 1] = ml.y;
@@ -575,12 +703,24 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     part_o = static_cast<float*>(ws);
     part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 4, 256));
   }
-  if (cv.latent_fmt == DSA_LATENT_NVFP4)
-    hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, idx, phys,
-                       q_lat, k, ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
-  else
-    hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(nsplit, R, kHQ / kMlaGroup), dim3(NTM), 0, stream, idx, phys,
-                       q_lat, k, ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
+  auto go = [&](auto nv, auto group) {
+    constexpr bool N = decltype(nv)::value;
+    constexpr int G = decltype(group)::value;
+    hipLaunchKernelGGL((sparse_mla_kernel<N, G>), dim3(nsplit, R, kHQ / G), dim3(NTM), 0, stream, idx, phys, q_lat, k,
+                       ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
+  };
+  const bool nvf = cv.latent_fmt == DSA_LATENT_NVFP4;
+  if (mla_group(R) == 16) {
+    if (nvf)
+      go(std::true_type{}, std::integral_constant<int, 16>{});
+    else
+      go(std::false_type{}, std::integral_constant<int, 16>{});
+  } else {
+    if (nvf)
+      go(std::true_type{}, std::integral_constant<int, 32>{});
+    else
+      go(std::false_type{}, std::integral_constant<int, 32>{});
+  }
   if (nsplit > 1)
     hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ * kMergeParts, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out,
                        lse);

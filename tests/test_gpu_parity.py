@@ -503,6 +503,14 @@ def test_nvfp4_latents_ragged(dev, bs):
     full_check(c, dev)
 
 
+def test_nvfp4_latents_batch_of_six(dev):
+    """Batches above four rows run sparse MLA with 32 heads per workgroup (16 below):
+    the NVFP4 path of the wider group."""
+    say("case: NVFP4 latents, batch 6")
+    c = make_case([300, 5000, 9001, 40000, 1500, 17000], block_size=64, seed=127, k=2048, latent_fmt="nvfp4")
+    full_check(c, dev)
+
+
 def test_nvfp4_latents_with_mxfp4_keys_and_empty_rows(dev):
     """The pages' smallest cache: NVFP4 latents with MXFP4 index keys, block size 128, two
     layers; an empty row gives zeros and -inf."""
