@@ -642,11 +642,12 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
 // spread over several times as many CUs as heads: lane s reads split s's (m, l); each
 // lane then loads its value columns of every split at once (splits past nsplit repeat
 // the last one with weight 0), so the whole merge is one round of loads.
+// MS: a power of two >= nsplit (the loads are unrolled over MS splits).
+template <int MS>
 __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml, int nsplit,
                                                        float* __restrict__ out, float* __restrict__ lse) {
-  constexpr int MS = kMaxK / kMlaChunk;  // most splits a row can have
-  static_assert(MS <= 64, "one split per lane");
+  static_assert(MS <= 64 && MS <= kMaxK / kMlaChunk, "one split per lane");
   const int h = blockIdx.x / kMergeParts, q = blockIdx.x % kMergeParts, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (int64_t)r * nsplit * kHQ + h;
@@ -721,9 +722,17 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     else
       go(std::false_type{}, std::integral_constant<int, 32>{});
   }
-  if (nsplit > 1)
-    hipLaunchKernelGGL(mla_merge_kernel, dim3(kHQ * kMergeParts, R), dim3(NT), 0, stream, part_o, part_ml, nsplit, out,
-                       lse);
+  if (nsplit > 1) {
+    const dim3 mg(kHQ * kMergeParts, R);
+    if (nsplit <= 4)
+      hipLaunchKernelGGL(mla_merge_kernel<4>, mg, dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
+    else if (nsplit <= 8)
+      hipLaunchKernelGGL(mla_merge_kernel<8>, mg, dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
+    else if (nsplit <= 16)
+      hipLaunchKernelGGL(mla_merge_kernel<16>, mg, dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
+    else
+      hipLaunchKernelGGL(mla_merge_kernel<32>, mg, dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
+  }
   return hipGetLastError();
 }
 
