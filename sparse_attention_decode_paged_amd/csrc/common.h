@@ -157,36 +157,6 @@ template <int J>
 __device__ __forceinline__ float xshflf(float v) {
   return __uint_as_float(xshfl<J>(__float_as_uint(v)));
 }
-template <int J>
-__device__ __forceinline__ uint64_t xshfl64(uint64_t v) {
-  return ((uint64_t)xshfl<J>((uint32_t)(v >> 32)) << 32) | xshfl<J>((uint32_t)v);
-}
-
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v += xshfl<1>(v); v += xshfl<2>(v); v += xshfl<4>(v);
-  v += xshfl<8>(v); v += xshfl<16>(v); v += xshfl<32>(v);
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-  uint64_t o;
-  o = xshfl64<1>(v); v = o < v ? o : v;
-  o = xshfl64<2>(v); v = o < v ? o : v;
-  o = xshfl64<4>(v); v = o < v ? o : v;
-  o = xshfl64<8>(v); v = o < v ? o : v;
-  o = xshfl64<16>(v); v = o < v ? o : v;
-  o = xshfl64<32>(v); v = o < v ? o : v;
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint64_t o;
-  o = xshfl64<1>(v); v = o > v ? o : v;
-  o = xshfl64<2>(v); v = o > v ? o : v;
-  o = xshfl64<4>(v); v = o > v ? o : v;
-  o = xshfl64<8>(v); v = o > v ? o : v;
-  o = xshfl64<16>(v); v = o > v ? o : v;
-  o = xshfl64<32>(v); v = o > v ? o : v;
-  return v;
-}
 
 // One compare-exchange stage of a descending bitonic network across the wave.
 template <int K, int J>
@@ -206,13 +176,6 @@ __device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v, int lane) {
   v = bitonic_desc_step<32, 2>(v, lane);  v = bitonic_desc_step<32, 1>(v, lane);
   v = bitonic_desc_step<64, 32>(v, lane); v = bitonic_desc_step<64, 16>(v, lane); v = bitonic_desc_step<64, 8>(v, lane);
   v = bitonic_desc_step<64, 4>(v, lane);  v = bitonic_desc_step<64, 2>(v, lane);  v = bitonic_desc_step<64, 1>(v, lane);
-  return v;
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 

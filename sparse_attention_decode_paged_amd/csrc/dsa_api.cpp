@@ -258,7 +258,7 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_c
   CacheView st{};  // no cache: carries only the status word
   st.status = status_word();
   hipError_t e = launch_topk_send(scores, ld_scores, row_ctx, R, max_ctx, tw, s);
-  if (e == hipSuccess) e = launch_topk_select(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, nullptr, nullptr, &st, nullptr, s);
+  if (e == hipSuccess) e = launch_topk_select(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, nullptr, &st, nullptr, s);
   return hip_status(e, "topk");
 }
 
@@ -279,7 +279,7 @@ dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer, const uint
   if (mla_splits(R, k) > 1 && (workspace == nullptr || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (R == 0) return ok();
-  return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, nullptr, nullptr, R, k, sm_scale, out, lse, workspace,
+  return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, nullptr, R, k, sm_scale, out, lse, workspace,
                                       static_cast<hipStream_t>(stream)),
                     "sparse_mla");
 }
@@ -335,10 +335,10 @@ dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, con
   p += align_up((size_t)R * k * 4, 256);
   void* mla_ws = p;
   hipError_t e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld, &tw, s);
-  if (e == hipSuccess) e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, idx, tw, phys, nullptr, &cv, &rm, s);
+  if (e == hipSuccess) e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, idx, tw, phys, &cv, &rm, s);
   if (e == hipSuccess) {
     // the selected tokens lie below max_ctx, so the row map's bound is unchanged
-    e = launch_sparse_mla(cv, rm, q_lat, idx, phys, nullptr, R, k, sm_scale, out, lse, mla_ws, s);
+    e = launch_sparse_mla(cv, rm, q_lat, idx, phys, R, k, sm_scale, out, lse, mla_ws, s);
   }
   return hip_status(e, "decode_step");
 }

@@ -161,17 +161,17 @@ hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uin
 hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx,
                             const TopkWs& ws, hipStream_t stream);
 // Selection; when `phys` is non-null it also receives, per selected token, its page
-// slot (physical block * block_size + slot) and `pscale` the token's latent scale,
-// for the attention kernel.
+// slot (physical block * block_size + slot) for the attention kernel (cv and rm are
+// then required; without page slots cv may carry just the status word, or be null).
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
-                              int32_t* idx, const TopkWs& ws, int32_t* phys, float* pscale, const CacheView* cv,
-                              const RowMap* rm, hipStream_t stream);
+                              int32_t* idx, const TopkWs& ws, int32_t* phys, const CacheView* cv, const RowMap* rm,
+                              hipStream_t stream);
 
-// Sparse MLA over idx; when `phys` / `pscale` (page slots and latent scales from the
-// selection) are non-null they replace the block-table lookups and scale loads.
+// Sparse MLA over idx; when `phys` (page slots from the selection) is non-null it
+// replaces the block-table lookups.
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
-                             const int32_t* phys, const float* pscale, int R, int k, float sm_scale, float* out,
-                             float* lse, void* ws, hipStream_t stream);
+                             const int32_t* phys, int R, int k, float sm_scale, float* out, float* lse, void* ws,
+                             hipStream_t stream);
 
 // Exact top-k merge of decode context parallelism over W token-strided shards, emulated
 // on one GPU (ws: dcp_ws_bytes). resend_mask / words may be null.

@@ -691,9 +691,8 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
 }
 
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
-                             const int32_t* phys, const float* pscale, int R, int k, float sm_scale, float* out,
-                             float* lse, void* ws, hipStream_t stream) {
-  (void)pscale;
+                             const int32_t* phys, int R, int k, float sm_scale, float* out, float* lse, void* ws,
+                             hipStream_t stream) {
   if (R <= 0) return hipSuccess;
   const int nsplit = mla_splits(R, k);
   const int ts = mla_split_tokens(k, nsplit);

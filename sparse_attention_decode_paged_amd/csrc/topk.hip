@@ -841,9 +841,8 @@ hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_
 }
 
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
-                              int32_t* idx, const TopkWs& ws, int32_t* phys, float* pscale, const CacheView* cv,
-                              const RowMap* rm, hipStream_t stream) {
-  (void)pscale;
+                              int32_t* idx, const TopkWs& ws, int32_t* phys, const CacheView* cv, const RowMap* rm,
+                              hipStream_t stream) {
   if (R <= 0) return hipSuccess;
   CacheView c{};
   RowMap m{};
