@@ -26,15 +26,15 @@
 //   O += P'' . codes on 16x16x32 fp16 MFMAs (each wave: 64 of the 512 value
 //   columns); e4m3 codes are exact in fp16, and fp16 P keeps 11 significant bits
 //   (bf16's 8 were visibly too few on rows dominated by a handful of tokens).
-// Sixteen heads per workgroup spread a row over twice as many CUs and keep the FP8
-// kernel at 128 registers (two workgroups per CU): the choice for batches of up to 4
-// rows. Larger batches fill the GPU anyway and take 32, which gathers each latent once
-// per 32 heads instead of once per 16.
 //   The chunk's scale factor joins the per-head softmax rescale.
 // e4m3 codes convert to bf16 exactly; the per-token scale is applied to the
 // logit and folded into P'. With one split the workgroup writes out / lse; with
 // several it writes unnormalised partials (O, m, l) that the merge kernel
 // combines by log-sum-exp.
+// Sixteen heads per workgroup spread a row over twice as many CUs and keep the FP8
+// kernel at 128 registers (two workgroups per CU): the choice for batches of up to 4
+// rows. Larger batches fill the GPU anyway and take 32, which gathers each latent and
+// reads the value tile once per 32 heads instead of once per 16.
 //
 // NVFP4 latents (page 1, KV-cache section: 352 B per token; the record holds the 512
 // value dims as e2m1 codes with one e4m3 scale per 16 dims and the last 64 dims as
