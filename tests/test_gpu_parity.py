@@ -392,6 +392,19 @@ def test_device_status_word(dev):
     assert torch.equal(before, c.pool)
 
 
+def test_hbm_read_probe_reads_without_writing(dev):
+    """The streaming-read reference launches at every grid size bench.py uses, over a
+    buffer with a partial last chunk, and writes nothing: its XOR of zeros never equals
+    the sink's trigger constant, so the sink keeps its sentinel."""
+    say("case: hbm read probe")
+    buf = torch.zeros((1 << 20) + 48, dtype=torch.uint8, device=dev)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=dev)
+    for grid in (256, 512, 1024, 2048, 4096):
+        dsa.dsa_hbm_read_probe(buf, sink, grid)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+
+
 def test_select_paths_mixed_batch(dev):
     """One batch whose rows take every selection path: ctx <= k, whole row in LDS
     (<= 16384), and block candidates with rescans (> 16384)."""
