@@ -303,7 +303,8 @@ dsa_status dsa_device_status(void* stream, int32_t clear, uint32_t* status);
  * Measurement reference, not a step of the method: reads every byte of
  * [p, p + bytes) once (16-byte nontemporal loads; `grid` workgroups of 256 threads
  * take 16-KB chunks in turn) and writes nothing, except *sink in the practically
- * impossible case that the XOR of all words read equals 0x9E3779B9. Timed over a
+ * impossible case that the XOR of the words one thread read equals 0x9E3779B9 (the
+ * condition keeps the loads from being optimised away). Timed over a
  * buffer much larger than the last-level cache it gives the streaming-read rate the
  * indexer's HBM roofline can be compared with. p 16-byte aligned, bytes a multiple of
  * 16 (DSA_ERR_ALIGN), grid in [1, 65535] (DSA_ERR_ARG), sink a device uint32.
