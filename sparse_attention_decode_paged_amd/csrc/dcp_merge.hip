@@ -252,6 +252,11 @@ __global__ __launch_bounds__(kNT) void dcp_merge_kernel(const float* __restrict_
   }
   __syncthreads();
   const uint32_t nsel = S.nsel < (uint32_t)k ? S.nsel : (uint32_t)k;
+  // Bitonic sort, one pair per thread. A stage of stride <= 64 keeps every element inside
+  // the 128-element block of one wave (wave w: [128 w, 128 w + 128)), and one wave's LDS
+  // operations execute in order, so two consecutive such stages need no workgroup
+  // barrier; a stage of stride >= 128 crosses waves and is fenced on both sides.
+  static_assert(kNT * 2 == kMaxK, "one pair per thread");
   for (int size = 2; size <= kMaxK; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const int lo = 2 * stride * (tid / stride) + (tid % stride), hi = lo + stride;
@@ -261,7 +266,11 @@ __global__ __launch_bounds__(kNT) void dcp_merge_kernel(const float* __restrict_
         S.sel[lo] = b;
         S.sel[hi] = a;
       }
-      __syncthreads();
+      const int next = stride > 1 ? stride >> 1 : size;  // the next stage's stride
+      if (stride >= 128 || next >= 128 || (stride == 1 && size == kMaxK))
+        __syncthreads();
+      else
+        __builtin_amdgcn_wave_barrier();
     }
   }
   for (int j = tid; j < k; j += kNT) idx[(int64_t)r * k + j] = j < (int)nsel ? S.sel[j] : -1;
