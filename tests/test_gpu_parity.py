@@ -240,6 +240,64 @@ def test_long_context_1m_planted(dev):
     assert hit >= 0.95 * planted.size
 
 
+def test_decode_256k_24_layers_graph_replay(dev):
+    """The 262,144-token decode step in the form the benchmark times it: 24 layers in one
+    packed cache row, the step for every layer captured in one HIP graph on a side stream
+    and replayed. Every replay is compared bit for bit with eager calls (eager work and
+    synchronisations between replays), and two layers are checked against the oracle in full
+    (all 262,144 scores, the selection, all 96 heads)."""
+    L, ctx = 24, 262144
+    say(f"case: decode B=1 ctx {ctx}, {L} layers, bs 64, graph replay")
+    c = make_case([ctx], block_size=64, num_layers=L, seed=0, device=dev, k=2048,
+                  name="decode_b1_ctx262144_x24layers")
+    R, K, M = c.num_rows, c.k, c.max_ctx     # M read once: no device sync may run under capture
+    ws = torch.empty(dsa.dsa_workspace_bytes(dsa.DSA_OP_DECODE_STEP, R, M, K), dtype=torch.uint8, device=dev)
+    bufs = [(torch.empty((R, K), dtype=torch.int32, device=dev), torch.empty((R, 96, 512), device=dev),
+             torch.empty((R, 96), device=dev)) for _ in range(L)]
+
+    def step(l, b):
+        dsa.dsa_decode_step(c.pool, c.layout, l, c.q_idx[l], c.q_idx_scale[l], c.w[l], c.q_lat[l], c.block_table,
+                            c.row_seq, c.row_ctx, M, K, c.sm_scale, idx=b[0], out=b[1], lse=b[2], workspace=ws)
+
+    check_layers = (0, L - 1)
+    eager, eager_scores = [], {}
+    for l in range(L):
+        step(l, bufs[l])
+        if l in check_layers:
+            eager_scores[l] = dsa.decode_scores_view(ws, R, M).cpu().numpy().copy()
+        eager.append(tuple(x.cpu().numpy().copy() for x in bufs[l]))
+    torch.cuda.synchronize()
+
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(torch.cuda.current_stream(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for l in range(L):
+            step(l, bufs[l])
+    torch.cuda.synchronize()
+    scratch = tuple(torch.empty_like(x) for x in bufs[0])
+    for rep in range(3):
+        for b in bufs:
+            for x in b:
+                x.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            for got, want in zip(bufs[l], eager[l]):
+                assert np.array_equal(got.cpu().numpy(), want), f"replay {rep} layer {l} differs from eager"
+        step((rep * 7) % L, scratch)        # eager work between replays
+        torch.cuda.synchronize()
+    say("  3 replays bit-identical to eager")
+
+    hc = HostCase(c)
+    for l in check_layers:
+        say(f"  oracle layer {l}")
+        ref = hc.oracle(0, l)
+        check_scores(eager_scores[l][0], ref, ctx)
+        sel = check_selection(eager_scores[l][0], eager[l][0][0], ref, ctx, K)
+        check_attention(hc, 0, sel, eager[l][1][0], eager[l][2][0], l)
+
+
 def test_prefill_append_150k(dev):
     """2048 appended rows on a 150,000-token prefix; row r sees t <= 150000 + r."""
     say("case: prefill-append 2048 rows on 150000 prefix")
