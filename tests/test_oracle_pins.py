@@ -529,3 +529,134 @@ def test_generator_writes_nvfp4_records_as_the_oracle_reads_them():
     for i in range(16):
         want, ws = O.quantize_nvfp4_latent(x[i])
         assert np.array_equal(rec[i].numpy(), want) and np.float32(s[i].item()) == ws
+
+
+# ------------------------------------------------------------------ pins for index_query's
+# FP8 per-head scale, decode_row past one 65,536-token key chunk, and indexer_magnitude
+def _e4m3_lib(codes):
+    """e4m3 codes -> float64 through torch's float8_e4m3fn (a library decode)."""
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _hand_pool_fp8(bs, n_blocks):
+    """Zeroed single-layer FP8 pool laid out by hand: latent page (bs x 576 codes, bs
+    fp32 scales) then index page (bs x 128 codes, bs fp32 scales)."""
+    lat_page = bs * (576 + 4)
+    row = lat_page + bs * (128 + 4)
+    lay = dict(block_size=bs, index_fmt="fp8", row_bytes=row, lat_off=[0], idx_off=[lat_page])
+    return np.zeros((n_blocks, row), np.uint8), lay
+
+
+def _put_key(pool, lay, bt, t, codes, scale):
+    bs = lay["block_size"]
+    blk, s = int(bt[t // bs]), t % bs
+    o = lay["idx_off"][0]
+    pool[blk, o + s * 128:o + (s + 1) * 128] = codes
+    pool[blk, o + bs * 128 + 4 * s:o + bs * 128 + 4 * s + 4] = np.frombuffer(np.float32(scale).tobytes(), np.uint8)
+
+
+def _finite_e4m3_codes(shape):
+    c = rng.integers(0, 0x7F, size=shape, dtype=np.uint8)        # 0x00..0x7E: finite
+    return c | (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+
+
+def test_index_query_fp8_per_head_scale_closed_form():
+    """s_t = sum_h w_h * ReLU(sq_h * sk_t * (codes_q[h] . codes_k[t])), one fp32 scale
+    per query head. Each head in turn is the only live one, with scales that differ
+    from head to head, so a dropped, shared or misindexed query scale changes the
+    result. The code dot products are exact in float64 (e4m3 products have 8
+    significant bits and 128 of them fit in 53), decoded through torch."""
+    bs, nb, n = 16, 6, 90
+    pool, lay = _hand_pool_fp8(bs, nb)
+    bt = rng.permutation(nb).astype(np.int32)
+    kc = _finite_e4m3_codes((n, 128))
+    ks = rng.uniform(0.25, 4.0, size=n).astype(np.float32)
+    for t in range(n):
+        _put_key(pool, lay, bt, t, kc[t], ks[t])
+    qc_all = _finite_e4m3_codes((32, 128))
+    qs = (2.0 ** rng.integers(-6, 7, size=32) * rng.uniform(1.0, 2.0, size=32)).astype(np.float32)
+    assert len(set(qs.tolist())) == 32
+    w = (rng.standard_normal(32) / math.sqrt(32)).astype(np.float32)
+    dots = _e4m3_lib(kc) @ _e4m3_lib(qc_all).T                    # [n, 32] exact integer-scaled sums
+    ql = np.zeros((96, 576), np.uint16)
+    for h in (0, 5, 17, 31):
+        qc = np.zeros((32, 128), np.uint8)
+        qc[h] = qc_all[h]
+        r = O.decode_row(pool, lay, 0, bt, n, qc, qs, w, ql, 8, 1 / 24)
+        ref = float(w[h]) * np.maximum(float(qs[h]) * ks.astype(np.float64) * dots[:, h], 0.0)
+        assert np.allclose(r["scores"], ref, rtol=1e-12, atol=0), h
+        assert np.count_nonzero(ref) > 0
+    # every head live at once: the per-head sum of the same closed form
+    r = O.decode_row(pool, lay, 0, bt, n, qc_all, qs, w, ql, 8, 1 / 24)
+    ref = (np.maximum(dots * qs.astype(np.float64)[None, :] * ks.astype(np.float64)[:, None], 0.0)
+           * w.astype(np.float64)[None, :]).sum(axis=1)
+    assert np.allclose(r["scores"], ref, rtol=1e-12, atol=1e-300)
+
+
+def test_decode_row_past_one_key_chunk_closed_form():
+    """A 70,000-token context: every key is zero except one-hot tokens spread over
+    both 65,536-token chunks and straddling the chunk boundary, so each score is
+    known in closed form, s_t = sum_h w_h * ReLU(sq_h * e4m3(q[h, d_t]) * v_t * sk_t),
+    and the top-k is the positive scores, then the zero scores by token order."""
+    bs, ctx = 1024, 70000
+    nb = -(-ctx // bs)
+    pool, lay = _hand_pool_fp8(bs, nb)
+    bt = rng.permutation(nb).astype(np.int32)
+    sc1 = np.frombuffer(np.float32(1.0).tobytes(), np.uint8)
+    o = lay["idx_off"][0]
+    pool[:, o + bs * 128:o + bs * 132] = np.tile(sc1, bs)[None, :]
+    hot = sorted(set([0, 5, 40000, 65534, 65535, 65536, 65537, 69999]
+                     + rng.integers(0, ctx, size=40).tolist()))
+    dpos = rng.integers(0, 128, size=len(hot))
+    vcode = _finite_e4m3_codes(len(hot))
+    vcode[vcode == 0] = 0x38
+    vcode[vcode == 0x80] = 0xB8
+    ksc = rng.uniform(0.5, 2.0, size=len(hot)).astype(np.float32)
+    for i, t in enumerate(hot):
+        c = np.zeros(128, np.uint8)
+        c[dpos[i]] = vcode[i]
+        _put_key(pool, lay, bt, t, c, ksc[i])
+    qc = _finite_e4m3_codes((32, 128))
+    qs = rng.uniform(0.01, 0.1, size=32).astype(np.float32)
+    w = (rng.standard_normal(32) / math.sqrt(32)).astype(np.float32)
+    qv = _e4m3_lib(qc) * qs.astype(np.float64)[:, None]
+    vv = _e4m3_lib(vcode)
+    ref = np.zeros(ctx)
+    for i, t in enumerate(hot):
+        ref[t] = sum(float(w[h]) * max(0.0, qv[h, dpos[i]] * vv[i] * float(ksc[i])) for h in range(32))
+    k = 2048
+    r = O.decode_row(pool, lay, 0, bt, ctx, qc, qs, w, np.zeros((96, 576), np.uint16), k, 1 / 24)
+    assert r["scores"].shape == (ctx,)
+    assert np.allclose(r["scores"], ref, rtol=1e-12, atol=0)
+    assert np.count_nonzero(r["scores"][[t for t in range(ctx) if t not in set(hot)]]) == 0
+    s32 = ref.astype(np.float32)
+    expect = sorted(sorted(range(ctx), key=lambda t: (-float(s32[t]), t))[:k])
+    assert np.array_equal(r["idx"], np.array(expect))
+    assert any(t >= 65536 for t in r["idx"]) and {65535, 65536} & set(r["idx"].tolist()) == \
+        {t for t in (65535, 65536) if s32[t] >= 0}
+
+
+def test_indexer_magnitude_brute_force_and_bound():
+    """mag_t = sum_h |w_h| sum_d |q_hd k_td| by explicit loops; |s_t| <= mag_t; and
+    with non-negative q, k and w every term is added at full size, so mag_t = s_t."""
+    q = rng.standard_normal((32, 128))
+    w = rng.standard_normal(32).astype(np.float32)
+    keys = rng.standard_normal((7, 128))
+    got = O.indexer_magnitude(q, w, keys)
+    ref = []
+    for t in range(keys.shape[0]):
+        m = 0.0
+        for h in range(32):
+            a = 0.0
+            for d in range(128):
+                a += abs(q[h, d] * keys[t, d])
+            m += abs(float(w[h])) * a
+        ref.append(m)
+    assert np.allclose(got, np.array(ref), rtol=1e-12, atol=0)
+    keys = rng.standard_normal((3000, 128))
+    s = O.indexer_scores(q, w, keys)
+    mag = O.indexer_magnitude(q, w, keys)
+    assert np.all(np.abs(s) <= mag * (1 + 1e-12))
+    qp, kp, wp = np.abs(q), np.abs(keys[:50]), np.abs(w)
+    assert np.allclose(O.indexer_magnitude(qp, wp, kp), O.indexer_scores(qp, wp, kp), rtol=1e-12, atol=0)
