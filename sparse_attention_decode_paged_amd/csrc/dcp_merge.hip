@@ -267,10 +267,16 @@ __global__ __launch_bounds__(kNT) void dcp_merge_kernel(const float* __restrict_
         S.sel[hi] = a;
       }
       const int next = stride > 1 ? stride >> 1 : size;  // the next stage's stride
-      if (stride >= 128 || next >= 128 || (stride == 1 && size == kMaxK))
+      if (stride >= 128 || next >= 128 || (stride == 1 && size == kMaxK)) {
         __syncthreads();
-      else
+      } else {
+        // wave-scope release / acquire around the wave barrier: the exchange goes
+        // through LDS between lanes of one wave, so the stores must be ordered
+        // before the partner lanes' loads (free at this scope)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
     }
   }
   for (int j = tid; j < k; j += kNT) idx[(int64_t)r * k + j] = j < (int)nsel ? S.sel[j] : -1;

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
                                                                const float* __restrict__ w, float* __restrict__ scores,
                                                                int64_t ld, TopkWs tw, int R, int G) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kTileBytes];
-  __shared__ uint32_t send_lds[2][68];  // double-buffered by row: a wave runs at most one row ahead
+  __shared__ uint32_t send_lds[2][68];  // double-buffered over the rows that take the 256-token send
   __shared__ float wf_s[kRowsPerGroupMax * kHIdx];  // folded head weights w * q_scale of the group's rows
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -50,14 +50,17 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
   if (blockIdx.x * 256 >= gmax) return;  // whole workgroup
   const int tok0 = blockIdx.x * 256 + wid * 64;
   const int bs_mask = cv.block_size - 1;
-  const int last_tile = (gmax - 1) & ~(kTileTok - 1);
-  const int tb1 = tok0 + kTileTok < last_tile ? tok0 + kTileTok : last_tile;
-  const int tb0 = tok0 < last_tile ? tok0 : last_tile;
   const int wpos = swz(lane >> 3, lane & 7);
 
   v8bf kb[2][8];  // B operands of both tiles (keys of the current sequence, as bf16)
   float ksc = 0.f;  // key scale of token tok0 + lane
-  auto load_keys = [&](int seq) {
+  // Keys of sequence `seq` for the run of rows that starts at row r and shares it: tile
+  // starts are clamped into the run's longest row (smax >= 1), so no block-table entry
+  // past that sequence's own tokens is read.
+  auto load_keys = [&](int seq, int smax) {
+    const int last_tile = (smax - 1) & ~(kTileTok - 1);
+    const int tb1 = tok0 + kTileTok < last_tile ? tok0 + kTileTok : last_tile;
+    const int tb0 = tok0 < last_tile ? tok0 : last_tile;
     v4i kv[2][4];
     int64_t toff[2];
     if (PAGED32) {
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           int t = tb + 8 * i + (lane >> 3);
-          t = t < gmax ? t : gmax - 1;
+          t = t < smax ? t : smax - 1;
           const uint8_t* key = row_base(cv, token_block(cv, rm, seq, t)) + cv.idx_off + (int64_t)(t & bs_mask) * kDIdx;
           kv[j][i] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(key + 16 * (lane & 7)));
         }
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     }
     {
       int t = tok0 + lane;
-      t = t < gmax ? t : gmax - 1;
+      t = t < smax ? t : smax - 1;
       const int64_t off = PAGED32 ? ((t & ~(kTileTok - 1)) == tb1 ? toff[1] : toff[0])
                                   : token_block(cv, rm, seq, t) * cv.row_bytes + cv.idx_off;
       ksc = *reinterpret_cast<const float*>(cv.pool + off + (int64_t)cv.block_size * kDIdx + (int64_t)(t & bs_mask) * 4);
@@ -124,6 +127,11 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
   if (!SEND) q_frag(r0, qr);
 
   int seq_cur = -1;
+  // Send buffers alternate between rows that take the 256-token send (the only form
+  // that uses LDS, and it ends its writes with a workgroup barrier): counting those rows
+  // rather than all rows keeps a wave from reusing a buffer that a slower wave may
+  // still read, also when shorter rows without that barrier sit in between.
+  int nsend256 = 0;
   for (int r = r0; r < r1; ++r) {
     v4i qn[4] = {};
     if (SEND)
@@ -133,7 +141,12 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     const int seq = rm.row_seq[r];
     const int ctx = row_len(rm, r, cv.status);
     if (seq != seq_cur) {  // uniform
-      load_keys(seq);
+      int smax = ctx;  // longest row of the run of rows on this sequence
+      for (int q = r + 1; q < r1 && rm.row_seq[q] == seq; ++q) {
+        const int c = row_len(rm, q, nullptr);
+        smax = c > smax ? c : smax;
+      }
+      if (smax > 0) load_keys(seq, smax);  // an empty run stores and sends nothing
       seq_cur = seq;
     }
     v8bf qa[8];
@@ -169,7 +182,10 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     const float sc = (g ? res[1] : res[0]) * ksc;
     if (t < ctx) scores[(int64_t)r * ld + t] = sc;
     // the workgroup's span must reach into the row, or its unit would lie past the row
-    if (SEND && blockIdx.x * 256 < ctx) send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds[r & 1]);
+    if (SEND && blockIdx.x * 256 < ctx) {  // uniform
+      send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds[nsend256 & 1]);
+      nsend256 += cand_plan(ctx).unit == 256 ? 1 : 0;
+    }
     if (!SEND) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) qr[i] = qn[i];
