@@ -36,8 +36,8 @@ INDEXER_SRC = os.path.join(ROOT, "sparse_attention_decode_paged_amd", "csrc", "i
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2400)
-    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--steps", type=int, default=240)
+    p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--ctx", type=int, default=CTX)
     p.add_argument("--layers", type=int, default=LAYERS)
     p.add_argument("--batch", type=int, default=1)
@@ -424,58 +424,53 @@ def main():
                             case.block_table, case.row_seq, case.row_ctx, max_ctx, K, case.sm_scale,
                             idx=idx, out=out, lse=lse, workspace=ws, rows_per_seq=rows_per_seq)
 
-    # Steps run from HIP graphs: one graph holds G steps (the layer rotation, repeated up
-    # to at least 24 steps so that one replay's launch cost is spread thin), and
-    # single-step graphs cover a remainder, so exactly `steps` layer-steps are timed
-    # with no host launch cost inside the timed region.
-    G = a.layers * -(-24 // a.layers)
+    # One launch form for any --steps: the timed region is one replay of a HIP graph that
+    # holds exactly `steps` layer-steps, rotating over the layers (layer i % layers), so no
+    # host launch cost falls inside it. Warm-up: eager steps before capture, then one replay
+    # of a graph of `warmup` steps (and one of the timed graph).
     cap = torch.cuda.Stream(dev)
     cap.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(cap):
         for i in range(2 * a.layers):  # eager warm-up before capture
             step(i)
     torch.cuda.synchronize()
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all, stream=cap):
-        for i in range(G):
-            step(i)
-    rem = a.steps % G
-    g_rem = []
-    for i in range(rem):
+
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            step(i)
-        g_rem.append(g)
-    torch.cuda.synchronize()
+            for i in range(n):
+                step(i)
+        return g
 
-    def run(nsteps):
-        for _ in range(nsteps // G):
-            g_all.replay()
-        for g in g_rem[: nsteps % G]:
-            g.replay()
-
-    run(max(a.warmup, G))
+    g_steps = capture(a.steps)
+    if a.warmup > 0:
+        g_warm = capture(a.warmup)
+        g_warm.replay()
+        del g_warm
+    g_steps.replay()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    run(a.steps)
+    g_steps.replay()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
 
-    # spread: each replay of the layer-rotation graph timed alone
-    nrep = max(5, min(100, a.steps // G))
+    # spread: more replays of the same graph, each timed alone
+    nrep = 9
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
     ev[0].record(stream)
     for i in range(nrep):
-        g_all.replay()
+        g_steps.replay()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    per = sorted(1000.0 * ev[i].elapsed_time(ev[i + 1]) / G for i in range(nrep))
+    per = sorted(1000.0 * ev[i].elapsed_time(ev[i + 1]) / a.steps for i in range(nrep))
     spread = {"p10": round(per[int(0.1 * (nrep - 1))], 3), "p50": round(per[(nrep - 1) // 2], 3),
-              "p90": round(per[int(0.9 * (nrep - 1))], 3), "replays": nrep, "steps_per_replay": G}
+              "p90": round(per[int(0.9 * (nrep - 1))], 3), "replays": nrep, "steps_per_replay": a.steps}
+    del g_steps
+    G = a.layers * -(-24 // a.layers)
     # the read ceiling needs a buffer far beyond the 256 MB last-level cache
     pool_bytes = case.pool.numel() * case.pool.element_size()
     ceiling = hbm_read_ceiling(dsa, case.pool) if pool_bytes >= (1 << 30) else None
@@ -519,7 +514,7 @@ def main():
             "name": a.config,
             "batch": R, "ctx": max_ctx, "k": K, "block_size": a.block_size, "layers_rotated": a.layers,
             "index_fmt": a.index_fmt, "latent_fmt": a.latent_fmt, "rows_per_seq": rows_per_seq,
-            "launch": "HIP graph replay, one decode step per layer",
+            "launch": "one HIP graph replay of exactly `steps` decode steps, layer i % layers for step i",
         },
         "step_us": spread,
         "step_hbm_gbps": round(step_gbps, 1) if step_gbps else None,

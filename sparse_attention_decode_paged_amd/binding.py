@@ -180,12 +180,15 @@ def dsa_indexer_score(pool, layout, layer, q_idx, q_idx_scale, w, block_table, r
     if scores is None:
         scores = torch.empty((R, ld_scores), dtype=torch.float32, device=pool.device)
     d = make_cache_desc(pool, layout)
-    st = L.dsa_indexer_score_multi(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
-                                   _dev(w, "w", torch.float32), _dev(block_table, "block_table", torch.int32),
-                                   _bt_stride(block_table), _dev(row_seq, "row_seq", torch.int32),
-                                   _dev(row_ctx, "row_ctx", torch.int32), R, int(max_ctx), int(rows_per_seq),
-                                   _dev(scores, "scores", torch.float32), int(ld_scores), _stream(pool.device))
-    _check(st, "dsa_indexer_score_multi")
+    args = [ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+            _dev(w, "w", torch.float32), _dev(block_table, "block_table", torch.int32),
+            _bt_stride(block_table), _dev(row_seq, "row_seq", torch.int32),
+            _dev(row_ctx, "row_ctx", torch.int32), R, int(max_ctx)]
+    tail = [_dev(scores, "scores", torch.float32), int(ld_scores), _stream(pool.device)]
+    if int(rows_per_seq) == 1:
+        _check(L.dsa_indexer_score(*args, *tail), "dsa_indexer_score")
+    else:
+        _check(L.dsa_indexer_score_multi(*args, int(rows_per_seq), *tail), "dsa_indexer_score_multi")
     return scores
 
 
@@ -303,15 +306,16 @@ def dsa_decode_step(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_tab
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     d = make_cache_desc(pool, layout)
-    st = L.dsa_decode_step_multi(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
-                                 _dev(w, "w", torch.float32), _dev(q_lat, "q_lat", torch.bfloat16),
-                                 _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
-                                 _dev(row_seq, "row_seq", torch.int32), _dev(row_ctx, "row_ctx", torch.int32), R,
-                                 int(max_ctx), int(k), int(rows_per_seq), float(sm_scale),
-                                 _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
-                                 _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
-                                 workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(st, "dsa_decode_step_multi")
+    head = [ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+            _dev(w, "w", torch.float32), _dev(q_lat, "q_lat", torch.bfloat16),
+            _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
+            _dev(row_seq, "row_seq", torch.int32), _dev(row_ctx, "row_ctx", torch.int32), R, int(max_ctx), int(k)]
+    tail = [_dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32), _dev(lse, "lse", torch.float32),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(dev)]
+    if int(rows_per_seq) == 1:
+        _check(L.dsa_decode_step(*head, float(sm_scale), *tail), "dsa_decode_step")
+    else:
+        _check(L.dsa_decode_step_multi(*head, int(rows_per_seq), float(sm_scale), *tail), "dsa_decode_step_multi")
     return idx, out, lse, workspace
 
 

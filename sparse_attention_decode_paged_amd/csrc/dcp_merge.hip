@@ -295,10 +295,10 @@ hipError_t launch_topk_dcp(const float* scores, int64_t ld, const int32_t* row_c
   const int RW = R * W;
   if (e == hipSuccess) e = launch_topk_send(d.shard, d.ls, d.shard_ctx, RW, lmax, d.tw, stream);
   if (e == hipSuccess)
-    e = launch_topk_select(d.shard, d.ls, d.shard_ctx, RW, lmax, M, d.idx_m, d.tw, nullptr, nullptr, nullptr,
+    e = launch_topk_select(d.shard, d.ls, d.shard_ctx, RW, lmax, M, 512, d.idx_m, d.tw, nullptr, nullptr, nullptr,
                            stream);
   if (e == hipSuccess)
-    e = launch_topk_select(d.shard, d.ls, d.shard_ctx, RW, lmax, k, d.idx_k, d.tw, nullptr, nullptr, nullptr,
+    e = launch_topk_select(d.shard, d.ls, d.shard_ctx, RW, lmax, k, 512, d.idx_k, d.tw, nullptr, nullptr, nullptr,
                            stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(dcp_merge_kernel, dim3(R), dim3(kNT), 0, stream, scores, ld, W, M, k, d.shard_ctx, d.idx_m,

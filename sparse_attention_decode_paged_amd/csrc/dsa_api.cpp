@@ -258,7 +258,8 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* row_c
   CacheView st{};  // no cache: carries only the status word
   st.status = status_word();
   hipError_t e = launch_topk_send(scores, ld_scores, row_ctx, R, max_ctx, tw, s);
-  if (e == hipSuccess) e = launch_topk_select(scores, ld_scores, row_ctx, R, max_ctx, k, idx, tw, nullptr, &st, nullptr, s);
+  if (e == hipSuccess)
+    e = launch_topk_select(scores, ld_scores, row_ctx, R, max_ctx, k, 512, idx, tw, nullptr, &st, nullptr, s);
   return hip_status(e, "topk");
 }
 
@@ -335,7 +336,10 @@ dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, con
   p += align_up((size_t)R * k * 4, 256);
   void* mla_ws = p;
   hipError_t e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld, &tw, s);
-  if (e == hipSuccess) e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, idx, tw, phys, &cv, &rm, s);
+  if (e == hipSuccess) {
+    const int umax = send_umax(cache->index_fmt == DSA_INDEX_FP8, rows_per_seq);
+    e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, umax, idx, tw, phys, &cv, &rm, s);
+  }
   if (e == hipSuccess) {
     // the selected tokens lie below max_ctx, so the row map's bound is unchanged
     e = launch_sparse_mla(cv, rm, q_lat, idx, phys, R, k, sm_scale, out, lse, mla_ws, s);

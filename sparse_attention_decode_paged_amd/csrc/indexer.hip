@@ -26,8 +26,10 @@
 // uniform loads; key scales come with one load and scores leave with one store per
 // 64 tokens.
 //
-// Epilogue for the exact top-k: each unit of 64 or 256 tokens sends its best m keys
-// (in token order) plus a floor (topk_send.h).
+// Epilogue for the exact top-k: each unit of 64, 256 or 512 tokens sends its best m
+// keys (in token order) plus a floor (topk_send.h). Workgroups of 512 tokens let rows
+// longer than 131,072 tokens use 512-token units, which halves the candidates the
+// select searches at 262,144 tokens (8,192 instead of 16,384).
 #include <type_traits>
 
 #include "common.h"
@@ -39,14 +41,16 @@ namespace dsa {
 namespace {
 constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kDIdx;  // 4 KB
+constexpr int NTI = 512;                      // threads (and tokens) of a workgroup
+constexpr int NWI = NTI / 64;
 
 // 16-byte chunk c of tile token tn sits at LDS byte tn*128 + 16*(c ^ (tn & 7)).
 __device__ __forceinline__ int swz(int tn, int c) { return tn * kDIdx + 16 * (c ^ (tn & 7)); }
 }  // namespace
 
-// One workgroup = 4 waves = 256 consecutive tokens of one row; wave w owns tokens
+// One workgroup = 8 waves = 512 consecutive tokens of one row; wave w owns tokens
 // [64w, 64w + 64) of it. PAGED32: block size >= 32, so a tile lies inside one page.
-// Waves past the row's end stay to the epilogue, whose 256-token units take a
+// Waves past the row's end stay to the epilogue, whose 256- and 512-token units take a
 // workgroup barrier. SEND: also run stage 1 of the top-k on the fresh scores.
 // EARLY (launches of several rows): workgroups past their row's end leave before
 // loading keys.
@@ -55,15 +59,15 @@ __device__ __forceinline__ int swz(int tn, int c) { return tn * kDIdx + 16 * (c 
 // arguments, not structures): the first loads of the dependent chain row -> block
 // table -> keys need no kernel-argument fetch before them.
 template <bool PAGED32, bool SEND, bool EARLY>
-__global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restrict__ row_seq,
+__global__ __launch_bounds__(NTI) void indexer_fp8_kernel(const int32_t* __restrict__ row_seq,
                                                           const int32_t* __restrict__ row_ctx,
                                                           const int32_t* __restrict__ block_table, CacheView cv,
                                                           RowMap rm, const uint8_t* __restrict__ q_idx,
                                                           const float* __restrict__ q_scale,
                                                           const float* __restrict__ w, float* __restrict__ scores,
                                                           int64_t ld, TopkWs tw) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4][kTileBytes];
-  __shared__ uint32_t send_lds[68];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NWI][kTileBytes];
+  __shared__ uint32_t send_lds[send_lds_words<NTI>()];
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -79,10 +83,10 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restr
     ctx = rm.max_ctx;
   }
   ctx = ctx < 0 ? 0 : ctx;
-  const bool past = blockIdx.x * 256 >= ctx;  // whole workgroup
+  const bool past = blockIdx.x * NTI >= ctx;  // whole workgroup
   if (EARLY && past) return;                  // no barrier reached
   ctx = ctx > 0 ? ctx : 1;
-  const int tok0 = blockIdx.x * 256 + wid * 64;
+  const int tok0 = blockIdx.x * NTI + wid * 64;
   const int bs_mask = cv.block_size - 1;
 
   // ---- key loads for both tiles: 4 x 1 KB of whole lines each. No branches: a tile
@@ -190,13 +194,13 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(const int32_t* __restr
   const int t = tok0 + lane;
   const float sc = (g ? res[1] : res[0]) * ksc;
   if (t < ctx) scores[(int64_t)r * ld + t] = sc;
-  if (SEND) send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds);
+  if (SEND) send_candidates<NTI>(sc, t < ctx, ctx, blockIdx.x * NTI, r, tw, send_lds);
 }
 
 hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const float* q_scale,
                               const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
                               hipStream_t stream) {
-  int nx = (rm.max_ctx + 255) / 256;
+  int nx = (rm.max_ctx + NTI - 1) / NTI;
   if (nx < 1) nx = 1;
   TopkWs tw = ws ? *ws : TopkWs{nullptr, nullptr, nullptr};
   const int send = (ws != nullptr && rm.max_ctx > kTopkFullRow) ? 1 : 0;
@@ -205,16 +209,16 @@ hipError_t launch_indexer_fp8(const CacheView& cv, const RowMap& rm, const uint8
   auto go = [&](auto early) {
     constexpr bool E = decltype(early)::value;
     if (send && p32)
-      hipLaunchKernelGGL((indexer_fp8_kernel<true, true, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+      hipLaunchKernelGGL((indexer_fp8_kernel<true, true, E>), grid, dim3(NTI), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
                          rm, q_idx, q_scale, w, scores, ld, tw);
     else if (send)
-      hipLaunchKernelGGL((indexer_fp8_kernel<false, true, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+      hipLaunchKernelGGL((indexer_fp8_kernel<false, true, E>), grid, dim3(NTI), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
                          rm, q_idx, q_scale, w, scores, ld, tw);
     else if (p32)
-      hipLaunchKernelGGL((indexer_fp8_kernel<true, false, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+      hipLaunchKernelGGL((indexer_fp8_kernel<true, false, E>), grid, dim3(NTI), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
                          rm, q_idx, q_scale, w, scores, ld, tw);
     else
-      hipLaunchKernelGGL((indexer_fp8_kernel<false, false, E>), grid, dim3(256), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
+      hipLaunchKernelGGL((indexer_fp8_kernel<false, false, E>), grid, dim3(NTI), 0, stream, rm.row_seq, rm.row_ctx, rm.block_table, cv,
                          rm, q_idx, q_scale, w, scores, ld, tw);
   };
   if (R > 1)

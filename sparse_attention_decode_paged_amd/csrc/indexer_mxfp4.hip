@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __res
                                                             const float* __restrict__ w, float* __restrict__ scores,
                                                             int64_t ld, TopkWs tw) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kTileBytes];
-  __shared__ uint32_t send_lds[68];
+  __shared__ uint32_t send_lds[send_lds_words<256>()];
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_kernel(const int32_t* __res
   const int t = tok0 + lane;
   const float sc = g ? res[1] : res[0];
   if (t < ctx) scores[(int64_t)r * ld + t] = sc;
-  if (SEND) send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds);
+  if (SEND) send_candidates<256>(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds);
 }
 
 hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const uint8_t* q_e8,

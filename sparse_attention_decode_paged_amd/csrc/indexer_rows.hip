@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
                                                                const float* __restrict__ w, float* __restrict__ scores,
                                                                int64_t ld, TopkWs tw, int R, int G) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kTileBytes];
-  __shared__ uint32_t send_lds[2][68];  // double-buffered over the rows that take the 256-token send
+  __shared__ uint32_t send_lds[2][send_lds_words<256>()];  // double-buffered over the rows that take the 256-token send
   __shared__ float wf_s[kRowsPerGroupMax * kHIdx];  // folded head weights w * q_scale of the group's rows
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     if (t < ctx) scores[(int64_t)r * ld + t] = sc;
     // the workgroup's span must reach into the row, or its unit would lie past the row
     if (SEND && blockIdx.x * 256 < ctx) {  // uniform
-      send_candidates(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds[nsend256 & 1]);
-      nsend256 += cand_plan(ctx).unit == 256 ? 1 : 0;
+      send_candidates<256>(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds[nsend256 & 1]);
+      nsend256 += cand_plan(ctx, 256).unit == 256 ? 1 : 0;
     }
     if (!SEND) {
 #pragma unroll

@@ -12,7 +12,6 @@ namespace dsa {
 // ---- top-k workspace -------------------------------------------------------------
 constexpr int kTopkFullRow = 16384;   // rows up to this length are selected from all their scores
 constexpr int kCandRowCap = 16384;    // candidate keys a row sends in total (select stage registers)
-constexpr int kCandPerUnitMax = 16;   // candidate keys a unit sends, at most
 constexpr int kMaxCtx = 1 << 20;      // largest supported context
 constexpr int kFloorRowCap = kMaxCtx / 256;  // units of a row, at most
 
@@ -21,7 +20,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // A candidate key is kept as two words at the same slot of two arrays, so that the
 // select can load the score words (all its search passes need) ahead of the tokens.
 struct TopkWs {
-  uint32_t* cand_hi;  // [R][kCandRowCap]: score word of rank q of unit u at cand_slot(q, u, m); 0 = empty
+  uint32_t* cand_hi;  // [R][kCandRowCap]: score word of rank q of unit u at slot u m + q; 0 = empty
   uint32_t* cand_lo;  // [R][kCandRowCap]: its token word (0xFFFFFFFF - token)
   uint32_t* floors;   // [R][kFloorRowCap]: score word bounding the keys a unit did not send (0: sent all)
 };
@@ -163,9 +162,16 @@ hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_
 // Selection; when `phys` is non-null it also receives, per selected token, its page
 // slot (physical block * block_size + slot) for the attention kernel (cv and rm are
 // then required; without page slots cv may carry just the status word, or be null).
+// umax: the largest unit (tokens) of the candidate producer, its workgroup size (256 or
+// 512), which fixes every row's candidate plan.
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
-                              int32_t* idx, const TopkWs& ws, int32_t* phys, const CacheView* cv, const RowMap* rm,
-                              hipStream_t stream);
+                              int umax, int32_t* idx, const TopkWs& ws, int32_t* phys, const CacheView* cv,
+                              const RowMap* rm, hipStream_t stream);
+// Workgroup size of the candidate producer the decode step uses for a key format and
+// row grouping (the FP8 per-row indexer and the standalone send run 512 threads).
+inline int send_umax(int32_t index_fmt_is_fp8, int32_t rows_per_seq) {
+  return (index_fmt_is_fp8 && rows_per_seq <= 1) ? 512 : 256;
+}
 
 // Sparse MLA over idx; when `phys` (page slots from the selection) is non-null it
 // replaces the block-table lookups.

@@ -189,8 +189,8 @@ __device__ __forceinline__ void block_minmax32(uint32_t& lo, uint32_t& hi, SelSh
 }
 
 // The need-th largest (1 <= need <= number of live keys) of the nonzero keys in
-// kh[]/kl[] and, with EXTRA, in xs[0, nx) (LDS, thread t reading xs[t + SEL_NT j]), held
-// across the workgroup. Keys are distinct.
+// kh[0, N)/kl[0, N) and, with EXTRA, in xs[0, nx) (LDS, thread t reading xs[t + SEL_NT j]),
+// held across the workgroup. Keys are distinct.
 __device__ __forceinline__ void clear_hist(SelShared& S) {
   constexpr int Q = (NBIN * NREP / 4 + SEL_NT - 1) / SEL_NT;  // 16-byte stores per thread
   v4i* hz = reinterpret_cast<v4i*>(S.a.hist);
@@ -223,7 +223,7 @@ __device__ __forceinline__ void bin_pair(const SelShared& S, int tid, uint32_t& 
 // while the digit scan runs. PRECLEARED: the caller has already zeroed the histogram
 // and the bucket count (before its first barrier).
 template <int N, bool EXTRA, bool PRECLEARED = false, typename Late>
-__device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[N], const uint32_t (&kl)[N], const uint64_t* xs,
+__device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[PER], const uint32_t (&kl)[PER], const uint64_t* xs,
                                                 uint32_t nx, uint32_t need, SelShared& S, int& par, Late&& late) {
   const int tid = threadIdx.x, lane = tid & 63;
   // fn(score word, token word) over the register keys, then (only when the LDS list
@@ -382,31 +382,6 @@ __device__ __forceinline__ int32_t page_slot(const CacheView& cv, const RowMap& 
 
 __device__ __forceinline__ int key_token(uint64_t c) { return (int)(0xFFFFFFFFu - (uint32_t)c); }
 
-// Page slot of token t, from the staged block-table row when `btl`.
-__device__ __forceinline__ int32_t slot_of(const SelShared& S, bool btl, const CacheView& cv, const RowMap& rm, int seq,
-                                           int t) {
-  if (btl) return S.bt[t >> cv.log2_bs] * cv.block_size + (t & (cv.block_size - 1));
-  return page_slot(cv, rm, seq, t);
-}
-
-// Second half of the output write: S.a.hist (free once the search is done) holds the
-// `total` selected tokens in output order; every thread writes positions tid and
-// tid + 1024 of the index row (and of the page-slot row), -1 past the selection.
-__device__ __forceinline__ void flush_selection(uint32_t total, int k, int32_t* __restrict__ orow,
-                                                int32_t* __restrict__ prow, const CacheView& cv, const RowMap& rm,
-                                                int seq, bool btl, const SelShared& S) {
-  const uint32_t nout = total < (uint32_t)k ? total : (uint32_t)k;
-#pragma unroll
-  for (int q = 0; q < kMaxK / SEL_NT; ++q) {
-    const int i = (int)threadIdx.x + SEL_NT * q;
-    if (i < k) {
-      const int t = (uint32_t)i < nout ? (int)S.a.hist[i] : -1;
-      orow[i] = t;
-      if (prow) prow[i] = t >= 0 ? slot_of(S, btl, cv, rm, seq, t) : -1;
-    }
-  }
-}
-
 // Exact selection over the whole row straight from global memory (8-bit digits,
 // per-wave LDS histograms), then a sort of the k tokens. Only reached when the
 // rescans outgrow LDS (e.g. scores tied across far more than k tokens).
@@ -487,386 +462,445 @@ __device__ __forceinline__ void select_row_global(const float* __restrict__ srow
 }  // namespace
 
 // Stage 1 over an existing score array (the standalone top-k entry point): one
-// workgroup per 256 tokens of a row, all threads reaching the send.
-__global__ __launch_bounds__(256) void topk_send_kernel(const float* __restrict__ scores, int64_t ld,
+// workgroup of 512 threads per 512 tokens of a row, all threads reaching the send.
+__global__ __launch_bounds__(512) void topk_send_kernel(const float* __restrict__ scores, int64_t ld,
                                                         const int32_t* __restrict__ row_ctx, int max_ctx,
                                                         TopkWs ws) {
-  __shared__ uint32_t send_lds[68];
+  __shared__ uint32_t send_lds[send_lds_words<512>()];
   const int r = blockIdx.y;
   const int ctx = clamp_ctx(row_ctx, r, max_ctx, nullptr);  // the select reports it
-  const int base = blockIdx.x * 256;
+  const int base = blockIdx.x * 512;
   if (base >= ctx) return;  // whole workgroup
   const int t = base + threadIdx.x;
   const bool valid = t < ctx;
   const float s = valid ? scores[(int64_t)r * ld + t] : 0.f;
-  send_candidates(s, valid, ctx, base, r, ws, send_lds);
+  send_candidates<512>(s, valid, ctx, base, r, ws, send_lds);
 }
 
-// CAND: rows may be longer than kTopkFullRow, so candidates were sent.
-template <bool CAND>
-// The candidate arrays lead the argument list so that their addresses arrive preloaded in
-// scalar registers (kernel-argument preloading covers leading scalar and pointer
-// arguments, not structures) and the candidate loads start with the kernel.
-__global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __restrict__ cand_hi,
-                                                             const uint32_t* __restrict__ cand_lo,
-                                                             const uint32_t* __restrict__ floors,
-                                                             const float* __restrict__ scores, int64_t ld,
-                                                             const int32_t* __restrict__ row_ctx, int max_ctx, int k,
-                                                             int32_t* __restrict__ idx, int32_t* __restrict__ phys,
-                                                             CacheView cv, RowMap rm) {
-  const TopkWs ws{const_cast<uint32_t*>(cand_hi), const_cast<uint32_t*>(cand_lo), const_cast<uint32_t*>(floors)};
-  __shared__ SelShared S;
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  // The candidates' score words load first, alone: their addresses need only the kernel
-  // arguments, so they go out with the row's length (slots the row's plan does not use
-  // are cleared once the length is known), and the first search needs nothing else. The
-  // token words, unit floors and block-table entries are issued after the search's first
-  // histogram pass, so that one workgroup's load bandwidth goes to the score words first.
-  uint32_t kh[PER], kl[PER];
-  uint32_t fl[4] = {0u, 0u, 0u, 0u};
-  if (CAND) {
-    const uint32_t* ch = ws.cand_hi + (int64_t)r * kCandRowCap;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) kh[i] = ch[i * SEL_NT + tid];
-  }
-  const int ctx = clamp_ctx(row_ctx, r, max_ctx, cv.status);
-  const int seq = rm.row_seq[r];  // the launch points row_seq at row_ctx when there are no page slots
-  int32_t* orow = idx + (int64_t)r * k;
-  int32_t* prow = phys ? phys + (int64_t)r * k : nullptr;
-  const float* srow = scores + (int64_t)r * ld;
-  int par = 0;
-  auto write_all = [&]() {  // ctx <= k: every token, in order
-    for (int i = tid; i < k; i += SEL_NT) {
-      orow[i] = i < ctx ? i : -1;
-      if (prow) prow[i] = i < ctx ? page_slot(cv, rm, seq, i) : -1;
-    }
-  };
-  if (!CAND && ctx <= k) {
-    write_all();
-    return;
-  }
+namespace {
 
-  // the row's block-table entries for the page slots of the output, staged in LDS;
-  // one dependent global load per written token would otherwise sit on the write path
-  const int nblk = (ctx + cv.block_size - 1) >> cv.log2_bs;
-  const bool btl = prow != nullptr && nblk <= BTCAP;
+// Register i of thread t holds slot (candidate rows) or token (own-key rows)
+// 8 t + i for i < 8 ("run A") and 8192 + 8 t + (i - 8) for i >= 8 ("run B"): thread
+// order is slot order inside each run, and run A precedes run B.
+__device__ __forceinline__ int reg_slot(int i) {
+  return (i < 8 ? 0 : kCandRowCap / 2 - 8) + 8 * (int)threadIdx.x + i;
+}
+
+// Eight consecutive words at p (16-byte aligned) into v[0..8).
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, T* v) {
+  const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
+  v[0] = __builtin_bit_cast(T, a.x); v[1] = __builtin_bit_cast(T, a.y);
+  v[2] = __builtin_bit_cast(T, a.z); v[3] = __builtin_bit_cast(T, a.w);
+  v[4] = __builtin_bit_cast(T, b.x); v[5] = __builtin_bit_cast(T, b.y);
+  v[6] = __builtin_bit_cast(T, b.z); v[7] = __builtin_bit_cast(T, b.w);
+}
+
+// Everything the per-row body needs besides the register keys.
+struct SelRow {
+  int ctx, k, seq;
+  const float* srow;
+  const uint32_t* clo;   // the row's candidate token words
+  const uint32_t* flr;   // the row's unit floors
+  int32_t* orow;
+  int32_t* prow;
+  CacheView cv;
+  RowMap rm;
+};
+
+// Page slot of token t from the row's block-table entries staged in LDS (btl) or read.
+__device__ __forceinline__ int32_t out_slot(const SelShared& S, bool btl, const SelRow& R, int t) {
+  return btl ? S.bt[t >> R.cv.log2_bs] * R.cv.block_size + (t & (R.cv.block_size - 1))
+             : page_slot(R.cv, R.rm, R.seq, t);
+}
+
+// The row's block-table entries go to LDS for the output's page slots when they fit.
+struct BtStage {
+  bool btl;
+  int nblk;
   int32_t bv[BTCAP / SEL_NT];
-  auto load_bt = [&]() {
+  __device__ __forceinline__ void load(const SelRow& R) {
+    nblk = (R.ctx + R.cv.block_size - 1) >> R.cv.log2_bs;
+    btl = R.prow != nullptr && nblk <= BTCAP;
     if (!btl) return;
-    const int32_t* btr = rm.block_table + (int64_t)seq * rm.bt_stride;
+    const int32_t* btr = R.rm.block_table + (int64_t)R.seq * R.rm.bt_stride;
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
-      const int i = tid + SEL_NT * q;
+      const int i = (int)threadIdx.x + SEL_NT * q;
       bv[q] = i < nblk ? btr[i] : 0;
     }
-  };
-  if (!CAND) load_bt();
-  // The entries reach LDS after the first search: they sit one scalar round trip
-  // further down the load chain than the candidates, and a store waiting for them
-  // ahead of the search's first barrier would hold every wave.
-  auto stage_bt = [&]() {
+  }
+  __device__ __forceinline__ void stage(const SelRow& R, SelShared& S) {
     if (!btl) return;
-    const int64_t nb = cv.num_blocks;
+    const int64_t nb = R.cv.num_blocks;
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
-      const int i = tid + SEL_NT * q;
+      const int i = (int)threadIdx.x + SEL_NT * q;
       int64_t b = bv[q];
       if (i < nblk && (uint64_t)b >= (uint64_t)nb) {
-        raise_status(cv.status, kStBlockClamped);
+        raise_status(R.cv.status, kStBlockClamped);
         b = b < 0 ? 0 : nb - 1;
       }
       if (i < nblk) S.bt[i] = (int32_t)b;
     }
-  };
+  }
+};
 
-  // The row's own keys (rows of at most kTopkFullRow tokens): thread t holds tokens
-  // [16 t, 16 t + 16), one 16-key unit per thread.
-  auto load_own = [&]() {
-    const int t0 = tid * PER;
-    float f[PER];
-    if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0 && t0 + PER <= ctx) {
-      const float4* p4 = reinterpret_cast<const float4*>(srow + t0);
+// Second half of the output: S.a.hist (free once the search is done) holds the `total`
+// selected tokens in output order; every thread writes positions tid and tid + 1024 of
+// the index row (and of the page-slot row), -1 past the selection.
+__device__ __forceinline__ void flush_list(uint32_t total, const SelRow& R, const BtStage& B, const SelShared& S) {
+  const uint32_t nout = total < (uint32_t)R.k ? total : (uint32_t)R.k;
 #pragma unroll
-      for (int x = 0; x < PER / 4; ++x) {
-        const float4 v = p4[x];
-        f[4 * x] = v.x;
-        f[4 * x + 1] = v.y;
-        f[4 * x + 2] = v.z;
-        f[4 * x + 3] = v.w;
+  for (int q = 0; q < kMaxK / SEL_NT; ++q) {
+    const int i = (int)threadIdx.x + SEL_NT * q;
+    if (i < R.k) {
+      const int t = (uint32_t)i < nout ? (int)S.a.hist[i] : -1;
+      R.orow[i] = t;
+      if (R.prow) R.prow[i] = t >= 0 ? out_slot(S, B.btl, R, t) : -1;
+    }
+  }
+}
+
+// Rows whose own scores are held (at most 16384 tokens): N = 8 or 16 tokens per thread.
+template <int N>
+__device__ __forceinline__ void select_own(SelShared& S, uint32_t (&kh)[PER], uint32_t (&kl)[PER], const SelRow& R,
+                                           int& par) {
+  BtStage B;
+  B.load(R);
+  // the row's keys: tokens reg_slot(i) < ctx
+  {
+    const int t0 = 8 * (int)threadIdx.x;
+    const bool al = (reinterpret_cast<uintptr_t>(R.srow) & 15u) == 0;
+#pragma unroll
+    for (int h = 0; h < N / 8; ++h) {
+      const int b0 = t0 + h * (kCandRowCap / 2);
+      float f[8];
+      if (al && b0 + 8 <= R.ctx) {
+        load8(R.srow + b0, f);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = b0 + i < R.ctx ? R.srow[b0 + i] : 0.f;
       }
-    } else {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) f[i] = t0 + i < ctx ? srow[t0 + i] : 0.f;
+      for (int i = 0; i < 8; ++i) {
+        const int t = b0 + i;
+        const uint64_t key = t < R.ctx ? composite_key(f[i], t) : 0ull;
+        kh[8 * h + i] = (uint32_t)(key >> 32);
+        kl[8 * h + i] = (uint32_t)key;
+      }
     }
+  }
+  const uint64_t cstar = kth_largest<N, false>(kh, kl, nullptr, 0u, (uint32_t)R.k, S, par, [] {});
+  B.stage(R, S);
+  uint32_t bits = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int t = t0 + i;
-      const uint64_t key = t < ctx ? composite_key(f[i], t) : 0ull;
-      kh[i] = (uint32_t)(key >> 32);
-      kl[i] = (uint32_t)key;
-    }
-  };
+  for (int i = 0; i < N; ++i)
+    if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
+  uint32_t v[4] = {(uint32_t)__popc(bits & 0xFFu), (uint32_t)__popc(bits >> 8), 0u, 0u}, off[4], tot[4];
+  excl_scan4(v, off, tot, N / 8, S);
+  const uint32_t base[2] = {off[0], tot[0] + off[1]};
+  uint32_t* list = S.a.hist;  // free since the search
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t o = base[i >> 3] + (uint32_t)__popc(bits & (0xFFu << (i & ~7)) & ((1u << i) - 1u));
+    if (((bits >> i) & 1u) && o < (uint32_t)R.k) list[o] = 0xFFFFFFFFu - kl[i];
+  }
+  __syncthreads();
+  flush_list(tot[0] + (N > 8 ? tot[1] : 0u), R, B, S);
+}
 
-  // Unit layout of the register keys: thread t holds units t + 1024 j (j < upt) with m
-  // keys each, unit j in slots [m j, m j + m). Candidates: slot q + m j = rank q of unit
-  // t + 1024 j. Own keys: m = 16, upt = 1.
-  int m = PER, lm = 4, upt = 1;
-  uint32_t fmask = 0, fbase = 0, nflag = 0;
-  uint64_t cstar;
-  if (!CAND) {
-    load_own();
-    cstar = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par, [] {});
-    stage_bt();
-  } else {
-    const CandPlan p = cand_plan(ctx);
-    m = p.m;
-    lm = 31 - __clz(m);
-    upt = (p.nu + SEL_NT - 1) / SEL_NT;  // 1, 2 or 4; upt * m <= 16
-    uint32_t umine = 0;                  // this thread's units that exist
+// Candidate rows: register slots hold the units' sent keys (plan p, N = p.per).
+// Segment j of a thread's registers: m >= 8 -> j = 0 (registers 0..7) and j = 2
+// (8..15), one unit each; m = 4 -> j = 0..3, registers [4 j, 4 j + 4), one unit each.
+template <int N>
+__device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], uint32_t (&kl)[PER], const SelRow& R,
+                                            const CandPlan& p, int& par) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nslot = p.nu * p.m;
+  const bool quarter = p.m < 8;  // m = 4: four one-unit segments of four registers
+  const uint32_t segmask[4] = {quarter ? 0x000Fu : 0x00FFu, quarter ? 0x00F0u : 0u,
+                               quarter ? 0x0F00u : (N > 8 ? 0xFF00u : 0u), quarter ? 0xF000u : 0u};
+  int segu[4];  // unit of each segment (-1: none)
+  bool segfirst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int s0 = (j < 2 ? 0 : kCandRowCap / 2) + 8 * tid + (quarter ? 4 * (j & 1) : 0);
+    const bool has = segmask[j] != 0u && s0 < nslot && (j < 2 || N > 8);
+    segu[j] = has ? s0 / p.m : -1;
+    segfirst[j] = has && (s0 % p.m) == 0;
+  }
+  // slots past the row's units hold no candidate
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (reg_slot(i) >= nslot) kh[i] = 0u;
+
+  BtStage B;
+  uint32_t fl[4] = {0u, 0u, 0u, 0u};
+  auto late = [&]() {
+#pragma unroll
+    for (int h = 0; h < N / 8; ++h) load8(R.clo + 8 * tid + h * (kCandRowCap / 2), kl + 8 * h);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (j < upt && tid + SEL_NT * j < p.nu) umine |= 1u << j;
-    // the search's histogram and bucket count are cleared while the score words are in
-    // flight (ordered before the first pass by the search's first barrier)
-    if (tid == 0) S.bcount = 0u;
-    clear_hist(S);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (!((umine >> (i >> lm)) & 1u)) kh[i] = 0u;
-    auto late = [&]() {
-      const uint32_t* cl = ws.cand_lo + (int64_t)r * kCandRowCap;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) kl[i] = cl[i * SEL_NT + tid];
-      const uint32_t* rf = ws.floors + (int64_t)r * kFloorRowCap;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < upt) fl[j] = rf[tid + SEL_NT * j];
-      load_bt();
-    };
-    // The first search comes before the short-row exits so that nothing between the
-    // kernel's start and the first use of the candidates is a branch (a branch lets
-    // the compiler sink the loads behind the row-length round trip).
-    const uint64_t c1 = kth_largest<PER, false, true>(kh, kl, nullptr, 0u, (uint32_t)k, S, par, late);
-    if (ctx <= k) {
-      write_all();
-      return;
-    }
-    if (ctx <= kTopkFullRow) {
-      // A short row in a launch with longer rows: its own scores, read whole, take one
-      // search. (Its 64-token units sent a quarter of their tokens, which can be fewer
-      // than k, and every unit would need a rescan.)
-      load_own();
-      cstar = kth_largest<PER, false>(kh, kl, nullptr, 0u, (uint32_t)k, S, par, [] {});
-      stage_bt();
-      m = PER;
-      lm = 4;
-      upt = 1;
-    } else {
-      stage_bt();
-      // Rows longer than kTopkFullRow sent at least 4096 >= k candidates (a 64-token unit
-      // sends a quarter of its tokens, a 256-token unit m with nu * m >= 4096).
-      const uint64_t cu = c1;
-      const uint32_t cu_hi = (uint32_t)(cu >> 32);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (((umine >> j) & 1u) && fl[j] != 0u && fl[j] >= cu_hi) fmask |= 1u << j;
-      cstar = c1;
-      if (upt < 4) {
-        // Common case first: one block scan gives both the number of flagged units and,
-        // were there none, every unit's output offset, so with no flagged unit the
-        // selection is written without a second scan.
-        uint32_t bits = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-          if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= c1) bits |= 1u << i;
-        const uint32_t umask = m >= 16 ? 0xFFFFu : ((1u << m) - 1u);
-        uint32_t v[4] = {(uint32_t)__popc(fmask), 0u, 0u, 0u}, off[4], tot[4];
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-          if (j < upt) v[1 + j] = (uint32_t)__popc(bits & ((umask << (m * j)) & 0xFFFFu));
-        excl_scan4(v, off, tot, upt + 1, S);
-        nflag = tot[0];
-        fbase = off[0];
-        if (nflag == 0) {
-          uint32_t base = 0, uoff[3];
-#pragma unroll
-          for (int j = 0; j < 3; ++j) {
-            uoff[j] = base + off[1 + j];
-            base += j < upt ? tot[1 + j] : 0u;
-          }
-          const uint32_t total = base;
-          uint32_t* list = S.a.hist;  // free since the search
-#pragma unroll
-          for (int i = 0; i < PER; ++i) {
-            const int j = i >> lm;
-            const uint32_t oj = j == 0 ? uoff[0] : j == 1 ? uoff[1] : uoff[2];
-            const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
-            if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = 0xFFFFFFFFu - kl[i];
-          }
-          __syncthreads();
-          flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
-          return;
-        }
-        __syncthreads();  // the write path below runs its own scan4
-      } else {
-        fbase = excl_scan((uint32_t)__popc(fmask), nflag, S, par);
-      }
-      if (nflag > 0) {
-        if (nflag > (uint32_t)FCAP) {
-          select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
-          return;
-        }
-        // ---- resend: each flagged unit's keys >= c_u, rescanned by one wave per unit ----
-        {
-          uint32_t fm = fmask, sl = fbase;
-          while (fm) {
-            const int j = __ffs(fm) - 1;
-            fm &= fm - 1u;
-            S.funit[sl++] = (uint32_t)(tid + SEL_NT * j);
-          }
-        }
-        if (tid == 0) S.ecount = 0u;
-        __syncthreads();
-        const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1 or 4
-        for (uint32_t sl = wid; sl < nflag; sl += NW) {
-          const int t0 = (int)S.funit[sl] * p.unit;
-          float f[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int t = t0 + 64 * c + lane;
-            f[c] = (c < chunks && t < ctx) ? srow[t] : 0.f;
-          }
-          uint64_t bal[4];
-          uint32_t tot = 0;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int t = t0 + 64 * c + lane;
-            const bool keep = c < chunks && t < ctx && composite_key(f[c], t) >= cu;
-            bal[c] = __ballot(keep);
-            tot += (uint32_t)__popcll(bal[c]);
-          }
-          uint32_t st = 0;
-          if (lane == 0) st = atomicAdd(&S.ecount, tot);
-          st = (uint32_t)__shfl((int)st, 0, 64);
-          uint32_t run = st;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int t = t0 + 64 * c + lane;
-            const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
-            if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
-            run += (uint32_t)__popcll(bal[c]);
-          }
-          if (lane == 0) {
-            S.fstart[sl] = st;
-            S.flen[sl] = tot;
-          }
-        }
-        __syncthreads();
-        const uint32_t ne = S.ecount;
-        if (ne > (uint32_t)ECAP) {
-          select_row_global(srow, ctx, k, S, orow, prow, cv, rm, seq);
-          return;
-        }
-        // union: unflagged candidates >= c_u in registers, rescanned keys from LDS
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const bool flagged = (fmask >> (i >> lm)) & 1u;
-          if (flagged || (((uint64_t)kh[i] << 32) | kl[i]) < cu) kh[i] = 0u;
-        }
-        cstar = kth_largest<PER, true>(kh, kl, S.a.ext, ne, (uint32_t)k, S, par, [] {});
-        // selected keys of each rescanned unit
-        for (uint32_t sl = wid; sl < nflag; sl += NW) {
-          const uint32_t st = S.fstart[sl], len = S.flen[sl];
-          uint32_t c = 0;
-          for (uint32_t q0 = 0; q0 < len; q0 += 64) {
-            const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
-            c += (uint32_t)__popcll(__ballot(sel));
-          }
-          if (lane == 0) S.fcnt[sl] = c;
-        }
-        __syncthreads();
-      }
-    }  // rows longer than kTopkFullRow
-  }
-
-  // ---- ordered write: unit counts, prefix sums over units (unit u = tid + 1024 j) ----
-  uint32_t bits = 0;  // selected register keys
-#pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
-  const uint32_t umask = m >= 16 ? 0xFFFFu : ((1u << m) - 1u);  // keys of one unit
-  uint32_t cnt[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t mj = j < upt ? (umask << (m * j)) & 0xFFFFu : 0u;
-    cnt[j] = (fmask >> j) & 1u ? S.fcnt[fbase + (uint32_t)__popc(fmask & ((1u << j) - 1u))]
-                               : (uint32_t)__popc(bits & mj);
-  }
-  uint32_t off[4], tot[4];
-  excl_scan4(cnt, off, tot, upt, S);
-  uint32_t base = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    off[j] += base;
-    base += tot[j];
-  }
-  const uint32_t total = base;
+      if (segu[j] >= 0) fl[j] = R.flr[segu[j]];
+    B.load(R);
+  };
+  // the search's histogram and bucket count were cleared by the caller
+  const uint64_t cu = kth_largest<N, false, true>(kh, kl, nullptr, 0u, (uint32_t)R.k, S, par, late);
+  B.stage(R, S);
+  const uint32_t cu_hi = (uint32_t)(cu >> 32);
+  uint32_t fmask = 0;  // flagged segments: their unit may hold unsent keys >= cu
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    if ((fmask >> j) & 1u) S.foff[fbase + (uint32_t)__popc(fmask & ((1u << j) - 1u))] = off[j];
-  // selected tokens go to their output positions in an LDS list first (the histogram
-  // is free now), then one coalesced pass writes the index and page-slot rows
-  uint32_t* list = S.a.hist;
+    if (segu[j] >= 0 && fl[j] != 0u && fl[j] >= cu_hi) fmask |= 1u << j;
+  // Common case first: one scan gives the number of flagged units and, were there none,
+  // every register key's output offset.
+  uint32_t bits = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int j = i >> lm;
-    const uint32_t oj = j == 0 ? off[0] : j == 1 ? off[1] : j == 2 ? off[2] : off[3];
-    const uint32_t o = oj + (uint32_t)__popc(bits & (umask << (m * j)) & ((1u << i) - 1u));
-    if (((bits >> i) & 1u) && o < (uint32_t)k) list[o] = 0xFFFFFFFFu - kl[i];
-  }
-  if (nflag > 0) {
+  for (int i = 0; i < N; ++i)
+    if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cu) bits |= 1u << i;
+  uint32_t nfl[2] = {0u, 0u};  // flagged units this thread registers, runs A and B
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (((fmask >> j) & 1u) && segfirst[j]) nfl[j >> 1]++;
+  {
+    uint32_t v[4] = {nfl[0], nfl[1], (uint32_t)__popc(bits & 0xFFu), (uint32_t)__popc(bits >> 8)}, off[4], tot[4];
+    excl_scan4(v, off, tot, N > 8 ? 4 : 3, S);
+    const uint32_t nflag = tot[0] + tot[1];
+    if (nflag == 0) {
+      const uint32_t base[2] = {off[2], tot[2] + off[3]};
+      uint32_t* list = S.a.hist;  // free since the search
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const uint32_t o = base[i >> 3] + (uint32_t)__popc(bits & (0xFFu << (i & ~7)) & ((1u << i) - 1u));
+        if (((bits >> i) & 1u) && o < (uint32_t)R.k) list[o] = 0xFFFFFFFFu - kl[i];
+      }
+      __syncthreads();
+      flush_list(tot[2] + (N > 8 ? tot[3] : 0u), R, B, S);
+      return;
+    }
+    if (nflag > (uint32_t)FCAP) {
+      select_row_global(R.srow, R.ctx, R.k, S, R.orow, R.prow, R.cv, R.rm, R.seq);
+      return;
+    }
+    // ---- resend: each flagged unit's keys >= cu, rescanned by one wave per unit ----
+    uint32_t sl[2] = {off[0], tot[0] + off[1]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (((fmask >> j) & 1u) && segfirst[j]) S.funit[sl[j >> 1]++] = (uint32_t)segu[j];
+    if (tid == 0) S.ecount = 0u;
     __syncthreads();
-    for (uint32_t sl = wid; sl < nflag; sl += NW) {
-      const uint32_t st = S.fstart[sl], len = S.flen[sl];
-      uint32_t o = S.foff[sl];
+    const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1, 4 or 8
+    for (uint32_t q = wid; q < nflag; q += NW) {
+      const int t0 = (int)S.funit[q] * p.unit;
+      float f[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int t = t0 + 64 * c + lane;
+        f[c] = (c < chunks && t < R.ctx) ? R.srow[t] : 0.f;
+      }
+      uint64_t bal[8];
+      uint32_t tot8 = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int t = t0 + 64 * c + lane;
+        const bool keep = c < chunks && t < R.ctx && composite_key(f[c], t) >= cu;
+        bal[c] = __ballot(keep);
+        tot8 += (uint32_t)__popcll(bal[c]);
+      }
+      uint32_t st = 0;
+      if (lane == 0) st = atomicAdd(&S.ecount, tot8);
+      st = (uint32_t)__shfl((int)st, 0, 64);
+      uint32_t run = st;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int t = t0 + 64 * c + lane;
+        const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
+        if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
+        run += (uint32_t)__popcll(bal[c]);
+      }
+      if (lane == 0) {
+        S.fstart[q] = st;
+        S.flen[q] = tot8;
+      }
+    }
+    __syncthreads();
+    const uint32_t ne = S.ecount;
+    if (ne > (uint32_t)ECAP) {
+      select_row_global(R.srow, R.ctx, R.k, S, R.orow, R.prow, R.cv, R.rm, R.seq);
+      return;
+    }
+    // union: unflagged candidates >= cu in registers, rescanned keys from LDS
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = quarter ? (i >> 2) : ((i >> 3) << 1);
+      if (((fmask >> j) & 1u) || (((uint64_t)kh[i] << 32) | kl[i]) < cu) kh[i] = 0u;
+    }
+    const uint64_t cstar = kth_largest<N, true>(kh, kl, S.a.ext, ne, (uint32_t)R.k, S, par, [] {});
+    // selected keys of each rescanned unit
+    for (uint32_t q = wid; q < nflag; q += NW) {
+      const uint32_t st = S.fstart[q], len = S.flen[q];
+      uint32_t c = 0;
+      for (uint32_t q0 = 0; q0 < len; q0 += 64) {
+        const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
+        c += (uint32_t)__popcll(__ballot(sel));
+      }
+      if (lane == 0) S.fcnt[q] = c;
+    }
+    __syncthreads();
+    // ---- ordered write: segment counts in token order, one scan per run ----
+    bits = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
+    uint32_t segc[4];
+    uint32_t fsl[2] = {off[0], tot[0] + off[1]};  // this thread's first registered slot per run
+    int fslot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      fslot[j] = -1;
+      if ((fmask >> j) & 1u) {
+        if (segfirst[j]) {
+          fslot[j] = (int)fsl[j >> 1]++;
+          segc[j] = S.fcnt[fslot[j]];
+        } else {
+          segc[j] = 0u;
+        }
+      } else {
+        segc[j] = (uint32_t)__popc(bits & segmask[j]);
+      }
+    }
+    uint32_t v2[4] = {segc[0] + segc[1], segc[2] + segc[3], 0u, 0u}, off2[4], tot2[4];
+    __syncthreads();  // the first scan's partials are rewritten
+    excl_scan4(v2, off2, tot2, N > 8 ? 2 : 1, S);
+    uint32_t segoff[4];
+    segoff[0] = off2[0];
+    segoff[1] = off2[0] + segc[0];
+    segoff[2] = tot2[0] + off2[1];
+    segoff[3] = segoff[2] + segc[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (fslot[j] >= 0) S.foff[fslot[j]] = segoff[j];
+    uint32_t* list = S.a.hist;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = quarter ? (i >> 2) : ((i >> 3) << 1);
+      const uint32_t o = segoff[j] + (uint32_t)__popc(bits & segmask[j] & ((1u << i) - 1u));
+      if (((bits >> i) & 1u) && o < (uint32_t)R.k) list[o] = 0xFFFFFFFFu - kl[i];
+    }
+    __syncthreads();
+    for (uint32_t q = wid; q < nflag; q += NW) {
+      const uint32_t st = S.fstart[q], len = S.flen[q];
+      uint32_t o = S.foff[q];
       for (uint32_t q0 = 0; q0 < len; q0 += 64) {
         const uint64_t c = q0 + (uint32_t)lane < len ? S.a.ext[st + q0 + lane] : 0ull;
         const bool sel = c != 0ull && c >= cstar;
         const uint64_t bal = __ballot(sel);
         const uint32_t pos = o + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        if (sel && pos < (uint32_t)k) list[pos] = (uint32_t)key_token(c);
+        if (sel && pos < (uint32_t)R.k) list[pos] = (uint32_t)key_token(c);
         o += (uint32_t)__popcll(bal);
       }
     }
+    __syncthreads();
+    flush_list(tot2[0] + (N > 8 ? tot2[1] : 0u), R, B, S);
   }
-  __syncthreads();
-  flush_selection(total, k, orow, prow, cv, rm, seq, btl, S);
+}
+
+}  // namespace
+
+// CAND: rows may be longer than kTopkFullRow, so candidates were sent by producers whose
+// units are at most `umax` tokens. load_b: the host's plan for max_ctx uses 16 keys per
+// thread, so run B's score words are loaded with run A's as the kernel starts.
+// The candidate arrays lead the argument list so that their addresses arrive preloaded in
+// scalar registers (kernel-argument preloading covers leading scalar and pointer
+// arguments, not structures) and the candidate loads start with the kernel.
+template <bool CAND>
+__global__ __launch_bounds__(SEL_NT) void topk_select_kernel(const uint32_t* __restrict__ cand_hi,
+                                                             const uint32_t* __restrict__ cand_lo,
+                                                             const uint32_t* __restrict__ floors,
+                                                             const float* __restrict__ scores, int64_t ld,
+                                                             const int32_t* __restrict__ row_ctx, int max_ctx, int k,
+                                                             int umax, int load_b, int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ phys, CacheView cv, RowMap rm) {
+  __shared__ SelShared S;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  // The candidates' score words load first: their addresses need only the kernel
+  // arguments, so they go out with the row's length; the first search needs nothing
+  // else. Token words, unit floors and block-table entries follow after the search's
+  // first histogram pass.
+  uint32_t kh[PER], kl[PER];
+  const uint32_t* ch = cand_hi + (int64_t)r * kCandRowCap;
+  if (CAND) {
+    load8(ch + 8 * tid, kh);
+    if (load_b) load8(ch + kCandRowCap / 2 + 8 * tid, kh + 8);
+  }
+  SelRow R;
+  R.ctx = clamp_ctx(row_ctx, r, max_ctx, cv.status);
+  R.k = k;
+  R.seq = rm.row_seq[r];  // the launch points row_seq at row_ctx when there are no page slots
+  R.srow = scores + (int64_t)r * ld;
+  R.clo = cand_lo + (int64_t)r * kCandRowCap;
+  R.flr = floors + (int64_t)r * kFloorRowCap;
+  R.orow = idx + (int64_t)r * k;
+  R.prow = phys ? phys + (int64_t)r * k : nullptr;
+  R.cv = cv;
+  R.rm = rm;
+  if (CAND) {
+    // the search's histogram and bucket count are cleared while the score words are in
+    // flight (ordered before the first pass by the search's first barrier)
+    if (tid == 0) S.bcount = 0u;
+    clear_hist(S);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int par = 0;
+  if (R.ctx <= k) {  // every token, in order
+    for (int i = tid; i < k; i += SEL_NT) {
+      R.orow[i] = i < R.ctx ? i : -1;
+      if (R.prow) R.prow[i] = i < R.ctx ? page_slot(cv, rm, R.seq, i) : -1;
+    }
+    return;
+  }
+  const CandPlan p = cand_plan(R.ctx, umax);
+  if (!CAND || p.unit == 0) {
+    __syncthreads();  // the clear above (if any) is done before the search clears again
+    if (R.ctx <= kCandRowCap / 2)
+      select_own<8>(S, kh, kl, R, par);
+    else
+      select_own<16>(S, kh, kl, R, par);
+    return;
+  }
+  if (p.per == 16) {
+    if (!load_b) load8(ch + kCandRowCap / 2 + 8 * tid, kh + 8);
+    select_cand<16>(S, kh, kl, R, p, par);
+  } else {
+    select_cand<8>(S, kh, kl, R, p, par);
+  }
 }
 
 hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx,
                             const TopkWs& ws, hipStream_t stream) {
   if (R <= 0 || max_ctx <= kTopkFullRow) return hipSuccess;
-  dim3 grid((max_ctx + 255) / 256, R);
-  hipLaunchKernelGGL(topk_send_kernel, grid, dim3(256), 0, stream, scores, ld, row_ctx, max_ctx, ws);
+  dim3 grid((max_ctx + 511) / 512, R);
+  hipLaunchKernelGGL(topk_send_kernel, grid, dim3(512), 0, stream, scores, ld, row_ctx, max_ctx, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
-                              int32_t* idx, const TopkWs& ws, int32_t* phys, const CacheView* cv, const RowMap* rm,
-                              hipStream_t stream) {
+                              int umax, int32_t* idx, const TopkWs& ws, int32_t* phys, const CacheView* cv,
+                              const RowMap* rm, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
   CacheView c{};
   RowMap m{};
   if (cv) c = *cv;  // without page slots only its status word is used
   if (phys) m = *rm;
   if (!phys) m.row_seq = row_ctx;  // read, never used
+  const int load_b = cand_plan(max_ctx, umax).per == 16 ? 1 : 0;
   if (max_ctx > kTopkFullRow)
     hipLaunchKernelGGL(topk_select_kernel<true>, dim3(R), dim3(SEL_NT), 0, stream, ws.cand_hi, ws.cand_lo, ws.floors,
-                       scores, ld, row_ctx, max_ctx, k, idx, phys, c, m);
+                       scores, ld, row_ctx, max_ctx, k, umax, load_b, idx, phys, c, m);
   else
     hipLaunchKernelGGL(topk_select_kernel<false>, dim3(R), dim3(SEL_NT), 0, stream, ws.cand_hi, ws.cand_lo, ws.floors,
-                       scores, ld, row_ctx, max_ctx, k, idx, phys, c, m);
+                       scores, ld, row_ctx, max_ctx, k, umax, 0, idx, phys, c, m);
   return hipGetLastError();
 }
 

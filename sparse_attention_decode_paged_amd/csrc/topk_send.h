@@ -1,26 +1,34 @@
 // Stage 1 of the exact top-k: every unit of a row (a run of consecutive tokens)
 // sends its m best keys, in token order, and a floor. Shared by the indexer
-// epilogue and the standalone top-k kernel, which both hand it one workgroup of
-// 4 waves covering 256 consecutive tokens (wave w: tokens 64 w .. 64 w + 63, lane =
-// token).
+// epilogues and the standalone send kernel, which hand it one workgroup of NT = 256
+// or 512 threads covering NT consecutive tokens (wave w: tokens 64 w .. 64 w + 63,
+// lane = token).
 //
-// Unit size and m depend only on the row length (see cand_plan): 64-token units
-// (one wave, m = 16) up to 65,536 tokens, 256-token units (the workgroup, m = 16, 8
-// or 4) above. A unit of 256 tokens holds on average 2 of the top 2048 of a
-// 262,144-token row, so 16 sent keys leave it short only when it holds 17 or more.
+// Plan (cand_plan, a function of the row length and of the largest unit the producer
+// supports, umax = NT): rows of at most kTopkFullRow tokens send nothing (the select
+// reads their scores whole); up to 65,536 tokens a unit is one wave's 64 tokens; above,
+// 256 tokens (four waves), or 512 (eight waves) when the producer's workgroups hold 512
+// and the row is longer than 131,072 tokens. The expected number of the row's top 2048
+// in one unit is lam = 2048 / nu (nu = units of the row); a unit sends m >= lam +
+// 4 sqrt(lam) + 2 keys (m = 8, 16 or 32), so that a unit holding more of the top k than
+// it sent is rare (the select then rescans it; exactness never depends on m). With
+// 512-token units a 262,144-token row sends 512 x 16 = 8,192 candidates.
 //
-// Ranking uses a 32-bit packed key per token: the score's order-preserving bits with
-// the low 8 bits replaced by (255 - position in the workgroup). Packed keys are
-// distinct within the workgroup and ordered like the scores up to those 8 bits. The
-// m largest packed keys of a unit are sent with their full 64-bit composite keys
-// (score word and token word, in two arrays) at slot cand_slot(q, u, m), q = rank in
-// token order, u = unit: slot row i = q + m (u / 1024), lane u % 1024, at
-// i * 1024 + u % 1024. The select's thread t then reads slots i * 1024 + t for
-// i < 16, addresses that do not depend on the row length. The floor is a score word f such that every unsent token's composite key is below
-// (f << 32) | 0xFFFFFFFF, so an unsent key can reach a threshold c only if
-// f >= c >> 32; f = 0 when the unit sent all of its valid tokens. Sorting uses DPP /
-// permlane exchanges inside a wave; 256-token units merge the four waves' best 16
-// through LDS with one barrier (a bitonic merge of the four sorted lists).
+// Layout: unit u's m keys sit at slots [u m, u m + m) of the row's candidate arrays
+// (score words in cand_hi, token words in cand_lo), ranks in token order; rank slots the
+// unit does not fill hold score word 0. Every token order is slot order. floors[u] is a
+// score word f such that every key the unit did not send has a composite key below
+// (f << 32) | 0xFFFFFFFF (f = 0 when it sent all of its tokens).
+//
+// Ranking inside a unit uses a 32-bit packed key per token: the score's order-preserving
+// bits with the low LB bits (NT = 2^LB) replaced by (NT - 1 - position in the
+// workgroup). Packed keys are distinct within the workgroup and ordered like the scores
+// up to those bits; the floor ORs them back in. A wave sorts its 64 packed keys (DPP /
+// permlane bitonic network); units of 4 or 8 waves merge the waves' best 16 or 8 through
+// LDS with one barrier (each wave of the unit repeats the merge, so no second barrier is
+// needed). The best key a wave kept back joins the floor: a 64-token wave of a row longer
+// than 65,536 tokens holds 17 of its top 2048 practically never (nor 9 above 131,072
+// tokens), and if it does the rescan covers it.
 #pragma once
 
 #include "common.h"
@@ -29,40 +37,44 @@
 namespace dsa {
 
 struct CandPlan {
-  int unit;  // tokens per unit: 64 or 256
+  int unit;  // tokens per unit: 64, 256 or 512; 0 = the row sends nothing
   int m;     // keys sent per unit
   int nu;    // units of the row
+  int per;   // keys per select thread: 8 (at most 8,192 candidates) or 16
 };
 
-// Every row of a launch whose row-length bound exceeds kTopkFullRow sends; launches
-// with a smaller bound send nothing (their select reads the rows whole).
-__host__ __device__ inline CandPlan cand_plan(int ctx) {
-  CandPlan p{0, 0, 0};
-  if (ctx <= 4 * kTopkFullRow) {
-    p.unit = 64;
-    p.m = kCandPerUnitMax;
-  } else {
-    p.unit = 256;
-    // largest power of two m <= 16 with nu * m <= kCandRowCap
-    const int nu = (ctx + 255) / 256;
-    p.m = nu <= 1024 ? 16 : nu <= 2048 ? 8 : nu <= 4096 ? 4 : nu <= 8192 ? 2 : 1;
+__host__ __device__ inline CandPlan cand_plan(int ctx, int umax) {
+  CandPlan p{0, 0, 0, 16};
+  if (ctx <= kTopkFullRow) {
+    p.per = ctx <= kCandRowCap / 2 ? 8 : 16;
+    return p;
   }
+  p.unit = ctx <= 4 * kTopkFullRow ? 64 : (umax >= 512 && ctx > 8 * kTopkFullRow ? 512 : 256);
   p.nu = (ctx + p.unit - 1) / p.unit;
+  // lam = 2048 / nu: nu < 410 <=> lam > 5 (m = 32 covers lam <= 14); nu < 1517 <=> lam > 1.35
+  p.m = p.nu < 410 ? 32 : p.nu < 1517 ? 16 : 8;
+  while (p.nu * p.m > kCandRowCap) p.m >>= 1;
+  p.per = p.nu * p.m <= kCandRowCap / 2 ? 8 : 16;
   return p;
 }
-static_assert(kCandPerUnitMax == 16 && kCandRowCap == 16 * 1024, "candidate slot layout");
 
-// Position of rank q of unit u in a row's candidate array (m keys per unit).
-__host__ __device__ inline int cand_slot(int q, int u, int m) { return (q + m * (u >> 10)) * 1024 + (u & 1023); }
+// Called by all NT threads of a workgroup (no thread may have returned): thread
+// 64 w + l holds the score of token base + 64 w + l. `lds` is send_lds_words<NT>() words.
+template <int NT>
+constexpr int send_lds_words() { return 17 * (NT / 64); }
 
-// Called by all 256 threads of a workgroup (no thread may have returned): thread
-// 64 w + l holds the score of token base + 64 w + l. `lds` is 68 words of LDS.
+template <int NT>
 __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx, int base, int row,
                                                 const TopkWs& tw, uint32_t* lds) {
-  const CandPlan p = cand_plan(ctx);
+  static_assert(NT == 256 || NT == 512, "workgroup of 4 or 8 waves");
+  constexpr int LB = NT == 256 ? 8 : 9;
+  constexpr uint32_t LM = (1u << LB) - 1u;
+  constexpr int NWG = NT / 64;
+  const CandPlan p = cand_plan(ctx, NT);
+  if (p.unit == 0) return;  // uniform: the row sends nothing
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int pos = threadIdx.x;  // position in the workgroup
-  const uint32_t packed = valid ? ((float_key(score) & ~255u) | (255u - (uint32_t)pos)) : 0u;
+  const uint32_t packed = valid ? ((float_key(score) & ~LM) | (LM - (uint32_t)pos)) : 0u;
   const uint32_t sorted = wave_sort_desc_u32(packed, lane);
   uint32_t* cand_hi = tw.cand_hi + (int64_t)row * kCandRowCap;
   uint32_t* cand_lo = tw.cand_lo + (int64_t)row * kCandRowCap;
@@ -79,24 +91,43 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
     const uint64_t bal = __ballot(sent);
     const uint32_t nsent = (uint32_t)__popcll(bal);
     const uint32_t q = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+    const int s0 = u * p.m;
     if (sent) {
-      cand_hi[cand_slot((int)q, u, p.m)] = (uint32_t)(key >> 32);
-      cand_lo[cand_slot((int)q, u, p.m)] = (uint32_t)key;
+      cand_hi[s0 + (int)q] = (uint32_t)(key >> 32);
+      cand_lo[s0 + (int)q] = (uint32_t)key;
     }
-    if ((uint32_t)lane >= nsent && lane < p.m) cand_hi[cand_slot(lane, u, p.m)] = 0u;  // unused ranks
-    if (lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
+    if ((uint32_t)lane >= nsent && lane < p.m) cand_hi[s0 + lane] = 0u;  // unused ranks
+    if (lane == 0) floors[u] = nxt != 0u ? (nxt | LM) : 0u;
     return;
   }
 
-  // one unit per workgroup: merge the waves' best 16 (and each wave's 17th) in LDS.
-  // Odd waves store theirs reversed, so lanes [0, 32) and [32, 64) each hold a bitonic
-  // sequence and the last two phases of a bitonic sort (11 steps) order all 64.
-  if (lane < 16) lds[wid * 16 + ((wid & 1) ? 15 - lane : lane)] = sorted;
-  if (lane == 16) lds[64 + wid] = sorted;
+  // Units of W = unit / 64 waves. Every wave puts its best cw = 64 / W keys (16 of a
+  // 4-wave unit, 8 of an 8-wave one) into the unit's 64-entry LDS region, odd waves
+  // reversed so that each pair of waves forms a bitonic sequence, and its (cw + 1)-th
+  // into wnx[]; after one barrier every wave of the unit sorts the 64 entries. (An
+  // 8-wave unit belongs to a row of more than 131,072 tokens, where a 64-token wave
+  // holds on average at most one of the top 2048: nine or more are practically never.)
+  const int W = p.unit >> 6;                 // 4 or 8 (uniform)
+  const int cw = 64 / W;                     // keys each wave contributes: 16 or 8
+  const int wi = W == 8 ? wid : (wid & 3);   // wave index inside the unit
+  const int ub = wid - wi;                   // first wave of the unit
+  uint32_t* reg = lds + 16 * ub;             // the unit's 64 entries
+  uint32_t* wnx = lds + 16 * NWG;            // one per wave of the workgroup
+  if (lane < cw) reg[cw * wi + ((wi & 1) ? cw - 1 - lane : lane)] = sorted;
+  if (lane == cw) wnx[wid] = sorted;
   __syncthreads();
-  const uint32_t all = lds[lane];
-  const uint32_t w17 = max(max(lds[64], lds[65]), max(lds[66], lds[67]));
-  uint32_t msort = all;
+  uint32_t ra = reg[lane];
+  uint32_t wmax = 0u;
+  for (int j = 0; j < W; ++j) wmax = max(wmax, wnx[ub + j]);
+  // remaining phases of a bitonic sort of the 64 entries: runs of cw = 8 first merge into
+  // sorted 16-runs of alternating direction (4 steps), then 32-runs (5), then all 64 (6)
+  uint32_t msort = ra;
+  if (W == 8) {
+    msort = bitonic_desc_step<16, 8>(msort, lane);
+    msort = bitonic_desc_step<16, 4>(msort, lane);
+    msort = bitonic_desc_step<16, 2>(msort, lane);
+    msort = bitonic_desc_step<16, 1>(msort, lane);
+  }
   msort = bitonic_desc_step<32, 16>(msort, lane);
   msort = bitonic_desc_step<32, 8>(msort, lane);
   msort = bitonic_desc_step<32, 4>(msort, lane);
@@ -109,20 +140,26 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
   msort = bitonic_desc_step<64, 2>(msort, lane);
   msort = bitonic_desc_step<64, 1>(msort, lane);
   const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)msort, p.m - 1);
-  const uint32_t nxt = max((uint32_t)__builtin_amdgcn_readlane((int)msort, p.m), w17);
-  // keys this wave sends, and how many lower waves send (all within their best 16)
-  const bool sent = packed != 0u && packed >= thr;
+  const uint32_t nxt = max((uint32_t)__builtin_amdgcn_readlane((int)msort, p.m), wmax);
+  // a key is sent when it is among its wave's best cw and reaches the m-th of the merge
+  const uint32_t wcw = (uint32_t)__builtin_amdgcn_readlane((int)sorted, cw - 1);
+  const bool sent = packed != 0u && packed >= thr && packed >= wcw;
   const uint64_t bal = __ballot(sent);
-  const uint32_t before = (uint32_t)__popcll(__ballot(all != 0u && all >= thr && lane < 16 * wid));
+  // sent keys of the unit's lower waves (LDS entry e belongs to wave e / cw)
+  const uint32_t before = (uint32_t)__popcll(__ballot(ra != 0u && ra >= thr && lane < cw * wi));
   const uint32_t q = before + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-  const int u = base >> 8;
+  const int u = (base + 64 * ub) / p.unit;
+  if (u >= p.nu) return;  // wave-uniform: the unit lies past the row
+  const int s0 = u * p.m;
   if (sent) {
-    cand_hi[cand_slot((int)q, u, p.m)] = (uint32_t)(key >> 32);
-    cand_lo[cand_slot((int)q, u, p.m)] = (uint32_t)key;
+    cand_hi[s0 + (int)q] = (uint32_t)(key >> 32);
+    cand_lo[s0 + (int)q] = (uint32_t)key;
   }
-  const uint32_t ntot = (uint32_t)__popcll(__ballot(all != 0u && all >= thr));
-  if (wid == 0 && (uint32_t)lane >= ntot && lane < p.m) cand_hi[cand_slot(lane, u, p.m)] = 0u;  // unused ranks
-  if (wid == 0 && lane == 0) floors[u] = nxt != 0u ? (nxt | 255u) : 0u;
+  if (wi == 0) {
+    const uint32_t ntot = (uint32_t)__popcll(__ballot(ra != 0u && ra >= thr));
+    if ((uint32_t)lane >= ntot && lane < p.m) cand_hi[s0 + lane] = 0u;  // unused ranks
+    if (lane == 0) floors[u] = nxt != 0u ? (nxt | LM) : 0u;
+  }
 }
 
 }  // namespace dsa
