@@ -300,6 +300,30 @@ dsa_status dsa_topk_dcp(const float* scores, int64_t ld_scores, const int32_t* r
 dsa_status dsa_device_status(void* stream, int32_t clear, uint32_t* status);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): dsa_decode_step_multi without a
+ * workspace argument. Its workspace is a static device array of DSA_STATIC_SCRATCH_BYTES
+ * that every GPU running this library holds until the process ends; its address on a
+ * device is looked up (hipGetSymbolAddress) on the call's first use there. The call
+ * allocates and frees nothing. It returns DSA_ERR_WORKSPACE, before anything is enqueued,
+ * when dsa_workspace_bytes(DSA_OP_DECODE_STEP, R, max_ctx, k) exceeds the array (32 MiB
+ * covers e.g. one row of 1,048,576 tokens, or 16 rows of 65,536), and DSA_ERR_HIP when
+ * the address lookup fails. Every call on one GPU uses the same array, which keeps the
+ * last call's contents (the step needs no initial contents): calls that overlap in time
+ * on one device (several streams or host threads) race, and the caller must serialise
+ * them. Other arguments and errors as for dsa_decode_step_multi.
+ */
+#define DSA_STATIC_SCRATCH_BYTES (32u << 20)
+dsa_status dsa_decode_step_noalloc(const dsa_cache_desc* cache, int32_t layer,
+                                   const void* q_idx, const void* q_idx_scale, const float* w,
+                                   const uint16_t* q_lat,
+                                   const int32_t* block_table, int32_t bt_stride,
+                                   const int32_t* row_seq, const int32_t* row_ctx,
+                                   int32_t R, int32_t max_ctx, int32_t k, int32_t rows_per_seq,
+                                   float sm_scale, int32_t* idx, float* out, float* lse,
+                                   void* stream);
+
+/*
  * Measurement reference, not a step of the method: reads every byte of
  * [p, p + bytes) once (16-byte nontemporal loads; `grid` workgroups of 256 threads
  * take 16-KB chunks in turn) and writes nothing, except *sink in the practically

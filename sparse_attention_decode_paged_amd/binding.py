@@ -29,7 +29,7 @@ EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_last_error_detail", "ds
             "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step",
             "dsa_indexer_score_multi", "dsa_decode_step_multi", "dsa_cache_append",
             "dsa_topk_dcp_workspace_bytes", "dsa_topk_dcp", "dsa_device_status",
-            "dsa_hbm_read_probe")
+            "dsa_hbm_read_probe", "dsa_decode_step_noalloc")
 
 
 class DSAError(RuntimeError):
@@ -98,6 +98,9 @@ def load_library(path: str = LIB_PATH):
     L.dsa_topk_dcp.argtypes = [_vp, _i64, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     L.dsa_device_status.restype = _i32
     L.dsa_device_status.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_uint32)]
+    L.dsa_decode_step_noalloc.restype = _i32
+    L.dsa_decode_step_noalloc.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _f32, _vp, _vp, _vp, _vp]
     L.dsa_hbm_read_probe.restype = _i32
     L.dsa_hbm_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
     _lib = L
@@ -317,6 +320,34 @@ def dsa_decode_step(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_tab
     else:
         _check(L.dsa_decode_step_multi(*head, int(rows_per_seq), float(sm_scale), *tail), "dsa_decode_step_multi")
     return idx, out, lse, workspace
+
+
+DSA_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def dsa_decode_step_noalloc(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_table, row_seq, row_ctx, max_ctx,
+                            k, sm_scale, idx=None, out=None, lse=None, rows_per_seq=1):
+    """The decode step on the library's static per-GPU scratch (no workspace argument):
+    returns (idx, out, lse). Calls that overlap on one GPU race (shared scratch)."""
+    L = load_library()
+    R = row_seq.shape[0]
+    dev = pool.device
+    if idx is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((R, H_Q, D_V), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((R, H_Q), dtype=torch.float32, device=dev)
+    d = make_cache_desc(pool, layout)
+    st = L.dsa_decode_step_noalloc(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+                                   _dev(w, "w", torch.float32), _dev(q_lat, "q_lat", torch.bfloat16),
+                                   _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
+                                   _dev(row_seq, "row_seq", torch.int32), _dev(row_ctx, "row_ctx", torch.int32), R,
+                                   int(max_ctx), int(k), int(rows_per_seq), float(sm_scale),
+                                   _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
+                                   _dev(lse, "lse", torch.float32), _stream(dev))
+    _check(st, "dsa_decode_step_noalloc")
+    return idx, out, lse
 
 
 def dsa_cache_append(pool, layout, layer, block_table, row_seq, pos, idx_key=None, latent=None):

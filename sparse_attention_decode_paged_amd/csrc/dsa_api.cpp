@@ -41,6 +41,31 @@ uint32_t* status_word() {
   return static_cast<uint32_t*>(a);
 }
 
+// The decode step's workspace for callers that cannot allocate (dsa_decode_step_noalloc):
+// one array per GPU. As with the status word, host code never passes the symbol's name;
+// scratch_addr() looks up this device's address once and keeps it.
+static __device__ __align__(256) uint8_t scratch[DSA_STATIC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// This device's address of `scratch`, looked up (with the device current) on the first
+// call on the device; NULL when the lookup fails.
+void* scratch_addr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  void* a = nullptr;
+  if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || a == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_addr[dev].store(a, std::memory_order_release);
+  return a;
+}
+
 thread_local std::string g_detail;
 
 dsa_status fail(dsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -354,6 +379,25 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const voi
                            void* stream) {
   return dsa_decode_step_multi(cache, layer, q_idx, q_idx_scale, w, q_lat, block_table, bt_stride, row_seq, row_ctx, R,
                                max_ctx, k, 1, sm_scale, idx, out, lse, workspace, ws_bytes, stream);
+}
+
+dsa_status dsa_decode_step_noalloc(const dsa_cache_desc* cache, int32_t layer, const void* q_idx,
+                                   const void* q_idx_scale, const float* w, const uint16_t* q_lat,
+                                   const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
+                                   const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k,
+                                   int32_t rows_per_seq, float sm_scale, int32_t* idx, float* out, float* lse,
+                                   void* stream) {
+  if (R < 0 || R > 65535) return fail(DSA_ERR_ARG, "R %d out of [0, 65535]", R);
+  if (max_ctx < 0 || max_ctx > kMaxCtx) return fail(DSA_ERR_ARG, "max_ctx %d out of [0, %d]", max_ctx, kMaxCtx);
+  if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
+  const size_t need = decode_ws(R, max_ctx, k);
+  if (need > (size_t)DSA_STATIC_SCRATCH_BYTES)
+    return fail(DSA_ERR_WORKSPACE, "the step needs %zu bytes of workspace, more than the %u-byte static scratch",
+                need, (unsigned)DSA_STATIC_SCRATCH_BYTES);
+  void* ws = scratch_addr();
+  if (ws == nullptr) return fail(DSA_ERR_HIP, "the static scratch has no address on this device");
+  return dsa_decode_step_multi(cache, layer, q_idx, q_idx_scale, w, q_lat, block_table, bt_stride, row_seq, row_ctx, R,
+                               max_ctx, k, rows_per_seq, sm_scale, idx, out, lse, ws, DSA_STATIC_SCRATCH_BYTES, stream);
 }
 
 size_t dsa_topk_dcp_workspace_bytes(int32_t R, int32_t max_ctx, int32_t k, int32_t W) {
