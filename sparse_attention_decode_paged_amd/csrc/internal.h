@@ -81,7 +81,7 @@ inline int mla_split_tokens(int k, int nsplit) {
 inline size_t mla_ws_bytes(int R, int k) {
   int s = mla_splits(R, k);
   if (s <= 1) return 256;
-  return align_up((size_t)R * s * kHQ * kDV * 4, 256) + align_up((size_t)R * s * kHQ * 2 * 4, 256);
+  return align_up((size_t)R * s * kHQ * kDV * 2, 256) + align_up((size_t)R * s * kHQ * 2 * 4, 256);
 }
 
 // ---- context-parallel merge emulation workspace -------------------------------------

@@ -29,8 +29,8 @@
 //   The chunk's scale factor joins the per-head softmax rescale.
 // e4m3 codes convert to bf16 exactly; the per-token scale is applied to the
 // logit and folded into P'. With one split the workgroup writes out / lse; with
-// several it writes unnormalised partials (O, m, l) that the merge kernel
-// combines by log-sum-exp.
+// several it writes its split's softmax average O / l in fp16 and (m, l) in fp32,
+// which the merge kernel combines by log-sum-exp.
 // Sixteen heads per workgroup spread a row over twice as many CUs and keep the FP8
 // kernel at 128 registers (two workgroups per CU): the choice for batches of up to 4
 // rows. Larger batches fill the GPU anyway and take 32, which gathers each latent and
@@ -62,7 +62,7 @@ namespace dsa {
 namespace {
 using v8h = v8hf;
 constexpr int NT = 64;    // merge workgroup: one wave
-constexpr int kMergeCols = 2;                         // value columns per merge lane
+constexpr int kMergeCols = 2;                         // adjacent value columns per merge lane
 constexpr int kMergeParts = kDV / (kMergeCols * NT);  // merge workgroups per head
 constexpr int NTM = 512;  // attention workgroup: 8 waves, two per SIMD
 constexpr int NWM = NTM / 64;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
                                                         const uint16_t* __restrict__ q_lat, int k, int ts, float c2,
                                                         CacheView cv, RowMap rm,
                                                         float* __restrict__ out, float* __restrict__ lse,
-                                                        float* __restrict__ part_o, float* __restrict__ part_ml,
+                                                        _Float16* __restrict__ part_o, float* __restrict__ part_ml,
                                                         int nsplit) {
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -611,22 +611,28 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
       lse[(int64_t)r * kHQ + hg * G + tid] = ml.y > 0.f ? (ml.x + log2f(ml.y)) * 0.69314718055994531f : kNegInf;
     }
   } else {
+    // The split's own softmax average O / l (bounded by the latents' magnitude) in fp16:
+    // half the bytes of fp32 partials, 11 significant bits; (m, l) stay fp32.
     const int64_t pbase = ((int64_t)r * nsplit + split) * kHQ + hg * G;
     if constexpr (G == 16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * (lane >> 4) + i;
-        float* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 15);
+        const float lv = ml_s[h].y;
+        const float f = lv > 0.f ? s_run / lv : 0.f;
+        _Float16* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 15);
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) __builtin_nontemporal_store(acc[cb][i] * s_run, orow + 16 * cb);
+        for (int cb = 0; cb < 4; ++cb) __builtin_nontemporal_store((_Float16)(acc[cb][i] * f), orow + 16 * cb);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int h = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        float* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 31);
+        const float lv = ml_s[h].y;
+        const float f = lv > 0.f ? s_run / lv : 0.f;
+        _Float16* orow = part_o + (pbase + h) * kDV + 64 * wid + (lane & 31);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) __builtin_nontemporal_store(accw[c][i] * s_run, orow + 32 * c);
+        for (int c = 0; c < 2; ++c) __builtin_nontemporal_store((_Float16)(accw[c][i] * f), orow + 32 * c);
       }
     }
     if (tid < G) {
@@ -637,14 +643,15 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   }
 }
 
-// out[r][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s ; empty splits (m = -inf)
-// weigh 0. One wave per (row, head, 64 kMergeCols value columns), so that the partials
-// spread over several times as many CUs as heads: lane s reads split s's (m, l); each
-// lane then loads its value columns of every split at once (splits past nsplit repeat
-// the last one with weight 0), so the whole merge is one round of loads.
+// out[r][h] = sum_s w_s A_s / sum_s w_s with w_s = 2^(m_s - M) l_s and A_s = O_s / l_s
+// (the fp16 split averages); empty splits (m = -inf) weigh 0. One wave per (row, head,
+// 128 value columns), so that the partials spread over several times as many CUs as
+// heads: lane s reads split s's (m, l); each lane then loads its two adjacent columns of
+// every split at once (one 32-bit word per split; splits past nsplit repeat the last one
+// with weight 0), so the whole merge is one round of loads.
 // MS: a power of two >= nsplit (the loads are unrolled over MS splits).
 template <int MS>
-__global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(NT) void mla_merge_kernel(const _Float16* __restrict__ part_o,
                                                        const float* __restrict__ part_ml, int nsplit,
                                                        float* __restrict__ out, float* __restrict__ lse) {
   static_assert(MS <= 64 && MS <= kMaxK / kMlaChunk, "one split per lane");
@@ -652,13 +659,12 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
   const int tid = threadIdx.x, lane = tid & 63;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (int64_t)r * nsplit * kHQ + h;
   const float2 e = lane < nsplit ? ml[(int64_t)lane * kHQ] : float2{kNegInf, 0.f};
-  const float* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + kMergeCols * NT * q + tid;
-  float x[kMergeCols][MS];
+  const _Float16* po = part_o + ((int64_t)r * nsplit * kHQ + h) * kDV + kMergeCols * NT * q + kMergeCols * tid;
+  v2h x[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
     const int sc = s < nsplit ? s : nsplit - 1;
-#pragma unroll
-    for (int c = 0; c < kMergeCols; ++c) x[c][s] = po[(int64_t)sc * kHQ * kDV + NT * c];
+    x[s] = *reinterpret_cast<const v2h*>(po + (int64_t)sc * kHQ * kDV);
   }
   float M = e.x;
   M = fmaxf(M, xshflf<1>(M));
@@ -667,25 +673,24 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const float* __restrict__
   M = fmaxf(M, xshflf<8>(M));
   M = fmaxf(M, xshflf<16>(M));
   M = fmaxf(M, xshflf<32>(M));
-  const float wgt = (e.x == kNegInf) ? 0.f : exp2f(e.x - M);
-  float L = wgt * e.y;
+  const float wgt = (e.x == kNegInf) ? 0.f : exp2f(e.x - M) * e.y;
+  float L = wgt;
   L += xshflf<1>(L);
   L += xshflf<2>(L);
   L += xshflf<4>(L);
   L += xshflf<8>(L);
   L += xshflf<16>(L);
   L += xshflf<32>(L);
-  float o[kMergeCols] = {};
+  float o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
     const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s));
-#pragma unroll
-    for (int c = 0; c < kMergeCols; ++c) o[c] = fmaf(ws, x[c][s], o[c]);
+    o0 = fmaf(ws, (float)x[s][0], o0);
+    o1 = fmaf(ws, (float)x[s][1], o1);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* orow = out + ((int64_t)r * kHQ + h) * kDV + kMergeCols * NT * q;
-#pragma unroll
-  for (int c = 0; c < kMergeCols; ++c) orow[tid + NT * c] = o[c] * inv;
+  float2* orow = reinterpret_cast<float2*>(out + ((int64_t)r * kHQ + h) * kDV + kMergeCols * NT * q) + tid;
+  *orow = float2{o0 * inv, o1 * inv};
   if (lse != nullptr && q == 0 && tid == 0)
     lse[(int64_t)r * kHQ + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
@@ -697,11 +702,11 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
   const int nsplit = mla_splits(R, k);
   const int ts = mla_split_tokens(k, nsplit);
   const float c2 = (float)((double)sm_scale * 1.4426950408889634);
-  float* part_o = nullptr;
+  _Float16* part_o = nullptr;
   float* part_ml = nullptr;
   if (nsplit > 1) {
-    part_o = static_cast<float*>(ws);
-    part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 4, 256));
+    part_o = static_cast<_Float16*>(ws);
+    part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 2, 256));
   }
   auto go = [&](auto nv, auto group) {
     constexpr bool N = decltype(nv)::value;
