@@ -30,7 +30,8 @@ LAYERS = 24
 K = 2048
 BS = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-INDEXER_SRC = os.path.join(ROOT, "sparse_attention_decode_paged_amd", "csrc", "indexer.hip")
+INDEXER_SRCS = [os.path.join(ROOT, "sparse_attention_decode_paged_amd", "csrc", f)
+                for f in ("indexer.hip", "topk_send.h", "common.h")]
 
 
 def parse():
@@ -66,18 +67,21 @@ def parse():
     return p.parse_args()
 
 
-def src_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def src_sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_src):
-    """HBM bytes per launch from committed counter summaries, if taken on this source."""
+def traffic_for(kernel_srcs):
+    """HBM bytes per launch from committed counter summaries, if taken on these sources."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = t.get("indexer_fp8")
-    if not e or e.get("source_sha") != src_sha(kernel_src):
+    e = t.get("indexer_fp8_step")
+    if not e or e.get("source_sha") != src_sha(kernel_srcs):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -206,21 +210,20 @@ def cpu_configs(dev):
     print(json.dumps(res), flush=True)
 
 
-def timed_indexer_us(dsa, case, layers, max_ctx, reps, rows_per_seq=1, per_graph=None):
-    """Average duration of the scoring kernel alone (dsa_indexer_score): a HIP graph
-    holds `per_graph` launches back to back (rotating over the layers), and the graph
-    is replayed `reps` times between one pair of events, so no host launch cost falls
+def timed_stage_us(dsa, case, ws, bufs, layers, max_ctx, stage, reps, rows_per_seq=1, per_graph=24):
+    """Average duration of one kernel of the decode step, launched alone through
+    dsa_decode_step_stages on the step's own workspace: a HIP graph holds `per_graph`
+    launches back to back (layer i % layers for launch i) and is replayed `reps` times
+    between one pair of events on the stream it runs on, so no host launch cost falls
     inside the timing."""
-    per_graph = per_graph or layers
     import torch
-    R = case.num_rows
     dev = case.pool.device
-    scores = torch.empty((R, max_ctx), dtype=torch.float32, device=dev)
+    idx, out, lse = bufs
 
     def launch(l):
-        dsa.dsa_indexer_score(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l],
-                              case.block_table, case.row_seq, case.row_ctx, max_ctx, scores=scores,
-                              rows_per_seq=rows_per_seq)
+        dsa.dsa_decode_step_stages(case.pool, case.layout, l, case.q_idx[l], case.q_idx_scale[l], case.w[l],
+                                   case.q_lat[l], case.block_table, case.row_seq, case.row_ctx, max_ctx, K,
+                                   case.sm_scale, idx, out, lse, ws, stage, rows_per_seq=rows_per_seq)
 
     cap = torch.cuda.Stream(dev)
     cap.wait_stream(torch.cuda.current_stream(dev))
@@ -230,8 +233,8 @@ def timed_indexer_us(dsa, case, layers, max_ctx, reps, rows_per_seq=1, per_graph
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):
-        for l in range(per_graph):
-            launch(l % layers)
+        for i in range(per_graph):
+            launch(i % layers)
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
@@ -470,14 +473,23 @@ def main():
     spread = {"p10": round(per[int(0.1 * (nrep - 1))], 3), "p50": round(per[(nrep - 1) // 2], 3),
               "p90": round(per[int(0.9 * (nrep - 1))], 3), "replays": nrep, "steps_per_replay": a.steps}
     del g_steps
-    G = a.layers * -(-24 // a.layers)
     # the read ceiling needs a buffer far beyond the 256 MB last-level cache
     pool_bytes = case.pool.numel() * case.pool.element_size()
     ceiling = hbm_read_ceiling(dsa, case.pool) if pool_bytes >= (1 << 30) else None
 
-    ix_us = timed_indexer_us(dsa, case, a.layers, max_ctx, max(2, min(a.steps, 480) // G), rows_per_seq, G)
-
+    # each kernel of the step timed alone (the step's own launches, on its workspace)
+    reps = max(2, min(a.steps, 480) // 24)
+    bufs = (idx, out, lse)
+    st_us = {name: timed_stage_us(dsa, case, ws, bufs, a.layers, max_ctx, bit, reps, rows_per_seq)
+             for name, bit in (("indexer", dsa.DSA_STAGE_INDEXER), ("topk", dsa.DSA_STAGE_TOPK),
+                               ("attention", dsa.DSA_STAGE_ATTENTION), ("merge", dsa.DSA_STAGE_MERGE))}
+    ix_us = st_us["indexer"]
     ctxs = [int(c) for c in case.row_ctx.tolist()]
+    ix_kernel = {("fp8", False): "indexer_fp8_kernel<PAGED32, SEND=true>", ("fp8", True): "indexer_fp8_rows_kernel",
+                 ("mxfp4", False): "indexer_mxfp4_kernel<PAGED32, SEND=true>"}.get(
+        (a.index_fmt, rows_per_seq > 1), "indexer")
+    if max_ctx <= 16384:
+        ix_kernel = ix_kernel.replace("SEND=true", "SEND=false")
     if rows_per_seq > 1:
         # rows share one sequence's keys: bytes are not the bound, the contraction is
         step_bytes = None
@@ -489,12 +501,26 @@ def main():
         step_bytes = A.layer_step_bytes(ctxs, K, a.index_fmt, a.latent_fmt)
         ix_bytes = sum(A.indexer_bytes(c, a.index_fmt) for c in ctxs)
         ix_gbps = ix_bytes / (ix_us * 1e-6) / 1e9
-        traffic = (traffic_for(INDEXER_SRC) if a.index_fmt == "fp8" and a.config == "headline" and a.batch == 1
+        traffic = (traffic_for(INDEXER_SRCS) if a.index_fmt == "fp8" and a.config == "headline" and a.batch == 1
                    and a.ctx == CTX and a.block_size == BS else None)
         roof = {"bound": "hbm", "achieved": round(ix_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ix_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic, "algorithmic_bytes_per_launch": ix_bytes,
                 "frac_of_measured_read_ceiling": round(ix_gbps / ceiling["gbps"], 4) if ceiling else None}
     step_gbps = step_bytes / (ms * 1e-3) / 1e9 if step_bytes else None
+    # the other kernels of the step against their own algorithmic bytes (select: the 4 B
+    # per token of scores it decides over; attention: the gathered latents, query, indices
+    # and output); latency-bound at one row, reported for what they cost
+    sel_bytes = 4 * sum(ctxs)
+    att_bytes = sum(A.attention_bytes(c, K, a.latent_fmt) for c in ctxs)
+    kernels = {
+        "topk_select": {"avg_launch_us": round(st_us["topk"], 3), "algorithmic_bytes": sel_bytes,
+                        "achieved_gbps": round(sel_bytes / (st_us["topk"] * 1e-6) / 1e9, 1),
+                        "frac_of_peak": round(sel_bytes / (st_us["topk"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "sparse_mla": {"avg_launch_us": round(st_us["attention"], 3), "algorithmic_bytes": att_bytes,
+                       "achieved_gbps": round(att_bytes / (st_us["attention"] * 1e-6) / 1e9, 1),
+                       "frac_of_peak": round(att_bytes / (st_us["attention"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "split_merge": {"avg_launch_us": round(st_us["merge"], 3)},
+    }
 
     res = {
         "metric": METRIC,
@@ -520,9 +546,9 @@ def main():
         "step_hbm_gbps": round(step_gbps, 1) if step_gbps else None,
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4) if step_gbps else None,
         "step_algorithmic_bytes": step_bytes,
-        "roofline": dict({"kernel": (f"indexer_{a.index_fmt}" + ("_rows" if rows_per_seq > 1 else "") +
-                                     "_kernel (scoring only, as dsa_indexer_score launches it)")},
+        "roofline": dict({"kernel": ix_kernel + " (the step's indexer launch, with the top-k candidate stage)"},
                          **roof, avg_launch_us=round(ix_us, 3)),
+        "step_kernels": kernels,
         "hbm_read_ceiling": ceiling,
         "gen_seconds": round(gen_s, 1),
     }

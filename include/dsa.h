@@ -300,6 +300,31 @@ dsa_status dsa_topk_dcp(const float* scores, int64_t ld_scores, const int32_t* r
 dsa_status dsa_device_status(void* stream, int32_t clear, uint32_t* status);
 
 /*
+ * Measurement entry point, not a step of the method: dsa_decode_step_multi with the
+ * same arguments and workspace, enqueuing only the kernels of the chosen stages, in
+ * the step's order, so that each kernel of a decode step can be timed alone (the
+ * benchmark's roofline times the step's own indexer launch this way). Running
+ * DSA_STAGE_INDEXER, then DSA_STAGE_TOPK, then DSA_STAGE_ATTENTION | DSA_STAGE_MERGE on
+ * one workspace equals one dsa_decode_step_multi call; a stage reads what the stages
+ * before it left in the workspace (or in idx), so running a later stage alone repeats
+ * its work on the previous call's intermediate results. DSA_ERR_ARG for an empty mask
+ * or unknown bits.
+ */
+#define DSA_STAGE_INDEXER 1u    /* indexer scores and the top-k candidate stage */
+#define DSA_STAGE_TOPK 2u       /* exact top-k selection (writes idx) */
+#define DSA_STAGE_ATTENTION 4u  /* sparse MLA over idx */
+#define DSA_STAGE_MERGE 8u      /* merge of the rows' split partials (when rows are split) */
+#define DSA_STAGE_ALL 15u
+dsa_status dsa_decode_step_stages(const dsa_cache_desc* cache, int32_t layer,
+                                  const void* q_idx, const void* q_idx_scale, const float* w,
+                                  const uint16_t* q_lat,
+                                  const int32_t* block_table, int32_t bt_stride,
+                                  const int32_t* row_seq, const int32_t* row_ctx,
+                                  int32_t R, int32_t max_ctx, int32_t k, int32_t rows_per_seq,
+                                  float sm_scale, int32_t* idx, float* out, float* lse,
+                                  void* workspace, size_t ws_bytes, uint32_t stages, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): dsa_decode_step_multi without a
  * workspace argument. Its workspace is a static device array of DSA_STATIC_SCRATCH_BYTES

@@ -12,7 +12,8 @@ from .binding import (  # noqa: F401
     dsa_abi_version, dsa_status_string, dsa_workspace_bytes, dsa_decode_scores_ld,
     dsa_indexer_score, dsa_topk, dsa_sparse_mla, dsa_decode_step, dsa_cache_append,
     dsa_topk_dcp, dcp_send_count, dsa_device_status, dsa_hbm_read_probe, dsa_decode_step_noalloc,
-    DSA_STATIC_SCRATCH_BYTES,
+    DSA_STATIC_SCRATCH_BYTES, dsa_decode_step_stages, DSA_STAGE_INDEXER, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION,
+    DSA_STAGE_MERGE, DSA_STAGE_ALL,
     DSA_DEV_CTX_CLAMPED, DSA_DEV_BLOCK_CLAMPED, DSA_DEV_INDEX_RANGE,
     DSA_INDEX_FP8, DSA_INDEX_MXFP4, DSA_LATENT_FP8, DSA_LATENT_NVFP4, DSA_OP_TOPK, DSA_OP_SPARSE_MLA, DSA_OP_DECODE_STEP,
 )

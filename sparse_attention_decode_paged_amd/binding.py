@@ -29,7 +29,7 @@ EXPORTED = ("dsa_abi_version", "dsa_status_string", "dsa_last_error_detail", "ds
             "dsa_decode_scores_ld", "dsa_indexer_score", "dsa_topk", "dsa_sparse_mla", "dsa_decode_step",
             "dsa_indexer_score_multi", "dsa_decode_step_multi", "dsa_cache_append",
             "dsa_topk_dcp_workspace_bytes", "dsa_topk_dcp", "dsa_device_status",
-            "dsa_hbm_read_probe", "dsa_decode_step_noalloc")
+            "dsa_hbm_read_probe", "dsa_decode_step_noalloc", "dsa_decode_step_stages")
 
 
 class DSAError(RuntimeError):
@@ -101,6 +101,9 @@ def load_library(path: str = LIB_PATH):
     L.dsa_decode_step_noalloc.restype = _i32
     L.dsa_decode_step_noalloc.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                                           _f32, _vp, _vp, _vp, _vp]
+    L.dsa_decode_step_stages.restype = _i32
+    L.dsa_decode_step_stages.argtypes = [P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                         _f32, _vp, _vp, _vp, _vp, _sz, ctypes.c_uint32, _vp]
     L.dsa_hbm_read_probe.restype = _i32
     L.dsa_hbm_read_probe.argtypes = [_vp, _sz, _vp, _i32, _vp]
     _lib = L
@@ -348,6 +351,28 @@ def dsa_decode_step_noalloc(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, b
                                    _dev(lse, "lse", torch.float32), _stream(dev))
     _check(st, "dsa_decode_step_noalloc")
     return idx, out, lse
+
+
+DSA_STAGE_INDEXER, DSA_STAGE_TOPK, DSA_STAGE_ATTENTION, DSA_STAGE_MERGE, DSA_STAGE_ALL = 1, 2, 4, 8, 15
+
+
+def dsa_decode_step_stages(pool, layout, layer, q_idx, q_idx_scale, w, q_lat, block_table, row_seq, row_ctx, max_ctx,
+                           k, sm_scale, idx, out, lse, workspace, stages, rows_per_seq=1):
+    """Enqueue only the chosen stages (DSA_STAGE_* bits) of a decode step on `workspace`
+    (a measurement entry point: each kernel of the step timed alone)."""
+    L = load_library()
+    R = row_seq.shape[0]
+    dev = pool.device
+    d = make_cache_desc(pool, layout)
+    st = L.dsa_decode_step_stages(ctypes.byref(d), layer, _dev(q_idx, "q_idx"), _dev(q_idx_scale, "q_idx_scale"),
+                                  _dev(w, "w", torch.float32), _dev(q_lat, "q_lat", torch.bfloat16),
+                                  _dev(block_table, "block_table", torch.int32), _bt_stride(block_table),
+                                  _dev(row_seq, "row_seq", torch.int32), _dev(row_ctx, "row_ctx", torch.int32), R,
+                                  int(max_ctx), int(k), int(rows_per_seq), float(sm_scale),
+                                  _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
+                                  _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), int(stages), _stream(dev))
+    _check(st, "dsa_decode_step_stages")
 
 
 def dsa_cache_append(pool, layout, layer, block_table, row_seq, pos, idx_key=None, latent=None):

@@ -305,7 +305,7 @@ dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer, const uint
   if (mla_splits(R, k) > 1 && (workspace == nullptr || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (R == 0) return ok();
-  return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, nullptr, R, k, sm_scale, out, lse, workspace,
+  return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, nullptr, R, k, sm_scale, out, lse, workspace, 3,
                                       static_cast<hipStream_t>(stream)),
                     "sparse_mla");
 }
@@ -329,12 +329,12 @@ dsa_status dsa_cache_append(const dsa_cache_desc* cache, int32_t layer, const in
                     "cache_append");
 }
 
-dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, const void* q_idx,
-                                 const void* q_idx_scale, const float* w, const uint16_t* q_lat,
-                                 const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
-                                 const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k, int32_t rows_per_seq,
-                                 float sm_scale, int32_t* idx, float* out, float* lse, void* workspace,
-                                 size_t ws_bytes, void* stream) {
+dsa_status dsa_decode_step_stages(const dsa_cache_desc* cache, int32_t layer, const void* q_idx,
+                                  const void* q_idx_scale, const float* w, const uint16_t* q_lat,
+                                  const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
+                                  const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k, int32_t rows_per_seq,
+                                  float sm_scale, int32_t* idx, float* out, float* lse, void* workspace,
+                                  size_t ws_bytes, uint32_t stages, void* stream) {
   CacheView cv;
   RowMap rm;
   dsa_status st = check_cache(cache, layer, &cv);
@@ -344,6 +344,7 @@ dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, con
     return fail(DSA_ERR_NULL, "q_idx / q_idx_scale / w / q_lat / idx / out is NULL");
   if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
   if (rows_per_seq < 1) return fail(DSA_ERR_ARG, "rows_per_seq %d < 1", rows_per_seq);
+  if (stages == 0u || (stages & ~(uint32_t)DSA_STAGE_ALL) != 0u) return fail(DSA_ERR_ARG, "stages 0x%x", stages);
   if (!aligned16(q_idx) || !aligned16(q_lat)) return fail(DSA_ERR_ALIGN, "q_idx / q_lat is not 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(q_idx_scale) & 3u) return fail(DSA_ERR_ALIGN, "q_idx_scale is not 4-byte aligned");
   const size_t need = decode_ws(R, max_ctx, k);
@@ -360,16 +361,28 @@ dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, con
   int32_t* phys = reinterpret_cast<int32_t*>(p);
   p += align_up((size_t)R * k * 4, 256);
   void* mla_ws = p;
-  hipError_t e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld, &tw, s);
-  if (e == hipSuccess) {
+  hipError_t e = hipSuccess;
+  if (stages & DSA_STAGE_INDEXER)
+    e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld, &tw, s);
+  if (e == hipSuccess && (stages & DSA_STAGE_TOPK)) {
     const int umax = send_umax(cache->index_fmt == DSA_INDEX_FP8, rows_per_seq);
     e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, umax, idx, tw, phys, &cv, &rm, s);
   }
-  if (e == hipSuccess) {
-    // the selected tokens lie below max_ctx, so the row map's bound is unchanged
-    e = launch_sparse_mla(cv, rm, q_lat, idx, phys, R, k, sm_scale, out, lse, mla_ws, s);
-  }
+  // the selected tokens lie below max_ctx, so the row map's bound is unchanged
+  const int parts = ((stages & DSA_STAGE_ATTENTION) ? 1 : 0) | ((stages & DSA_STAGE_MERGE) ? 2 : 0);
+  if (e == hipSuccess && parts) e = launch_sparse_mla(cv, rm, q_lat, idx, phys, R, k, sm_scale, out, lse, mla_ws, parts, s);
   return hip_status(e, "decode_step");
+}
+
+dsa_status dsa_decode_step_multi(const dsa_cache_desc* cache, int32_t layer, const void* q_idx,
+                                 const void* q_idx_scale, const float* w, const uint16_t* q_lat,
+                                 const int32_t* block_table, int32_t bt_stride, const int32_t* row_seq,
+                                 const int32_t* row_ctx, int32_t R, int32_t max_ctx, int32_t k, int32_t rows_per_seq,
+                                 float sm_scale, int32_t* idx, float* out, float* lse, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  return dsa_decode_step_stages(cache, layer, q_idx, q_idx_scale, w, q_lat, block_table, bt_stride, row_seq, row_ctx, R,
+                                max_ctx, k, rows_per_seq, sm_scale, idx, out, lse, workspace, ws_bytes, DSA_STAGE_ALL,
+                                stream);
 }
 
 dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer, const void* q_idx, const void* q_idx_scale,

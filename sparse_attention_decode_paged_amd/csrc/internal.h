@@ -175,9 +175,11 @@ inline int send_umax(int32_t index_fmt_is_fp8, int32_t rows_per_seq) {
 
 // Sparse MLA over idx; when `phys` (page slots from the selection) is non-null it
 // replaces the block-table lookups.
+// parts: 1 = the attention kernel, 2 = the split merge (a kernel of its own when the
+// rows are split), 3 = both.
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
                              const int32_t* phys, int R, int k, float sm_scale, float* out, float* lse, void* ws,
-                             hipStream_t stream);
+                             int parts, hipStream_t stream);
 
 // Exact top-k merge of decode context parallelism over W token-strided shards, emulated
 // on one GPU (ws: dcp_ws_bytes). resend_mask / words may be null.

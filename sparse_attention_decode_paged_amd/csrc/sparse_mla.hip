@@ -697,7 +697,7 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const _Float16* __restric
 
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,
                              const int32_t* phys, int R, int k, float sm_scale, float* out, float* lse, void* ws,
-                             hipStream_t stream) {
+                             int parts, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
   const int nsplit = mla_splits(R, k);
   const int ts = mla_split_tokens(k, nsplit);
@@ -715,7 +715,8 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
                        ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
   };
   const bool nvf = cv.latent_fmt == DSA_LATENT_NVFP4;
-  if (mla_group(R) == 16) {
+  if (!(parts & 1)) {
+  } else if (mla_group(R) == 16) {
     if (nvf)
       go(std::true_type{}, std::integral_constant<int, 16>{});
     else
@@ -726,7 +727,7 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     else
       go(std::false_type{}, std::integral_constant<int, 32>{});
   }
-  if (nsplit > 1) {
+  if (nsplit > 1 && (parts & 2)) {
     const dim3 mg(kHQ * kMergeParts, R);
     if (nsplit <= 4)
       hipLaunchKernelGGL(mla_merge_kernel<4>, mg, dim3(NT), 0, stream, part_o, part_ml, nsplit, out, lse);
