@@ -53,12 +53,15 @@ def parse():
                    help="instead of the decode step, time the exact top-k merge of decode context parallelism "
                         "emulated over W token-strided shards, beside the plain top-k, on the indexer's scores")
     p.add_argument("--cpu-layers", type=int, default=4, help="layer-steps the CPU oracle runs for cpu_baseline")
-    p.add_argument("--config", choices=["headline", "small", "batch16", "long1m", "prefill", "mixed_mxfp4"],
+    p.add_argument("--config", choices=["headline", "small", "batch16", "long1m", "prefill", "mixed_mxfp4", "verify"],
                    default="headline",
                    help="workload: headline (batch x ctx from --batch/--ctx/--layers, the default), or one of the "
                         "other measured workloads: small (1 x 8,192), batch16 (16 rows, 16K-64K), long1m (1 x 1M, "
                         "2,048 planted keys, 2 layers), prefill (2,048 rows on a 150,000-token prefix), mixed_mxfp4 "
-                        "(64 rows, 4K-256K log-uniform, bs 128, MXFP4 keys, 24 layers)")
+                        "(64 rows, 4K-256K log-uniform, bs 128, MXFP4 keys, 24 layers), verify (speculative "
+                        "verification: 16 sequences x 4 rows on 65,536-token contexts, keys per --index-fmt, bs 128)")
+    p.add_argument("--rows-per-seq", type=int, default=0,
+                   help="override the workload's rows_per_seq hint (0: the workload's own; 1: row by row)")
     p.add_argument("--cpu-configs", action="store_true",
                    help="only time the CPU oracle on bounded samples of the other workloads (8K, batch 16, 1M, "
                         "prefill-append, batch-64 MXFP4) and print one JSON line")
@@ -378,6 +381,15 @@ def build_workload(a, dev):
         return (config_prefill_append(seed=a.seed, device=dev), 2048,
                 "DSA prefill-append, 2,048 query rows on a 150,000-token prefix (row r sees tokens <= 150,000 + r), "
                 "top-2048 per row, block size 64, FP8 keys and latents, one layer")
+    if a.config == "verify":
+        S, T, L = 16, 4, 65536
+        row_seq = [b for b in range(S) for _ in range(T)]
+        row_ctx = [L - T + j + 1 for _ in range(S) for j in range(T)]
+        case = make_case(row_ctx, row_seq=row_seq, ctx_lens_are_rows=True, block_size=128, seed=a.seed, device=dev,
+                         k=K, index_fmt=a.index_fmt, name="verify_16x4_ctx64k")
+        return (case, T, f"DSA speculative verification: 16 sequences x 4 query rows (row j sees {L - T} + j + 1 "
+                         f"tokens of its sequence), top-2048 per row, block size 128, "
+                         f"{'MXFP4' if a.index_fmt == 'mxfp4' else 'FP8'} index keys, FP8 latents, one layer")
     return (config_mixed_mxfp4(seed=a.seed, device=dev), 1,
             "DSA decode, batch 64, contexts log-uniform on [4,096, 262,144], top-2048, block size 128, MXFP4 index "
             "keys and FP8 latents, 24 layers in one packed row, rotated")
@@ -409,6 +421,8 @@ def main():
 
     t0 = time.time()
     case, rows_per_seq, workload = build_workload(a, dev)
+    if a.rows_per_seq > 0:
+        rows_per_seq = a.rows_per_seq
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     a.layers = case.layout.num_layers
@@ -486,11 +500,24 @@ def main():
     ix_us = st_us["indexer"]
     ctxs = [int(c) for c in case.row_ctx.tolist()]
     ix_kernel = {("fp8", False): "indexer_fp8_kernel<PAGED32, SEND=true>", ("fp8", True): "indexer_fp8_rows_kernel",
-                 ("mxfp4", False): "indexer_mxfp4_kernel<PAGED32, SEND=true>"}.get(
+                 ("mxfp4", False): "indexer_mxfp4_kernel<PAGED32, SEND=true>",
+                 ("mxfp4", True): "indexer_mxfp4_rows_kernel"}.get(
         (a.index_fmt, rows_per_seq > 1), "indexer")
     if max_ctx <= 16384:
         ix_kernel = ix_kernel.replace("SEND=true", "SEND=false")
-    if rows_per_seq > 1:
+    if a.config == "verify":
+        # a few rows per sequence: each key is read once for its sequence's rows, so the
+        # scan stays bound by the key bytes of the sequences
+        step_bytes = None
+        seqs = {}
+        for q, c in zip(case.row_seq.tolist(), ctxs):
+            seqs[q] = max(seqs.get(q, 0), c)
+        ix_bytes = sum(A.indexer_bytes(c, a.index_fmt) for c in seqs.values()) + \
+            (len(ctxs) - len(seqs)) * (A.Q_IDX if a.index_fmt == "fp8" else A.Q_IDX_MX)
+        ix_gbps = ix_bytes / (ix_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ix_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ix_gbps / PEAK_HBM_GBPS, 4), "traffic": None, "algorithmic_bytes_per_launch": ix_bytes}
+    elif rows_per_seq > 1:
         # rows share one sequence's keys: bytes are not the bound, the contraction is
         step_bytes = None
         ix_flops = A.indexer_flops(ctxs)

@@ -196,15 +196,15 @@ dsa_status dsa_decode_step(const dsa_cache_desc* cache, int32_t layer,
 /*
  * Several query rows per sequence (page 1: the 2K-token append on a 150K prefix,
  * every appended token a query row; the AMD section: several speculative-verify
- * tokens per sequence whose queries share one key scan). Same as dsa_indexer_score
- * / dsa_decode_step, plus
+ * tokens per sequence whose queries share one key scan, keys reused across query
+ * rows). Same as dsa_indexer_score / dsa_decode_step, plus
  *   rows_per_seq  >= 1: rows come in runs of this many consecutive rows that share
  *                 a sequence (row_seq equal), e.g. T for a T-token append or the
  *                 draft length + 1 for speculative verification; 1 = no sharing.
- * With FP8 keys and rows_per_seq > 1 the indexer reads and converts each key once
- * for up to 16 consecutive rows. It is a performance hint only: a row whose row_seq
- * differs from the row before it reloads the keys, so results never depend on it.
- * (MXFP4 keys are scored row by row.) DSA_ERR_ARG if rows_per_seq < 1.
+ * With rows_per_seq > 1 the indexer reads each key once (FP8: and converts it once)
+ * for up to 16 consecutive rows, for FP8 and MXFP4 keys alike. It is a performance
+ * hint only: a row whose row_seq differs from the row before it reloads the keys, so
+ * results never depend on it. DSA_ERR_ARG if rows_per_seq < 1.
  */
 dsa_status dsa_indexer_score_multi(const dsa_cache_desc* cache, int32_t layer,
                                    const void* q_idx, const void* q_idx_scale, const float* w,

@@ -162,8 +162,8 @@ size_t decode_ws(int32_t R, int32_t max_ctx, int32_t k) {
 
 // The indexer for the cache's key format: FP8 (q_idx_scale = R x 32 fp32) or MXFP4
 // (q_idx_scale = R x 32 x 4 E8M0 bytes).
-// rows_per_seq > 1 (FP8): runs of that many consecutive rows share a sequence, so the
-// row-group kernel reads each key once per group of up to kRowsPerGroupMax rows.
+// rows_per_seq > 1: runs of that many consecutive rows share a sequence, so the row-group
+// kernel (FP8 or MXFP4) reads each key once per group of up to kRowsPerGroupMax rows.
 hipError_t launch_indexer(int32_t index_fmt, const CacheView& cv, const RowMap& rm, const void* q_idx,
                           const void* q_idx_scale, const float* w, int R, int32_t rows_per_seq, float* scores,
                           int64_t ld, const TopkWs* ws, hipStream_t s) {
@@ -171,6 +171,11 @@ hipError_t launch_indexer(int32_t index_fmt, const CacheView& cv, const RowMap& 
     const int G = rows_per_seq < kRowsPerGroupMax ? rows_per_seq : kRowsPerGroupMax;
     return launch_indexer_fp8_rows(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const float*>(q_idx_scale),
                                    w, R, G, scores, ld, ws, s);
+  }
+  if (index_fmt == DSA_INDEX_MXFP4 && rows_per_seq > 1) {
+    const int G = rows_per_seq < kRowsPerGroupMax ? rows_per_seq : kRowsPerGroupMax;
+    return launch_indexer_mxfp4_rows(cv, rm, static_cast<const uint8_t*>(q_idx),
+                                     static_cast<const uint8_t*>(q_idx_scale), w, R, G, scores, ld, ws, s);
   }
   if (index_fmt == DSA_INDEX_MXFP4)
     return launch_indexer_mxfp4(cv, rm, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(q_idx_scale), w,
@@ -365,7 +370,7 @@ dsa_status dsa_decode_step_stages(const dsa_cache_desc* cache, int32_t layer, co
   if (stages & DSA_STAGE_INDEXER)
     e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld, &tw, s);
   if (e == hipSuccess && (stages & DSA_STAGE_TOPK)) {
-    const int umax = send_umax(cache->index_fmt == DSA_INDEX_FP8, rows_per_seq);
+    const int umax = send_umax(rows_per_seq);
     e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, umax, idx, tw, phys, &cv, &rm, s);
   }
   // the selected tokens lie below max_ctx, so the row map's bound is unchanged

@@ -151,6 +151,11 @@ hipError_t launch_cache_append(const CacheView& cv, int32_t index_fmt, const int
                                const int32_t* row_seq, const int32_t* pos, const float* idx_key,
                                const float* latent, int R, hipStream_t stream);
 
+// Row-group indexer over MXFP4 keys (G consecutive rows per workgroup share each key tile).
+hipError_t launch_indexer_mxfp4_rows(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx,
+                                     const uint8_t* q_e8, const float* w, int R, int G, float* scores, int64_t ld,
+                                     const TopkWs* ws, hipStream_t stream);
+
 // Indexer over MXFP4 keys (q_idx: R x 32 x 64 packed e2m1, q_e8: R x 32 x 4 E8M0).
 hipError_t launch_indexer_mxfp4(const CacheView& cv, const RowMap& rm, const uint8_t* q_idx, const uint8_t* q_e8,
                                 const float* w, int R, float* scores, int64_t ld, const TopkWs* ws,
@@ -167,11 +172,9 @@ hipError_t launch_topk_send(const float* scores, int64_t ld, const int32_t* row_
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
                               int umax, int32_t* idx, const TopkWs& ws, int32_t* phys, const CacheView* cv,
                               const RowMap* rm, hipStream_t stream);
-// Workgroup size of the candidate producer the decode step uses for a key format and
-// row grouping (the FP8 per-row indexer and the standalone send run 512 threads).
-inline int send_umax(int32_t index_fmt_is_fp8, int32_t rows_per_seq) {
-  return (index_fmt_is_fp8 && rows_per_seq <= 1) ? 512 : 256;
-}
+// Workgroup size of the candidate producer the decode step uses for a row grouping (the
+// per-row indexers and the standalone send run 512 threads, the row-group indexers 256).
+inline int send_umax(int32_t rows_per_seq) { return rows_per_seq <= 1 ? 512 : 256; }
 
 // Sparse MLA over idx; when `phys` (page slots from the selection) is non-null it
 // replaces the block-table lookups.

@@ -373,11 +373,13 @@ def test_mixed_mxfp4_b64_24_layers_full_size(dev):
         del pool
 
 
-def test_prefill_append_row_groups(dev):
+@pytest.mark.parametrize("fmt,bs", [("fp8", 64), ("mxfp4", 128)])
+def test_prefill_append_row_groups(dev, fmt, bs):
     """The row-group indexer (rows_per_seq = all rows) on a 300-row append to a 20,000-token
-    prefix: identical bytes to the row-by-row path, and oracle parity on sampled rows."""
-    say("case: prefill-append 300 rows on 20000 prefix, rows_per_seq 300 vs 1")
-    c = make_prefill_case(20000, 300, block_size=64, seed=81, device=dev)
+    prefix, FP8 or MXFP4 keys: identical bytes to the row-by-row path, and oracle parity on
+    sampled rows."""
+    say(f"case: prefill-append 300 rows on 20000 prefix, {fmt} keys, rows_per_seq 300 vs 1")
+    c = make_prefill_case(20000, 300, block_size=bs, seed=81, device=dev, index_fmt=fmt)
     hc = HostCase(c)
     a = run_step(c, dev, rows_per_seq=1)
     b = run_step(c, dev, rows_per_seq=c.num_rows)
@@ -395,17 +397,20 @@ def test_prefill_append_row_groups(dev):
         check_attention(hc, r, sel, b[2][r], b[3][r])
 
 
-@pytest.mark.parametrize("hint", [4, 3])
-def test_speculative_verify_rows(dev, hint):
+@pytest.mark.parametrize("fmt,bs,hint", [("fp8", 64, 4), ("fp8", 64, 3), ("mxfp4", 128, 4), ("mxfp4", 128, 3),
+                                         ("mxfp4", 16, 4)])
+def test_speculative_verify_rows(dev, fmt, bs, hint):
     """Speculative verification: 5 sequences x 4 verify tokens, row j of sequence b sees
-    t < L_b + j + 1. hint 4 matches the runs; hint 3 makes workgroups straddle sequences,
-    which reload keys: the result must not change. Every row against the oracle."""
-    say(f"case: speculative verify 5 x 4 rows, rows_per_seq {hint}")
+    t < L_b + j + 1, with FP8 or MXFP4 index keys. hint 4 matches the runs; hint 3 makes
+    workgroups straddle sequences, which reload keys: the result must not change. Every
+    row against the oracle."""
+    say(f"case: speculative verify 5 x 4 rows, {fmt} keys, bs {bs}, rows_per_seq {hint}")
     lens = [3000, 17000, 40000, 9000, 70000]
     T = 4
     row_seq = [b for b in range(len(lens)) for _ in range(T)]
     row_ctx = [lens[b] + j + 1 for b in range(len(lens)) for j in range(T)]
-    c = make_case(row_ctx, row_seq=row_seq, ctx_lens_are_rows=True, block_size=64, seed=90, k=2048, device=dev)
+    c = make_case(row_ctx, row_seq=row_seq, ctx_lens_are_rows=True, block_size=bs, seed=90, k=2048, device=dev,
+                  index_fmt=fmt)
     hc = HostCase(c)
     base = run_step(c, dev, rows_per_seq=1)
     got = run_step(c, dev, rows_per_seq=hint)
