@@ -89,6 +89,15 @@ __global__ __launch_bounds__(NTI) void indexer_fp8_kernel(const int32_t* __restr
   const int tok0 = blockIdx.x * NTI + wid * 64;
   const int bs_mask = cv.block_size - 1;
 
+  // ---- query fragment (head n, bytes [64g, 64g + 64)), issued ahead of the key stream:
+  // vector loads return in issue order, so the first tile's contraction then waits only
+  // for its own keys and overlaps the second tile's arrival ----
+  v4i qr[4];
+  {
+    const v4i* qp = reinterpret_cast<const v4i*>(q_idx + ((int64_t)r * kHIdx + n) * kDIdx + 64 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qr[i] = qp[i];
+  }
   // ---- key loads for both tiles: 4 x 1 KB of whole lines each. No branches: a tile
   // start past the row's end is clamped to the row's last tile, so every load reads
   // valid keys; results for tokens >= ctx are never stored ----
@@ -140,17 +149,10 @@ __global__ __launch_bounds__(NTI) void indexer_fp8_kernel(const int32_t* __restr
     ksc = *reinterpret_cast<const float*>(cv.pool + off + (int64_t)cv.block_size * kDIdx + (int64_t)(t & bs_mask) * 4);
   }
 
-  // ---- query fragment (head n, bytes [64g, 64g+64)) and folded head weights, issued
-  // behind the key stream (needed only once keys are in) ----
-  v4i qr[4];
-  {
-    const v4i* qp = reinterpret_cast<const v4i*>(q_idx + ((int64_t)r * kHIdx + n) * kDIdx + 64 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qr[i] = qp[i];
-  }
+  // folded head weights (uniform: scalar loads, kept in scalar registers)
   float W[kHIdx];
 #pragma unroll
-  for (int h = 0; h < kHIdx; ++h)  // uniform: scalar loads, kept in scalar registers
+  for (int h = 0; h < kHIdx; ++h)
     W[h] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w[r * kHIdx + h] * q_scale[r * kHIdx + h])));
 
   // every load of the wave is in flight before anything waits on one

@@ -89,6 +89,17 @@ __global__ __launch_bounds__(NTI) void indexer_mxfp4_kernel(const int32_t* __res
   const int bs_mask = cv.block_size - 1;
   const int64_t sc_off = (int64_t)cv.block_size * kKeyBytes;  // E8M0 bytes follow the codes in a page
 
+  // ---- query operands (head n, code bytes [16 g, +16) and [32 + 16 g, +16)) with their
+  // E8M0 exponents, issued ahead of the key stream: vector loads return in issue order,
+  // so the first tile's MFMAs wait only for its own keys ----
+  v4i qr[2];
+  {
+    const uint8_t* qp = q_idx + ((int64_t)r * kHIdx + n) * kKeyBytes + 16 * g;
+    qr[0] = *reinterpret_cast<const v4i*>(qp);
+    qr[1] = *reinterpret_cast<const v4i*>(qp + 32);
+  }
+  const uint32_t qe = *reinterpret_cast<const uint32_t*>(q_e8 + ((int64_t)r * kHIdx + n) * 4);
+
   // ---- code loads for both tiles (2 x 1 KB of whole lines each), branch-free: a tile
   // start past the row's end is clamped to the row's last tile ----
   v4i kv[2][2];
@@ -136,15 +147,7 @@ __global__ __launch_bounds__(NTI) void indexer_mxfp4_kernel(const int32_t* __res
     }
   }
 
-  // ---- query operands (head n, code bytes [16 g, +16) and [32 + 16 g, +16)) with their
-  // E8M0 exponents, and the head weights (uniform: scalar loads), behind the key stream ----
-  v4i qr[2];
-  {
-    const uint8_t* qp = q_idx + ((int64_t)r * kHIdx + n) * kKeyBytes + 16 * g;
-    qr[0] = *reinterpret_cast<const v4i*>(qp);
-    qr[1] = *reinterpret_cast<const v4i*>(qp + 32);
-  }
-  const uint32_t qe = *reinterpret_cast<const uint32_t*>(q_e8 + ((int64_t)r * kHIdx + n) * 4);
+  // head weights (uniform: scalar loads)
   float W[kHIdx];
 #pragma unroll
   for (int h = 0; h < kHIdx; ++h) W[h] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w[r * kHIdx + h])));
