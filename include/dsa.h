@@ -307,8 +307,11 @@ dsa_status dsa_device_status(void* stream, int32_t clear, uint32_t* status);
  * DSA_STAGE_INDEXER, then DSA_STAGE_TOPK, then DSA_STAGE_ATTENTION | DSA_STAGE_MERGE on
  * one workspace equals one dsa_decode_step_multi call; a stage reads what the stages
  * before it left in the workspace (or in idx), so running a later stage alone repeats
- * its work on the previous call's intermediate results. DSA_ERR_ARG for an empty mask
- * or unknown bits.
+ * its work on the previous call's intermediate results. A mask holding both
+ * DSA_STAGE_TOPK and DSA_STAGE_ATTENTION may run them as one launch (the step does so
+ * for one row with FP8 latents); that launch keeps the selected tokens' page slots on
+ * chip, so a later DSA_STAGE_ATTENTION alone reads those of the last DSA_STAGE_TOPK run
+ * without DSA_STAGE_ATTENTION. DSA_ERR_ARG for an empty mask or unknown bits.
  */
 #define DSA_STAGE_INDEXER 1u    /* indexer scores and the top-k candidate stage */
 #define DSA_STAGE_TOPK 2u       /* exact top-k selection (writes idx) */

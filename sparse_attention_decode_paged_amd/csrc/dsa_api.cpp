@@ -369,12 +369,17 @@ dsa_status dsa_decode_step_stages(const dsa_cache_desc* cache, int32_t layer, co
   hipError_t e = hipSuccess;
   if (stages & DSA_STAGE_INDEXER)
     e = launch_indexer(cache->index_fmt, cv, rm, q_idx, q_idx_scale, w, R, rows_per_seq, scores, ld, &tw, s);
-  if (e == hipSuccess && (stages & DSA_STAGE_TOPK)) {
-    const int umax = send_umax(rows_per_seq);
+  const int umax = send_umax(rows_per_seq);
+  // the selected tokens lie below max_ctx, so the row map's bound is unchanged
+  int parts = ((stages & DSA_STAGE_ATTENTION) ? 1 : 0) | ((stages & DSA_STAGE_MERGE) ? 2 : 0);
+  if (e == hipSuccess && (stages & DSA_STAGE_TOPK) && (parts & 1) && select_mla_fused(cv, R, k)) {
+    // select and attention in one launch; the page slots stay on chip
+    e = launch_select_mla(scores, ld, row_ctx, R, max_ctx, k, umax, idx, tw, cv, rm, q_lat, sm_scale, out, lse,
+                          mla_ws, s);
+    parts &= 2;
+  } else if (e == hipSuccess && (stages & DSA_STAGE_TOPK)) {
     e = launch_topk_select(scores, ld, row_ctx, R, max_ctx, k, umax, idx, tw, phys, &cv, &rm, s);
   }
-  // the selected tokens lie below max_ctx, so the row map's bound is unchanged
-  const int parts = ((stages & DSA_STAGE_ATTENTION) ? 1 : 0) | ((stages & DSA_STAGE_MERGE) ? 2 : 0);
   if (e == hipSuccess && parts) e = launch_sparse_mla(cv, rm, q_lat, idx, phys, R, k, sm_scale, out, lse, mla_ws, parts, s);
   return hip_status(e, "decode_step");
 }

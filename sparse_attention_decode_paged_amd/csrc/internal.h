@@ -184,6 +184,18 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
                              const int32_t* phys, int R, int k, float sm_scale, float* out, float* lse, void* ws,
                              int parts, hipStream_t stream);
 
+// The select and the sparse-MLA attention as one launch (the merge stays a launch of its
+// own): every attention workgroup runs its row's select and keeps the list on chip. For
+// FP8 latents and grids of at most kSelMlaMaxGroups workgroups (one per CU of the
+// 256-CU part); select_mla_fused tells whether the decode step takes it. Writes idx
+// (not the page slots) and the same out / lse / partials as the two launches.
+constexpr int kSelMlaMaxGroups = 256;
+bool select_mla_fused(const CacheView& cv, int R, int k);
+hipError_t launch_select_mla(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
+                             int umax, int32_t* idx, const TopkWs& tw, const CacheView& cv, const RowMap& rm,
+                             const uint16_t* q_lat, float sm_scale, float* out, float* lse, void* ws,
+                             hipStream_t stream);
+
 // Exact top-k merge of decode context parallelism over W token-strided shards, emulated
 // on one GPU (ws: dcp_ws_bytes). resend_mask / words may be null.
 hipError_t launch_topk_dcp(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k, int W,

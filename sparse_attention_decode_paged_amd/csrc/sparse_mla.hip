@@ -56,6 +56,7 @@
 #include "dsa.h"
 #include "common.h"
 #include "internal.h"
+#include "topk_select.h"
 
 namespace dsa {
 
@@ -112,54 +113,87 @@ __device__ __forceinline__ int nv_col(int col) {
 
 }  // namespace
 
-// The index list, page slots and queries lead the argument list so that their
-// addresses arrive preloaded in scalar registers (kernel-argument preloading covers
-// leading scalar and pointer arguments, not structures): the head of the load chain
-// needs no kernel-argument fetch before it.
+// Where a workgroup reads the token ids and page slots of its split: the index and
+// page-slot rows in global memory, or an LDS copy of the split's (token, page slot)
+// entries (the fused select + attention kernel).
+struct MlaIds {
+  const int32_t* irow;  // index row (global), used when lds == nullptr
+  const int32_t* prow;  // page-slot row (global) or nullptr
+  const int2* lds;      // entries of list positions j0.. (LDS) or nullptr
+  int j0;
+  __device__ __forceinline__ bool slots() const { return lds != nullptr || prow != nullptr; }
+  __device__ __forceinline__ void get(int j, int& t, int& ps) const {
+    if (lds != nullptr) {
+      const int2 e = lds[j - j0];
+      t = e.x;
+      ps = e.y;
+    } else {
+      t = irow[j];
+      if (prow != nullptr) ps = prow[j];
+    }
+  }
+};
+
+constexpr int a16(int x) { return (x + 15) & ~15; }
+// The attention workgroup's LDS, carved from one raw buffer (the fused kernel lays the
+// select's LDS over the same bytes): the latent tile (Q passes through it first), the
+// scaled logits (head-major; G = 16: one array per half of the dims), the chunk's token
+// scales, the NVFP4 query powers of two, the chunk's P'' (head-major), each head's
+// rescale factor and running (max, sum).
 template <bool NV, int G>
-__global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ phys,
-                                                        const uint16_t* __restrict__ q_lat, int k, int ts, float c2,
-                                                        CacheView cv, RowMap rm,
-                                                        float* __restrict__ out, float* __restrict__ lse,
-                                                        _Float16* __restrict__ part_o, float* __restrict__ part_ml,
-                                                        int nsplit) {
-  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+struct MlaLds {
+  static constexpr int LAT = 0;
+  static constexpr int X = a16(LAT + Tile<NV>::BYTES);
+  static constexpr int SC = a16(X + (G == 16 ? 2 : 1) * G * XROW * 4);
+  static constexpr int QE = a16(SC + CH * 4);
+  static constexpr int P = a16(QE + G * 4);
+  static constexpr int AL = a16(P + G * PROW * 2);
+  static constexpr int ML = a16(AL + G * 4);
+  static constexpr int BYTES = a16(ML + G * 8);
+};
+
+constexpr int mla_qn(int G) { return (G * (kDLat / 8) + NTM - 1) / NTM; }  // 16-byte Q pieces per thread
+
+// Q is read from HBM coalesced (rows of this head group are contiguous): thread tid
+// takes pieces tid + NTM q of the group's G x 72 16-byte pieces.
+template <int G>
+__device__ __forceinline__ void mla_load_q(const uint16_t* __restrict__ q_lat, int r, int hg, v4i (&qv)[mla_qn(G)]) {
+  constexpr int QALL = G * (kDLat / 8);
+  const int tid = threadIdx.x;
+  const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * G) * kDLat);
+#pragma unroll
+  for (int q = 0; q < mla_qn(G); ++q)
+    if (tid + NTM * q < QALL) qv[q] = qg[tid + NTM * q];
+}
+
+// One workgroup of NTM threads (the first NTM of a larger one in the fused kernel):
+// split `split` (list positions [j0, j1)) of row r for head group hg. (t_n, ps_n) is
+// the first chunk's gather token of this thread, already fetched from `src`; qv its Q
+// pieces (mla_load_q).
+template <bool NV, int G>
+__device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, const v4i (&qv)[mla_qn(G)], int j0,
+                                         int j1, float c2, const CacheView& cv, const RowMap& rm, int r, int hg,
+                                         int split, float* __restrict__ out, float* __restrict__ lse,
+                                         _Float16* __restrict__ part_o, float* __restrict__ part_ml, int nsplit,
+                                         uint8_t* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-
+  using L = MlaLds<NV, G>;
   constexpr int LROW = Tile<NV>::ROW;
-  __shared__ __attribute__((aligned(16))) uint8_t lat_s[Tile<NV>::BYTES];
-  // scaled logits, head-major (G = 16: one array per half of the dims)
-  __shared__ __attribute__((aligned(16))) float x_s[(G == 16 ? 2 : 1) * G * XROW];
-  __shared__ __attribute__((aligned(16))) float sc_s[CH];
-  __shared__ float qe_s[G];  // NVFP4: the power of two each head's fp16 query was scaled down by
-  __shared__ __attribute__((aligned(16))) _Float16 p_s[G * PROW];  // the chunk's P'', head-major
-  __shared__ float al_s[G];   // each head's rescale factor for the chunk
-  __shared__ float2 ml_s[G];  // each head's running (max, sum), kept by its owning wave
-
-  const int32_t* irow = idx + (int64_t)r * k;
-  const int j0 = split * ts;
-  const int j1 = (j0 + ts < k) ? j0 + ts : k;
+  uint8_t* lat_s = smem + L::LAT;
+  float* x_s = reinterpret_cast<float*>(smem + L::X);
+  float* sc_s = reinterpret_cast<float*>(smem + L::SC);
+  float* qe_s = reinterpret_cast<float*>(smem + L::QE);
+  _Float16* p_s = reinterpret_cast<_Float16*>(smem + L::P);
+  float* al_s = reinterpret_cast<float*>(smem + L::AL);
+  float2* ml_s = reinterpret_cast<float2*>(smem + L::ML);
   // gather: 8 threads per token. FP8: 16-byte pieces q8 + 8 q (q < 5) of 36. NVFP4: code
   // bytes [32 q8, +32) (dims [64 q8, +64)), their 4 block scales and, for q8 < 4, tail
   // bytes [16 q8, +16) (dims 512 + 16 q8 ..)
   const int tt_g = tid >> 3, q8 = tid & 7;
-
-  // token id and page slot of this thread's gather token: the head of the load chain,
-  // issued before anything else
-  int t_n = -1, ps_n = 0;
-  {
-    const int j = j0 + tt_g;
-    if (j < j1) {
-      t_n = irow[j];
-      if (phys != nullptr) ps_n = phys[(int64_t)r * k + j];
-    }
-  }
   // Q stays in registers for the whole workgroup: wave w holds the MFMA A fragments of
   // heads [16 (w >> 2), +16) over all 576 dims (lane: head lane & 15, dims 32 kk +
-  // 8 (lane >> 4) ..+8). Q is read from HBM coalesced (rows of this head group are
-  // contiguous) and passes through the latent tile's LDS bytes, which the first chunk's
-  // latents overwrite after a barrier.
+  // 8 (lane >> 4) ..+8). Q passes through the latent tile's LDS bytes, which the first
+  // chunk's latents overwrite after a barrier.
   const int hrow = lane & 15, kq = 8 * (lane >> 4);
   // QK tile of this wave: tokens 16 tg..; G = 16: all heads, dims 288 wq..;
   // G = 32: heads 16 wq.., all dims
@@ -167,19 +201,9 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   constexpr int KQ = G == 16 ? kDLat / 64 : kDLat / 32;  // steps of 32 dims
   constexpr int QP = kDLat / 8;           // 72 16-byte pieces per head row
   constexpr int QALL = G * QP;
-  constexpr int QN = (QALL + NTM - 1) / NTM;
-  v4i qv[QN];
-  {
-    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * G) * kDLat);
-#pragma unroll
-    for (int q = 0; q < QN; ++q)
-      if (tid + NTM * q < QALL) qv[q] = qg[tid + NTM * q];
-  }
-  // Only now the loads that need the structure arguments (fetched from memory, unlike the
-  // leading pointers): the id and query loads above go out without waiting for them.
+  constexpr int QN = mla_qn(G);
   // The row's block-table row is needed only without page slots.
-  __builtin_amdgcn_sched_barrier(0);
-  const int seq = phys == nullptr ? rm.row_seq[r] : 0;
+  const int seq = src.slots() ? 0 : rm.row_seq[r];
   const int bs_mask = cv.block_size - 1;
   v8bf qa[KQ];
   v8h qh[KQ];  // NVFP4: the same fragments in fp16, scaled by a power of two per head
@@ -213,7 +237,7 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
     const int tc = t >= 0 ? t : 0;  // every load below stays in the pool; empty slots are masked
     int64_t blk;
     int slot;
-    if (phys != nullptr) {
+    if (src.slots()) {
       const int ps = ps_n >= 0 ? ps_n : 0;
       blk = (int64_t)ps >> cv.log2_bs;
       blk = blk < cv.num_blocks ? blk : cv.num_blocks - 1;
@@ -242,10 +266,7 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   auto fetch_ids = [&](int c0) {
     const int j = c0 + tt_g;
     t_n = -1;
-    if (j < j1) {
-      t_n = irow[j];
-      if (phys != nullptr) ps_n = phys[(int64_t)r * k + j];
-    }
+    if (j < j1) src.get(j, t_n, ps_n);
   };
   issue();
   fetch_ids(j0 + CH);
@@ -643,6 +664,98 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
   }
 }
 
+// The index list, page slots and queries lead the argument list so that their
+// addresses arrive preloaded in scalar registers (kernel-argument preloading covers
+// leading scalar and pointer arguments, not structures): the head of the load chain
+// needs no kernel-argument fetch before it.
+template <bool NV, int G>
+__global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ phys,
+                                                        const uint16_t* __restrict__ q_lat, int k, int ts, float c2,
+                                                        CacheView cv, RowMap rm,
+                                                        float* __restrict__ out, float* __restrict__ lse,
+                                                        _Float16* __restrict__ part_o, float* __restrict__ part_ml,
+                                                        int nsplit) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MlaLds<NV, G>::BYTES];
+  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+  const int j0 = split * ts;
+  const int j1 = (j0 + ts < k) ? j0 + ts : k;
+  const MlaIds src{idx + (int64_t)r * k, phys != nullptr ? phys + (int64_t)r * k : nullptr, nullptr, j0};
+  // token id and page slot of this thread's gather token: the head of the load chain,
+  // issued before anything else
+  int t_n = -1, ps_n = 0;
+  {
+    const int j = j0 + ((int)threadIdx.x >> 3);
+    if (j < j1) src.get(j, t_n, ps_n);
+  }
+  v4i qv[mla_qn(G)];
+  mla_load_q<G>(q_lat, r, hg, qv);
+  // only now the loads that need the structure arguments (fetched from memory, unlike
+  // the leading pointers): the id and query loads above go out without waiting for them
+  __builtin_amdgcn_sched_barrier(0);
+  mla_body<NV, G>(src, t_n, ps_n, qv, j0, j1, c2, cv, rm, r, hg, split, out, lse, part_o, part_ml, nsplit, smem);
+}
+
+// The select and the attention in one launch (batches of up to 4 rows, FP8 latents,
+// 16 heads per workgroup). Every workgroup of a row runs the row's select itself on
+// all SEL_NT threads (the same exact computation as the select kernel, so all of them
+// reach the same list), keeps the selection in LDS, and its first NTM threads attend
+// over their split of it: the list and the page slots never leave the CU, and the
+// select's launch and the attention's id loads drop out of the step. The workgroup of
+// split 0, head group 0 writes the row's index output. The select's LDS and the
+// attention's share the same bytes; the split's (token, page slot) entries sit apart.
+template <bool CAND>
+__global__ __launch_bounds__(SEL_NT) void select_mla_kernel(const uint32_t* __restrict__ cand_hi,
+                                                            const uint32_t* __restrict__ cand_lo,
+                                                            const uint32_t* __restrict__ floors,
+                                                            const float* __restrict__ scores, int64_t ld,
+                                                            const int32_t* __restrict__ row_ctx, int max_ctx, int k,
+                                                            int umax, int load_b, int32_t* __restrict__ idx,
+                                                            const uint16_t* __restrict__ q_lat, int ts, float c2,
+                                                            CacheView cv, RowMap rm, float* __restrict__ out,
+                                                            float* __restrict__ lse, _Float16* __restrict__ part_o,
+                                                            float* __restrict__ part_ml, int nsplit) {
+  constexpr int G = 16;
+  constexpr int SB = sizeof(SelShared) > (size_t)MlaLds<false, G>::BYTES ? (int)sizeof(SelShared)
+                                                                          : MlaLds<false, G>::BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SB];
+  __shared__ int2 ids_s[kMaxK];
+  SelShared& S = *reinterpret_cast<SelShared*>(smem);
+  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+  const int tid = threadIdx.x;
+  v4i qv[mla_qn(G)];
+  // the query goes out right behind the select's candidate loads
+  select_row<CAND>(cand_hi, cand_lo, floors, scores, ld, row_ctx, max_ctx, k, umax, load_b,
+                   (split == 0 && hg == 0) ? idx : nullptr, nullptr, true, cv, rm, r, S, [&] {
+                     if (tid < NTM) mla_load_q<G>(q_lat, r, hg, qv);
+                   });
+  // the split's list entries with their page slots (the block-table row staged by the
+  // select when it fits, else read), -1 past the selection
+  const int j0 = split * ts;
+  const int j1 = (j0 + ts < k) ? j0 + ts : k;
+  {
+    const uint32_t nsel = S.nsel;
+    const bool btl = S.btl != 0u;
+    const int seq = rm.row_seq[r];
+    for (int j = j0 + tid; j < j1; j += SEL_NT) {
+      const int t = (uint32_t)j < nsel ? (int)S.a.hist[j] : -1;
+      int ps = -1;
+      if (t >= 0)
+        ps = btl ? S.bt[t >> cv.log2_bs] * cv.block_size + (t & (cv.block_size - 1)) : page_slot(cv, rm, seq, t);
+      ids_s[j - j0] = int2{t, ps};
+    }
+  }
+  __syncthreads();  // the entries are in; the select's LDS is free for the attention
+  if (tid >= NTM) return;  // whole waves: the attention runs on the first NTM threads
+  const MlaIds src{nullptr, nullptr, ids_s, j0};
+  int t_n = -1, ps_n = 0;
+  {
+    const int j = j0 + (tid >> 3);
+    if (j < j1) src.get(j, t_n, ps_n);
+  }
+  mla_body<false, G>(src, t_n, ps_n, qv, j0, j1, c2, cv, rm, r, hg, split, out, lse, part_o, part_ml, nsplit, smem);
+}
+
 // out[r][h] = sum_s w_s A_s / sum_s w_s with w_s = 2^(m_s - M) l_s and A_s = O_s / l_s
 // (the fp16 split averages); empty splits (m = -inf) weigh 0. One wave per (row, head,
 // 128 value columns), so that the partials spread over several times as many CUs as
@@ -693,6 +806,39 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const _Float16* __restric
   *orow = float2{o0 * inv, o1 * inv};
   if (lse != nullptr && q == 0 && tid == 0)
     lse[(int64_t)r * kHQ + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
+}
+
+bool select_mla_fused(const CacheView& cv, int R, int k) {
+  if (cv.latent_fmt != DSA_LATENT_FP8 || R <= 0 || mla_group(R) != 16) return false;
+  // one workgroup per CU (the select's LDS): the whole grid in one round
+  return (int64_t)mla_splits(R, k) * R * (kHQ / 16) <= kSelMlaMaxGroups;
+}
+
+hipError_t launch_select_mla(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
+                             int umax, int32_t* idx, const TopkWs& tw, const CacheView& cv, const RowMap& rm,
+                             const uint16_t* q_lat, float sm_scale, float* out, float* lse, void* ws,
+                             hipStream_t stream) {
+  if (R <= 0) return hipSuccess;
+  const int nsplit = mla_splits(R, k);
+  const int ts = mla_split_tokens(k, nsplit);
+  const float c2 = (float)((double)sm_scale * 1.4426950408889634);
+  _Float16* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (nsplit > 1) {
+    part_o = static_cast<_Float16*>(ws);
+    part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)R * nsplit * kHQ * kDV * 2, 256));
+  }
+  const int load_b = cand_plan(max_ctx, umax).per == 16 ? 1 : 0;
+  const dim3 grid(nsplit, R, kHQ / 16);
+  if (max_ctx > kTopkFullRow)
+    hipLaunchKernelGGL(select_mla_kernel<true>, grid, dim3(SEL_NT), 0, stream, tw.cand_hi, tw.cand_lo, tw.floors,
+                       scores, ld, row_ctx, max_ctx, k, umax, load_b, idx, q_lat, ts, c2, cv, rm, out, lse, part_o,
+                       part_ml, nsplit);
+  else
+    hipLaunchKernelGGL(select_mla_kernel<false>, grid, dim3(SEL_NT), 0, stream, tw.cand_hi, tw.cand_lo, tw.floors,
+                       scores, ld, row_ctx, max_ctx, k, umax, 0, idx, q_lat, ts, c2, cv, rm, out, lse, part_o,
+                       part_ml, nsplit);
+  return hipGetLastError();
 }
 
 hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16_t* q_lat, const int32_t* idx,

@@ -184,6 +184,33 @@ def test_determinism_and_staged_calls(dev):
     assert np.array_equal(o.cpu().numpy(), a[2]) and np.array_equal(l.cpu().numpy(), a[3])
 
 
+@pytest.mark.parametrize("ctxs", [[200000], [70000, 30000], [9000]])
+def test_stages_equal_step(dev, ctxs):
+    """The step runs the select and the attention as one launch for these batches; the
+    stage-by-stage launches (indexer, select, attention + merge: separate kernels) must
+    give the same scores, indices, output and lse bit for bit."""
+    say(f"case: staged launches vs the step, ctx {ctxs}")
+    c = make_case(ctxs, block_size=64, seed=41, k=2048).to(dev)
+    s_f, i_f, o_f, l_f = run_step(c, dev)
+    R = c.num_rows
+    ws = torch.empty(dsa.dsa_workspace_bytes(dsa.DSA_OP_DECODE_STEP, R, c.max_ctx, c.k), dtype=torch.uint8,
+                     device=dev)
+    idx = torch.empty((R, c.k), dtype=torch.int32, device=dev)
+    out = torch.empty((R, 96, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, 96), dtype=torch.float32, device=dev)
+    for bits in (dsa.DSA_STAGE_INDEXER, dsa.DSA_STAGE_TOPK, dsa.DSA_STAGE_ATTENTION | dsa.DSA_STAGE_MERGE):
+        dsa.dsa_decode_step_stages(c.pool, c.layout, 0, c.q_idx[0], c.q_idx_scale[0], c.w[0], c.q_lat[0],
+                                   c.block_table, c.row_seq, c.row_ctx, c.max_ctx, c.k, c.sm_scale, idx, out, lse,
+                                   ws, bits)
+    torch.cuda.synchronize()
+    s_s = dsa.decode_scores_view(ws, R, c.max_ctx).cpu().numpy()
+    for r in range(R):
+        ctx = int(c.row_ctx[r])
+        assert np.array_equal(s_s[r, :ctx], s_f[r, :ctx])
+    assert np.array_equal(idx.cpu().numpy(), i_f)
+    assert np.array_equal(out.cpu().numpy(), o_f) and np.array_equal(lse.cpu().numpy(), l_f)
+
+
 def test_batch_invariance(dev):
     """A row's scores and selection do not depend on the batch it runs in (bit for bit).
     Its attention output may: sparse MLA splits a row's tokens into a number of splits
