@@ -701,9 +701,10 @@ __global__ __launch_bounds__(NTM) void sparse_mla_kernel(const int32_t* __restri
 // all SEL_NT threads (the same exact computation as the select kernel, so all of them
 // reach the same list), keeps the selection in LDS, and its first NTM threads attend
 // over their split of it: the list and the page slots never leave the CU, and the
-// select's launch and the attention's id loads drop out of the step. The workgroup of
-// split 0, head group 0 writes the row's index output. The select's LDS and the
-// attention's share the same bytes; the split's (token, page slot) entries sit apart.
+// select's launch and the attention's id loads drop out of the step. The workgroups of
+// head group 0 write the row's index output, each its split's positions. The select's
+// LDS and the attention's share the same bytes; the split's (token, page slot) entries
+// sit apart.
 template <bool CAND>
 __global__ __launch_bounds__(SEL_NT) void select_mla_kernel(const uint32_t* __restrict__ cand_hi,
                                                             const uint32_t* __restrict__ cand_lo,
@@ -724,16 +725,16 @@ __global__ __launch_bounds__(SEL_NT) void select_mla_kernel(const uint32_t* __re
   const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
   const int tid = threadIdx.x;
   v4i qv[mla_qn(G)];
-  // the query goes out right behind the select's candidate loads
-  select_row<CAND>(cand_hi, cand_lo, floors, scores, ld, row_ctx, max_ctx, k, umax, load_b,
-                   (split == 0 && hg == 0) ? idx : nullptr, nullptr, true, cv, rm, r, S, [&] {
-                     if (tid < NTM) mla_load_q<G>(q_lat, r, hg, qv);
-                   });
-  // the split's list entries with their page slots (the block-table row staged by the
-  // select when it fits, else read), -1 past the selection
   const int j0 = split * ts;
   const int j1 = (j0 + ts < k) ? j0 + ts : k;
+  // the query goes out right behind the select's candidate loads
+  select_row<CAND>(cand_hi, cand_lo, floors, scores, ld, row_ctx, max_ctx, k, umax, load_b, nullptr, nullptr, true, cv,
+                   rm, r, S, [&] {
+                     if (tid < NTM) mla_load_q<G>(q_lat, r, hg, qv);
+                   });
   {
+    // the split's list entries with their page slots (the block-table row staged by the
+    // select when it fits, else read), -1 past the selection
     const uint32_t nsel = S.nsel;
     const bool btl = S.btl != 0u;
     const int seq = rm.row_seq[r];
@@ -744,8 +745,11 @@ __global__ __launch_bounds__(SEL_NT) void select_mla_kernel(const uint32_t* __re
         ps = btl ? S.bt[t >> cv.log2_bs] * cv.block_size + (t & (cv.block_size - 1)) : page_slot(cv, rm, seq, t);
       ids_s[j - j0] = int2{t, ps};
     }
+    __syncthreads();  // the entries are in; the select's LDS is free for the attention
   }
-  __syncthreads();  // the entries are in; the select's LDS is free for the attention
+  // the row's index output, each split's positions written by its head-group-0 workgroup
+  if (hg == 0)
+    for (int j = j0 + tid; j < j1; j += SEL_NT) idx[(int64_t)r * k + j] = ids_s[j - j0].x;
   if (tid >= NTM) return;  // whole waves: the attention runs on the first NTM threads
   const MlaIds src{nullptr, nullptr, ids_s, j0};
   int t_n = -1, ps_n = 0;
