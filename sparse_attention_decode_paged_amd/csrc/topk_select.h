@@ -165,12 +165,19 @@ __device__ __forceinline__ void excl_scan4(const uint32_t (&v)[4], uint32_t (&of
     if (lane == 63) S.scan4[j][wid] = inc[j];
   }
   __syncthreads();
+  // one 16-lane row per sum: lane 16 j + w reads wave w's total of sum j, a scan down
+  // each row, and lane reads give this wave's offsets and the totals
+  uint32_t x = (lane & 15) < NW && (lane >> 4) < nj ? S.scan4[lane >> 4][lane & 15] : 0u;
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int w = __builtin_amdgcn_readfirstlane(wid);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    uint32_t before = 0, tot = 0;
-    if (j < nj) tot = wave_totals(S.scan4[j], before);
+    const uint32_t before = w > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)x, 16 * j + w - 1) : 0u;
     off[j] = before + inc[j] - v[j];
-    total[j] = tot;
+    total[j] = (uint32_t)__builtin_amdgcn_readlane((int)x, 16 * j + NW - 1);
   }
 }
 
@@ -184,13 +191,17 @@ __device__ __forceinline__ void block_minmax32(uint32_t& lo, uint32_t& hi, SelSh
     S.r32[par][1][wid] = hi;
   }
   __syncthreads();
-  lo = 0xFFFFFFFFu;
-  hi = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    lo = min(lo, S.r32[par][0][w]);
-    hi = max(hi, S.r32[par][1][w]);
-  }
+  // lanes 0..NW-1 take the waves' minima, lanes 16..16+NW-1 the complements of their
+  // maxima; one min-scan down each 16-lane row leaves both results in lanes 15 and 31
+  uint32_t x = 0xFFFFFFFFu;
+  if (lane < NW) x = S.r32[par][0][lane];
+  else if (lane >= 16 && lane < 16 + NW) x = ~S.r32[par][1][lane - 16];
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  lo = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  hi = ~(uint32_t)__builtin_amdgcn_readlane((int)x, 31);
   par ^= 1;
 }
 
