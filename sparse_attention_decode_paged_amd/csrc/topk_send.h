@@ -6,9 +6,12 @@
 //
 // Plan (cand_plan, a function of the row length and of the largest unit the producer
 // supports, umax = NT): rows of at most kTopkFullRow tokens send nothing (the select
-// reads their scores whole); up to 65,536 tokens a unit is one wave's 64 tokens; above,
-// 256 tokens (four waves), or 512 (eight waves) when the producer's workgroups hold 512
-// and the row is longer than 131,072 tokens. The expected number of the row's top 2048
+// reads their scores whole). With 512-token workgroups (the per-row indexers and the
+// standalone send) a unit is one wave's 64 tokens up to 65,536 tokens, 256 tokens (four
+// waves) up to 131,072 and 512 (eight waves) above. The row-group indexers (256-token
+// workgroups, one send per row and wave) keep one-wave units up to 262,144 tokens: no
+// barrier and no cross-wave merge per row, at the price of m = 4 above 131,072 tokens,
+// where a unit that holds 5 of the top 2048 (a few per row) is rescanned by the select. The expected number of the row's top 2048
 // in one unit is lam = 2048 / nu (nu = units of the row); a unit sends m >= lam +
 // 4 sqrt(lam) + 2 keys (m = 8, 16 or 32), so that a unit holding more of the top k than
 // it sent is rare (the select then rescans it; exactness never depends on m). With
@@ -49,7 +52,10 @@ __host__ __device__ inline CandPlan cand_plan(int ctx, int umax) {
     p.per = ctx <= kCandRowCap / 2 ? 8 : 16;
     return p;
   }
-  p.unit = ctx <= 4 * kTopkFullRow ? 64 : (umax >= 512 && ctx > 8 * kTopkFullRow ? 512 : 256);
+  if (umax >= 512)
+    p.unit = ctx <= 4 * kTopkFullRow ? 64 : (ctx > 8 * kTopkFullRow ? 512 : 256);
+  else  // row-group producers: one-wave units up to the floor capacity (4,096 units)
+    p.unit = ctx <= 16 * kTopkFullRow ? 64 : 256;
   p.nu = (ctx + p.unit - 1) / p.unit;
   // lam = 2048 / nu: nu < 410 <=> lam > 5 (m = 32 covers lam <= 14); nu < 1517 <=> lam > 1.35
   p.m = p.nu < 410 ? 32 : p.nu < 1517 ? 16 : 8;
