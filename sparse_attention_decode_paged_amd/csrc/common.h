@@ -179,6 +179,19 @@ __device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v, int lane) {
   return v;
 }
 
+// Largest of 64 values (one per lane), returned uniform: running maxima down each 16-lane
+// row (shifts of 1, 2, 4, 8), then the row maxima carried by the row broadcasts; lane 63
+// ends with the wave's maximum.
+__device__ __forceinline__ uint32_t wave_max_u32_last(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));   // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));   // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));   // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));   // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Inclusive prefix sum across a 64-lane wave: shifts of 1, 2, 4, 8 inside each
 // 16-lane row (zero fill), then the row totals carried by the row broadcasts.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {

@@ -81,7 +81,6 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int pos = threadIdx.x;  // position in the workgroup
   const uint32_t packed = valid ? ((float_key(score) & ~LM) | (LM - (uint32_t)pos)) : 0u;
-  const uint32_t sorted = wave_sort_desc_u32(packed, lane);
   uint32_t* cand_hi = tw.cand_hi + (int64_t)row * kCandRowCap;
   uint32_t* cand_lo = tw.cand_lo + (int64_t)row * kCandRowCap;
   uint32_t* floors = tw.floors + (int64_t)row * kFloorRowCap;
@@ -91,8 +90,21 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
     // one unit per wave
     const int u = (base >> 6) + wid;
     if (u >= p.nu) return;  // wave-uniform, past the row
-    const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)sorted, p.m - 1);
-    const uint32_t nxt = (uint32_t)__builtin_amdgcn_readlane((int)sorted, p.m);
+    uint32_t thr, nxt;
+    if (p.m == 4) {  // uniform: the 4 best packed keys and the next one by repeated maxima
+      uint32_t v = packed, mx[5];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) {
+        mx[q] = wave_max_u32_last(v);
+        v = v == mx[q] ? 0u : v;  // packed keys are distinct: one lane leaves the race
+      }
+      thr = mx[3];
+      nxt = mx[4];
+    } else {
+      const uint32_t sorted = wave_sort_desc_u32(packed, lane);
+      thr = (uint32_t)__builtin_amdgcn_readlane((int)sorted, p.m - 1);
+      nxt = (uint32_t)__builtin_amdgcn_readlane((int)sorted, p.m);
+    }
     const bool sent = packed != 0u && packed >= thr;
     const uint64_t bal = __ballot(sent);
     const uint32_t nsent = (uint32_t)__popcll(bal);
@@ -113,6 +125,7 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
   // into wnx[]; after one barrier every wave of the unit sorts the 64 entries. (An
   // 8-wave unit belongs to a row of more than 131,072 tokens, where a 64-token wave
   // holds on average at most one of the top 2048: nine or more are practically never.)
+  const uint32_t sorted = wave_sort_desc_u32(packed, lane);
   const int W = p.unit >> 6;                 // 4 or 8 (uniform)
   const int cw = 64 / W;                     // keys each wave contributes: 16 or 8
   const int wi = W == 8 ? wid : (wid & 3);   // wave index inside the unit
