@@ -92,9 +92,10 @@ struct SelShared {
   };
   uint32_t funit[FCAP];   // rescanned unit of each slot, in unit order
   uint32_t fstart[FCAP];  // its segment in ext
-  uint32_t flen[FCAP];
+  uint32_t flen[FCAP];    // the segment's length, then the selected ext keys before it
   uint32_t fcnt[FCAP];    // selected keys of the segment
   uint32_t foff[FCAP];    // their first output position
+  uint16_t fmap[kFloorRowCap];  // rescanned unit -> its slot
   uint64_t bucket[64];    // keys of the last histogram bucket
   uint64_t res64;
   uint32_t r32[2][2][NW];  // block min / max partials, double buffered
@@ -618,6 +619,60 @@ __device__ __forceinline__ void select_own(SelShared& S, uint32_t (&kh)[PER], ui
   flush_list(tot[0] + (N > 8 ? tot[1] : 0u), R, B, S);
 }
 
+// The resend: the keys >= cu of the flagged units S.funit[0, nflag) go to S.a.ext, each
+// unit's as one segment in token order (S.fstart, S.flen), segments in any order;
+// S.ecount gets the total. Wave w takes units w, w + NW, ...; it issues the score loads
+// of up to UPR of its units (CPU 64-token chunks each) before it ranks any of them, so
+// that one round of loads covers up to 16 UPR units (32 of 512 tokens).
+constexpr int RS_CPW = 16;  // 64-token chunks a wave loads per round
+template <int CPU>
+__device__ __forceinline__ void rescan_units(SelShared& S, const SelRow& R, uint32_t nflag, uint64_t cu) {
+  constexpr int UPR = RS_CPW / CPU < 8 ? RS_CPW / CPU : 8;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (uint32_t q0 = (uint32_t)wid; q0 < nflag; q0 += NW * UPR) {  // wave-uniform
+    float f[UPR * CPU];
+    int t0[UPR];
+#pragma unroll
+    for (int u = 0; u < UPR; ++u) {
+      const uint32_t q = q0 + (uint32_t)(NW * u);
+      t0[u] = __builtin_amdgcn_readfirstlane(q < nflag ? (int)S.funit[q] * (64 * CPU) : -1);
+#pragma unroll
+      for (int c = 0; c < CPU; ++c) {
+        const int t = t0[u] + 64 * c + lane;
+        f[u * CPU + c] = (t0[u] >= 0 && t < R.ctx) ? R.srow[t] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UPR; ++u) {
+      const uint32_t q = q0 + (uint32_t)(NW * u);
+      if (q >= nflag) break;  // uniform
+      uint64_t bal[CPU];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int c = 0; c < CPU; ++c) {
+        const int t = t0[u] + 64 * c + lane;
+        bal[c] = __ballot(t < R.ctx && composite_key(f[u * CPU + c], t) >= cu);
+        tot += (uint32_t)__popcll(bal[c]);
+      }
+      uint32_t st = 0;
+      if (lane == 0) st = atomicAdd(&S.ecount, tot);
+      st = (uint32_t)__shfl((int)st, 0, 64);
+      uint32_t run = st;
+#pragma unroll
+      for (int c = 0; c < CPU; ++c) {
+        const int t = t0[u] + 64 * c + lane;
+        const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
+        if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[u * CPU + c], t);
+        run += (uint32_t)__popcll(bal[c]);
+      }
+      if (lane == 0) {
+        S.fstart[q] = st;
+        S.flen[q] = tot;
+      }
+    }
+  }
+}
+
 // Candidate rows: register slots hold the units' sent keys (plan p, N = p.per).
 // Segment j of a thread's registers: m >= 8 -> j = 0 (registers 0..7) and j = 2
 // (8..15), one unit each; m = 4 -> j = 0..3, registers [4 j, 4 j + 4), one unit each.
@@ -691,47 +746,23 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
       select_row_global(R.srow, R.ctx, R.k, S, R.orow, R.prow, R.cv, R.rm, R.seq);
       return;
     }
-    // ---- resend: each flagged unit's keys >= cu, rescanned by one wave per unit ----
+    // ---- resend: the flagged units' keys >= cu are rescanned from the scores ----
     uint32_t sl[2] = {off[0], tot[0] + off[1]};
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (((fmask >> j) & 1u) && segfirst[j]) S.funit[sl[j >> 1]++] = (uint32_t)segu[j];
+      if (((fmask >> j) & 1u) && segfirst[j]) {
+        const uint32_t q = sl[j >> 1]++;
+        S.funit[q] = (uint32_t)segu[j];
+        S.fmap[segu[j]] = (uint16_t)q;
+      }
     if (tid == 0) S.ecount = 0u;
     __syncthreads();
-    const int chunks = p.unit >> 6;  // 64-token chunks per unit: 1, 4 or 8
-    for (uint32_t q = wid; q < nflag; q += NW) {
-      const int t0 = (int)S.funit[q] * p.unit;
-      float f[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int t = t0 + 64 * c + lane;
-        f[c] = (c < chunks && t < R.ctx) ? R.srow[t] : 0.f;
-      }
-      uint64_t bal[8];
-      uint32_t tot8 = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int t = t0 + 64 * c + lane;
-        const bool keep = c < chunks && t < R.ctx && composite_key(f[c], t) >= cu;
-        bal[c] = __ballot(keep);
-        tot8 += (uint32_t)__popcll(bal[c]);
-      }
-      uint32_t st = 0;
-      if (lane == 0) st = atomicAdd(&S.ecount, tot8);
-      st = (uint32_t)__shfl((int)st, 0, 64);
-      uint32_t run = st;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int t = t0 + 64 * c + lane;
-        const uint32_t pos = run + (uint32_t)__popcll(bal[c] & ((1ull << lane) - 1ull));
-        if (((bal[c] >> lane) & 1ull) && pos < (uint32_t)ECAP) S.a.ext[pos] = composite_key(f[c], t);
-        run += (uint32_t)__popcll(bal[c]);
-      }
-      if (lane == 0) {
-        S.fstart[q] = st;
-        S.flen[q] = tot8;
-      }
-    }
+    if (p.unit == 512)
+      rescan_units<8>(S, R, nflag, cu);
+    else if (p.unit == 256)
+      rescan_units<4>(S, R, nflag, cu);
+    else
+      rescan_units<1>(S, R, nflag, cu);
     __syncthreads();
     const uint32_t ne = S.ecount;
     if (ne > (uint32_t)ECAP) {
@@ -745,15 +776,31 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
       if (((fmask >> j) & 1u) || (((uint64_t)kh[i] << 32) | kl[i]) < cu) kh[i] = 0u;
     }
     const uint64_t cstar = kth_largest<N, true>(kh, kl, S.a.ext, ne, (uint32_t)R.k, S, par, [] {});
-    // selected keys of each rescanned unit
-    for (uint32_t q = wid; q < nflag; q += NW) {
-      const uint32_t st = S.fstart[q], len = S.flen[q];
-      uint32_t c = 0;
-      for (uint32_t q0 = 0; q0 < len; q0 += 64) {
-        const bool sel = q0 + (uint32_t)lane < len && S.a.ext[st + q0 + lane] >= cstar;
-        c += (uint32_t)__popcll(__ballot(sel));
-      }
-      if (lane == 0) S.fcnt[q] = c;
+    // ---- selected rescanned keys: thread t takes ext entries [XPER t, XPER t + XPER);
+    // one block scan counts the selected entries before each thread's, and one thread per
+    // segment turns its ends into the segment's count and the selected entries before it
+    static_assert(XPER == 8 && XPER * SEL_NT == ECAP, "eight ext entries per thread");
+    uint32_t xb = 0;
+#pragma unroll
+    for (int x = 0; x < XPER; ++x) {
+      const uint32_t pe = (uint32_t)(XPER * tid + x);
+      const uint64_t c = pe < ne ? S.a.ext[pe] : 0ull;
+      if (c != 0ull && c >= cstar) xb |= 1u << x;
+    }
+    uint32_t xtot;
+    const uint32_t xbefore = excl_scan((uint32_t)__popc(xb), xtot, S, par);
+    uint32_t* xw = S.a.hist + 4096;  // per thread: selected entries before its own, its bits
+    xw[tid] = (xbefore << 8) | xb;
+    __syncthreads();
+    auto sel_before = [&](uint32_t pe) -> uint32_t {  // selected ext entries below entry pe
+      if (pe >= ne) return xtot;
+      const uint32_t w = xw[pe >> 3];
+      return (w >> 8) + (uint32_t)__popc(w & 0xFFu & ((1u << (pe & 7u)) - 1u));
+    };
+    for (uint32_t q = (uint32_t)tid; q < nflag; q += SEL_NT) {
+      const uint32_t st = S.fstart[q], e0 = sel_before(st);
+      S.fcnt[q] = sel_before(st + S.flen[q]) - e0;
+      S.flen[q] = e0;
     }
     __syncthreads();
     // ---- ordered write: segment counts in token order, one scan per run ----
@@ -779,7 +826,6 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
       }
     }
     uint32_t v2[4] = {segc[0] + segc[1], segc[2] + segc[3], 0u, 0u}, off2[4], tot2[4];
-    __syncthreads();  // the first scan's partials are rewritten
     excl_scan4(v2, off2, tot2, N > 8 ? 2 : 1, S);
     uint32_t segoff[4];
     segoff[0] = off2[0];
@@ -789,7 +835,7 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (fslot[j] >= 0) S.foff[fslot[j]] = segoff[j];
-    uint32_t* list = S.a.hist;
+    uint32_t* list = S.a.hist;  // below xw
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int j = quarter ? (i >> 2) : ((i >> 3) << 1);
@@ -797,18 +843,17 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
       if (((bits >> i) & 1u) && o < (uint32_t)R.k) list[o] = 0xFFFFFFFFu - kl[i];
     }
     __syncthreads();
-    for (uint32_t q = wid; q < nflag; q += NW) {
-      const uint32_t st = S.fstart[q], len = S.flen[q];
-      uint32_t o = S.foff[q];
-      for (uint32_t q0 = 0; q0 < len; q0 += 64) {
-        const uint64_t c = q0 + (uint32_t)lane < len ? S.a.ext[st + q0 + lane] : 0ull;
-        const bool sel = c != 0ull && c >= cstar;
-        const uint64_t bal = __ballot(sel);
-        const uint32_t pos = o + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-        if (sel && pos < (uint32_t)R.k) list[pos] = (uint32_t)key_token(c);
-        o += (uint32_t)__popcll(bal);
+    // a selected ext entry goes to its segment's first position plus its rank there
+    const int lu = 31 - __clz(p.unit);
+#pragma unroll
+    for (int x = 0; x < XPER; ++x)
+      if ((xb >> x) & 1u) {
+        const uint64_t c = S.a.ext[XPER * tid + x];
+        const int t = key_token(c);
+        const uint32_t q = S.fmap[t >> lu];
+        const uint32_t pos = S.foff[q] + xbefore + (uint32_t)__popc(xb & ((1u << x) - 1u)) - S.flen[q];
+        if (pos < (uint32_t)R.k) list[pos] = (uint32_t)t;
       }
-    }
     __syncthreads();
     flush_list(tot2[0] + (N > 8 ? tot2[1] : 0u), R, B, S);
   }
