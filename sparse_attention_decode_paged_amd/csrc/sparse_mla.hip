@@ -9,8 +9,8 @@
 //
 // Grid (split, row, head group of G = 16 or 32 heads). A workgroup walks its split's
 // slice of the row's index list 64 tokens at a time (the steps below are for G = 16;
-// G = 32 keeps all 576 dims per wave and splits the heads, 4 heads per wave in the
-// softmax and 32x32x16 MFMAs for O):
+// G = 32 computes two blocks of 16 heads from each converted latent fragment, and
+// takes 4 heads per wave in the softmax and 32x32x16 MFMAs for O):
 //   the chunk's token ids / page slots are the head of a load chain (ids -> latent
 //   rows), so they are fetched first; the 64 latents (576 e4m3 bytes each) of chunk
 //   c + 1 are loaded into registers while chunk c is computed (the ids of c + 2
@@ -137,14 +137,14 @@ struct MlaIds {
 constexpr int a16(int x) { return (x + 15) & ~15; }
 // The attention workgroup's LDS, carved from one raw buffer (the fused kernel lays the
 // select's LDS over the same bytes): the latent tile (Q passes through it first), the
-// scaled logits (head-major; G = 16: one array per half of the dims), the chunk's token
+// scaled logits (head-major, one array per half of the dims), the chunk's token
 // scales, the NVFP4 query powers of two, the chunk's P'' (head-major), each head's
 // rescale factor and running (max, sum).
 template <bool NV, int G>
 struct MlaLds {
   static constexpr int LAT = 0;
   static constexpr int X = a16(LAT + Tile<NV>::BYTES);
-  static constexpr int SC = a16(X + (G == 16 ? 2 : 1) * G * XROW * 4);
+  static constexpr int SC = a16(X + 2 * G * XROW * 4);
   static constexpr int QE = a16(SC + CH * 4);
   static constexpr int P = a16(QE + G * 4);
   static constexpr int AL = a16(P + G * PROW * 2);
@@ -195,10 +195,11 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
   // 8 (lane >> 4) ..+8). Q passes through the latent tile's LDS bytes, which the first
   // chunk's latents overwrite after a barrier.
   const int hrow = lane & 15, kq = 8 * (lane >> 4);
-  // QK tile of this wave: tokens 16 tg..; G = 16: all heads, dims 288 wq..;
-  // G = 32: heads 16 wq.., all dims
+  // QK tile of this wave: tokens 16 tg.., all heads (G = 32: two blocks of 16), dims
+  // 288 wq ..; each latent fragment is converted once and feeds every head block
   const int tg = wid & 3, wq = wid >> 2;
-  constexpr int KQ = G == 16 ? kDLat / 64 : kDLat / 32;  // steps of 32 dims
+  constexpr int KH = kDLat / 64;  // steps of 32 dims per half
+  constexpr int KQ = G / 16 * KH;  // query fragments: head block kk / KH, step kk % KH
   constexpr int QP = kDLat / 8;           // 72 16-byte pieces per head row
   constexpr int QALL = G * QP;
   constexpr int QN = mla_qn(G);
@@ -315,13 +316,13 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
       if (part == 0) qe_s[h] = __uint_as_float((uint32_t)(127 + ex) << 23);
       }
       __syncthreads();
-      const uint16_t* qrow = q_s + (G == 16 ? hrow : 16 * wq + hrow) * QROW + kq + (G == 16 ? (kDLat / 2) * wq : 0);
+      const uint16_t* qrow = q_s + hrow * QROW + kq + (kDLat / 2) * wq;
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) qh[kk] = *reinterpret_cast<const v8h*>(qrow + 32 * kk);
+      for (int kk = 0; kk < KQ; ++kk) qh[kk] = *reinterpret_cast<const v8h*>(qrow + 16 * (kk / KH) * QROW + 32 * (kk % KH));
     } else {
-      const uint16_t* qrow = q_s + (G == 16 ? hrow : 16 * wq + hrow) * QROW + kq + (G == 16 ? (kDLat / 2) * wq : 0);
+      const uint16_t* qrow = q_s + hrow * QROW + kq + (kDLat / 2) * wq;
 #pragma unroll
-      for (int kk = 0; kk < KQ; ++kk) qa[kk] = *reinterpret_cast<const v8bf*>(qrow + 32 * kk);
+      for (int kk = 0; kk < KQ; ++kk) qa[kk] = *reinterpret_cast<const v8bf*>(qrow + 16 * (kk / KH) * QROW + 32 * (kk % KH));
     }
     __syncthreads();  // every wave holds its fragments before the latents overwrite them
   }
@@ -381,38 +382,49 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
       smax = v > 0.f ? v : 1.f;
     }
 
-    // ---- S = Q . C^T : wave w -> tokens [16 (w & 3), +16), all 16 heads, dims
+    // ---- S = Q . C^T : wave w -> tokens [16 (w & 3), +16), all heads, dims
     // [288 (w >> 2), +288); each half's scaled logits (log2 domain) go to LDS and the
     // softmax adds the two ----
     {
-      v4f s0 = {0.f, 0.f, 0.f, 0.f};
+      constexpr int NB = G / 16;  // head blocks
+      v4f s0[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) s0[b] = v4f{0.f, 0.f, 0.f, 0.f};
       if constexpr (NV) {
         const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW;
 #pragma unroll
-        for (int kk = 0; kk < KQ; ++kk) {
-          const v8h b = *reinterpret_cast<const v8h*>(lrow + nv_col(kq + (G == 16 ? (kDLat / 2) * wq : 0) + 32 * kk));
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[kk], b, s0, 0, 0, 0);
+        for (int kk = 0; kk < KH; ++kk) {
+          const v8h b = *reinterpret_cast<const v8h*>(lrow + nv_col(kq + (kDLat / 2) * wq + 32 * kk));
+#pragma unroll
+          for (int hb2 = 0; hb2 < NB; ++hb2)
+            s0[hb2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[KH * hb2 + kk], b, s0[hb2], 0, 0, 0);
         }
       } else {
-        const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW + kq + (G == 16 ? (kDLat / 2) * wq : 0);
+        const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW + kq + (kDLat / 2) * wq;
 #pragma unroll
-        for (int kk = 0; kk < KQ; ++kk) {
+        for (int kk = 0; kk < KH; ++kk) {
           uint2 raw = *reinterpret_cast<const uint2*>(lrow + 32 * kk);
           v8bf b = e4m3x8_to_bf16(raw.x, raw.y);
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], b, s0, 0, 0, 0);
+#pragma unroll
+          for (int hb2 = 0; hb2 < NB; ++hb2)
+            s0[hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[KH * hb2 + kk], b, s0[hb2], 0, 0, 0);
         }
       }
       const int tt = 16 * tg + hrow;
       const float sct = sc_s[tt];
       const bool ok = sct != kNegInf;
-      const int hb = (G == 16 ? 0 : 16 * wq) + 4 * (lane >> 4);
-      float* xh = x_s + (G == 16 ? wq * G * XROW : 0);
-      if constexpr (NV) {
+      float* xh = x_s + wq * G * XROW;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xh[(hb + i) * XROW + tt] = ok ? s0[i] * qe_s[hb + i] * (sct * c2) : kNegInf;
-      } else {
+      for (int hb2 = 0; hb2 < NB; ++hb2) {
+        const int hb = 16 * hb2 + 4 * (lane >> 4);
+        if constexpr (NV) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xh[(hb + i) * XROW + tt] = ok ? s0[i] * (sct * c2) : kNegInf;
+          for (int i = 0; i < 4; ++i)
+            xh[(hb + i) * XROW + tt] = ok ? s0[hb2][i] * qe_s[hb + i] * (sct * c2) : kNegInf;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xh[(hb + i) * XROW + tt] = ok ? s0[hb2][i] * (sct * c2) : kNegInf;
+        }
       }
     }
     __syncthreads();
@@ -464,9 +476,10 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
     // lane l head 4w + (l >> 4) and tokens 4 (l & 15) .. +4 ----
     {
       const int h = 4 * wid + (lane >> 4), t4 = 4 * (lane & 15);
-      const float4 x4 = *reinterpret_cast<const float4*>(x_s + h * XROW + t4);
+      const float4 xa = *reinterpret_cast<const float4*>(x_s + h * XROW + t4);
+      const float4 xb = *reinterpret_cast<const float4*>(x_s + (G + h) * XROW + t4);
       const float4 s4 = *reinterpret_cast<const float4*>(sc_s + t4);
-      const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+      const float xv[4] = {xa.x + xb.x, xa.y + xb.y, xa.z + xb.z, xa.w + xb.w};  // -inf for an empty slot
       const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
       float cm = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
       cm = fmaxf(cm, xshflf<1>(cm));
