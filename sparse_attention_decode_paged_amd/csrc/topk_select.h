@@ -262,14 +262,15 @@ __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[PER], const
     if (tid == 0) S.bcount = 0u;  // the bucket gather is ordered after this by the barriers below
     clear_hist(S);                // ordered before the first pass by the min / max barrier
   }
+  // the least live score word via min(w - 1) (an empty slot, w = 0, wraps to the
+  // identity), the largest via max(w) (0 changes nothing)
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   for_keys([&](uint32_t w, uint32_t) {
-    if (w != 0u) {
-      lo = min(lo, w);
-      hi = max(hi, w);
-    }
+    lo = min(lo, w - 1u);
+    hi = max(hi, w);
   });
   block_minmax32(lo, hi, S, par);
+  lo += 1u;
   // score-word bits fixed so far: (w & mask) == prefix
   // bits above `top` are common to every live score word; (w & mask) == prefix
   // selects the keys still in play. 64-bit shifts keep every shift count defined.
@@ -290,9 +291,15 @@ __device__ __forceinline__ uint64_t kth_largest(const uint32_t (&kh)[PER], const
     }
     first = false;
     const uint32_t rep = (uint32_t)tid & (NREP - 1);
-    for_keys([&](uint32_t w, uint32_t) {
-      if (w != 0u && (w & mask) == prefix) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
-    });
+    if (pass0) {  // every live key lies in [lo, hi], so it shares the bits above top
+      for_keys([&](uint32_t w, uint32_t) {
+        if (w != 0u) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
+      });
+    } else {
+      for_keys([&](uint32_t w, uint32_t) {
+        if (w != 0u && (w & mask) == prefix) atomicAdd(&S.a.hist[((w >> sh) & dm) * NREP + rep], 1u);
+      });
+    }
     __syncthreads();
     if (pass0) late();
     // thread t holds bins NBIN-1-2t (upper) and NBIN-2-2t: thread order = descending digits
@@ -538,16 +545,16 @@ struct BtStage {
   __device__ __forceinline__ void stage(const SelRow& R, SelShared& S) {
     if (threadIdx.x == 0) S.btl = btl ? 1u : 0u;
     if (!btl) return;
-    const int64_t nb = R.cv.num_blocks;
+    const uint32_t nb = R.cv.num_blocks < 0x7FFFFFFF ? (uint32_t)R.cv.num_blocks : 0x7FFFFFFFu;
 #pragma unroll
     for (int q = 0; q < BTCAP / SEL_NT; ++q) {
       const int i = (int)threadIdx.x + SEL_NT * q;
-      int64_t b = bv[q];
-      if (i < nblk && (uint64_t)b >= (uint64_t)nb) {
+      int32_t b = bv[q];
+      if (i < nblk && (uint32_t)b >= nb) {  // negative entries too
         raise_status(R.cv.status, kStBlockClamped);
-        b = b < 0 ? 0 : nb - 1;
+        b = b < 0 ? 0 : (int32_t)nb - 1;
       }
-      if (i < nblk) S.bt[i] = (int32_t)b;
+      if (i < nblk) S.bt[i] = b;
     }
   }
 };
@@ -680,7 +687,7 @@ template <int N>
 __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], uint32_t (&kl)[PER], const SelRow& R,
                                             const CandPlan& p, int& par) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nslot = p.nu * p.m;
+  const int nslot = p.nu << p.lm;
   const bool quarter = p.m < 8;  // m = 4: four one-unit segments of four registers
   const uint32_t segmask[4] = {quarter ? 0x000Fu : 0x00FFu, quarter ? 0x00F0u : 0u,
                                quarter ? 0x0F00u : (N > 8 ? 0xFF00u : 0u), quarter ? 0xF000u : 0u};
@@ -690,8 +697,8 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
   for (int j = 0; j < 4; ++j) {
     const int s0 = (j < 2 ? 0 : kCandRowCap / 2) + 8 * tid + (quarter ? 4 * (j & 1) : 0);
     const bool has = segmask[j] != 0u && s0 < nslot && (j < 2 || N > 8);
-    segu[j] = has ? s0 / p.m : -1;
-    segfirst[j] = has && (s0 % p.m) == 0;
+    segu[j] = has ? s0 >> p.lm : -1;
+    segfirst[j] = has && (s0 & (p.m - 1)) == 0;
   }
   // slots past the row's units hold no candidate
 #pragma unroll
@@ -727,11 +734,17 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
   for (int j = 0; j < 4; ++j)
     if (((fmask >> j) & 1u) && segfirst[j]) nfl[j >> 1]++;
   {
-    uint32_t v[4] = {nfl[0], nfl[1], (uint32_t)__popc(bits & 0xFFu), (uint32_t)__popc(bits >> 8)}, off[4], tot[4];
-    excl_scan4(v, off, tot, N > 8 ? 4 : 3, S);
+    // one prefix sum per run, packed: selected keys in the low half-word (at most 8,192
+    // per run), flagged units in the high one
+    uint32_t v[4] = {(uint32_t)__popc(bits & 0xFFu) | (nfl[0] << 16), (uint32_t)__popc(bits >> 8) | (nfl[1] << 16), 0u,
+                     0u},
+             pk[4], pt[4];
+    excl_scan4(v, pk, pt, N > 8 ? 2 : 1, S);
+    const uint32_t off[2] = {pk[0] >> 16, pk[1] >> 16}, tot[2] = {pt[0] >> 16, N > 8 ? pt[1] >> 16 : 0u};
     const uint32_t nflag = tot[0] + tot[1];
     if (nflag == 0) {
-      const uint32_t base[2] = {off[2], tot[2] + off[3]};
+      const uint32_t totA = pt[0] & 0xFFFFu;
+      const uint32_t base[2] = {pk[0] & 0xFFFFu, totA + (pk[1] & 0xFFFFu)};
       uint32_t* list = S.a.hist;  // free since the search
 #pragma unroll
       for (int i = 0; i < N; ++i) {
@@ -739,7 +752,7 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
         if (((bits >> i) & 1u) && o < (uint32_t)R.k) list[o] = 0xFFFFFFFFu - kl[i];
       }
       __syncthreads();
-      flush_list(tot[2] + (N > 8 ? tot[3] : 0u), R, B, S);
+      flush_list(totA + (N > 8 ? pt[1] & 0xFFFFu : 0u), R, B, S);
       return;
     }
     if (nflag > (uint32_t)FCAP) {
@@ -844,7 +857,7 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
     }
     __syncthreads();
     // a selected ext entry goes to its segment's first position plus its rank there
-    const int lu = 31 - __clz(p.unit);
+    const int lu = p.lu;
 #pragma unroll
     for (int x = 0; x < XPER; ++x)
       if ((xb >> x) & 1u) {
@@ -888,9 +901,9 @@ __device__ __forceinline__ void select_row(const uint32_t* __restrict__ cand_hi,
   }
   early();
   SelRow R;
-  R.ctx = clamp_ctx(row_ctx, r, max_ctx, cv.status);
+  R.ctx = __builtin_amdgcn_readfirstlane(clamp_ctx(row_ctx, r, max_ctx, cv.status));  // uniform: scalar plan
   R.k = k;
-  R.seq = rm.row_seq[r];  // the launch points row_seq at row_ctx when there are no page slots
+  R.seq = __builtin_amdgcn_readfirstlane(rm.row_seq[r]);  // row_seq is row_ctx when there are no page slots
   R.srow = scores + (int64_t)r * ld;
   R.clo = cand_lo + (int64_t)r * kCandRowCap;
   R.flr = floors + (int64_t)r * kFloorRowCap;

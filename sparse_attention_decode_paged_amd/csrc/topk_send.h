@@ -44,22 +44,26 @@ struct CandPlan {
   int m;     // keys sent per unit
   int nu;    // units of the row
   int per;   // keys per select thread: 8 (at most 8,192 candidates) or 16
+  int lu;    // log2 of unit
+  int lm;    // log2 of m
 };
 
 __host__ __device__ inline CandPlan cand_plan(int ctx, int umax) {
-  CandPlan p{0, 0, 0, 16};
+  CandPlan p{0, 0, 0, 16, 0, 0};
   if (ctx <= kTopkFullRow) {
     p.per = ctx <= kCandRowCap / 2 ? 8 : 16;
     return p;
   }
   if (umax >= 512)
-    p.unit = ctx <= 4 * kTopkFullRow ? 64 : (ctx > 8 * kTopkFullRow ? 512 : 256);
+    p.lu = ctx <= 4 * kTopkFullRow ? 6 : (ctx > 8 * kTopkFullRow ? 9 : 8);
   else  // row-group producers: one-wave units up to the floor capacity (4,096 units)
-    p.unit = ctx <= 16 * kTopkFullRow ? 64 : 256;
-  p.nu = (ctx + p.unit - 1) / p.unit;
+    p.lu = ctx <= 16 * kTopkFullRow ? 6 : 8;
+  p.unit = 1 << p.lu;
+  p.nu = (ctx + p.unit - 1) >> p.lu;
   // lam = 2048 / nu: nu < 410 <=> lam > 5 (m = 32 covers lam <= 14); nu < 1517 <=> lam > 1.35
-  p.m = p.nu < 410 ? 32 : p.nu < 1517 ? 16 : 8;
-  while (p.nu * p.m > kCandRowCap) p.m >>= 1;
+  p.lm = p.nu < 410 ? 5 : p.nu < 1517 ? 4 : 3;
+  while ((p.nu << p.lm) > kCandRowCap) --p.lm;
+  p.m = 1 << p.lm;
   p.per = p.nu * p.m <= kCandRowCap / 2 ? 8 : 16;
   return p;
 }
