@@ -108,22 +108,24 @@ struct SelShared {
   int32_t bt[BTCAP];  // the row's block-table entries (clamped into the pool) when they fit
 };
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = min(v, xshfl<1>(v));
-  v = min(v, xshfl<2>(v));
-  v = min(v, xshfl<4>(v));
-  v = min(v, xshfl<8>(v));
-  v = min(v, xshfl<16>(v));
-  v = min(v, xshfl<32>(v));
+// Wave minimum / maximum, complete in lane 63: shifts of 1, 2, 4, 8 inside each 16-lane
+// row, then the row broadcasts (lanes without a source keep their own value).
+__device__ __forceinline__ uint32_t wave_min_u32_in63(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
   return v;
 }
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, xshfl<1>(v));
-  v = max(v, xshfl<2>(v));
-  v = max(v, xshfl<4>(v));
-  v = max(v, xshfl<8>(v));
-  v = max(v, xshfl<16>(v));
-  v = max(v, xshfl<32>(v));
+__device__ __forceinline__ uint32_t wave_max_u32_in63(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
   return v;
 }
 
@@ -185,9 +187,9 @@ __device__ __forceinline__ void excl_scan4(const uint32_t (&v)[4], uint32_t (&of
 // Block-wide min and max of 32-bit values.
 __device__ __forceinline__ void block_minmax32(uint32_t& lo, uint32_t& hi, SelShared& S, int& par) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (lane == 0) {
+  lo = wave_min_u32_in63(lo);
+  hi = wave_max_u32_in63(hi);
+  if (lane == 63) {
     S.r32[par][0][wid] = lo;
     S.r32[par][1][wid] = hi;
   }
@@ -612,7 +614,7 @@ __device__ __forceinline__ void select_own(SelShared& S, uint32_t (&kh)[PER], ui
   uint32_t bits = 0;
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
+    if ((((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
   uint32_t v[4] = {(uint32_t)__popc(bits & 0xFFu), (uint32_t)__popc(bits >> 8), 0u, 0u}, off[4], tot[4];
   excl_scan4(v, off, tot, N / 8, S);
   const uint32_t base[2] = {off[0], tot[0] + off[1]};
@@ -728,7 +730,7 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
   uint32_t bits = 0;
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cu) bits |= 1u << i;
+    if ((((uint64_t)kh[i] << 32) | kl[i]) >= cu) bits |= 1u << i;  // an empty slot (kh = 0) is below
   uint32_t nfl[2] = {0u, 0u};  // flagged units this thread registers, runs A and B
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -820,7 +822,7 @@ __device__ __forceinline__ void select_cand(SelShared& S, uint32_t (&kh)[PER], u
     bits = 0;
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      if (kh[i] != 0u && (((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
+      if ((((uint64_t)kh[i] << 32) | kl[i]) >= cstar) bits |= 1u << i;
     uint32_t segc[4];
     uint32_t fsl[2] = {off[0], tot[0] + off[1]};  // this thread's first registered slot per run
     int fslot[4];
