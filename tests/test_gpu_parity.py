@@ -211,6 +211,35 @@ def test_stages_equal_step(dev, ctxs):
     assert np.array_equal(out.cpu().numpy(), o_f) and np.array_equal(lse.cpu().numpy(), l_f)
 
 
+@pytest.mark.parametrize("ctxs", [[100000, 40000]])
+def test_planted_rescans_staged_and_fused(dev, ctxs):
+    """Rows whose top 2,048 crowd into a few units: 2,048 elevated keys log-uniform over each
+    row, so the first units hold far more of them than they send and the select rescans
+    those units from the scores (256-token units at 100,000 tokens, 64-token units at
+    40,000). The step (select and attention in one launch) is checked against the oracle,
+    and the staged launches (the standalone select) must equal it bit for bit."""
+    say(f"case: planted keys, rescanned units, ctx {ctxs}")
+    c = make_case(ctxs, block_size=64, seed=43, k=2048, plant=2048).to(dev)
+    s_f, i_f, o_f, l_f = full_check(c, dev)
+    for r in range(c.num_rows):
+        planted = np.array(c.planted[(0, r)])
+        hit = np.intersect1d(planted, i_f[r]).size
+        say(f"  row {r}: planted selected {hit}/{planted.size}")
+    R = c.num_rows
+    ws = torch.empty(dsa.dsa_workspace_bytes(dsa.DSA_OP_DECODE_STEP, R, c.max_ctx, c.k), dtype=torch.uint8,
+                     device=dev)
+    idx = torch.empty((R, c.k), dtype=torch.int32, device=dev)
+    out = torch.empty((R, 96, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, 96), dtype=torch.float32, device=dev)
+    for bits in (dsa.DSA_STAGE_INDEXER, dsa.DSA_STAGE_TOPK, dsa.DSA_STAGE_ATTENTION | dsa.DSA_STAGE_MERGE):
+        dsa.dsa_decode_step_stages(c.pool, c.layout, 0, c.q_idx[0], c.q_idx_scale[0], c.w[0], c.q_lat[0],
+                                   c.block_table, c.row_seq, c.row_ctx, c.max_ctx, c.k, c.sm_scale, idx, out, lse,
+                                   ws, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), i_f)
+    assert np.array_equal(out.cpu().numpy(), o_f) and np.array_equal(lse.cpu().numpy(), l_f)
+
+
 def test_batch_invariance(dev):
     """A row's scores and selection do not depend on the batch it runs in (bit for bit).
     Its attention output may: sparse MLA splits a row's tokens into a number of splits
