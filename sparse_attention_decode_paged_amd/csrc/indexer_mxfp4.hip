@@ -210,9 +210,16 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_rows_kernel(CacheView cv, R
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = blockIdx.y * G;
   const int r1 = r0 + G < R ? r0 + G : R;
-  int gmax = 0;  // the group's longest row decides which tiles exist
+  // the group's rows, lane i holding row r0 + i's length and sequence (G <= 16); the
+  // longest row decides which tiles exist
+  int rl_v = 0, rs_v = -1;
+  if (lane < r1 - r0) {
+    rl_v = row_len(rm, r0 + lane, cv.status);
+    rs_v = rm.row_seq[r0 + lane];
+  }
+  int gmax = 0;
   for (int r = r0; r < r1; ++r) {
-    const int c = row_len(rm, r, cv.status);
+    const int c = __builtin_amdgcn_readlane(rl_v, r - r0);
     gmax = c > gmax ? c : gmax;
   }
   if (blockIdx.x * 256 >= gmax) return;  // whole workgroup
@@ -290,12 +297,12 @@ __global__ __launch_bounds__(256) void indexer_mxfp4_rows_kernel(CacheView cv, R
     const v4i q0 = *reinterpret_cast<const v4i*>(qp);
     const v4i q1 = *reinterpret_cast<const v4i*>(qp + 32);
     const uint32_t qe = *reinterpret_cast<const uint32_t*>(q_e8 + ((int64_t)r * kHIdx + n) * 4);
-    const int seq = rm.row_seq[r];
-    const int ctx = row_len(rm, r, cv.status);
+    const int seq = __builtin_amdgcn_readlane(rs_v, r - r0);
+    const int ctx = __builtin_amdgcn_readlane(rl_v, r - r0);
     if (seq != seq_cur) {  // uniform
       int smax = ctx;
-      for (int q = r + 1; q < r1 && rm.row_seq[q] == seq; ++q) {
-        const int c = row_len(rm, q, nullptr);
+      for (int q = r + 1; q < r1 && __builtin_amdgcn_readlane(rs_v, q - r0) == seq; ++q) {
+        const int c = __builtin_amdgcn_readlane(rl_v, q - r0);
         smax = c > smax ? c : smax;
       }
       if (smax > 0) load_keys(seq, smax);  // an empty run stores and sends nothing

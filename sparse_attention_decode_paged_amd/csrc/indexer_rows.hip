@@ -30,21 +30,30 @@ __device__ __forceinline__ int swz(int tn, int c) { return tn * kDIdx + 16 * (c 
 // owns tokens [64w, 64w + 64) as two 32-token tiles. PAGED32: block size >= 32.
 // SEND: also run stage 1 of the top-k for every row.
 template <bool PAGED32, bool SEND>
-__global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, RowMap rm, const uint8_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256, 3) void indexer_fp8_rows_kernel(CacheView cv, RowMap rm, const uint8_t* __restrict__ q_idx,
                                                                const float* __restrict__ q_scale,
                                                                const float* __restrict__ w, float* __restrict__ scores,
                                                                int64_t ld, TopkWs tw, int R, int G) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[4][kTileBytes];
   __shared__ uint32_t send_lds[2][send_lds_words<256>()];  // double-buffered over the rows that take the 256-token send
   __shared__ float wf_s[kRowsPerGroupMax * kHIdx];  // folded head weights w * q_scale of the group's rows
+  // the current and the next row's query codes as bf16: 16-byte chunk c (dims 8c .. 8c + 7)
+  // of head h at byte 256 h + 16 (c ^ (h & 15)), so the operand reads are conflict free
+  __shared__ __attribute__((aligned(16))) uint8_t qs_l[2][kHIdx * kDIdx * 2];
   const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = blockIdx.y * G;
   const int r1 = r0 + G < R ? r0 + G : R;
-  // the group's longest row decides which tiles exist
+  // the group's rows, lane i holding row r0 + i's length and sequence (G <= 16); the
+  // longest row decides which tiles exist
+  int rl_v = 0, rs_v = -1;
+  if (lane < r1 - r0) {
+    rl_v = row_len(rm, r0 + lane, cv.status);
+    rs_v = rm.row_seq[r0 + lane];
+  }
   int gmax = 0;
   for (int r = r0; r < r1; ++r) {
-    const int c = row_len(rm, r, cv.status);
+    const int c = __builtin_amdgcn_readlane(rl_v, r - r0);
     gmax = c > gmax ? c : gmax;
   }
   if (blockIdx.x * 256 >= gmax) return;  // whole workgroup
@@ -111,20 +120,23 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
     }
   };
 
-  // The group's folded head weights go to LDS once, and (without the send epilogue, whose
-  // registers would cost a wave per SIMD) each row's query fragment is fetched one row
-  // ahead, so no row waits on a global load of its own.
+  // The group's folded head weights go to LDS once. Each row's query is converted to
+  // bf16 once per workgroup (each thread converts 16 of its 4,096 codes) into one of two
+  // LDS buffers; the next row's codes are loaded while the current row runs.
   for (int i = threadIdx.x; i < (r1 - r0) * kHIdx; i += 256)
     wf_s[i] = w[(int64_t)r0 * kHIdx + i] * q_scale[(int64_t)r0 * kHIdx + i];
-  __syncthreads();
-  // query fragment of a row: head n, bytes [64g, 64g + 64)
-  auto q_frag = [&](int rr, v4i (&qf)[4]) {
-    const v4i* qp = reinterpret_cast<const v4i*>(q_idx + ((int64_t)rr * kHIdx + n) * kDIdx + 64 * g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qf[i] = qp[i];
+  auto q_load = [&](int rr) -> v4i {
+    return *reinterpret_cast<const v4i*>(q_idx + (int64_t)rr * kHIdx * kDIdx + 16 * threadIdx.x);
   };
-  v4i qr[4];
-  if (!SEND) q_frag(r0, qr);
+  auto q_store = [&](v4i v, int buf) {
+    const int h = threadIdx.x >> 3, c = 2 * (threadIdx.x & 7);
+    *reinterpret_cast<v8bf*>(&qs_l[buf][h * 256 + 16 * (c ^ (h & 15))]) =
+        e4m3x8_to_bf16((uint32_t)v[0], (uint32_t)v[1]);
+    *reinterpret_cast<v8bf*>(&qs_l[buf][h * 256 + 16 * ((c + 1) ^ (h & 15))]) =
+        e4m3x8_to_bf16((uint32_t)v[2], (uint32_t)v[3]);
+  };
+  q_store(q_load(r0), 0);
+  __syncthreads();
 
   int seq_cur = -1;
   // Send buffers alternate between rows that take the 256-token send (the only form
@@ -133,28 +145,25 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
   // still read, also when shorter rows without that barrier sit in between.
   int nsend256 = 0;
   for (int r = r0; r < r1; ++r) {
-    v4i qn[4] = {};
-    if (SEND)
-      q_frag(r, qr);
-    else if (r + 1 < r1)  // uniform
-      q_frag(r + 1, qn);
-    const int seq = rm.row_seq[r];
-    const int ctx = row_len(rm, r, cv.status);
+    v4i qnext = {};
+    if (r + 1 < r1) qnext = q_load(r + 1);  // uniform
+    const int qb = (r - r0) & 1;
+    const int seq = __builtin_amdgcn_readlane(rs_v, r - r0);
+    const int ctx = __builtin_amdgcn_readlane(rl_v, r - r0);
     if (seq != seq_cur) {  // uniform
       int smax = ctx;  // longest row of the run of rows on this sequence
-      for (int q = r + 1; q < r1 && rm.row_seq[q] == seq; ++q) {
-        const int c = row_len(rm, q, nullptr);
+      for (int q = r + 1; q < r1 && __builtin_amdgcn_readlane(rs_v, q - r0) == seq; ++q) {
+        const int c = __builtin_amdgcn_readlane(rl_v, q - r0);
         smax = c > smax ? c : smax;
       }
       if (smax > 0) load_keys(seq, smax);  // an empty run stores and sends nothing
       seq_cur = seq;
     }
+    // A operands: head n, dims 64 g + 8 kk .. + 8 (chunk 8 g + kk)
     v8bf qa[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qa[2 * i] = e4m3x8_to_bf16((uint32_t)qr[i][0], (uint32_t)qr[i][1]);
-      qa[2 * i + 1] = e4m3x8_to_bf16((uint32_t)qr[i][2], (uint32_t)qr[i][3]);
-    }
+    for (int kk = 0; kk < 8; ++kk)
+      qa[kk] = *reinterpret_cast<const v8bf*>(&qs_l[qb][n * 256 + 16 * ((8 * g + kk) ^ (n & 15))]);
     // accumulator element rr of lane (n, g) is head 8 (rr >> 2) + 4 g + (rr & 3)
     float wq[16];
 #pragma unroll
@@ -186,10 +195,9 @@ __global__ __launch_bounds__(256) void indexer_fp8_rows_kernel(CacheView cv, Row
       send_candidates<256>(sc, t < ctx, ctx, blockIdx.x * 256, r, tw, send_lds[nsend256 & 1]);
       nsend256 += cand_plan(ctx, 256).unit == 256 ? 1 : 0;
     }
-    if (!SEND) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qr[i] = qn[i];
-    }
+    // the other buffer was last read in the previous row, which every wave has left
+    if (r + 1 < r1) q_store(qnext, qb ^ 1);  // uniform
+    __syncthreads();
   }
 }
 
