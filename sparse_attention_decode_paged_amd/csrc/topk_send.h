@@ -29,9 +29,11 @@
 // up to those bits; the floor ORs them back in. A wave sorts its 64 packed keys (DPP /
 // permlane bitonic network); units of 4 or 8 waves merge the waves' best 16 or 8 through
 // LDS with one barrier (each wave of the unit repeats the merge, so no second barrier is
-// needed). The best key a wave kept back joins the floor: a 64-token wave of a row longer
-// than 65,536 tokens holds 17 of its top 2048 practically never (nor 9 above 131,072
-// tokens), and if it does the rescan covers it.
+// needed); the best key a wave kept back joins the floor (a 64-token wave of a row longer
+// than 65,536 tokens holds 17 of its top 2048 practically never, nor 9 above 131,072
+// tokens, and if it does the rescan covers it). Units of 8 waves that send at most 16 keys
+// first take a cheaper exact route: a threshold from each wave's second-best key, the keys
+// reaching it gathered in LDS and sorted once by one wave (described at the code).
 #pragma once
 
 #include "common.h"
@@ -121,6 +123,84 @@ __device__ __forceinline__ void send_candidates(float score, bool valid, int ctx
     if ((uint32_t)lane >= nsent && lane < p.m) cand_hi[s0 + lane] = 0u;  // unused ranks
     if (lane == 0) floors[u] = nxt != 0u ? (nxt | LM) : 0u;
     return;
+  }
+
+  // Eight-wave units sending m <= 16 keys (rows of more than 209,408 tokens: m = 16, and
+  // m = 8 above 776,192). A key threshold tau first: each wave's
+  // second-best packed key goes to LDS and tau is the least of the eight, so at least 16
+  // keys of the unit reach it and the unit's best m are among them. The keys >= tau (about
+  // 34 for independent scores) are appended to a 64-entry LDS list that wave 0 sorts: its
+  // m-th entry is the send threshold, its (m+1)-th the best key kept back (when m or fewer
+  // keys reach tau, all of them are sent and tau - 1 bounds the rest). Wave 0 also counts
+  // each wave's sent keys from the sorted list, so that every wave places its own in token
+  // order after one more barrier. Two wave maxima per wave and one sort per unit replace a
+  // sort per wave and a merge in every wave, and the unit sends its best m keys outright
+  // (the general path below takes the best m among each wave's best 8). More than 64 keys
+  // at tau (about one unit in a hundred, or many tied scores) take the general path.
+  if (NT == 512 && p.unit == 512 && p.m <= 16) {
+    uint32_t* le = lds;       // [64] keys >= tau
+    uint32_t* lc = lds + 64;  // [8] each wave's second-best key
+    uint32_t* lo = lds + 72;  // [8] sent keys of the waves below each wave
+    uint32_t* lv = lds + 80;  // [0] list length, [1] send threshold
+    static_assert(send_lds_words<512>() >= 82, "send LDS");
+    if (threadIdx.x == 0) lv[0] = 0u;
+    uint32_t v = packed;
+    const uint32_t b1 = wave_max_u32_last(v);
+    v = v == b1 ? 0u : v;  // packed keys are distinct: one lane leaves the race
+    const uint32_t b2 = wave_max_u32_last(v);
+    if (lane == 0) lc[wid] = b2;
+    __syncthreads();
+    uint32_t tau = lc[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) tau = min(tau, lc[w]);
+    const bool in = packed != 0u && packed >= tau;
+    const uint64_t bin = __ballot(in);
+    uint32_t wb = 0u;
+    if (lane == 0 && bin != 0ull) wb = atomicAdd(&lv[0], (uint32_t)__popcll(bin));
+    wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)wb);
+    const uint32_t at = wb + (uint32_t)__popcll(bin & ((1ull << lane) - 1ull));
+    if (in && at < 64u) le[at] = packed;
+    __syncthreads();
+    const uint32_t ne = lv[0];
+    if (ne <= 64u) {  // uniform
+      const int u = base / p.unit;
+      const int s0 = u * p.m;
+      if (wid == 0) {
+        const uint32_t srt = wave_sort_desc_u32((uint32_t)lane < ne ? le[lane] : 0u, lane);
+        const uint32_t thr = (uint32_t)__builtin_amdgcn_readlane((int)srt, p.m - 1);
+        const uint32_t nx = (uint32_t)__builtin_amdgcn_readlane((int)srt, p.m);
+        const uint32_t nxt = ne > (uint32_t)p.m ? nx : (tau != 0u ? tau - 1u : 0u);
+        // sorted entry -> its wave (position in the workgroup from the packed low bits)
+        const bool s = lane < p.m && srt != 0u;
+        const uint32_t pw = (LM - (srt & LM)) >> 6;
+        uint32_t below = 0u;  // lane w: sent keys of the waves below w
+#pragma unroll
+        for (int w = 0; w < 7; ++w) {
+          const uint32_t c = (uint32_t)__popcll(__ballot(s && pw == (uint32_t)w));
+          below += lane > w ? c : 0u;
+        }
+        if (lane < 8) lo[lane] = below;
+        if (lane == 0) lv[1] = thr;
+        const uint32_t ntot = (uint32_t)__popcll(__ballot(s));
+        if (u < p.nu) {
+          if ((uint32_t)lane >= ntot && lane < p.m) cand_hi[s0 + lane] = 0u;  // unused ranks
+          if (lane == 0) floors[u] = nxt != 0u ? (nxt | LM) : 0u;
+        }
+      }
+      __syncthreads();
+      if (u >= p.nu) return;  // uniform: the unit lies past the row
+      // with fewer than m entries the sorted threshold is 0 and tau selects them all
+      const uint32_t thr = max(lv[1], tau);
+      const bool sent = packed != 0u && packed >= thr;
+      const uint64_t bal = __ballot(sent);
+      const uint32_t q = lo[wid] + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+      if (sent) {
+        cand_hi[s0 + (int)q] = (uint32_t)(key >> 32);
+        cand_lo[s0 + (int)q] = (uint32_t)key;
+      }
+      return;
+    }
+    __syncthreads();  // every wave has read the list length before the general path reuses the LDS
   }
 
   // Units of W = unit / 64 waves. Every wave puts its best cw = 64 / W keys (16 of a
