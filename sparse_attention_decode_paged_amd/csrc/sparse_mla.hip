@@ -139,7 +139,7 @@ constexpr int a16(int x) { return (x + 15) & ~15; }
 // select's LDS over the same bytes): the latent tile (Q passes through it first), the
 // scaled logits (head-major, one array per half of the dims), the chunk's token
 // scales, the NVFP4 query powers of two, the chunk's P'' (head-major), each head's
-// rescale factor and running (max, sum).
+// rescale factor and running (max, sum), and the chunk's "some head's max moved" flag.
 template <bool NV, int G>
 struct MlaLds {
   static constexpr int LAT = 0;
@@ -149,7 +149,8 @@ struct MlaLds {
   static constexpr int P = a16(QE + G * 4);
   static constexpr int AL = a16(P + G * PROW * 2);
   static constexpr int ML = a16(AL + G * 4);
-  static constexpr int BYTES = a16(ML + G * 8);
+  static constexpr int FL = a16(ML + G * 8);
+  static constexpr int BYTES = a16(FL + 4);
 };
 
 constexpr int mla_qn(int G) { return (G * (kDLat / 8) + NTM - 1) / NTM; }  // 16-byte Q pieces per thread
@@ -186,6 +187,7 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
   _Float16* p_s = reinterpret_cast<_Float16*>(smem + L::P);
   float* al_s = reinterpret_cast<float*>(smem + L::AL);
   float2* ml_s = reinterpret_cast<float2*>(smem + L::ML);
+  uint32_t* fl_s = reinterpret_cast<uint32_t*>(smem + L::FL);
   // gather: 8 threads per token. FP8: 16-byte pieces q8 + 8 q (q < 5) of 36. NVFP4: code
   // bytes [32 q8, +32) (dims [64 q8, +64)), their 4 block scales and, for q8 < 4, tail
   // bytes [16 q8, +16) (dims 512 + 16 q8 ..)
@@ -222,7 +224,11 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
   for (int cb = 0; cb < 4; ++cb) acc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 2; ++c) accw[c] = v16f{};
-  float s_run = 1.f;  // acc holds O / s_run (token scales folded into P per chunk)
+  // acc holds O / s_run: the token scales are folded into P'' relative to s_run, the
+  // largest token scale so far (1 before the first chunk), so that acc needs rescaling only
+  // in the chunks where that maximum or some head's running logit maximum moves
+  float s_run = 1.f;
+  float s_max = 0.f;
 
   // ---- gather, software-pipelined: the latents of chunk c + 1 are loaded into
   // registers (each thread up to 5 of its token's 36 16-byte pieces, and the scale)
@@ -357,19 +363,25 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
           *reinterpret_cast<v8h*>(trow + nv_col(kDV + 16 * q8 + 8 * h)) = o;
         }
       }
-    } else {
+    } else if (__ballot(!tv) == 0ull) {  // uniform: every slot of this wave holds a token
+#pragma unroll
+      for (int q = 0; q < PN; ++q)
+        if (q8 + 8 * q < PIECES) *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (q8 + 8 * q)) = v[q];
+    } else {  // an empty slot's codes (read at a clamped address) are zeroed: no NaN code reaches PV
 #pragma unroll
       for (int q = 0; q < PN; ++q)
         if (q8 + 8 * q < PIECES)
           *reinterpret_cast<v4i*>(lat_s + tt_g * LROW + 16 * (q8 + 8 * q)) = tv ? v[q] : v4i{0, 0, 0, 0};
     }
     if (q8 == 0) sc_s[tt_g] = tv ? sv : kNegInf;  // -inf marks an empty slot
+    if (tid == 0) *fl_s = 0u;  // the previous chunk's PV read it before its closing barrier
     __syncthreads();
     if (c0 + CH < j1) {  // uniform
       issue();
       fetch_ids(c0 + 2 * CH);
     }
-    // largest token scale of the chunk, computed by every wave
+    // largest token scale so far (this chunk's by every wave, then the running maximum;
+    // token scales are non-negative, -inf marks an empty slot)
     float smax;
     {
       float v = sc_s[lane];
@@ -379,7 +391,8 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
       v = fmaxf(v, xshflf<8>(v));
       v = fmaxf(v, xshflf<16>(v));
       v = fmaxf(v, xshflf<32>(v));
-      smax = v > 0.f ? v : 1.f;
+      s_max = fmaxf(s_max, v);
+      smax = s_max > 0.f ? s_max : 1.f;
     }
 
     // ---- S = Q . C^T : wave w -> tokens [16 (w & 3), +16), all heads, dims
@@ -447,16 +460,17 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
       cm = fmaxf(cm, xshflf<8>(cm));
       cm = fmaxf(cm, xshflf<16>(cm));
       const float mn = fmaxf(m_run, cm);
-      const float alpha = (mn == kNegInf) ? 1.f : exp2f(m_run - mn);
-      const float inv_smax = 1.f / smax;
+      // 2^x by the hardware instruction (2^-inf = 0); mb keeps x from being -inf - -inf
+      const float mb = mn == kNegInf ? 0.f : mn;
+      const float alpha = mn == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - mb);
+      const float inv_smax = __builtin_amdgcn_rcpf(smax);
       float psum = 0.f;
       v2h ph;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float p = (xv[e] == kNegInf) ? 0.f : exp2f(xv[e] - mn);
+        const float p = __builtin_amdgcn_exp2f(xv[e] - mb);  // 0 for an empty slot
         psum += p;
-        const float sfac = sv[e] != kNegInf ? sv[e] * inv_smax : 0.f;
-        ph[e] = (_Float16)(p * sfac);
+        ph[e] = (_Float16)(p * (fmaxf(sv[e], 0.f) * inv_smax));
       }
       psum += xshflf<1>(psum);
       psum += xshflf<2>(psum);
@@ -487,16 +501,16 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
       cm = fmaxf(cm, xshflf<4>(cm));
       cm = fmaxf(cm, xshflf<8>(cm));
       const float mn = fmaxf(m_run, cm);
-      const float alpha = (mn == kNegInf) ? 1.f : exp2f(m_run - mn);
-      const float inv_smax = 1.f / smax;
+      const float mb = mn == kNegInf ? 0.f : mn;
+      const float alpha = mn == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - mb);
+      const float inv_smax = __builtin_amdgcn_rcpf(smax);
       float psum = 0.f;
       v4h ph;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = (xv[e] == kNegInf) ? 0.f : exp2f(xv[e] - mn);
+        const float p = __builtin_amdgcn_exp2f(xv[e] - mb);  // 0 for an empty slot
         psum += p;
-        const float sfac = sv[e] != kNegInf ? sv[e] * inv_smax : 0.f;
-        ph[e] = (_Float16)(p * sfac);
+        ph[e] = (_Float16)(p * (fmaxf(sv[e], 0.f) * inv_smax));
       }
       psum += xshflf<1>(psum);
       psum += xshflf<2>(psum);
@@ -508,6 +522,7 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
       if ((lane & 15) == 0) {
         al_s[h] = alpha;
         ml_s[h] = float2{m_run, l_run};
+        if (alpha != 1.f) *fl_s = 1u;
       }
     }
     }
@@ -522,9 +537,15 @@ __device__ __forceinline__ void mla_body(const MlaIds& src, int t_n, int ps_n, c
                        : *reinterpret_cast<const v8h*>(p_s + (lane & 31) * PROW + 16 * ks + 8 * (lane >> 5));
 
     // ---- acc = acc * alpha * (s_run / smax) + P'' . codes : wave w -> columns [64w, 64w+64) ----
-    const float rescale = s_run / smax;
+    // G = 32 (long splits at batch): the multiplies only in chunks where some head's max or
+    // the largest token scale moved, the factors being 1 exactly otherwise. (G = 16 runs few
+    // chunks per split and is held to 128 registers, which the branch would exceed.)
+    const float rescale = smax == s_run ? 1.f : s_run * __builtin_amdgcn_rcpf(smax);
     s_run = smax;
-    if constexpr (G == 16) {
+    const bool moved = G == 16 || __builtin_amdgcn_readfirstlane((int)*fl_s) != 0 ||
+                       __builtin_amdgcn_readfirstlane(__float_as_int(rescale)) != __float_as_int(1.f);
+    if (!moved) {
+    } else if constexpr (G == 16) {
       const float4 a4 = *reinterpret_cast<const float4*>(&al_s[4 * (lane >> 4)]);
       const float a[4] = {a4.x * rescale, a4.y * rescale, a4.z * rescale, a4.w * rescale};
 #pragma unroll
