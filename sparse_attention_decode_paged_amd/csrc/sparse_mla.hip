@@ -846,6 +846,315 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const _Float16* __restric
     lse[(int64_t)r * kHQ + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
 
+// ---- 32 heads on four waves: many unsplit rows (prefill-append), FP8 latents ----
+// The body above keeps one 512-thread workgroup per CU (its 32-head registers), and its
+// four barrier-separated phases per chunk (latents in, QK, softmax, PV) leave both waves
+// of a SIMD in the same phase, so the matrix cores and the vector ALUs rarely work at
+// once. Here a workgroup is four waves (one per SIMD) over 32-token chunks, held to 256
+// registers, so that two workgroups share each CU and drift apart: one's softmax and
+// format conversions overlap the other's MFMAs. Per chunk: 8 threads gather each of the 32
+// latents; wave w computes S for tokens [16 (w & 1), +16) over dims [288 (w >> 1), +288)
+// for both blocks of 16 heads; the softmax gives wave w heads 8w .. 8w + 7 (lane: head
+// 8w + (lane >> 3), 4 tokens); PV gives wave w value columns [128 w, +128). The numerics
+// are those of the 512-thread body (bf16 QK, fp16 P'' relative to the running largest
+// token scale, fp16 PV on e4m3 codes, fp16 split averages). It pays where each workgroup
+// walks many chunks and the grid holds more than one workgroup per CU (2,048 rows of a
+// prefill-append: attention 1.82 -> 1.55 ms); at batch 16 or 64 the extra splits it
+// would need to fill the CUs cost more than it saves, and the 512-thread body runs.
+namespace {
+constexpr int NT4 = 256;
+constexpr int C2 = 32;             // tokens per chunk
+constexpr int XROW2 = C2 + 16;     // logit rows
+constexpr int PROW2 = C2 + 8;      // P'' rows (fp16)
+constexpr int LROW4 = kDLat + 16;  // latent tile row (e4m3 codes, padded)
+constexpr int QN4 = (32 * (kDLat / 8) + NT4 - 1) / NT4;  // 16-byte Q pieces per thread
+struct MlaLds4 {
+  static constexpr int LAT = 0;    // the latent tile; Q passes through it first
+  static constexpr int LATB = C2 * LROW4 > 32 * QROW * 2 ? C2 * LROW4 : 32 * QROW * 2;
+  static constexpr int X = a16(LAT + LATB);
+  static constexpr int SC = a16(X + 2 * 32 * XROW2 * 4);
+  static constexpr int P = a16(SC + C2 * 4);
+  static constexpr int AL = a16(P + 32 * PROW2 * 2);
+  static constexpr int ML = a16(AL + 32 * 4);
+  static constexpr int FL = a16(ML + 32 * 8);
+  static constexpr int BYTES = a16(FL + 4);
+};
+}  // namespace
+
+__device__ __forceinline__ void mla_body_w4(const MlaIds& src, int t_n, int ps_n, const v4i (&qv)[QN4], int j0,
+                                            int j1, float c2, const CacheView& cv, const RowMap& rm, int r, int hg,
+                                            int split, float* __restrict__ out, float* __restrict__ lse,
+                                            _Float16* __restrict__ part_o, float* __restrict__ part_ml, int nsplit,
+                                            uint8_t* smem) {
+  constexpr int G = 32;
+  using L = MlaLds4;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint8_t* lat_s = smem + L::LAT;
+  float* x_s = reinterpret_cast<float*>(smem + L::X);
+  float* sc_s = reinterpret_cast<float*>(smem + L::SC);
+  _Float16* p_s = reinterpret_cast<_Float16*>(smem + L::P);
+  float* al_s = reinterpret_cast<float*>(smem + L::AL);
+  float2* ml_s = reinterpret_cast<float2*>(smem + L::ML);
+  uint32_t* fl_s = reinterpret_cast<uint32_t*>(smem + L::FL);
+  const int tt_g = tid >> 3, q8 = tid & 7;  // gather: token tt_g, 16-byte pieces q8 + 8 q
+  const int hrow = lane & 15, kq = 8 * (lane >> 4);
+  const int tg = wid & 1, wq = wid >> 1;    // QK: tokens [16 tg, +16), dims [288 wq, +288)
+  constexpr int KH = kDLat / 64;
+  constexpr int KQ = 2 * KH;
+  constexpr int QP = kDLat / 8;
+  const int seq = src.slots() ? 0 : rm.row_seq[r];
+  const int bs_mask = cv.block_size - 1;
+  v8bf qa[KQ];
+  float m_run = kNegInf, l_run = 0.f;  // softmax state of head 8 wid + (lane >> 3)
+  if (tid < G) ml_s[tid] = float2{kNegInf, 0.f};
+  // O: value columns 128 wid + 32 c + (lane & 31), row rr = head 8 (rr >> 2) + 4 (lane >> 5) + (rr & 3)
+  v16f accw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) accw[c] = v16f{};
+  float s_run = 1.f, s_max = 0.f;  // acc holds O / s_run; s_max: largest token scale so far
+
+  constexpr int PN = (PIECES + 7) / 8;
+  v4i v[PN];
+  float sv = 0.f;
+  bool tv = false;
+  auto issue = [&]() {
+    if (t_n >= rm.max_ctx) raise_status(cv.status, kStIndexRange);
+    const int t = t_n < rm.max_ctx ? t_n : -1;
+    const int tc = t >= 0 ? t : 0;  // every load stays in the pool; empty slots are masked
+    int64_t blk;
+    int slot;
+    if (src.slots()) {
+      const int ps = ps_n >= 0 ? ps_n : 0;
+      blk = (int64_t)ps >> cv.log2_bs;
+      blk = blk < cv.num_blocks ? blk : cv.num_blocks - 1;
+      slot = ps & bs_mask;
+    } else {
+      blk = token_block(cv, rm, seq, tc);
+      slot = tc & bs_mask;
+    }
+    const uint8_t* page = cv.pool + blk * cv.row_bytes + cv.lat_off;
+    const uint8_t* lrow = page + (int64_t)slot * kDLat;
+    if (q8 == 0) sv = *reinterpret_cast<const float*>(page + (int64_t)cv.block_size * kDLat + (int64_t)slot * 4);
+#pragma unroll
+    for (int q = 0; q < PN; ++q)
+      if (q8 + 8 * q < PIECES) v[q] = *reinterpret_cast<const v4i*>(lrow + 16 * (q8 + 8 * q));
+    tv = t >= 0;
+  };
+  auto fetch_ids = [&](int c0) {
+    const int j = c0 + tt_g;
+    t_n = -1;
+    if (j < j1) src.get(j, t_n, ps_n);
+  };
+  issue();
+  fetch_ids(j0 + C2);
+  {
+    uint16_t* q_s = reinterpret_cast<uint16_t*>(lat_s);
+#pragma unroll
+    for (int q = 0; q < QN4; ++q) {
+      const int i = tid + NT4 * q, h = i / QP, pc = i - h * QP;
+      if (i < G * QP) *reinterpret_cast<v4i*>(q_s + h * QROW + pc * 8) = qv[q];
+    }
+    __syncthreads();
+    const uint16_t* qrow = q_s + hrow * QROW + kq + (kDLat / 2) * wq;
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) qa[kk] = *reinterpret_cast<const v8bf*>(qrow + 16 * (kk / KH) * QROW + 32 * (kk % KH));
+    __syncthreads();  // every wave holds its fragments before the latents overwrite them
+  }
+
+  for (int c0 = j0; c0 < j1; c0 += C2) {
+    if (__ballot(!tv) == 0ull) {  // uniform: every slot of this wave holds a token
+#pragma unroll
+      for (int q = 0; q < PN; ++q)
+        if (q8 + 8 * q < PIECES) *reinterpret_cast<v4i*>(lat_s + tt_g * LROW4 + 16 * (q8 + 8 * q)) = v[q];
+    } else {  // an empty slot's codes (read at a clamped address) are zeroed
+#pragma unroll
+      for (int q = 0; q < PN; ++q)
+        if (q8 + 8 * q < PIECES)
+          *reinterpret_cast<v4i*>(lat_s + tt_g * LROW4 + 16 * (q8 + 8 * q)) = tv ? v[q] : v4i{0, 0, 0, 0};
+    }
+    if (q8 == 0) sc_s[tt_g] = tv ? sv : kNegInf;  // -inf marks an empty slot
+    if (tid == 0) *fl_s = 0u;
+    __syncthreads();
+    if (c0 + C2 < j1) {  // uniform
+      issue();
+      fetch_ids(c0 + 2 * C2);
+    }
+    float smax;
+    {
+      float x = lane < C2 ? sc_s[lane] : kNegInf;
+      x = fmaxf(x, xshflf<1>(x));
+      x = fmaxf(x, xshflf<2>(x));
+      x = fmaxf(x, xshflf<4>(x));
+      x = fmaxf(x, xshflf<8>(x));
+      x = fmaxf(x, xshflf<16>(x));
+      x = fmaxf(x, xshflf<32>(x));
+      s_max = fmaxf(s_max, x);
+      smax = s_max > 0.f ? s_max : 1.f;
+    }
+    // ---- S = Q . C^T (both head blocks from each converted latent fragment) ----
+    {
+      v4f s0[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+      const uint8_t* lrow = lat_s + (16 * tg + hrow) * LROW4 + kq + (kDLat / 2) * wq;
+#pragma unroll
+      for (int kk = 0; kk < KH; ++kk) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(lrow + 32 * kk);
+        const v8bf b = e4m3x8_to_bf16(raw.x, raw.y);
+#pragma unroll
+        for (int hb2 = 0; hb2 < 2; ++hb2)
+          s0[hb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[KH * hb2 + kk], b, s0[hb2], 0, 0, 0);
+      }
+      const int tt = 16 * tg + hrow;
+      const float sct = sc_s[tt];
+      const bool ok = sct != kNegInf;
+      float* xh = x_s + wq * G * XROW2;
+#pragma unroll
+      for (int hb2 = 0; hb2 < 2; ++hb2) {
+        const int hb = 16 * hb2 + 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xh[(hb + i) * XROW2 + tt] = ok ? s0[hb2][i] * (sct * c2) : kNegInf;
+      }
+    }
+    __syncthreads();
+    // ---- softmax: wave w owns heads 8w .. 8w + 7, lane l head 8w + (l >> 3), tokens 4 (l & 7) .. +4 ----
+    {
+      const int h = 8 * wid + (lane >> 3), t4 = 4 * (lane & 7);
+      const float4 xa = *reinterpret_cast<const float4*>(x_s + h * XROW2 + t4);
+      const float4 xb = *reinterpret_cast<const float4*>(x_s + (G + h) * XROW2 + t4);
+      const float4 s4 = *reinterpret_cast<const float4*>(sc_s + t4);
+      const float xv[4] = {xa.x + xb.x, xa.y + xb.y, xa.z + xb.z, xa.w + xb.w};  // -inf for an empty slot
+      const float svv[4] = {s4.x, s4.y, s4.z, s4.w};
+      float cm = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
+      cm = fmaxf(cm, xshflf<1>(cm));
+      cm = fmaxf(cm, xshflf<2>(cm));
+      cm = fmaxf(cm, xshflf<4>(cm));
+      const float mn = fmaxf(m_run, cm);
+      const float mb = mn == kNegInf ? 0.f : mn;
+      const float alpha = mn == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - mb);
+      const float inv_smax = __builtin_amdgcn_rcpf(smax);
+      float psum = 0.f;
+      v4h ph;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(xv[e] - mb);  // 0 for an empty slot
+        psum += p;
+        ph[e] = (_Float16)(p * (fmaxf(svv[e], 0.f) * inv_smax));
+      }
+      psum += xshflf<1>(psum);
+      psum += xshflf<2>(psum);
+      psum += xshflf<4>(psum);
+      l_run = l_run * alpha + psum;
+      m_run = mn;
+      *reinterpret_cast<v4h*>(p_s + h * PROW2 + t4) = ph;
+      if ((lane & 7) == 0) {
+        al_s[h] = alpha;
+        ml_s[h] = float2{m_run, l_run};
+        if (alpha != 1.f) *fl_s = 1u;
+      }
+    }
+    __syncthreads();
+    // P'' fragments (32x32x16 A operand): row = head lane & 31, k = tokens 16 ks + 8 (lane >> 5) .. +8
+    v8h pa[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pa[ks] = *reinterpret_cast<const v8h*>(p_s + (lane & 31) * PROW2 + 16 * ks + 8 * (lane >> 5));
+    // acc *= alpha * (s_run / smax) only in chunks where some head's max or the largest scale moved
+    const float rescale = smax == s_run ? 1.f : s_run * __builtin_amdgcn_rcpf(smax);
+    s_run = smax;
+    const bool moved = __builtin_amdgcn_readfirstlane((int)*fl_s) != 0 ||
+                       __builtin_amdgcn_readfirstlane(__float_as_int(rescale)) != __float_as_int(1.f);
+    if (moved) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&al_s[8 * jj + 4 * (lane >> 5)]);
+        const float a[4] = {a4.x * rescale, a4.y * rescale, a4.z * rescale, a4.w * rescale};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) accw[c][4 * jj + i] *= a[i];
+      }
+    }
+    // ---- O += P'' . codes: wave w -> value columns [128 w, +128); B operands by the
+    // transposing LDS read (as in the 512-thread body) ----
+    {
+      const int tr_off = (8 * (lane >> 5) + ((lane & 15) >> 1)) * LROW4 + 16 * ((lane >> 4) & 1) + 8 * (lane & 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint8_t* vp = lat_s + 16 * ks * LROW4 + 128 * wid + 32 * c + tr_off;
+          const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(vp));
+          const v8h b = e4m3x8_to_f16((uint32_t)t.x, (uint32_t)t.y);
+          accw[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pa[ks], b, accw[c], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // lat_s, x_s, sc_s, p_s, al_s and fl_s are rewritten by the next chunk
+  }
+
+  // ---- epilogue (the last barrier, or the staging barriers of an empty split, has ordered
+  // every head's final (max, sum) in ml_s) ----
+  if (nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const float lv = ml_s[h].y;
+      const float f = lv > 0.f ? s_run / lv : 0.f;
+      float* orow = out + ((int64_t)r * kHQ + hg * G + h) * kDV + 128 * wid + (lane & 31);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) orow[32 * c] = accw[c][i] * f;
+    }
+    if (lse != nullptr && tid < G) {
+      const float2 ml = ml_s[tid];
+      lse[(int64_t)r * kHQ + hg * G + tid] = ml.y > 0.f ? (ml.x + log2f(ml.y)) * 0.69314718055994531f : kNegInf;
+    }
+  } else {
+    const int64_t pbase = ((int64_t)r * nsplit + split) * kHQ + hg * G;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const float lv = ml_s[h].y;
+      const float f = lv > 0.f ? s_run / lv : 0.f;
+      _Float16* orow = part_o + (pbase + h) * kDV + 128 * wid + (lane & 31);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) __builtin_nontemporal_store((_Float16)(accw[c][i] * f), orow + 32 * c);
+    }
+    if (tid < G) {
+      const float2 ml = ml_s[tid];
+      part_ml[(pbase + tid) * 2 + 0] = ml.x;
+      part_ml[(pbase + tid) * 2 + 1] = ml.y;
+    }
+  }
+}
+
+// The 32-head, four-wave attention kernel (grid: split, row, head group of 32). Two
+// workgroups per CU: at most 256 registers per lane.
+__global__ __launch_bounds__(NT4, 2) void sparse_mla32_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ phys,
+                                                            const uint16_t* __restrict__ q_lat, int k, int ts,
+                                                            float c2, CacheView cv, RowMap rm, float* __restrict__ out,
+                                                            float* __restrict__ lse, _Float16* __restrict__ part_o,
+                                                            float* __restrict__ part_ml, int nsplit) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MlaLds4::BYTES];
+  const int split = blockIdx.x, r = blockIdx.y, hg = blockIdx.z;
+  const int j0 = split * ts;
+  const int j1 = (j0 + ts < k) ? j0 + ts : k;
+  const MlaIds src{idx + (int64_t)r * k, phys != nullptr ? phys + (int64_t)r * k : nullptr, nullptr, j0};
+  int t_n = -1, ps_n = 0;
+  {
+    const int j = j0 + ((int)threadIdx.x >> 3);
+    if (j < j1) src.get(j, t_n, ps_n);
+  }
+  v4i qv[QN4];
+  {
+    const int tid = threadIdx.x;
+    const v4i* qg = reinterpret_cast<const v4i*>(q_lat + ((int64_t)r * kHQ + hg * 32) * kDLat);
+#pragma unroll
+    for (int q = 0; q < QN4; ++q)
+      if (tid + NT4 * q < 32 * (kDLat / 8)) qv[q] = qg[tid + NT4 * q];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mla_body_w4(src, t_n, ps_n, qv, j0, j1, c2, cv, rm, r, hg, split, out, lse, part_o, part_ml, nsplit, smem);
+}
+
 bool select_mla_fused(const CacheView& cv, int R, int k) {
   if (cv.latent_fmt != DSA_LATENT_FP8 || R <= 0 || mla_group(R) != 16) return false;
   // one workgroup per CU (the select's LDS): the whole grid in one round
@@ -905,11 +1214,15 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
       go(std::true_type{}, std::integral_constant<int, 16>{});
     else
       go(std::false_type{}, std::integral_constant<int, 16>{});
+  } else if (nvf) {
+    go(std::true_type{}, std::integral_constant<int, 32>{});
+  } else if (nsplit == 1 && (int64_t)R * (kHQ / 32) > kMlaSlots) {
+    // unsplit rows filling more than one workgroup per CU (e.g. a prefill-append's rows):
+    // the four-wave kernel, two workgroups per CU
+    hipLaunchKernelGGL(sparse_mla32_kernel, dim3(nsplit, R, kHQ / 32), dim3(NT4), 0, stream, idx, phys, q_lat, k, ts,
+                       c2, cv, rm, out, lse, part_o, part_ml, nsplit);
   } else {
-    if (nvf)
-      go(std::true_type{}, std::integral_constant<int, 32>{});
-    else
-      go(std::false_type{}, std::integral_constant<int, 32>{});
+    go(std::false_type{}, std::integral_constant<int, 32>{});
   }
   if (nsplit > 1 && (parts & 2)) {
     const dim3 mg(kHQ * kMergeParts, R);
