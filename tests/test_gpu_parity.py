@@ -720,6 +720,38 @@ def test_nvfp4_append_then_decode(dev):
     full_check(c, dev)
 
 
+def test_topk_long_rows_send_paths(dev):
+    """dsa_topk on score rows long enough for 512-token send units (the threshold route of
+    eight-wave units), bit for bit against the exact selection: heavy ties (most units fall
+    back to the sort-and-merge route), a descending ramp (the whole top-k in four units),
+    last units with 10 and 40 valid tokens (a wave with no key, so the threshold is 0),
+    m = 8 above 776,192 tokens, all-negative scores, one unit holding 512 of the top k
+    (rescanned), and a 1,048,576-token row."""
+    say("case: dsa_topk on long synthetic rows")
+    rng = np.random.default_rng(77)
+    n = 262144
+    hot = rng.normal(0, 1, n)
+    hot[7 * 512:8 * 512] = 10.0 + rng.normal(0, 0.1, 512)
+    rows = [np.round(rng.normal(0, 1, n), 1), -np.arange(n, dtype=np.float64), rng.normal(0, 1, n + 10),
+            rng.normal(0, 1, 600 * 512 + 40), rng.normal(0, 1, 800000), rng.normal(-5.0, 1.0, n), hot,
+            rng.normal(0, 1, 1 << 20)]
+    rows = [x.astype(np.float32) for x in rows]
+    ctx = [len(x) for x in rows]
+    max_ctx = max(ctx)
+    S = np.zeros((len(rows), max_ctx), dtype=np.float32)
+    for r, x in enumerate(rows):
+        S[r, :len(x)] = x
+    idx = dsa.dsa_topk(torch.from_numpy(S).to(dev), torch.tensor(ctx, dtype=torch.int32, device=dev), max_ctx,
+                       2048)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for r, x in enumerate(rows):
+        say(f"  row {r} ctx {len(x)}")
+        assert np.array_equal(idx[r], O.select_topk(x, 2048)), f"row {r}: selection differs"
+    assert np.array_equal(idx[1], np.arange(2048)), "ramp: the first k tokens"
+    assert np.all(np.isin(np.arange(7 * 512, 8 * 512), idx[6])), "the hot unit's keys are all selected"
+
+
 # ----------------------------------------------------------------------------- context-parallel merge
 
 def _dcp_check(dev, rows, k, W):
