@@ -281,6 +281,51 @@ def hbm_read_ceiling(dsa, buf, reps=3, grids=(256, 512, 1024, 2048, 4096)):
                       "256-thread workgroup, over the whole layer-rotated cache pool)"}
 
 
+def size_matched_read(dsa, buf, nbytes, reps=5, per_graph=24, grids=(512, 1024, 2048, 4096)):
+    """One dsa_hbm_read_probe launch over exactly `nbytes` (a kernel's algorithmic bytes),
+    launched back to back from a HIP graph as the step launches its kernels: launch i
+    reads slice i % per_graph of `buf` (disjoint slices spread over the whole buffer, so
+    none is cache-resident when read). Per grid the average launch over `reps` replays;
+    the best grid's time is the shortest a launch reading that many bytes once took."""
+    import torch
+    dev = buf.device
+    total = buf.numel() * buf.element_size()
+    flat = buf.view(-1).view(torch.uint8)
+    n = (nbytes + 15) // 16 * 16
+    stride = (total // per_graph) // 16384 * 16384
+    if stride < n:
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cap = torch.cuda.Stream(dev)
+    res = {}
+    for grid in grids:
+        slices = [flat[i * stride:i * stride + n] for i in range(per_graph)]
+        cap.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(cap):
+            for sl in slices:
+                dsa.dsa_hbm_read_probe(sl, sink, grid)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for sl in slices:
+                dsa.dsa_hbm_read_probe(sl, sink, grid)
+        g.replay()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        res[grid] = 1000.0 * e0.elapsed_time(e1) / (reps * per_graph)
+        del g
+    best = min(res, key=res.get)
+    return {"us": round(res[best], 3), "grid": best, "bytes": n,
+            "us_by_grid": {str(k): round(v, 3) for k, v in res.items()}}
+
+
 def bench_dcp(a, dsa, case, dev):
     """Times dsa_topk_dcp (W emulated shards) and dsa_topk on the same indexer scores,
     one call per layer from a HIP graph; prints one JSON line."""
@@ -537,6 +582,13 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ix_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(ix_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic, "algorithmic_bytes_per_launch": ix_bytes,
                 "frac_of_measured_read_ceiling": round(ix_gbps / ceiling["gbps"], 4) if ceiling else None}
+        if ceiling:
+            # the same bytes read by the streaming probe in one graph-launched kernel: the
+            # launch's ramp and drain at this size, which no kernel of this size avoids
+            same = size_matched_read(dsa, case.pool, ix_bytes)
+            if same:
+                roof["size_matched_read"] = dict(same, kernel="hbm_read_kernel")
+                roof["frac_of_size_matched_read"] = round(same["us"] / ix_us, 4)
     step_gbps = step_bytes / (ms * 1e-3) / 1e9 if step_bytes else None
     # the other kernels of the step against their own algorithmic bytes (select: the 4 B
     # per token of scores it decides over; attention: the gathered latents, query, indices
