@@ -579,6 +579,25 @@ def test_select_paths_mixed_batch(dev):
     full_check(c, dev)
 
 
+def test_four_wave_attention_short_and_empty_rows(dev):
+    """160 rows take one attention split each (the cost model's choice once three head
+    groups per row overfill the CUs), so the step runs the four-wave 32-head kernel on
+    32-token chunks. Rows shorter than k leave -1 entries and partly empty chunks: an
+    empty row, one token, chunk edges (31, 32, 33, 63, 64, 65), k - 1, k, k + 1, and
+    longer rows up to 20,000 tokens (own-score and candidate selects). Every row with a
+    listed length and every 8th of the rest is checked against the oracle."""
+    say("case: four-wave attention, 160 rows, short and empty rows")
+    edge = [0, 1, 2, 31, 32, 33, 63, 64, 65, 100, 2047, 2048, 2049, 4097, 16384, 16385, 20000]
+    rng = np.random.default_rng(71)
+    ctxs = edge + [int(x) for x in rng.integers(1, 6000, size=160 - len(edge))]
+    c = make_case(ctxs, block_size=64, seed=71, k=2048)
+    R = c.num_rows
+    # one split per row: the attention needs no partials workspace
+    assert R * 3 > 256 and dsa.dsa_workspace_bytes(dsa.DSA_OP_SPARSE_MLA, R, 0, 2048) <= 256
+    rows = list(range(len(edge))) + list(range(len(edge), R, 8))
+    full_check(c, dev, rows=rows)
+
+
 def test_workspace_reuse_across_inputs(dev):
     """The workspace carries nothing from one call to the next."""
     say("case: workspace reuse")
