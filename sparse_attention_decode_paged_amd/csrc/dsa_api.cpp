@@ -307,7 +307,7 @@ dsa_status dsa_sparse_mla(const dsa_cache_desc* cache, int32_t layer, const uint
   if (k < 1 || k > DSA_MAX_K) return fail(DSA_ERR_ARG, "k %d out of [1, %d]", k, DSA_MAX_K);
   if (!aligned16(q_lat)) return fail(DSA_ERR_ALIGN, "q_lat is not 16-byte aligned");
   const size_t need = mla_ws_bytes(R, k);
-  if (mla_splits(R, k) > 1 && (workspace == nullptr || ws_bytes < need))
+  if (mla_plan(R, k, cv.latent_fmt == DSA_LATENT_FP8).nsplit > 1 && (workspace == nullptr || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (R == 0) return ok();
   return hip_status(launch_sparse_mla(cv, rm, q_lat, idx, nullptr, R, k, sm_scale, out, lse, workspace, 3,

@@ -50,36 +50,60 @@ constexpr int kMlaChunk = 64;   // tokens per inner iteration
 // many heads).
 inline int mla_group(int R) { return R <= 4 ? 16 : 32; }
 
-// Splits of a row's k tokens for sparse MLA. A workgroup (one per CU: its registers
-// allow no second) takes whole 64-token chunks; R rows x 3 head groups x s splits
-// run in rounds of kMlaSlots workgroups. The choice minimises the estimated time
-// rounds x (chunks per split + a prologue worth 1.5 chunks), plus one chunk's worth
-// for the merge kernel when s > 1; ties go to fewer splits.
+// Splits of a row's k tokens for sparse MLA, and which kernel runs them. An eight-wave
+// workgroup (one per CU: its registers allow no second) takes whole 64-token chunks;
+// R rows x 3 head groups (6 of 16 heads for up to 4 rows) x s splits run in rounds of
+// kMlaSlots workgroups, at an estimated rounds x (chunks per split + a prologue worth
+// 1.5 chunks), plus one chunk's worth for the merge kernel when s > 1; ties go to fewer
+// splits. When that choice needs more than one round and the latents are FP8, the
+// four-wave 32-head kernel runs instead, with its own split count: a CU holds
+// ceil(workgroups / kMlaSlots) of its workgroups and runs them two at a time, a pair
+// taking about 2.95 + 1.87 x (chunks per split) of those chunk times and an odd last
+// one alone 1.27 + 1.37 x (chunks per split), plus the merge's chunk when s > 1 (fitted
+// to measured batches of 16 to 64 rows; with one round or less the eight-wave kernel
+// was as fast or faster).
 constexpr int kMlaSlots = 256;  // CUs of the device
-inline int mla_splits(int R, int k) {
-  if (R <= 0) return 1;
+struct MlaPlan {
+  int nsplit;
+  bool four_wave;
+};
+inline MlaPlan mla_plan(int R, int k, bool fp8_latents) {
+  MlaPlan p8{1, false}, p4{0, true};
+  if (R <= 0) return p8;
   const int nch = (k + kMlaChunk - 1) / kMlaChunk;
-  int best = 1;
-  double best_cost = 0.0;
+  double c8_best = 0.0, c4_best = 0.0;
+  int64_t wgs8 = 0;
   for (int s = 1; s <= nch; ++s) {
     const int cps = (nch + s - 1) / s;  // chunks per split
     if ((nch + cps - 1) / cps != s) continue;  // s is not reached by whole chunks
     const int64_t wgs = (int64_t)R * (kHQ / mla_group(R)) * s;
-    const double rounds = (double)((wgs + kMlaSlots - 1) / kMlaSlots);
-    const double cost = rounds * (cps + 1.5) + (s > 1 ? 1.0 : 0.0);
-    if (s == 1 || cost < best_cost) {
-      best = s;
-      best_cost = cost;
+    const int64_t per_cu = (wgs + kMlaSlots - 1) / kMlaSlots;
+    const double merge = s > 1 ? 1.0 : 0.0;
+    const double c8 = (double)per_cu * (cps + 1.5) + merge;
+    if (s == 1 || c8 < c8_best) {
+      p8 = MlaPlan{s, false};
+      c8_best = c8;
+      wgs8 = wgs;
+    }
+    if (per_cu > 1) {
+      const double c4 = (double)(per_cu / 2) * (2.95 + 1.87 * cps) + (double)(per_cu % 2) * (1.27 + 1.37 * cps) + merge;
+      if (p4.nsplit == 0 || c4 < c4_best) {
+        p4.nsplit = s;
+        c4_best = c4;
+      }
     }
   }
-  return best;
+  const bool w4 = fp8_latents && mla_group(R) == 32 && wgs8 > kMlaSlots && p4.nsplit > 0;
+  return w4 ? p4 : p8;
 }
 inline int mla_split_tokens(int k, int nsplit) {
   int ts = (k + nsplit - 1) / nsplit;
   return (ts + kMlaChunk - 1) / kMlaChunk * kMlaChunk;
 }
+// The workspace does not depend on the latent format: it covers both plans.
 inline size_t mla_ws_bytes(int R, int k) {
-  int s = mla_splits(R, k);
+  const int s8 = mla_plan(R, k, false).nsplit, s4 = mla_plan(R, k, true).nsplit;
+  const int s = s8 > s4 ? s8 : s4;
   if (s <= 1) return 256;
   return align_up((size_t)R * s * kHQ * kDV * 2, 256) + align_up((size_t)R * s * kHQ * 2 * 4, 256);
 }

@@ -846,7 +846,7 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const _Float16* __restric
     lse[(int64_t)r * kHQ + h] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : kNegInf;
 }
 
-// ---- 32 heads on four waves: many unsplit rows (prefill-append), FP8 latents ----
+// ---- 32 heads on four waves: grids of more workgroups than CUs, FP8 latents ----
 // The body above keeps one 512-thread workgroup per CU (its 32-head registers), and its
 // four barrier-separated phases per chunk (latents in, QK, softmax, PV) leave both waves
 // of a SIMD in the same phase, so the matrix cores and the vector ALUs rarely work at
@@ -857,10 +857,12 @@ __global__ __launch_bounds__(NT) void mla_merge_kernel(const _Float16* __restric
 // for both blocks of 16 heads; the softmax gives wave w heads 8w .. 8w + 7 (lane: head
 // 8w + (lane >> 3), 4 tokens); PV gives wave w value columns [128 w, +128). The numerics
 // are those of the 512-thread body (bf16 QK, fp16 P'' relative to the running largest
-// token scale, fp16 PV on e4m3 codes, fp16 split averages). It pays where each workgroup
-// walks many chunks and the grid holds more than one workgroup per CU (2,048 rows of a
-// prefill-append: attention 1.82 -> 1.55 ms); at batch 16 or 64 the extra splits it
-// would need to fill the CUs cost more than it saves, and the 512-thread body runs.
+// token scale, fp16 PV on e4m3 codes, fp16 split averages). It pays where the grid holds
+// more than one workgroup per CU (2,048 rows of a prefill-append: attention 1.82 -> 1.55
+// ms; 32 to 128 decode rows with its own split count: 5 to 12 % less); where the
+// 512-thread body's grid fits one round (up to about 28 rows) that body is faster, since a
+// four-wave workgroup alone on a CU has one wave per SIMD. The split-count plan
+// chooses between the two.
 namespace {
 constexpr int NT4 = 256;
 constexpr int C2 = 32;             // tokens per chunk
@@ -1158,7 +1160,7 @@ __global__ __launch_bounds__(NT4, 2) void sparse_mla32_kernel(const int32_t* __r
 bool select_mla_fused(const CacheView& cv, int R, int k) {
   if (cv.latent_fmt != DSA_LATENT_FP8 || R <= 0 || mla_group(R) != 16) return false;
   // one workgroup per CU (the select's LDS): the whole grid in one round
-  return (int64_t)mla_splits(R, k) * R * (kHQ / 16) <= kSelMlaMaxGroups;
+  return (int64_t)mla_plan(R, k, true).nsplit * R * (kHQ / 16) <= kSelMlaMaxGroups;
 }
 
 hipError_t launch_select_mla(const float* scores, int64_t ld, const int32_t* row_ctx, int R, int max_ctx, int k,
@@ -1166,7 +1168,7 @@ hipError_t launch_select_mla(const float* scores, int64_t ld, const int32_t* row
                              const uint16_t* q_lat, float sm_scale, float* out, float* lse, void* ws,
                              hipStream_t stream) {
   if (R <= 0) return hipSuccess;
-  const int nsplit = mla_splits(R, k);
+  const int nsplit = mla_plan(R, k, true).nsplit;  // up to 4 rows: the 16-head eight-wave kernel
   const int ts = mla_split_tokens(k, nsplit);
   const float c2 = (float)((double)sm_scale * 1.4426950408889634);
   _Float16* part_o = nullptr;
@@ -1192,7 +1194,9 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
                              const int32_t* phys, int R, int k, float sm_scale, float* out, float* lse, void* ws,
                              int parts, hipStream_t stream) {
   if (R <= 0) return hipSuccess;
-  const int nsplit = mla_splits(R, k);
+  const bool nvf = cv.latent_fmt == DSA_LATENT_NVFP4;
+  const MlaPlan plan = mla_plan(R, k, !nvf);
+  const int nsplit = plan.nsplit;
   const int ts = mla_split_tokens(k, nsplit);
   const float c2 = (float)((double)sm_scale * 1.4426950408889634);
   _Float16* part_o = nullptr;
@@ -1207,7 +1211,6 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
     hipLaunchKernelGGL((sparse_mla_kernel<N, G>), dim3(nsplit, R, kHQ / G), dim3(NTM), 0, stream, idx, phys, q_lat, k,
                        ts, c2, cv, rm, out, lse, part_o, part_ml, nsplit);
   };
-  const bool nvf = cv.latent_fmt == DSA_LATENT_NVFP4;
   if (!(parts & 1)) {
   } else if (mla_group(R) == 16) {
     if (nvf)
@@ -1216,9 +1219,9 @@ hipError_t launch_sparse_mla(const CacheView& cv, const RowMap& rm, const uint16
       go(std::false_type{}, std::integral_constant<int, 16>{});
   } else if (nvf) {
     go(std::true_type{}, std::integral_constant<int, 32>{});
-  } else if (nsplit == 1 && (int64_t)R * (kHQ / 32) > kMlaSlots) {
-    // unsplit rows filling more than one workgroup per CU (e.g. a prefill-append's rows):
-    // the four-wave kernel, two workgroups per CU
+  } else if (plan.four_wave) {
+    // more workgroups than CUs (e.g. a prefill-append's unsplit rows, or batches of 32
+    // rows and up): the four-wave kernel, two workgroups per CU
     hipLaunchKernelGGL(sparse_mla32_kernel, dim3(nsplit, R, kHQ / 32), dim3(NT4), 0, stream, idx, phys, q_lat, k, ts,
                        c2, cv, rm, out, lse, part_o, part_ml, nsplit);
   } else {

@@ -598,6 +598,20 @@ def test_four_wave_attention_short_and_empty_rows(dev):
     full_check(c, dev, rows=rows)
 
 
+def test_four_wave_attention_uneven_splits(dev):
+    """32 rows: the eight-wave plan (8 splits) would take three rounds of workgroups, so
+    FP8 latents run the four-wave kernel over 5 splits of a row's list (448 tokens each,
+    the last 256) and the merge. Short rows leave whole splits empty. Every row is checked
+    against the oracle; the NVFP4-latent path keeps the eight-wave kernel and is covered
+    by the NVFP4 tests."""
+    say("case: four-wave attention, 32 rows, 5 splits")
+    edge = [0, 1, 40, 447, 448, 449, 1000, 1791, 1792, 1793, 2047, 2048, 2049, 30000]
+    rng = np.random.default_rng(72)
+    ctxs = edge + [int(x) for x in rng.integers(2048, 24000, size=32 - len(edge))]
+    c = make_case(ctxs, block_size=64, seed=72, k=2048)
+    full_check(c, dev)
+
+
 def test_workspace_reuse_across_inputs(dev):
     """The workspace carries nothing from one call to the next."""
     say("case: workspace reuse")
