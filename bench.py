@@ -605,7 +605,8 @@ def main():
     kernels = {
         "select_attention": {
             "kernels": "select_mla_kernel<CAND> (one launch)" if fused_sel
-            else "topk_select_kernel<CAND>, sparse_mla_kernel<NV, G>",
+            else "topk_select_kernel<CAND>, then sparse_mla_kernel<NV, G> or sparse_mla32_kernel (the "
+                 "split plan's choice)",
             "avg_us": round(sa_us, 3), "algorithmic_bytes": sa_bytes,
             "achieved_gbps": round(sa_bytes / (sa_us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(sa_bytes / (sa_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)},
