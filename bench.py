@@ -285,17 +285,17 @@ def size_matched_read(dsa, buf, nbytes, reps=5, per_graph=24, grids=(512, 1024, 
     """One dsa_hbm_read_probe launch over exactly `nbytes` (a kernel's algorithmic bytes),
     launched back to back from a HIP graph as the step launches its kernels: launch i
     reads slice i of `buf` (up to `per_graph` disjoint slices spread over the whole buffer,
-    together at least 1 GiB, so none is cache-resident when read). Per grid the average launch over `reps` replays;
+    together at least 512 MB, so none is cache-resident when read). Per grid the average launch over `reps` replays;
     the best grid's time is the shortest a launch reading that many bytes once took."""
     import torch
     dev = buf.device
     total = buf.numel() * buf.element_size()
     flat = buf.view(-1).view(torch.uint8)
     n = (nbytes + 15) // 16 * 16
-    # fewer slices when the bytes are large, as long as together they far exceed the
-    # 256 MB last-level cache
+    # fewer slices when the bytes are large, as long as together they hold at least twice
+    # the 256 MB last-level cache
     per_graph = min(per_graph, total // max(n, 1))
-    if per_graph < 2 or per_graph * n < (1 << 30):
+    if per_graph < 2 or per_graph * n < (512 << 20):
         return None
     stride = (total // per_graph) // 16384 * 16384
     if stride < n:
