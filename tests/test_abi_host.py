@@ -56,6 +56,18 @@ def test_workspace_sizes(lib):
     assert dsa.dsa_decode_scores_ld(8193) % 64 == 0 and dsa.dsa_decode_scores_ld(8193) >= 8193
 
 
+@pytest.mark.parametrize("R, splits", [(1, 32), (4, 8), (16, 5), (32, 8), (64, 4), (96, 4), (160, 1), (2048, 1)])
+def test_mla_workspace_holds_the_larger_plans_partials(lib, R, splits):
+    """The sparse-MLA workspace holds fp16 split averages (96 heads x 512) and fp32 (m, l)
+    for the split count of the plan that splits more, FP8 latents (which may take the
+    four-wave kernel: 5 splits at 32 rows, 3 at 96) or NVFP4 latents (the eight-wave
+    kernel: 8 at 32 rows, 4 at 96); unsplit rows need no partials."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    want = 256 if splits == 1 else a256(R * splits * 96 * 512 * 2) + a256(R * splits * 96 * 2 * 4)
+    assert dsa.dsa_workspace_bytes(dsa.DSA_OP_SPARSE_MLA, R, 0, 2048) == want
+
+
 def _desc(**over):
     d = dsa.CacheDesc()
     d.pool = 0x10000
